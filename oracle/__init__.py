@@ -1,0 +1,228 @@
+"""Plain CPU oracle for the batched speculative-verify + SAM-draft step.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product path
+(``sam_drafting_lossless_amd``) never imports it, and this package imports
+nothing from the product.
+
+The arithmetic lives in ``oracle.cpp`` (C++17, std::map suffix automaton,
+double-precision softmax and scalar rejection sampling); this module only
+marshals numpy arrays through ctypes. ``build()`` compiles it with g++.
+
+Pages followed (cited by title and section in ``oracle.cpp``):
+  [P1] "SAM投机推理：长序列强化学习训练加速利器", §1.1, §3.1.2
+  [P2] m.nxbn.cn speculative-sampling guide, §2.2
+  [P3] gogongxt.com notes "投机采样", "贪婪验证，拒绝采样"
+  [P4] SAM-Decoding summary (volcengine), §2, §3
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Status bits, as the oracle defines them.
+ST_TOKEN_RANGE = 1 << 1
+ST_DRAFT_LEN = 1 << 2
+ST_NONFINITE = 1 << 3
+ST_TEMPERATURE = 1 << 4
+ST_NO_UNIFORMS = 1 << 5
+
+
+def build() -> str:
+    """Compile oracle.cpp into liboracle.so (always recompiles)."""
+    cmd = ["g++", "-O2", "-std=c++17", "-Wall", "-fPIC", "-shared", "-pthread",
+           _SRC, "-o", _LIB + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.orc_sam_new.restype = P
+    lib.orc_sam_new.argtypes = []
+    lib.orc_sam_free.argtypes = [P]
+    lib.orc_sam_extend.argtypes = [P, P, i64]
+    lib.orc_sam_draft.argtypes = [P, i32, P, P]
+    lib.orc_sam_draft.restype = i32
+    for name in ("orc_sam_num_states", "orc_sam_num_edges", "orc_sam_length"):
+        getattr(lib, name).argtypes = [P]
+        getattr(lib, name).restype = i64
+    for name in ("orc_sam_last_walk_hops", "orc_sam_last"):
+        getattr(lib, name).argtypes = [P]
+        getattr(lib, name).restype = i32
+    lib.orc_sam_export.argtypes = [P, P, P, P, P]
+    lib.orc_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P,
+                               P, P, P, P, P, P, P, i32]
+    lib.orc_step.argtypes = [P, i32, i32, i32, P, i32, P, P, P, P, P,
+                             P, P, P, P, P, P, P, i32]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class SAM:
+    """One dynamic suffix automaton over a token history (std::map based)."""
+
+    def __init__(self, tokens=None):
+        self._lib = _load()
+        self._h = self._lib.orc_sam_new()
+        if tokens is not None and len(tokens):
+            self.extend(tokens)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.orc_sam_free(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def extend(self, tokens) -> None:
+        t = _c(np.atleast_1d(tokens), np.int32)
+        self._lib.orc_sam_extend(self._h, _ptr(t), t.size)
+
+    def draft(self, K: int):
+        """Returns (draft[K] int32 padded with -1, draft_len, match_len)."""
+        out = np.full(K, -1, np.int32)
+        ml = np.zeros(1, np.int32)
+        d = self._lib.orc_sam_draft(self._h, K, _ptr(out), _ptr(ml))
+        return out, int(d), int(ml[0])
+
+    @property
+    def last_walk_hops(self) -> int:
+        return int(self._lib.orc_sam_last_walk_hops(self._h))
+
+    @property
+    def num_states(self) -> int:
+        return int(self._lib.orc_sam_num_states(self._h))
+
+    @property
+    def num_edges(self) -> int:
+        return int(self._lib.orc_sam_num_edges(self._h))
+
+    @property
+    def length(self) -> int:
+        return int(self._lib.orc_sam_length(self._h))
+
+    @property
+    def last(self) -> int:
+        return int(self._lib.orc_sam_last(self._h))
+
+    def export(self):
+        """dict(len, link, min_endpos: int32[S]; edges: int32[E,3] sorted by
+        (src, token); last)."""
+        S, E = self.num_states, self.num_edges
+        ln = np.empty(S, np.int32)
+        lk = np.empty(S, np.int32)
+        me = np.empty(S, np.int32)
+        ed = np.empty((E, 3), np.int32)
+        self._lib.orc_sam_export(self._h, _ptr(ln), _ptr(lk), _ptr(me), _ptr(ed))
+        return {"len": ln, "link": lk, "min_endpos": me, "edges": ed,
+                "last": self.last}
+
+
+@dataclass
+class VerifyResult:
+    out_tokens: np.ndarray   # [B,K+1] int32, -1 padded
+    num_emitted: np.ndarray  # [B] int32
+    p_draft: np.ndarray      # [B,K] float64, -1 where not computed
+    alpha: np.ndarray        # [B,K] float64 min(1,p/q), NaN where unused
+    cdf_lo: np.ndarray       # [B] float64 breakpoints around the final draw
+    cdf_hi: np.ndarray       # [B]
+    status: np.ndarray       # [B] int32
+
+
+def verify(logits, draft, draft_len, temperature, uniforms=None, q=None,
+           nthreads: int = 1) -> VerifyResult:
+    """Verify one batch.
+
+    logits: [B,K+1,V] float32, or uint16 holding bfloat16 bit patterns.
+    draft: [B,K] int32; draft_len: [B] int32; temperature: [B] float32;
+    uniforms: [B,K+1] float32 or None; q: [B,K,V] float32 or None (one-hot).
+    """
+    lib = _load()
+    if logits.dtype == np.float32:
+        dtype = 0
+    elif logits.dtype == np.uint16:
+        dtype = 1
+    else:
+        raise TypeError("logits must be float32 or uint16 (bfloat16 bits)")
+    logits = np.ascontiguousarray(logits)
+    B, R, V = logits.shape
+    K = R - 1
+    draft = _c(draft, np.int32).reshape(B, K)
+    draft_len = _c(draft_len, np.int32).reshape(B)
+    temperature = _c(temperature, np.float32).reshape(B)
+    if uniforms is not None:
+        uniforms = _c(uniforms, np.float32).reshape(B, K + 1)
+    if q is not None:
+        q = _c(q, np.float32).reshape(B, K, V)
+    out = np.full((B, K + 1), -1, np.int32)
+    nem = np.zeros(B, np.int32)
+    pd = np.empty((B, K), np.float64)
+    al = np.empty((B, K), np.float64)
+    lo = np.empty(B, np.float64)
+    hi = np.empty(B, np.float64)
+    st = np.zeros(B, np.int32)
+    lib.orc_verify(_ptr(logits), dtype, B, K, V, _ptr(draft), _ptr(draft_len),
+                   _ptr(q), _ptr(temperature), _ptr(uniforms), _ptr(out),
+                   _ptr(nem), _ptr(pd), _ptr(al), _ptr(lo), _ptr(hi), _ptr(st),
+                   int(nthreads))
+    return VerifyResult(out, nem, pd, al, lo, hi, st)
+
+
+def step(sams, logits, temperature, uniforms, nthreads: int = 1):
+    """One whole oracle step over a batch of SAM objects: draft, verify,
+    extend. Returns (draft, draft_len, match_len, VerifyResult)."""
+    lib = _load()
+    logits = np.ascontiguousarray(logits)
+    dtype = 0 if logits.dtype == np.float32 else 1
+    B, R, V = logits.shape
+    K = R - 1
+    handles = (ctypes.c_void_p * B)(*[s.handle for s in sams])
+    temperature = _c(temperature, np.float32).reshape(B)
+    if uniforms is not None:
+        uniforms = _c(uniforms, np.float32).reshape(B, K + 1)
+    dr = np.full((B, K), -1, np.int32)
+    dl = np.zeros(B, np.int32)
+    ml = np.zeros(B, np.int32)
+    out = np.full((B, K + 1), -1, np.int32)
+    nem = np.zeros(B, np.int32)
+    pd = np.empty((B, K), np.float64)
+    al = np.empty((B, K), np.float64)
+    lo = np.empty(B, np.float64)
+    hi = np.empty(B, np.float64)
+    st = np.zeros(B, np.int32)
+    lib.orc_step(ctypes.cast(handles, ctypes.c_void_p), B, K, V, _ptr(logits),
+                 dtype, _ptr(temperature), _ptr(uniforms), _ptr(dr), _ptr(dl),
+                 _ptr(ml), _ptr(out), _ptr(nem), _ptr(pd), _ptr(al), _ptr(lo),
+                 _ptr(hi), _ptr(st), int(nthreads))
+    return dr, dl, ml, VerifyResult(out, nem, pd, al, lo, hi, st)
