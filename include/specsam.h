@@ -1,0 +1,198 @@
+/*
+ * specsam.h — C ABI of the MI355X (gfx950) batched speculative-decoding step:
+ * lossless verification of K drafted tokens against target logits, and
+ * SAM-Decoding's per-sequence dynamic suffix automaton (extend and draft).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [P1] "SAM投机推理：长序列强化学习训练加速利器" (CANN cann-recipes-train
+ *        article): §1.1 "SAM 原理" (endpos, link, min_endpos, dynamic SAM
+ *        updated after every verified token, the link-walk draft, acceptance
+ *        test eps <= alpha(x)); §3.1.2 "拒绝采样加速" (recovered token at the
+ *        rejected position, bonus token when all drafts pass).
+ *   [P2] speculative-sampling guide "1. 投机采样到底在解决什么问题"
+ *        (m.nxbn.cn): §2.2 "验证阶段的并行打分机制" (accept with
+ *        min(1, p/q), resample from the positive part of p - q, K+1 target
+ *        distributions from one forward, truncate at the first rejection).
+ *   [P3] notes "投机采样" (gogongxt.com): "贪婪采样" (T = 0: accept iff the
+ *        draft equals the target argmax), "SGLang 的实现" (coins per draft
+ *        slot plus one final coin; one-hot drafts when no draft
+ *        probabilities exist).
+ *   [P4] SAM-Decoding summary (developer.volcengine.com): §3 "Suffix
+ *        Automaton Construction" (Blumer's online construction, min_endpos),
+ *        "Drafting with Suffix Automaton", "Update of Suffix Automaton".
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers to memory of the current HIP device,
+ *     row-major and contiguous, owned by the caller. The library keeps no
+ *     global state and never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously on it; a state buffer or workspace must not be used on
+ *     two streams at once.
+ *   - Return codes are synchronous: SS_OK, or an SS_E* code for problems the
+ *     host can see (bad sizes, null pointers, launch failure). Problems that
+ *     depend on device data are reported per sequence in a sticky status word
+ *     (bitwise OR of SS_ST_*) without any host synchronisation; a sequence
+ *     flagged in a call is skipped by that call (its outputs are not written).
+ */
+#ifndef SPECSAM_H
+#define SPECSAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes -------------------------------------------------------- */
+#define SS_OK 0
+#define SS_EINVAL (-1)     /* invalid argument (sizes, null pointer, dtype) */
+#define SS_EWORKSPACE (-2) /* workspace too small */
+#define SS_ELAUNCH (-3)    /* HIP launch error; see ss_last_error_string() */
+
+/* ---- per-sequence status bits ------------------------------------------- */
+#define SS_ST_SAM_CAPACITY (1 << 0) /* extend would exceed max_len tokens */
+#define SS_ST_TOKEN_RANGE (1 << 1)  /* a token outside [0, V) */
+#define SS_ST_DRAFT_LEN (1 << 2)    /* draft_len outside [0, K] */
+#define SS_ST_NONFINITE (1 << 3)    /* row with NaN, +inf, or all -inf */
+#define SS_ST_TEMPERATURE (1 << 4)  /* temperature NaN, negative or inf */
+#define SS_ST_NO_UNIFORMS (1 << 5)  /* T > 0 but uniforms == NULL */
+#define SS_ST_COUNT (1 << 6)        /* extend count outside [0, ld_tokens] */
+
+#define SS_MAX_K 16            /* largest number of drafted tokens */
+#define SS_MAX_LEN (1 << 24)   /* largest automaton capacity, tokens */
+
+#define SS_DTYPE_F32 0
+#define SS_DTYPE_BF16 1
+
+/* Library version (major*10000 + minor*100 + patch). */
+int ss_version(void);
+
+/* Text of the last SS_ELAUNCH / SS_EINVAL on the calling thread. */
+const char* ss_last_error_string(void);
+
+/* ========================================================================= *
+ * Verification ([P2] §2.2, [P3] "贪婪采样" / "拒绝采样", [P1] §1.1, §3.1.2)
+ * ========================================================================= */
+
+/* Bytes of workspace spec_verify needs for (B, K, V). */
+size_t ss_verify_workspace_bytes(int B, int K, int V);
+
+/* Prepares a workspace once before its first spec_verify (zero-fills the
+ * completion counters). spec_verify leaves the workspace prepared. */
+int ss_verify_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * spec_verify — one batched verification step.
+ *
+ * For each sequence b with d = draft_len[b] drafts x_0..x_{d-1} and target
+ * logits rows l_0..l_d (row j scores the token after the prompt plus drafts
+ * x_0..x_{j-1}; rows j > d are never read):
+ *   T = temperature[b] == 0 (greedy): accept x_j iff x_j == argmax l_j (lowest
+ *     index on ties); the first mismatch emits argmax l_j and stops; if all d
+ *     pass, argmax l_d is emitted.
+ *   T > 0: p_j = softmax(l_j / T). Accept x_j iff u[b,j] <= p_j(x_j) / q_j(x_j)
+ *     where q_j(x_j) is q[b,j,x_j] (q given) or 1 (q == NULL: one-hot drafts).
+ *     At the first rejection j, emit a token drawn from max(0, p_j - q_j)
+ *     normalised (q given; falls back to p_j if that is zero everywhere) or
+ *     from p_j with x_j removed (one-hot), and stop. If all d pass, emit a
+ *     bonus token drawn from p_d. Draws use the final coin u[b,K]: the
+ *     smallest token i with (sum of weights of tokens <= i) > u * (total).
+ *
+ * Arguments:
+ *   logits      [B, K+1, V], dtype SS_DTYPE_F32 (float) or SS_DTYPE_BF16
+ *               (bfloat16, widened exactly to float).
+ *   draft       [B, K] int32; entries j >= draft_len[b] are ignored.
+ *   draft_len   [B] int32 in [0, K].
+ *   q           [B, K, V] float draft probabilities, or NULL for one-hot.
+ *   temperature [B] float >= 0.
+ *   uniforms    [B, K+1] float in [0, 1): columns 0..K-1 are the acceptance
+ *               coins, column K the final coin. May be NULL only if every
+ *               temperature is 0.
+ *   out_tokens  [B, K+1] int32: accepted drafts then the corrected / bonus
+ *               token; -1 after num_emitted.
+ *   num_emitted [B] int32 = accepted drafts + 1.
+ *   p_draft     [B, K] float or NULL: p_j(x_j) for j < num_emitted and j < d
+ *               at T > 0; -1 elsewhere.
+ *   status      [B] int32, OR-ed with SS_ST_* bits.
+ *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), prepared by
+ *               ss_verify_workspace_init.
+ * Limits: 1 <= B, 1 <= K <= SS_MAX_K, 1 <= V < 2^30, B*(K+1)*V < 2^40.
+ * Errors: SS_EINVAL for sizes/null pointers/dtype, SS_EWORKSPACE, SS_ELAUNCH.
+ */
+int spec_verify(const void* logits, int dtype, int B, int K, int V,
+                const int32_t* draft, const int32_t* draft_len, const float* q,
+                const float* temperature, const float* uniforms,
+                int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
+                int32_t* status, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/* ========================================================================= *
+ * Dynamic suffix automaton ([P1] §1.1, [P4] §3)
+ *
+ * One automaton per sequence over that sequence's committed tokens. State 0 is
+ * the root; every appended token creates one state ("cur") and at most one
+ * clone, numbered in creation order (cur before clone). Each state has len
+ * (longest string), link (suffix link, -1 for the root) and min_endpos (first
+ * end position of its strings, 0-indexed; -1 for the root). Capacity per
+ * sequence: max_len tokens, 2*max_len states, 3*max_len transitions.
+ * ========================================================================= */
+
+/* Bytes of one state buffer for B sequences of capacity max_len tokens. */
+size_t sam_state_bytes(int B, int max_len);
+
+/* Resets every sequence to the empty text (root only). V is the vocabulary
+ * size used to range-check appended tokens. */
+int sam_init(void* state, int B, int max_len, int V, void* stream);
+
+/*
+ * sam_extend — appends counts[b] tokens tokens[b*ld_tokens + 0 ..] to
+ * sequence b, in order, by Blumer's online extension ([P4] §3 "Update of
+ * Suffix Automaton": after verification the accepted tokens extend the
+ * automaton). Serves both prefill (counts = prompt lengths) and the per-step
+ * append (tokens = out_tokens, ld = K+1, counts = num_emitted).
+ * A sequence whose status is non-zero is skipped. Capacity overflow, a token
+ * outside [0, V) or a count outside [0, ld_tokens] sets the status bit and
+ * stops before that token; tokens appended before it stay appended.
+ */
+int sam_extend(void* state, int B, int max_len, const int32_t* tokens,
+               int ld_tokens, const int32_t* counts, void* stream);
+
+/*
+ * sam_draft — per sequence: from the state of the whole text follow suffix
+ * links until a state with an outgoing transition ([P1] §1.1, the ABCBC
+ * example); its len is the match length L and min_endpos p locates the first
+ * earlier occurrence of the matched suffix. L == 0 gives draft_len 0;
+ * otherwise draft_len = min(K, n-1-p) and draft[j] = text[p+1+j].
+ *   draft [B, K] int32 (-1 padded), draft_len [B], match_len [B] int32.
+ */
+int sam_draft(const void* state, int B, int max_len, int K, int32_t* draft,
+              int32_t* draft_len, int32_t* match_len, void* stream);
+
+/* Copies the sticky per-sequence status words to status_out [B] int32. */
+int sam_status(const void* state, int B, int max_len, int32_t* status_out,
+               void* stream);
+
+/*
+ * sam_export — debugging and parity: copies sequence b's automaton into
+ * caller device buffers.
+ *   header_out [8] int32: n (tokens), last, num_states, num_edges, status,
+ *              max_len, V, hash_slots.
+ *   states_out [2*max_len, 4] int32 rows (len, link, min_endpos, first_edge);
+ *              rows >= num_states are unspecified.
+ *   edges_out  [hash_slots, 4] int32 rows (src, token, dst, next); src == -1
+ *              marks an empty row. Each transition appears exactly once.
+ *   text_out   [max_len] int32: the committed tokens.
+ */
+int sam_export(const void* state, int B, int max_len, int b,
+               int32_t* header_out, int32_t* states_out, int32_t* edges_out,
+               int32_t* text_out, void* stream);
+
+/* Number of hash rows per sequence for capacity max_len (edges_out size). */
+int sam_hash_slots(int max_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECSAM_H */

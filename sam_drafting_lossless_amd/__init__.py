@@ -1,0 +1,266 @@
+"""Python binding of the MI355X speculative-verify + SAM-draft library.
+
+Thin ctypes marshalling over ``libspecsam.so`` (C ABI in ``include/specsam.h``):
+every step of the path runs in the library's HIP kernels; PyTorch provides
+device memory and the stream. The names follow the C entry points:
+``spec_verify``, ``sam_state_bytes``, ``sam_init``, ``sam_extend``,
+``sam_draft``, ``sam_status``, ``sam_export``, ``ss_verify_workspace_bytes``.
+
+The library must be built (``python -m sam_drafting_lossless_amd.build`` or
+``__graft_entry__.build()``); importing works without it, but every call
+raises if it is missing. There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so the library shares torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecsam.so")
+
+SS_OK, SS_EINVAL, SS_EWORKSPACE, SS_ELAUNCH = 0, -1, -2, -3
+ST_SAM_CAPACITY = 1 << 0
+ST_TOKEN_RANGE = 1 << 1
+ST_DRAFT_LEN = 1 << 2
+ST_NONFINITE = 1 << 3
+ST_TEMPERATURE = 1 << 4
+ST_NO_UNIFORMS = 1 << 5
+ST_COUNT = 1 << 6
+MAX_K = 16
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+_lib = None
+
+
+class SpecSamError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SpecSamError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m sam_drafting_lossless_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.ss_version.restype = i32
+    L.ss_last_error_string.restype = ctypes.c_char_p
+    L.ss_verify_workspace_bytes.argtypes = [i32, i32, i32]
+    L.ss_verify_workspace_bytes.restype = sz
+    L.ss_verify_workspace_init.argtypes = [P, sz, P]
+    L.ss_verify_workspace_init.restype = i32
+    L.spec_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                              P, sz, P]
+    L.spec_verify.restype = i32
+    L.sam_state_bytes.argtypes = [i32, i32]
+    L.sam_state_bytes.restype = sz
+    L.sam_hash_slots.argtypes = [i32]
+    L.sam_hash_slots.restype = i32
+    L.sam_init.argtypes = [P, i32, i32, i32, P]
+    L.sam_init.restype = i32
+    L.sam_extend.argtypes = [P, i32, i32, P, i32, P, P]
+    L.sam_extend.restype = i32
+    L.sam_draft.argtypes = [P, i32, i32, i32, P, P, P, P]
+    L.sam_draft.restype = i32
+    L.sam_status.argtypes = [P, i32, i32, P, P]
+    L.sam_status.restype = i32
+    L.sam_export.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+    L.sam_export.restype = i32
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != SS_OK:
+        msg = lib().ss_last_error_string().decode(errors="replace")
+        raise SpecSamError(f"{what} failed with code {rc}: {msg}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SpecSamError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise SpecSamError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise SpecSamError(f"{name} must have shape {tuple(shape)}, got "
+                           f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise SpecSamError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ------------------------------------------------------------- verification --
+def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(lib().ss_verify_workspace_bytes(B, K, V))
+
+
+def verify_workspace(B: int, K: int, V: int, device=None, stream=None):
+    """A prepared workspace tensor (uint8) for spec_verify."""
+    n = ss_verify_workspace_bytes(B, K, V)
+    if n == 0:
+        raise SpecSamError(f"unsupported sizes B={B} K={K} V={V}")
+    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    _check(lib().ss_verify_workspace_init(ws.data_ptr(), n, _stream(stream)),
+           "ss_verify_workspace_init")
+    return ws
+
+
+def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
+                workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
+                status=None, stream=None):
+    """Verify one batch (see include/specsam.h). Returns
+    (out_tokens [B,K+1] int32, num_emitted [B] int32, p_draft [B,K] float32,
+    status [B] int32)."""
+    if logits.dim() != 3:
+        raise SpecSamError("logits must be [B, K+1, V]")
+    B, R, V = logits.shape
+    K = R - 1
+    if logits.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise SpecSamError("logits must be float32 or bfloat16")
+    dev = logits.device
+    i32 = torch.int32
+    if workspace is None:
+        workspace = verify_workspace(B, K, V, dev, stream)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, R), dtype=i32, device=dev)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=i32, device=dev)
+    if p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.zeros(B, dtype=i32, device=dev)
+    args = (
+        _dev(logits, "logits"), dt, B, K, V,
+        _dev(draft, "draft", i32, (B, K)),
+        _dev(draft_len, "draft_len", i32, (B,)),
+        None if q is None else _dev(q, "q", torch.float32, (B, K, V)),
+        _dev(temperature, "temperature", torch.float32, (B,)),
+        None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
+                                           (B, R)),
+        _dev(out_tokens, "out_tokens", i32, (B, R)),
+        _dev(num_emitted, "num_emitted", i32, (B,)),
+        _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _dev(status, "status", i32, (B,)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream))
+    _check(lib().spec_verify(*args), "spec_verify")
+    return out_tokens, num_emitted, p_draft, status
+
+
+# ------------------------------------------------------- suffix automaton ----
+def sam_state_bytes(B: int, max_len: int) -> int:
+    return int(lib().sam_state_bytes(B, max_len))
+
+
+def sam_hash_slots(max_len: int) -> int:
+    return int(lib().sam_hash_slots(max_len))
+
+
+def sam_init(state, B: int, max_len: int, V: int, stream=None) -> None:
+    _check(lib().sam_init(_dev(state, "state", torch.uint8), B, max_len, V,
+                          _stream(stream)), "sam_init")
+
+
+def sam_extend(state, B: int, max_len: int, tokens, counts, stream=None) -> None:
+    if tokens.dim() != 2 or tokens.shape[0] != B:
+        raise SpecSamError("tokens must be [B, ld]")
+    _check(lib().sam_extend(_dev(state, "state", torch.uint8), B, max_len,
+                            _dev(tokens, "tokens", torch.int32),
+                            int(tokens.shape[1]),
+                            _dev(counts, "counts", torch.int32, (B,)),
+                            _stream(stream)), "sam_extend")
+
+
+def sam_draft(state, B: int, max_len: int, K: int, draft=None, draft_len=None,
+              match_len=None, stream=None):
+    dev = state.device
+    if draft is None:
+        draft = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if draft_len is None:
+        draft_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if match_len is None:
+        match_len = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib().sam_draft(_dev(state, "state", torch.uint8), B, max_len, K,
+                           _dev(draft, "draft", torch.int32, (B, K)),
+                           _dev(draft_len, "draft_len", torch.int32, (B,)),
+                           _dev(match_len, "match_len", torch.int32, (B,)),
+                           _stream(stream)), "sam_draft")
+    return draft, draft_len, match_len
+
+
+def sam_status(state, B: int, max_len: int, out=None, stream=None):
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=state.device)
+    _check(lib().sam_status(_dev(state, "state", torch.uint8), B, max_len,
+                            _dev(out, "status_out", torch.int32, (B,)),
+                            _stream(stream)), "sam_status")
+    return out
+
+
+def sam_export(state, B: int, max_len: int, b: int, stream=None):
+    """Sequence b's automaton as host numpy arrays: dict(n, last, num_states,
+    num_edges, status, len, link, min_endpos, first_edge, edges [E,3] sorted
+    by (src, token), text). Synchronises the stream."""
+    dev = state.device
+    H = sam_hash_slots(max_len)
+    hdr = torch.empty(8, dtype=torch.int32, device=dev)
+    st = torch.empty((2 * max_len, 4), dtype=torch.int32, device=dev)
+    ed = torch.empty((H, 4), dtype=torch.int32, device=dev)
+    tx = torch.empty(max_len, dtype=torch.int32, device=dev)
+    _check(lib().sam_export(_dev(state, "state", torch.uint8), B, max_len, b,
+                            hdr.data_ptr(), st.data_ptr(), ed.data_ptr(),
+                            tx.data_ptr(), _stream(stream)), "sam_export")
+    torch.cuda.synchronize(dev)
+    h = hdr.cpu().numpy()
+    n, last, S, E, status = (int(v) for v in h[:5])
+    st = st[:S].cpu().numpy()
+    ed = ed.cpu().numpy()
+    ed = ed[ed[:, 0] >= 0][:, :3]
+    order = (ed[:, 0].astype("int64") << 32) | ed[:, 1].astype("int64")
+    ed = ed[order.argsort(kind="stable")]
+    return {"n": n, "last": last, "num_states": S, "num_edges": E,
+            "status": status, "len": st[:, 0].copy(), "link": st[:, 1].copy(),
+            "min_endpos": st[:, 2].copy(), "first_edge": st[:, 3].copy(),
+            "edges": ed, "text": tx[:n].cpu().numpy()}
+
+
+class SamState:
+    """Device buffer holding B automata of capacity max_len tokens."""
+
+    def __init__(self, B: int, max_len: int, V: int, device="cuda", stream=None):
+        n = sam_state_bytes(B, max_len)
+        if n == 0:
+            raise SpecSamError(f"unsupported sizes B={B} max_len={max_len}")
+        self.B, self.max_len, self.V = B, max_len, V
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        sam_init(self.buf, B, max_len, V, stream)
+
+    def extend(self, tokens, counts, stream=None):
+        sam_extend(self.buf, self.B, self.max_len, tokens, counts, stream)
+
+    def draft(self, K: int, draft=None, draft_len=None, match_len=None,
+              stream=None):
+        return sam_draft(self.buf, self.B, self.max_len, K, draft, draft_len,
+                         match_len, stream)
+
+    def status(self, out=None, stream=None):
+        return sam_status(self.buf, self.B, self.max_len, out, stream)
+
+    def export(self, b: int):
+        return sam_export(self.buf, self.B, self.max_len, b)

@@ -1,0 +1,56 @@
+"""Compiles the HIP library for gfx950 in-tree.
+
+    python -m sam_drafting_lossless_amd.build
+
+produces ``sam_drafting_lossless_amd/libspecsam.so`` (the product library,
+C ABI in ``include/specsam.h``) and ``libspecsam_harness.so`` (synthetic
+target-model and measurement kernels used by tests and bench.py; not part of
+the verification or drafting path).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+LIB = os.path.join(PKG, "libspecsam.so")
+HARNESS_LIB = os.path.join(PKG, "libspecsam_harness.so")
+
+LIB_SOURCES = ["api.hip", "verify.hip", "sam.hip"]
+HARNESS_SOURCES = ["harness.hip"]
+
+# Packed FP32 instructions are disabled: hipcc would otherwise form them from
+# ordinary float code.
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile(sources, out, extra=()):
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, *[os.path.join(CSRC, s) for s in sources],
+           "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> None:
+    """Always recompiles both libraries."""
+    _compile(LIB_SOURCES, LIB)
+    if all(os.path.exists(os.path.join(CSRC, s)) for s in HARNESS_SOURCES):
+        _compile(HARNESS_SOURCES, HARNESS_LIB)
+    if verbose:
+        print("built", LIB, HARNESS_LIB)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,135 @@
+// Measurement and synthetic-workload kernels (libspecsam_harness.so).
+//
+// None of this is part of verification or drafting. It stands in for the
+// target model and measures the memory system:
+//   hs_boost_step  advances each sequence's committed length by the tokens the
+//                  previous step emitted, restores the logits a ring slot was
+//                  boosted with when last used, then saves and boosts the
+//                  logit of the true next token gt[b, n_b + j] in every row.
+//   hs_read_bw     streams a buffer with 16-byte non-temporal loads (the
+//                  achievable HBM read rate).
+//   hs_copy        copies a buffer (a known-size reference for hardware
+//                  byte counters).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float((unsigned)h << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (finite inputs).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ void boost_step_kernel(unsigned char* slot, int dtype, int B, int R,
+                                  int V, const int32_t* gt, int gt_ld,
+                                  int32_t* ncommit, const int32_t* nem_prev,
+                                  int32_t* saved_pos, float* saved_val,
+                                  const uint8_t* mask, float boost) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int n = ncommit[b];
+  if (nem_prev) n += max(nem_prev[b], 0);
+  ncommit[b] = n;
+  for (int j = 0; j < R; ++j) {
+    const int64_t rowoff = ((int64_t)b * R + j) * V;
+    const int64_t si = (int64_t)b * R + j;
+    const int old = saved_pos[si];  // always -1 or a valid column
+    if (dtype == 0) {
+      float* row = reinterpret_cast<float*>(slot) + rowoff;
+      if (old >= 0) row[old] = saved_val[si];
+      const int64_t g = (int64_t)n + j;
+      int pos = (g < gt_ld) ? gt[(int64_t)b * gt_ld + g] : -1;
+      if (pos >= V) pos = -1;
+      saved_pos[si] = pos;
+      if (pos >= 0) {
+        saved_val[si] = row[pos];
+        if (!mask || mask[si]) row[pos] = row[pos] + boost;
+      }
+    } else {
+      unsigned short* row = reinterpret_cast<unsigned short*>(slot) + rowoff;
+      if (old >= 0) row[old] = (unsigned short)__float_as_uint(saved_val[si]);
+      const int64_t g = (int64_t)n + j;
+      int pos = (g < gt_ld) ? gt[(int64_t)b * gt_ld + g] : -1;
+      if (pos >= V) pos = -1;
+      saved_pos[si] = pos;
+      if (pos >= 0) {
+        const unsigned short h = row[pos];
+        saved_val[si] = __uint_as_float((unsigned)h);  // raw bits kept exactly
+        if (!mask || mask[si]) row[pos] = f32_to_bf16(bf16_to_f32(h) + boost);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void read_bw_kernel(const u32x4* p, size_t n,
+                                                      unsigned* out) {
+  unsigned acc = 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;  // keeps the loads live
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(u32x4* dst, const u32x4* src,
+                                                   size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" int hs_boost_step(void* slot, int dtype, int B, int R, int V,
+                             const int32_t* gt, int gt_ld, int32_t* ncommit,
+                             const int32_t* nem_prev, int32_t* saved_pos,
+                             float* saved_val, const uint8_t* mask, float boost,
+                             void* stream) {
+  if (!slot || !gt || !ncommit || !saved_pos || !saved_val || B < 1 || R < 1 ||
+      V < 1)
+    return -1;
+  hipLaunchKernelGGL(boost_step_kernel, dim3((B + 255) / 256), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<unsigned char*>(slot), dtype, B, R, V, gt,
+                     gt_ld, ncommit, nem_prev, saved_pos, saved_val, mask, boost);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hs_read_bw(const void* buf, size_t bytes, unsigned* sink,
+                          int grid, void* stream) {
+  if (!buf || !sink || ((uintptr_t)buf & 15) || (bytes & 15)) return -1;
+  hipLaunchKernelGGL(read_bw_kernel, dim3(grid > 0 ? grid : 4096), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+extern "C" int hs_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || ((uintptr_t)dst & 15) || ((uintptr_t)src & 15) || (bytes & 15))
+    return -1;
+  const size_t n = bytes / 16;
+  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src),
+                     n);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}

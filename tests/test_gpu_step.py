@@ -1,0 +1,100 @@
+"""End-to-end parity of whole steps (draft -> verify -> extend) on the five
+workloads: the GPU path and the oracle run side by side on the same device
+bytes; drafts, emitted tokens and the automata must agree (T > 0 draws up to
+counted ties, after which the oracle follows the GPU's tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sam_drafting_lossless_amd as ssl
+import synth
+from _parity import Tally, compare_verify, dev, say, to_host_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_sam_workload(c, steps, **over):
+    cfg = synth.config(c, **over)
+    say(f"[gpu] steps {cfg.name} B={cfg.B} steps={steps}")
+    gt = synth.token_streams(cfg, steps)
+    H = cfg.hist_len
+    n = np.full(cfg.B, H, np.int32)
+    max_len = cfg.stream_len(steps)
+    st = ssl.SamState(cfg.B, max_len, cfg.V, "cuda")
+    st.extend(dev(gt[:, :H]), dev(np.full(cfg.B, H, np.int32)))
+    sams = [oracle.SAM(gt[b, :H]) for b in range(cfg.B)]
+    T = np.full(cfg.B, cfg.T, np.float32)
+    Td = dev(T)
+    ws = ssl.verify_workspace(cfg.B, cfg.K, cfg.V)
+    tally = Tally()
+    tokens_total = 0
+    for s in range(steps):
+        d, dl, ml = st.draft(cfg.K)
+        x = synth.target_logits(cfg, s, gt, n, device="cuda")
+        u = synth.uniforms(cfg, s)
+        out, nem, pd, status = ssl.spec_verify(x, d, dl, Td, dev(u), workspace=ws)
+        st.extend(out, nem)
+        torch.cuda.synchronize()
+        d, dl, ml = d.cpu().numpy(), dl.cpu().numpy(), ml.cpu().numpy()
+        g = (out.cpu().numpy(), nem.cpu().numpy(), pd.cpu().numpy(),
+             status.cpu().numpy())
+        for b in range(cfg.B):
+            od, odl, oml = sams[b].draft(cfg.K)
+            assert (od == d[b]).all() and odl == dl[b] and oml == ml[b], (s, b)
+        r = oracle.verify(to_host_logits(x), d, dl, T, u, nthreads=8)
+        compare_verify(*g, r, T, u, tally, what=f"{cfg.name} step {s}")
+        for b in range(cfg.B):
+            sams[b].extend(g[0][b, :g[1][b]])  # identical unless a counted tie
+        n = n + g[1]
+        tokens_total += int(g[1].sum())
+    for b in range(min(cfg.B, 4)):
+        e, o = st.export(b), sams[b].export()
+        np.testing.assert_array_equal(e["len"], o["len"])
+        np.testing.assert_array_equal(e["link"], o["link"])
+        np.testing.assert_array_equal(e["min_endpos"], o["min_endpos"])
+        np.testing.assert_array_equal(e["edges"], o["edges"])
+    assert (st.status().cpu().numpy() == 0).all()
+    say(f"    {tally}; mean tokens/step {tokens_total / (steps * cfg.B):.3f}")
+    return tally
+
+
+def test_c1_tiny_greedy_500_steps():
+    _run_sam_workload(1, 500)
+
+
+def test_c2_greedy_full_size():
+    _run_sam_workload(2, 6)
+
+
+def test_c3_one_hot_full_size():
+    _run_sam_workload(3, 4)
+
+
+def test_c4_bf16_long_history():
+    _run_sam_workload(4, 3)
+
+
+def test_c3_shape_high_acceptance():
+    """A sensitivity variant (boost +12) so that drafts are often accepted and
+    the automaton grows by several tokens per step."""
+    _run_sam_workload(3, 6, B=32, boost=12.0)
+
+
+def test_c5_draft_model_full_size():
+    cfg = synth.config(5)
+    say(f"[gpu] steps {cfg.name}")
+    T = np.full(cfg.B, cfg.T, np.float32)
+    tally = Tally()
+    for s in range(2):
+        x = synth.noise(cfg, s, "cuda")
+        q, draft = synth.draft_model_inputs(cfg, s, x, "cuda")
+        u = synth.uniforms(cfg, s)
+        dl = np.full(cfg.B, cfg.K, np.int32)
+        g = ssl.spec_verify(x, dev(draft), dev(dl), dev(T), dev(u), q)
+        torch.cuda.synchronize()
+        g = tuple(t.cpu().numpy() for t in g)
+        r = oracle.verify(x.cpu().numpy(), draft, dl, T, u, q.cpu().numpy(),
+                          nthreads=8)
+        compare_verify(*g, r, T, u, tally, what=f"c5 step {s}")
+    say(f"    {tally}")

@@ -1,0 +1,246 @@
+"""GPU parity of spec_verify against the oracle (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy import special, stats
+
+import oracle
+import sam_drafting_lossless_amd as ssl
+import synth
+from _parity import Tally, compare_verify, dev, say, to_host_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(logits, draft, dl, T, u=None, q=None, status0=None):
+    """Runs GPU and oracle on identical inputs; returns (gpu tuple, oracle)."""
+    B = logits.shape[0]
+    st = dev(np.zeros(B, np.int32) if status0 is None else status0)
+    g = ssl.spec_verify(logits, dev(draft, torch.int32), dev(dl, torch.int32),
+                        dev(T, torch.float32),
+                        None if u is None else dev(u, torch.float32),
+                        q, status=st)
+    torch.cuda.synchronize()
+    g = tuple(t.cpu().numpy() for t in g)
+    r = oracle.verify(to_host_logits(logits), draft, dl, T, u,
+                      None if q is None else q.cpu().numpy(), nthreads=8)
+    return g, r
+
+
+def _drafts_near_argmax(rng, logits_np, K, dl, flip=0.4):
+    am = logits_np[:, :K].argmax(-1).astype(np.int32)
+    B, V = logits_np.shape[0], logits_np.shape[2]
+    bad = rng.random((B, K)) < flip
+    am[bad] = rng.integers(0, V, int(bad.sum()))
+    return am
+
+
+SHAPES = [  # (B, K, V): tiny, one chunk, ragged chunks, scalar path, Qwen
+    (1, 3, 32), (3, 1, 1), (5, 4, 7), (7, 2, 8192), (6, 3, 8193),
+    (4, 5, 3 * 8192 + 4), (3, 16, 4099), (2, 3, 151936), (33, 2, 1000),
+]
+
+
+@pytest.mark.parametrize("B,K,V", SHAPES)
+def test_greedy_bit_exact(B, K, V):
+    say(f"[gpu] greedy B={B} K={K} V={V}")
+    rng = np.random.default_rng(B * 1000 + V)
+    x = rng.integers(-4, 5, (B, K + 1, V)).astype(np.float32)  # many ties
+    dl = rng.integers(0, K + 1, B).astype(np.int32)
+    draft = _drafts_near_argmax(rng, x, K, dl)
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, np.zeros(B, np.float32))
+    compare_verify(*g, r, np.zeros(B), None, what="greedy")
+
+
+@pytest.mark.parametrize("B,K,V", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sampling_one_hot(B, K, V, dtype):
+    say(f"[gpu] one-hot sampling {dtype} B={B} K={K} V={V}")
+    rng = np.random.default_rng(B * 77 + V + (dtype == "bf16"))
+    x = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(np.float32)
+    dl = rng.integers(0, K + 1, B).astype(np.int32)
+    draft = _drafts_near_argmax(rng, x, K, dl, flip=0.3)
+    # make drafts plausible so both accepts and rejects happen
+    for b in range(B):
+        for j in range(K):
+            x[b, j, draft[b, j]] += rng.uniform(0, 6)
+    T = rng.uniform(0.4, 1.6, B).astype(np.float32)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    g, r = _run(t, draft, dl, T, u)
+    tally = Tally()
+    compare_verify(*g, r, T, u, tally, what=f"one-hot {dtype}")
+    say(f"    {tally}")
+
+
+@pytest.mark.parametrize("B,K,V", [(4, 3, 32), (5, 2, 8193), (3, 5, 30011),
+                                   (2, 4, 151936)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sampling_given_q(B, K, V, dtype):
+    say(f"[gpu] given-q sampling {dtype} B={B} K={K} V={V}")
+    rng = np.random.default_rng(V + B + (dtype == "bf16"))
+    x = (rng.standard_normal((B, K + 1, V)) * 1.4).astype(np.float32)
+    T = rng.uniform(0.5, 1.2, B).astype(np.float32)
+    ql = x[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32) * 0.7
+    q = special.softmax(ql.astype(np.float64) / T[:, None, None], axis=-1)
+    draft = np.array([[rng.choice(V, p=q[b, j]) for j in range(K)]
+                      for b in range(B)], np.int32)
+    dl = rng.integers(0, K + 1, B).astype(np.int32)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    g, r = _run(t, draft, dl, T, u, q=torch.from_numpy(q.astype(np.float32)).cuda())
+    tally = Tally()
+    compare_verify(*g, r, T, u, tally, what=f"given-q {dtype}")
+    say(f"    {tally}")
+
+
+def test_mixed_greedy_and_sampling_batch_with_masked_tokens():
+    say("[gpu] mixed T, -inf entries")
+    rng = np.random.default_rng(9)
+    B, K, V = 24, 4, 20000
+    x = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    x[:, :, rng.choice(V, 5000, replace=False)] = -np.inf
+    T = np.where(rng.random(B) < 0.5, 0.0, 0.9).astype(np.float32)
+    dl = rng.integers(0, K + 1, B).astype(np.int32)
+    draft = _drafts_near_argmax(rng, np.nan_to_num(x, neginf=-1e9), K, dl)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
+    compare_verify(*g, r, T, u, Tally(), what="mixed")
+
+
+def test_status_words_match_oracle():
+    say("[gpu] status words")
+    V, K = 16, 2
+    x = np.zeros((7, K + 1, V), np.float32)
+    draft = np.zeros((7, K), np.int32)
+    dl = np.full(7, K, np.int32)
+    T = np.zeros(7, np.float32)
+    dl[0] = K + 1
+    draft[1, 1] = V
+    x[2, 1, 5] = np.nan
+    T[3] = -1.0
+    x[4, 0, :] = -np.inf
+    x[5, 2, 3] = np.inf
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T)
+    compare_verify(*g, r, T, None, what="status")
+    assert g[3][6] == 0 and g[1][6] == K + 1
+    # T > 0 without uniforms
+    g, r = _run(torch.from_numpy(x[6:]).cuda(), draft[6:], dl[6:],
+                np.ones(1, np.float32), None)
+    assert g[3].tolist() == [ssl.ST_NO_UNIFORMS] == r.status.tolist()
+
+
+def test_sticky_status_is_ored_and_untouched_outputs():
+    say("[gpu] sticky status")
+    x = torch.zeros((2, 2, 8), device="cuda")
+    st0 = np.array([ssl.ST_SAM_CAPACITY, 0], np.int32)
+    out = torch.full((2, 2), 77, dtype=torch.int32, device="cuda")
+    g = ssl.spec_verify(x, dev(np.array([[0], [0]]), torch.int32),
+                        dev(np.array([5, 1]), torch.int32),
+                        dev(np.zeros(2), torch.float32), status=dev(st0),
+                        out_tokens=out)
+    torch.cuda.synchronize()
+    assert g[3].cpu().tolist() == [ssl.ST_SAM_CAPACITY | ssl.ST_DRAFT_LEN, 0]
+    assert g[0][0].cpu().tolist() == [77, 77]
+    assert g[0][1].cpu().tolist() == [0, 0]
+
+
+def test_host_argument_errors():
+    x = torch.zeros((2, 4, 8), device="cuda")
+    i = torch.zeros((2, 3), dtype=torch.int32, device="cuda")
+    d = torch.zeros(2, dtype=torch.int32, device="cuda")
+    T = torch.zeros(2, device="cuda")
+    with pytest.raises(ssl.SpecSamError):
+        ssl.spec_verify(x.double(), i, d, T)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ssl.SpecSamError, match="workspace"):
+        ssl.spec_verify(x, i, d, T, workspace=ws)
+
+
+@pytest.mark.parametrize("mode", ["onehot", "given_q"])
+def test_gpu_chi_square_first_token(mode):
+    """Losslessness on the GPU: 10^6 sequences in one launch, V = 8."""
+    say(f"[gpu] chi-square {mode}")
+    rng = np.random.default_rng(21 if mode == "onehot" else 22)
+    V, N = 8, 1_000_000
+    lp = rng.standard_normal(V) * 1.2
+    p = special.softmax(lp)
+    x = torch.from_numpy(lp.astype(np.float32)).cuda().expand(N, 2, V).contiguous()
+    u = rng.random((N, 2)).astype(np.float32)
+    if mode == "onehot":
+        draft = rng.integers(0, V, (N, 1)).astype(np.int32)
+        q = None
+    else:
+        qv = special.softmax(rng.standard_normal(V) * 1.5)
+        draft = rng.choice(V, size=(N, 1), p=qv).astype(np.int32)
+        q = torch.from_numpy(qv.astype(np.float32)).cuda().expand(N, 1, V).contiguous()
+    out, nem, _, st = ssl.spec_verify(x, dev(draft), dev(np.ones(N, np.int32)),
+                                      dev(np.ones(N, np.float32)), dev(u), q)
+    first = out[:, 0].cpu().numpy()
+    assert (st.cpu().numpy() == 0).all()
+    counts = np.bincount(first, minlength=V)
+    pv = stats.chisquare(counts, p * N).pvalue
+    assert pv > 1e-3, (counts, p * N, pv)
+
+
+@pytest.mark.parametrize("alpha", [0.2, 0.5, 0.8])
+def test_gpu_mean_tokens_closed_form(alpha):
+    K, N = 3, 500_000
+    lg = np.log(np.array([alpha, 1 - alpha])).astype(np.float32)
+    x = torch.from_numpy(lg).cuda().expand(N, K + 1, 2).contiguous()
+    u = np.random.default_rng(5).random((N, K + 1)).astype(np.float32)
+    _, nem, _, _ = ssl.spec_verify(x, dev(np.zeros((N, K), np.int32)),
+                                   dev(np.full(N, K, np.int32)),
+                                   dev(np.ones(N, np.float32)), dev(u))
+    m = nem.double().mean().item()
+    want = (1 - alpha ** (K + 1)) / (1 - alpha)
+    sd = nem.double().std().item()
+    assert abs(m - want) < 5 * sd / math.sqrt(N)
+
+
+# ----------------------------------------------------- full-size workloads ---
+def _full_step(cfg, step=0):
+    gt = synth.token_streams(cfg, steps=2)
+    n = np.full(cfg.B, cfg.hist_len, np.int32)
+    x = synth.target_logits(cfg, step, gt, n, device="cuda")
+    return gt, n, x
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_full_size_sam_draft_shapes(c):
+    """One verify at the workload's full size, drafts taken from gt so that a
+    realistic share is accepted; every output compared."""
+    cfg = synth.config(c)
+    say(f"[gpu] full-size verify {cfg.name}")
+    rng = np.random.default_rng(c)
+    gt, n, x = _full_step(cfg)
+    draft = np.stack([gt[b, n[b]:n[b] + cfg.K] for b in range(cfg.B)]).astype(np.int32)
+    wrong = rng.random(draft.shape) < 0.3
+    draft[wrong] = rng.integers(0, cfg.V, int(wrong.sum()))
+    dl = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    T = np.full(cfg.B, cfg.T, np.float32)
+    u = synth.uniforms(cfg, 0)
+    g, r = _run(x, draft, dl, T, u)
+    tally = Tally()
+    compare_verify(*g, r, T, u, tally, what=cfg.name)
+    say(f"    {tally}")
+
+
+def test_full_size_draft_model_q():
+    cfg = synth.config(5)
+    say(f"[gpu] full-size verify {cfg.name}")
+    x = synth.noise(cfg, 0, "cuda")
+    q, draft = synth.draft_model_inputs(cfg, 0, x, "cuda")
+    T = np.full(cfg.B, cfg.T, np.float32)
+    u = synth.uniforms(cfg, 0)
+    dl = np.full(cfg.B, cfg.K, np.int32)
+    g, r = _run(x, draft, dl, T, u, q=q)
+    tally = Tally()
+    compare_verify(*g, r, T, u, tally, what=cfg.name)
+    say(f"    {tally}  mean tokens/step {g[1].mean():.3f}")
