@@ -55,7 +55,8 @@ extern "C" {
 #define SS_ST_TOKEN_RANGE (1 << 1)  /* a token outside [0, V) */
 #define SS_ST_DRAFT_LEN (1 << 2)    /* draft_len outside [0, K] */
 #define SS_ST_NONFINITE (1 << 3)    /* row with NaN, +inf, or all -inf */
-#define SS_ST_TEMPERATURE (1 << 4)  /* temperature NaN, negative or inf */
+#define SS_ST_TEMPERATURE (1 << 4)  /* T NaN, negative, inf, or positive
+                                       below the smallest normal float */
 #define SS_ST_NO_UNIFORMS (1 << 5)  /* T > 0 but uniforms == NULL */
 #define SS_ST_COUNT (1 << 6)        /* extend count outside [0, ld_tokens] */
 
@@ -75,12 +76,10 @@ const char* ss_last_error_string(void);
  * Verification ([P2] §2.2, [P3] "贪婪采样" / "拒绝采样", [P1] §1.1, §3.1.2)
  * ========================================================================= */
 
-/* Bytes of workspace spec_verify needs for (B, K, V). */
+/* Bytes of workspace spec_verify needs for (B, K, V); 0 if unsupported.
+ * The workspace is scratch owned by the caller: no initialisation is needed
+ * and its contents between calls do not matter. */
 size_t ss_verify_workspace_bytes(int B, int K, int V);
-
-/* Prepares a workspace once before its first spec_verify (zero-fills the
- * completion counters). spec_verify leaves the workspace prepared. */
-int ss_verify_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * spec_verify — one batched verification step.
@@ -115,9 +114,11 @@ int ss_verify_workspace_init(void* workspace, size_t ws_bytes, void* stream);
  *   p_draft     [B, K] float or NULL: p_j(x_j) for j < num_emitted and j < d
  *               at T > 0; -1 elsewhere.
  *   status      [B] int32, OR-ed with SS_ST_* bits.
- *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), prepared by
- *               ss_verify_workspace_init.
- * Limits: 1 <= B, 1 <= K <= SS_MAX_K, 1 <= V < 2^30, B*(K+1)*V < 2^40.
+ *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), 16-byte
+ *               aligned.
+ * Limits: 1 <= B, 1 <= K <= SS_MAX_K, 1 <= V <= 2^21. A temperature that is
+ * positive but below the smallest normal float is reported as
+ * SS_ST_TEMPERATURE.
  * Errors: SS_EINVAL for sizes/null pointers/dtype, SS_EWORKSPACE, SS_ELAUNCH.
  */
 int spec_verify(const void* logits, int dtype, int B, int K, int V,

@@ -262,7 +262,11 @@ void verify_one(const VerifyIO& io, int b) {
   const double T = (double)io.temperature[b];
   int32_t st = 0;
   if (d < 0 || d > K) st |= ST_DRAFT_LEN;
-  if (!(T >= 0.0) || std::isinf(T)) st |= ST_TEMPERATURE;
+  // T = 0 is greedy; a positive T must be a finite float no smaller than the
+  // smallest normal float (below it 1/T is not representable in float).
+  if (!(T == 0.0 || (T >= (double)std::numeric_limits<float>::min() &&
+                     std::isfinite(T))))
+    st |= ST_TEMPERATURE;
   if (T > 0.0 && io.uniforms == nullptr) st |= ST_NO_UNIFORMS;
   if (st == 0) {
     for (int j = 0; j < d; ++j) {

@@ -53,8 +53,6 @@ def lib():
     L.ss_last_error_string.restype = ctypes.c_char_p
     L.ss_verify_workspace_bytes.argtypes = [i32, i32, i32]
     L.ss_verify_workspace_bytes.restype = sz
-    L.ss_verify_workspace_init.argtypes = [P, sz, P]
-    L.ss_verify_workspace_init.restype = i32
     L.spec_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                               P, sz, P]
     L.spec_verify.restype = i32
@@ -106,15 +104,12 @@ def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
     return int(lib().ss_verify_workspace_bytes(B, K, V))
 
 
-def verify_workspace(B: int, K: int, V: int, device=None, stream=None):
-    """A prepared workspace tensor (uint8) for spec_verify."""
+def verify_workspace(B: int, K: int, V: int, device=None):
+    """A workspace tensor (uint8) for spec_verify."""
     n = ss_verify_workspace_bytes(B, K, V)
     if n == 0:
         raise SpecSamError(f"unsupported sizes B={B} K={K} V={V}")
-    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
-    _check(lib().ss_verify_workspace_init(ws.data_ptr(), n, _stream(stream)),
-           "ss_verify_workspace_init")
-    return ws
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
@@ -136,7 +131,7 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
     dev = logits.device
     i32 = torch.int32
     if workspace is None:
-        workspace = verify_workspace(B, K, V, dev, stream)
+        workspace = verify_workspace(B, K, V, dev)
     if out_tokens is None:
         out_tokens = torch.empty((B, R), dtype=i32, device=dev)
     if num_emitted is None:

@@ -29,43 +29,41 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One thread per (sequence b, row j). The committed lengths ping-pong between
+// two arrays so that no thread reads a length another thread is updating.
 __global__ void boost_step_kernel(unsigned char* slot, int dtype, int B, int R,
                                   int V, const int32_t* gt, int gt_ld,
-                                  int32_t* ncommit, const int32_t* nem_prev,
-                                  int32_t* saved_pos, float* saved_val,
-                                  const uint8_t* mask, float boost) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  int n = ncommit[b];
+                                  const int32_t* ncommit_in, int32_t* ncommit_out,
+                                  const int32_t* nem_prev, int32_t* saved_pos,
+                                  float* saved_val, const uint8_t* mask,
+                                  float boost) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * R) return;
+  const int b = i / R, j = i - b * R;
+  int n = ncommit_in[b];
   if (nem_prev) n += max(nem_prev[b], 0);
-  ncommit[b] = n;
-  for (int j = 0; j < R; ++j) {
-    const int64_t rowoff = ((int64_t)b * R + j) * V;
-    const int64_t si = (int64_t)b * R + j;
-    const int old = saved_pos[si];  // always -1 or a valid column
-    if (dtype == 0) {
-      float* row = reinterpret_cast<float*>(slot) + rowoff;
-      if (old >= 0) row[old] = saved_val[si];
-      const int64_t g = (int64_t)n + j;
-      int pos = (g < gt_ld) ? gt[(int64_t)b * gt_ld + g] : -1;
-      if (pos >= V) pos = -1;
-      saved_pos[si] = pos;
-      if (pos >= 0) {
-        saved_val[si] = row[pos];
-        if (!mask || mask[si]) row[pos] = row[pos] + boost;
-      }
-    } else {
-      unsigned short* row = reinterpret_cast<unsigned short*>(slot) + rowoff;
-      if (old >= 0) row[old] = (unsigned short)__float_as_uint(saved_val[si]);
-      const int64_t g = (int64_t)n + j;
-      int pos = (g < gt_ld) ? gt[(int64_t)b * gt_ld + g] : -1;
-      if (pos >= V) pos = -1;
-      saved_pos[si] = pos;
-      if (pos >= 0) {
-        const unsigned short h = row[pos];
-        saved_val[si] = __uint_as_float((unsigned)h);  // raw bits kept exactly
-        if (!mask || mask[si]) row[pos] = f32_to_bf16(bf16_to_f32(h) + boost);
-      }
+  if (j == 0) ncommit_out[b] = n;
+  const int64_t rowoff = (int64_t)i * V;
+  const int old = saved_pos[i];  // always -1 or a valid column
+  const int64_t g = (int64_t)n + j;
+  int pos = (g < gt_ld) ? gt[(int64_t)b * gt_ld + g] : -1;
+  if (pos >= V) pos = -1;
+  saved_pos[i] = pos;
+  if (dtype == 0) {
+    float* row = reinterpret_cast<float*>(slot) + rowoff;
+    if (old >= 0) row[old] = saved_val[i];
+    if (pos >= 0) {
+      const float v = row[pos];
+      saved_val[i] = v;
+      if (!mask || mask[i]) row[pos] = v + boost;
+    }
+  } else {
+    unsigned short* row = reinterpret_cast<unsigned short*>(slot) + rowoff;
+    if (old >= 0) row[old] = (unsigned short)__float_as_uint(saved_val[i]);
+    if (pos >= 0) {
+      const unsigned short h = row[pos];
+      saved_val[i] = __uint_as_float((unsigned)h);  // raw bits kept exactly
+      if (!mask || mask[i]) row[pos] = f32_to_bf16(bf16_to_f32(h) + boost);
     }
   }
 }
@@ -99,17 +97,20 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4* dst, const u32x4* src,
 }  // namespace
 
 extern "C" int hs_boost_step(void* slot, int dtype, int B, int R, int V,
-                             const int32_t* gt, int gt_ld, int32_t* ncommit,
+                             const int32_t* gt, int gt_ld,
+                             const int32_t* ncommit_in, int32_t* ncommit_out,
                              const int32_t* nem_prev, int32_t* saved_pos,
                              float* saved_val, const uint8_t* mask, float boost,
                              void* stream) {
-  if (!slot || !gt || !ncommit || !saved_pos || !saved_val || B < 1 || R < 1 ||
-      V < 1)
+  if (!slot || !gt || !ncommit_in || !ncommit_out || !saved_pos || !saved_val ||
+      B < 1 || R < 1 || V < 1)
     return -1;
-  hipLaunchKernelGGL(boost_step_kernel, dim3((B + 255) / 256), dim3(256), 0,
+  const int n = B * R;
+  hipLaunchKernelGGL(boost_step_kernel, dim3((n + 255) / 256), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<unsigned char*>(slot), dtype, B, R, V, gt,
-                     gt_ld, ncommit, nem_prev, saved_pos, saved_val, mask, boost);
+                     gt_ld, ncommit_in, ncommit_out, nem_prev, saved_pos,
+                     saved_val, mask, boost);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -8,19 +8,25 @@
 // max(0, p - q) normalised (p with x_j removed for one-hot drafts); if every
 // draft passes, a bonus token comes from the last row.
 //
-// Design for gfx950 (the hot path is one HBM stream over B*(K+1)*V logits):
-//   pass 1  grid over (row, chunk); each 256-thread workgroup streams one
-//           32 KiB chunk with non-temporal 16-byte loads (8 in flight per
-//           lane) and writes one partial: (max, argmax) at T = 0, or (max,
-//           sum exp2((l-max)*log2e/T)) at T > 0. Rows j > draft_len are
-//           skipped. The last workgroup of a sequence to finish (device-scope
-//           counter with release/acquire fences) combines the partials, runs
-//           the accept scan as a wavefront ballot, writes the outputs and,
-//           for one-hot drafts or the bonus, draws the token: it picks the
-//           chunk from the rescaled partials and re-reads only that chunk.
-//   pass 2  only when q is given: a grid over (sequence, chunk) of the
-//           rejected row computes chunk sums of max(0, p - q); the last
-//           workgroup picks the chunk and re-reads it for the draw.
+// Design for gfx950 (the hot path is one HBM stream over the needed rows):
+//   stats     grid over (sequence, row group, 32 KiB chunk). Each 256-thread
+//             workgroup streams its chunk of every row j <= draft_len in its
+//             group with non-temporal 16-byte loads (8 in flight per lane)
+//             and writes one partial per row: (max, lowest argmax) at T = 0,
+//             or (max, sum exp2((l - max) * log2e / T)) at T > 0. Rows past
+//             draft_len are never read. Row groups are sized on the host so
+//             the grid has enough workgroups to fill 256 CUs.
+//   finalize  one workgroup per sequence: combines the chunk partials of
+//             each row, judges the drafts with one wavefront (lane j judges
+//             draft j; a ballot finds the first rejection), writes the
+//             outputs and, for one-hot drafts or the bonus, draws the token:
+//             the chunk is picked from the rescaled partials and only that
+//             chunk is re-read.
+//   residual  only when q is given: chunk sums of max(0, p - q) over the
+//             rejected row (grid over sequence x chunk), then one workgroup
+//             per sequence picks the chunk and re-reads it for the draw.
+// Kernel boundaries order the passes; no workgroup waits on another.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -140,9 +146,10 @@ __device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
   }
 }
 
+
 struct Args {
   const unsigned char* logits;
-  int B, K, V, nchunks;
+  int B, K, V, nchunks, rows_per_wg, ngroups;
   const int32_t* draft;
   const int32_t* draft_len;
   const float* q;
@@ -152,14 +159,12 @@ struct Args {
   int32_t* nem;
   float* p_draft;
   int32_t* status;
-  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, argval, argidx)
-  i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T) for pass 2
-  unsigned* ctr1;   // [B] pass-1 completion counters (zero between calls)
-  unsigned* ctr2;   // [B] pass-2 completion counters
+  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, -, argidx)
+  i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
   float* rpart;     // [B*nchunks] residual chunk sums
 };
 
-// Host-invisible per-sequence checks, identical in every workgroup.
+// Per-sequence checks that need device data.
 __device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T) {
   *d = a.draft_len[b];
   *T = a.temperature[b];
@@ -167,7 +172,7 @@ __device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T)
   if (*d < 0 || *d > a.K) st |= SS_ST_DRAFT_LEN;
   // T = 0 is greedy; otherwise T must be a finite normal positive float so
   // that log2(e)/T stays finite.
-  if (!(*T == 0.0f || (*T >= 1.17549435e-38f && *T <= 3.4e38f)))
+  if (!(*T == 0.0f || (*T >= 1.17549435e-38f && isfinite(*T))))
     st |= SS_ST_TEMPERATURE;
   if (*T > 0.0f && a.uniforms == nullptr) st |= SS_ST_NO_UNIFORMS;
   return st;
@@ -191,16 +196,98 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os
 }
 
 // ---------------------------------------------------------------------------
-// Draw from a row given chunk weights. Shared by the one-hot / bonus draw
-// (weights exp2((l-m)*kk), optionally with one token removed) and the
-// residual draw (weights max(0, exp2((l-m)*kk)/S - q)).
+// stats: one partial per (row, chunk).
+// ---------------------------------------------------------------------------
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void verify_stats(Args a) {
+  __shared__ f32x4 red[kWaves];
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int R = a.K + 1;
+  const int c = blockIdx.x % a.nchunks;
+  const int bg = blockIdx.x / a.nchunks;
+  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
+  int d;
+  float T;
+  if (seq_check(a, b, &d, &T)) return;  // reported by finalize
+  const int j0 = g * a.rows_per_wg;
+  const int j1 = min(j0 + a.rows_per_wg, d + 1);
+  const bool greedy = (T == 0.0f);
+  const float kk = greedy ? 0.0f : kLog2e / T;
+  const int cstart = c * kChunk<DT>;
+  for (int j = j0; j < j1; ++j) {
+    const int64_t row = (int64_t)b * R + j;
+    const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
+    u32x4 raw[kLoads];
+    load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
+    if (greedy) {
+      float bv = kNegInf;
+      int bi = INT_MAX, nan = 0;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) {
+          const float v = elem<DT>(raw[it], k);
+          if (v > bv) {
+            bv = v;
+            bi = elem_index<DT, VP>(cstart, tid, it, k);
+          }
+          nan |= (v != v);
+        }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+      nan = wave_or(nan);
+      if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
+      __syncthreads();
+      if (tid == 0) {
+        float pv = red[0].x, pn = red[0].y;
+        int pi = __float_as_int(red[0].w);
+        for (int i = 1; i < kWaves; ++i) {
+          argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
+          pn = fmaxf(pn, red[i].y);
+        }
+        a.partials[row * a.nchunks + c] = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
+      }
+    } else {
+      float mx = kNegInf;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) mx = fmaxf(mx, elem<DT>(raw[it], k));
+      const float base = (mx == kNegInf) ? 0.0f : mx;
+      float s = 0.0f;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k)
+          s += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        lse_merge(mx, s, __shfl_xor(mx, o, kWave), __shfl_xor(s, o, kWave), kk);
+      if (l == 0) red[w] = f32x4{mx, s, 0.0f, 0.0f};
+      __syncthreads();
+      if (tid == 0) {
+        float pm = red[0].x, ps = red[0].y;
+        for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
+        a.partials[row * a.nchunks + c] = f32x4{pm, ps, 0.0f, 0.0f};
+      }
+    }
+    __syncthreads();  // red[] is reused by the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Draw from one row. Weights are exp2((l - m) * kk) with token `excl`
+// removed (one-hot residual, or none for the bonus), or, for RESIDUAL,
+// max(0, exp2((l - m) * kk) / S - q).
 //
-// Step 1 (wave 0): inclusive scan of the chunk weights in chunk order, pick
-// the first chunk whose running sum exceeds u*total (strict), or the last
-// chunk with positive weight if rounding leaves none. Step 2 (all lanes):
-// re-read that chunk as 256 contiguous segments, scan the lane sums, and let
-// the lane whose interval holds the target find the first token whose running
-// sum exceeds it. Ties in rounding fall back to the last positive weight.
+// Step 1 (wave 0): inclusive scan of the chunk weights in chunk order; take
+// the first chunk whose running sum exceeds u * total (strict), or the last
+// chunk with positive weight if rounding leaves none. Step 2 (whole
+// workgroup): re-read that chunk as 256 contiguous 128-byte segments held in
+// registers, scan the lane sums, and let the lane whose interval holds the
+// target find the first token whose running sum exceeds it. A rounding miss
+// falls back to the chunk's last positive weight.
 // ---------------------------------------------------------------------------
 struct DrawShared {
   float W[kMaxChunks];
@@ -212,14 +299,63 @@ struct DrawShared {
   int result;
 };
 
-template <int DT, bool RESIDUAL>
+// Loads lane tid's segment of chunk c (kSeg elements) into registers.
+template <int DT, bool VP>
+__device__ __forceinline__ void load_segment(const unsigned char* row, int s0,
+                                             int V, float (&x)[kSeg<DT>]) {
+  if constexpr (VP) {
+    constexpr int kVecs = kSeg<DT> / kVec<DT>;  // 8 loads of 16 bytes
+    const u32x4* p =
+        reinterpret_cast<const u32x4*>(row + (int64_t)s0 * Dt<DT>::kBytes);
+#pragma unroll
+    for (int v = 0; v < kVecs; ++v) {
+      if (s0 + v * kVec<DT> < V) {
+        const u32x4 r = p[v];
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) x[v * kVec<DT> + k] = elem<DT>(r, k);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) x[v * kVec<DT> + k] = kNegInf;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSeg<DT>; ++k)
+      x[k] = (s0 + k < V) ? load_one<DT>(row, s0 + k) : kNegInf;
+  }
+}
+
+template <int DT, bool VP>
+__device__ __forceinline__ void load_q_segment(const float* qrow, int s0, int V,
+                                               float (&x)[kSeg<DT>]) {
+  if constexpr (VP) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(qrow + s0);
+#pragma unroll
+    for (int v = 0; v < kSeg<DT> / 4; ++v) {
+      if (s0 + v * 4 < V) {
+        const f32x4 r = p[v];
+        x[4 * v] = r.x;
+        x[4 * v + 1] = r.y;
+        x[4 * v + 2] = r.z;
+        x[4 * v + 3] = r.w;
+      } else {
+        x[4 * v] = x[4 * v + 1] = x[4 * v + 2] = x[4 * v + 3] = 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSeg<DT>; ++k) x[k] = (s0 + k < V) ? qrow[s0 + k] : 0.0f;
+  }
+}
+
+template <int DT, bool VP, bool RESIDUAL>
 __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
-                        float m, float S, float kk, float u, int nc) {
+                        float m, float S, float kk, float u) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1;
+  const int R = a.K + 1, nc = a.nchunks;
   const unsigned char* row =
-      a.logits + ((int64_t)(b * R + r) * a.V) * Dt<DT>::kBytes;
-  const float* qrow = RESIDUAL ? a.q + (int64_t)(b * a.K + r) * a.V : nullptr;
+      a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
+  const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const float invS = RESIDUAL ? 1.0f / S : 0.0f;
   if (w == 0) {
     float wx = 0.0f;
@@ -229,14 +365,14 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
       cx = excl / kChunk<DT>;
     }
     float carry = 0.0f;
-    for (int g = 0; g < nc; g += kWave) {
-      const int c = g + l;
+    for (int g0 = 0; g0 < nc; g0 += kWave) {
+      const int c = g0 + l;
       float W = 0.0f;
       if (c < nc) {
         if constexpr (RESIDUAL) {
           W = a.rpart[(int64_t)b * nc + c];
         } else {
-          const f32x4 P = a.partials[(int64_t)(b * R + r) * nc + c];
+          const f32x4 P = a.partials[((int64_t)b * R + r) * nc + c];
           W = P.y * fast_exp2((P.x - m) * kk);
           if (c == cx) W = fmaxf(0.0f, W - wx);
         }
@@ -250,13 +386,13 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
     }
     const float t = u * carry;
     int chosen = -1, lastpos = -1;
-    for (int g = 0; g < nc && chosen < 0; g += kWave) {
-      const int c = g + l;
+    for (int g0 = 0; g0 < nc && chosen < 0; g0 += kWave) {
+      const int c = g0 + l;
       const bool ok = c < nc;
       const unsigned long long hit = __ballot(ok && sh.cum[c] > t);
       const unsigned long long pos = __ballot(ok && sh.W[c] > 0.0f);
-      if (hit) chosen = g + __ffsll((long long)hit) - 1;
-      if (pos) lastpos = g + 63 - __clzll((long long)pos);
+      if (hit) chosen = g0 + __ffsll((unsigned long long)hit) - 1;
+      if (pos) lastpos = g0 + 63 - __clzll((unsigned long long)pos);
     }
     if (l == 0) {
       if (chosen >= 0) {
@@ -270,23 +406,30 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
   }
   __syncthreads();
   const int c = sh.chunk;
-  if (c < 0) return -1;  // no positive weight at all (caller guards)
+  if (c < 0) return -1;
   const float t_in = sh.t_in;
-  // Contiguous segment of this lane within the chunk.
   const int s0 = c * kChunk<DT> + tid * kSeg<DT>;
-  const int s1 = min(s0 + kSeg<DT>, a.V);
+  float x[kSeg<DT>];
+  load_segment<DT, VP>(row, s0, a.V, x);
+  if constexpr (RESIDUAL) {
+    float qv[kSeg<DT>];
+    load_q_segment<DT, VP>(qrow, s0, a.V, qv);
+#pragma unroll
+    for (int k = 0; k < kSeg<DT>; ++k)
+      x[k] = fmaxf(0.0f, fast_exp2((x[k] - m) * kk) * invS - qv[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSeg<DT>; ++k)
+      x[k] = (s0 + k == excl) ? 0.0f : fast_exp2((x[k] - m) * kk);
+  }
   float tsum = 0.0f;
   int tlast = -1;
-  for (int i = s0; i < s1; ++i) {
-    float wi;
-    if constexpr (RESIDUAL)
-      wi = fmaxf(0.0f, fast_exp2((load_one<DT>(row, i) - m) * kk) * invS - qrow[i]);
-    else
-      wi = (i == excl) ? 0.0f : fast_exp2((load_one<DT>(row, i) - m) * kk);
-    tsum += wi;
-    if (wi > 0.0f) tlast = i;
+#pragma unroll
+  for (int k = 0; k < kSeg<DT>; ++k) {
+    tsum += x[k];
+    if (x[k] > 0.0f) tlast = s0 + k;
   }
-  // Block-wide inclusive scan of lane sums.
+  // Block-wide inclusive scan of the lane sums.
   float inc = wave_inclusive_sum(tsum);
   if (l == kWave - 1) sh.wsum[w] = inc;
   int wl = tlast;
@@ -302,34 +445,26 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
   if (tid == 0) {
     int cl = -1;
     for (int i = 0; i < kWaves; ++i) cl = max(cl, sh.wlast[i]);
-    sh.result = cl;  // default: last positive weight of the chunk
+    sh.result = cl;  // default: the chunk's last positive weight
   }
   __syncthreads();
-  if (exc <= t_in && t_in < inc) {
+  if (exc <= t_in && t_in < inc) {  // at most one lane's interval holds t_in
     const float tl = t_in - exc;
     float run = 0.0f;
-    int found = tlast;
-    for (int i = s0; i < s1; ++i) {
-      float wi;
-      if constexpr (RESIDUAL)
-        wi = fmaxf(0.0f,
-                   fast_exp2((load_one<DT>(row, i) - m) * kk) * invS - qrow[i]);
-      else
-        wi = (i == excl) ? 0.0f : fast_exp2((load_one<DT>(row, i) - m) * kk);
-      run += wi;
-      if (run > tl) {
-        found = i;
-        break;
-      }
+    int found = -1;
+#pragma unroll
+    for (int k = 0; k < kSeg<DT>; ++k) {
+      run += x[k];
+      if (found < 0 && run > tl) found = s0 + k;
     }
-    sh.result = found;  // at most one lane's interval holds t_in
+    sh.result = found >= 0 ? found : tlast;
   }
   __syncthreads();
   return sh.result;
 }
 
 // ---------------------------------------------------------------------------
-// Last workgroup of sequence b: combine partials, decide, emit.
+// finalize: one workgroup per sequence.
 // ---------------------------------------------------------------------------
 struct FinalShared {
   float m[kMaxRows];
@@ -341,14 +476,26 @@ struct FinalShared {
   DrawShared draw;
 };
 
-template <int DT>
-__device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
-                         float kk) {
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
+  __shared__ FinalShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int b = blockIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
+  int d;
+  float T;
+  const int st0 = seq_check(a, b, &d, &T);
+  if (st0) {
+    if (tid == 0) {
+      atomicOr(&a.status[b], st0);
+      a.seqinfo[b] = i32x4{0, 0, 0, 0};
+    }
+    return;
+  }
   const bool greedy = (T == 0.0f);
+  const float kk = greedy ? 0.0f : kLog2e / T;
   for (int j = w; j <= d; j += kWaves) {
-    const f32x4* P = a.partials + (int64_t)(b * R + j) * nc;
+    const f32x4* P = a.partials + ((int64_t)b * R + j) * nc;
     if (greedy) {
       float bv = kNegInf;
       int bi = INT_MAX, nan = 0;
@@ -395,6 +542,7 @@ __device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
       if (l == 0) {
         atomicOr(&a.status[b], st);
         sh.st = st;
+        sh.acc_len = 0;
       }
     } else {
       bool acc = true;
@@ -404,7 +552,7 @@ __device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
           acc = (x == sh.idx[l]);
         } else {
           const unsigned char* row =
-              a.logits + ((int64_t)(b * R + l) * a.V) * Dt<DT>::kBytes;
+              a.logits + ((int64_t)b * R + l) * a.V * Dt<DT>::kBytes;
           px = fast_exp2((load_one<DT>(row, x) - sh.m[l]) * kk) / sh.s[l];
           const float qx = a.q ? a.q[((int64_t)b * a.K + l) * a.V + x] : 1.0f;
           const float u = a.uniforms[(int64_t)b * R + l];
@@ -413,7 +561,7 @@ __device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
       }
       // Wavefront scan of the accept flags: the first rejection ends the run.
       const unsigned long long rej = __ballot(!acc);
-      const int al = rej ? __ffsll((long long)rej) - 1 : d;
+      const int al = rej ? __ffsll((unsigned long long)rej) - 1 : d;
       if (l < R) {
         if (l < al)
           a.out[(int64_t)b * R + l] = x;
@@ -423,7 +571,8 @@ __device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
           a.out[(int64_t)b * R + l] = -1;
       }
       if (a.p_draft && l < a.K)
-        a.p_draft[(int64_t)b * a.K + l] = (!greedy && l < d && l <= al) ? px : -1.0f;
+        a.p_draft[(int64_t)b * a.K + l] =
+            (!greedy && l < d && l <= al) ? px : -1.0f;
       if (l == 0) {
         a.nem[b] = al + 1;
         sh.acc_len = al;
@@ -432,121 +581,28 @@ __device__ void finalize(const Args& a, FinalShared& sh, int b, int d, float T,
     }
   }
   __syncthreads();
-  if (sh.st == 0 && !greedy) {
-    const int al = sh.acc_len;
-    if (al < d && a.q != nullptr) {
-      // Residual max(0, p - q) needs p over the whole row: pass 2 draws it.
-      if (tid == 0)
-        a.seqinfo[b] = i32x4{al + 1, __float_as_int(sh.m[al]),
-                             __float_as_int(sh.s[al]), __float_as_int(kk)};
-    } else {
-      const int excl = (al < d) ? a.draft[(int64_t)b * a.K + al] : -1;
-      const float u = a.uniforms[(int64_t)b * R + a.K];
-      const int tok = draw_row<DT, false>(a, sh.draw, b, al, excl, sh.m[al],
-                                          sh.s[al], kk, u, nc);
-      if (tid == 0) a.out[(int64_t)b * R + al] = tok;
-    }
+  const int al = sh.acc_len;
+  const bool residual = sh.st == 0 && !greedy && al < d && a.q != nullptr;
+  if (tid == 0)
+    a.seqinfo[b] = residual ? i32x4{al + 1, __float_as_int(sh.m[al]),
+                                    __float_as_int(sh.s[al]), __float_as_int(kk)}
+                            : i32x4{0, 0, 0, 0};
+  if (sh.st == 0 && !greedy && !residual) {
+    const int excl = (al < d) ? a.draft[(int64_t)b * a.K + al] : -1;
+    const float u = a.uniforms[(int64_t)b * R + a.K];
+    const int tok = draw_row<DT, VP, false>(a, sh.draw, b, al, excl, sh.m[al],
+                                            sh.s[al], kk, u);
+    if (tid == 0) a.out[(int64_t)b * R + al] = tok;
   }
-  if (tid == 0) a.ctr1[b] = 0u;  // leave the counter zero for the next call
 }
 
+// ---------------------------------------------------------------------------
+// residual (q given): chunk sums of max(0, p - q) over the rejected row, then
+// one workgroup per sequence draws from them.
+// ---------------------------------------------------------------------------
 template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void verify_pass1(Args a) {
-  __shared__ f32x4 red[kWaves];
-  __shared__ int last_flag;
-  __shared__ FinalShared fsh;
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1;
-  const int row = blockIdx.x / a.nchunks;
-  const int c = blockIdx.x - row * a.nchunks;
-  const int b = row / R, j = row - b * R;
-  int d;
-  float T;
-  const int st = seq_check(a, b, &d, &T);
-  if (st) {
-    if (j == 0 && c == 0 && tid == 0) atomicOr(&a.status[b], st);
-    return;
-  }
-  if (j > d) return;
-  const bool greedy = (T == 0.0f);
-  const float kk = greedy ? 0.0f : kLog2e / T;
-  const int cstart = c * kChunk<DT>;
-  const unsigned char* rowp = a.logits + ((int64_t)row * a.V) * Dt<DT>::kBytes;
-  u32x4 raw[kLoads];
-  load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
-
-  if (greedy) {
-    float bv = kNegInf;
-    int bi = INT_MAX, nan = 0;
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const float v = elem<DT>(raw[it], k);
-        if (v > bv) {
-          bv = v;
-          bi = elem_index<DT, VP>(cstart, tid, it, k);
-        }
-        nan |= (v != v);
-      }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
-    nan = wave_or(nan);
-    if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
-    __syncthreads();
-    if (tid == 0) {
-      f32x4 p = red[0];
-      float pv = p.x;
-      int pi = __float_as_int(p.w);
-      float pn = p.y;
-      for (int i = 1; i < kWaves; ++i) {
-        argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
-        pn = fmaxf(pn, red[i].y);
-      }
-      red[0] = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
-    }
-  } else {
-    float mx = kNegInf;
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) mx = fmaxf(mx, elem<DT>(raw[it], k));
-    const float base = (mx == kNegInf) ? 0.0f : mx;
-    float s = 0.0f;
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k)
-        s += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      lse_merge(mx, s, __shfl_xor(mx, o, kWave), __shfl_xor(s, o, kWave), kk);
-    if (l == 0) red[w] = f32x4{mx, s, 0.0f, 0.0f};
-    __syncthreads();
-    if (tid == 0) {
-      float pm = red[0].x, ps = red[0].y;
-      for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
-      red[0] = f32x4{pm, ps, 0.0f, 0.0f};
-    }
-  }
-  if (tid == 0) {
-    a.partials[(int64_t)row * a.nchunks + c] = red[0];
-    __threadfence();  // release the partial before counting it
-    const unsigned old = atomicAdd(&a.ctr1[b], 1u);
-    last_flag = (old == (unsigned)((d + 1) * a.nchunks - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();  // acquire: every partial of this sequence is visible
-  finalize<DT>(a, fsh, b, d, T, kk);
-}
-
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void verify_residual(Args a) {
+__global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
   __shared__ float red[kWaves];
-  __shared__ int last_flag;
-  __shared__ DrawShared dsh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int nc = a.nchunks;
   const int b = blockIdx.x / nc;
@@ -560,19 +616,33 @@ __global__ __launch_bounds__(kThreads) void verify_residual(Args a) {
   const int R = a.K + 1;
   const int cstart = c * kChunk<DT>;
   const unsigned char* rowp =
-      a.logits + ((int64_t)(b * R + r) * a.V) * Dt<DT>::kBytes;
-  const float* qrow = a.q + (int64_t)(b * a.K + r) * a.V;
+      a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
+  const float* qrow = a.q + ((int64_t)b * a.K + r) * a.V;
   u32x4 raw[kLoads];
   load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
   float s = 0.0f;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
+    if constexpr (VP) {
+      const int i0 = cstart + (it * kThreads + tid) * kVec<DT>;
+      if (i0 < a.V) {
 #pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const int i = elem_index<DT, VP>(cstart, tid, it, k);
-      if (i < a.V) {
-        const float qi = __builtin_nontemporal_load(qrow + i);
-        s += fmaxf(0.0f, fast_exp2((elem<DT>(raw[it], k) - m) * kk) * invS - qi);
+        for (int h = 0; h < kVec<DT> / 4; ++h) {
+          const f32x4 qv = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(qrow + i0) + h);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            s += fmaxf(0.0f, fast_exp2((elem<DT>(raw[it], 4 * h + k) - m) * kk) *
+                                     invS - qv[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const int i = elem_index<DT, false>(cstart, tid, it, k);
+        if (i < a.V)
+          s += fmaxf(0.0f, fast_exp2((elem<DT>(raw[it], k) - m) * kk) * invS -
+                               qrow[i]);
       }
     }
   }
@@ -583,41 +653,41 @@ __global__ __launch_bounds__(kThreads) void verify_residual(Args a) {
     float t = 0.0f;
     for (int i = 0; i < kWaves; ++i) t += red[i];
     a.rpart[(int64_t)b * nc + c] = t;
-    __threadfence();
-    const unsigned old = atomicAdd(&a.ctr2[b], 1u);
-    last_flag = (old == (unsigned)(nc - 1));
   }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+}
+
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
+  __shared__ DrawShared sh;
+  __shared__ float total_sh;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int b = blockIdx.x;
+  const int nc = a.nchunks;
+  const i32x4 info = a.seqinfo[b];
+  if (info.x == 0) return;
+  const int r = info.x - 1;
+  const float m = __int_as_float(info.y), S = __int_as_float(info.z);
+  const float kk = __int_as_float(info.w);
   if (w == 0) {
     float tot = 0.0f;
-    for (int cc = l; cc < nc; cc += kWave) tot += a.rpart[(int64_t)b * nc + cc];
+    for (int c = l; c < nc; c += kWave) tot += a.rpart[(int64_t)b * nc + c];
     tot = wave_sum(tot);
-    if (l == 0) red[0] = tot;
+    if (l == 0) total_sh = tot;
   }
   __syncthreads();
-  const float total = red[0];
-  const float u = a.uniforms[(int64_t)b * R + a.K];
-  int tok;
-  if (total > 0.0f) {
-    tok = draw_row<DT, true>(a, dsh, b, r, -1, m, S, kk, u, nc);
-  } else {
-    // max(0, p - q) vanished everywhere (p == q): draw from p itself.
-    tok = draw_row<DT, false>(a, dsh, b, r, -1, m, S, kk, u, nc);
-  }
-  if (tid == 0) {
-    a.out[(int64_t)b * R + r] = tok;
-    a.seqinfo[b] = i32x4{0, 0, 0, 0};
-    a.ctr2[b] = 0u;
-  }
+  const float u = a.uniforms[(int64_t)b * (a.K + 1) + a.K];
+  // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
+  const int tok = total_sh > 0.0f
+                      ? draw_row<DT, VP, true>(a, sh, b, r, -1, m, S, kk, u)
+                      : draw_row<DT, VP, false>(a, sh, b, r, -1, m, S, kk, u);
+  if (tid == 0) a.out[(int64_t)b * (a.K + 1) + r] = tok;
 }
 
 // ---------------------------------------------------------------------------
 // Workspace layout (bytes, each region 256-byte aligned).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t partials, seqinfo, ctr1, ctr2, rpart, total;
+  size_t partials, seqinfo, rpart, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -635,34 +705,40 @@ WsLayout ws_layout(int B, int K, int V) {
   o = align256(o + (size_t)B * (K + 1) * nc * sizeof(f32x4));
   L.seqinfo = o;
   o = align256(o + (size_t)B * sizeof(i32x4));
-  L.ctr1 = o;
-  o = align256(o + (size_t)B * sizeof(unsigned));
-  L.ctr2 = o;
-  o = align256(o + (size_t)B * sizeof(unsigned));
   L.rpart = o;
   o = align256(o + (size_t)B * nc * sizeof(float));
   L.total = o;
   return L;
 }
 
-__global__ void fill_zero_u32x4(u32x4* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = u32x4{0u, 0u, 0u, 0u};
-}
+// Workgroups the stats grid aims for: enough to keep every CU busy with
+// several resident workgroups.
+constexpr int64_t kTargetWorkgroups = 4096;
 
 template <int DT, bool VP>
-int launch(const Args& a, hipStream_t s) {
-  const int64_t grid1 = (int64_t)a.B * (a.K + 1) * a.nchunks;
+int launch(Args a, hipStream_t s) {
+  const int R = a.K + 1;
+  const int64_t base = (int64_t)a.B * a.nchunks;
+  int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
+  a.rows_per_wg = (R + ngroups - 1) / ngroups;
+  a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
+  const int64_t grid1 = base * a.ngroups;
   if (grid1 > INT_MAX) return set_error(SS_EINVAL, "spec_verify: grid too large");
-  hipLaunchKernelGGL((verify_pass1<DT, VP>), dim3((unsigned)grid1), dim3(kThreads),
+  hipLaunchKernelGGL((verify_stats<DT, VP>), dim3((unsigned)grid1), dim3(kThreads),
                      0, s, a);
-  int rc = check_launch("spec_verify pass 1");
+  int rc = check_launch("spec_verify stats");
+  if (rc != SS_OK) return rc;
+  hipLaunchKernelGGL((verify_finalize<DT, VP>), dim3((unsigned)a.B), dim3(kThreads),
+                     0, s, a);
+  rc = check_launch("spec_verify finalize");
   if (rc != SS_OK || a.q == nullptr) return rc;
-  const int64_t grid2 = (int64_t)a.B * a.nchunks;
-  hipLaunchKernelGGL((verify_residual<DT, VP>), dim3((unsigned)grid2),
+  hipLaunchKernelGGL((verify_residual_sums<DT, VP>), dim3((unsigned)base),
                      dim3(kThreads), 0, s, a);
-  return check_launch("spec_verify residual pass");
+  rc = check_launch("spec_verify residual sums");
+  if (rc != SS_OK) return rc;
+  hipLaunchKernelGGL((verify_residual_draw<DT, VP>), dim3((unsigned)a.B),
+                     dim3(kThreads), 0, s, a);
+  return check_launch("spec_verify residual draw");
 }
 
 }  // namespace
@@ -673,19 +749,6 @@ using namespace specsam;
 extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
   if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV) return 0;
   return ws_layout(B, K, V).total;
-}
-
-extern "C" int ss_verify_workspace_init(void* workspace, size_t ws_bytes,
-                                        void* stream) {
-  if (!workspace || ((uintptr_t)workspace & 15))
-    return set_error(SS_EINVAL, "ss_verify_workspace_init: workspace must be "
-                                "non-null and 16-byte aligned");
-  const size_t n = ws_bytes / 16;
-  if (n == 0) return SS_OK;
-  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(fill_zero_u32x4, dim3(grid), dim3(256), 0, as_stream(stream),
-                     reinterpret_cast<u32x4*>(workspace), n);
-  return check_launch("ss_verify_workspace_init");
 }
 
 extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
@@ -717,6 +780,8 @@ extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
   a.K = K;
   a.V = V;
   a.nchunks = nchunks_for(V, dtype);
+  a.rows_per_wg = 1;
+  a.ngroups = K + 1;
   a.draft = draft;
   a.draft_len = draft_len;
   a.q = q;
@@ -728,8 +793,6 @@ extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
   a.status = status;
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
-  a.ctr1 = reinterpret_cast<unsigned*>(ws + L.ctr1);
-  a.ctr2 = reinterpret_cast<unsigned*>(ws + L.ctr2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
   const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0) &&

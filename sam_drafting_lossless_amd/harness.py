@@ -21,8 +21,8 @@ def lib():
                                "`python -m sam_drafting_lossless_amd.build`")
         L = ctypes.CDLL(HARNESS_PATH)
         P, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
-        L.hs_boost_step.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P, P,
-                                    f32, P]
+        L.hs_boost_step.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P,
+                                    P, P, f32, P]
         L.hs_boost_step.restype = i32
         L.hs_read_bw.argtypes = [P, sz, P, i32, P]
         L.hs_read_bw.restype = i32
@@ -54,7 +54,9 @@ class Booster:
         dev = gt.device
         self.B, self.R, self.V, self.boost, self.dtype = B, R, V, boost, dtype
         self.gt = gt.contiguous()
-        self.ncommit = torch.as_tensor(n0, dtype=torch.int32, device=dev).clone()
+        n0 = torch.as_tensor(n0, dtype=torch.int32, device=dev)
+        self.ncommit = [n0.clone(), n0.clone()]  # ping-pong
+        self.calls = 0
         self.saved_pos = torch.full((nslots, B, R), -1, dtype=torch.int32,
                                     device=dev)
         self.saved_val = torch.zeros((nslots, B, R), dtype=torch.float32,
@@ -66,9 +68,12 @@ class Booster:
         m = None
         if self.mask is not None and step_index is not None:
             m = self.mask[step_index].data_ptr()
+        nin = self.ncommit[self.calls % 2]
+        nout = self.ncommit[(self.calls + 1) % 2]
+        self.calls += 1
         rc = lib().hs_boost_step(
             slot.data_ptr(), self.dtype, self.B, self.R, self.V,
-            self.gt.data_ptr(), self.gt.shape[1], self.ncommit.data_ptr(),
+            self.gt.data_ptr(), self.gt.shape[1], nin.data_ptr(), nout.data_ptr(),
             None if nem_prev is None else nem_prev.data_ptr(),
             self.saved_pos[slot_index].data_ptr(),
             self.saved_val[slot_index].data_ptr(), m, float(self.boost), _s(stream))

@@ -130,6 +130,13 @@ def test_status_words_match_oracle():
     g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T)
     compare_verify(*g, r, T, None, what="status")
     assert g[3][6] == 0 and g[1][6] == K + 1
+    # temperatures: denormal, smallest normal, inf, NaN
+    Tt = np.array([1e-40, np.finfo(np.float32).tiny, np.inf, np.nan], np.float32)
+    g, r = _run(torch.zeros((4, K + 1, V), device="cuda"),
+                np.zeros((4, K), np.int32), np.zeros(4, np.int32), Tt,
+                np.zeros((4, K + 1), np.float32))
+    assert g[3].tolist() == r.status.tolist() == [
+        ssl.ST_TEMPERATURE, 0, ssl.ST_TEMPERATURE, ssl.ST_TEMPERATURE]
     # T > 0 without uniforms
     g, r = _run(torch.from_numpy(x[6:]).cuda(), draft[6:], dl[6:],
                 np.ones(1, np.float32), None)

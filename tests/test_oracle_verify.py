@@ -274,6 +274,12 @@ def test_status_bits():
     assert (r.out_tokens[:5] == -1).all() and r.num_emitted[5] == K + 1
     r = oracle.verify(lg[5:], draft[5:], dl[5:], np.ones(1, np.float32), None)
     assert r.status.tolist() == [oracle.ST_NO_UNIFORMS]
+    # positive temperatures below the smallest normal float are rejected
+    tiny = np.array([1e-40, np.finfo(np.float32).tiny, np.inf], np.float32)
+    u = np.zeros((3, K + 1), np.float32)
+    r = oracle.verify(lg[:3] * 0, np.zeros((3, K), np.int32),
+                      np.zeros(3, np.int32), tiny, u)
+    assert r.status.tolist() == [oracle.ST_TEMPERATURE, 0, oracle.ST_TEMPERATURE]
 
 
 # ------------------------------------------------------- whole-step greedy ---
