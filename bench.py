@@ -123,7 +123,7 @@ def main():
     torch.cuda.set_device(dev)
     cfg = synth.config(3)
     B, K, V, R = cfg.B, cfg.K, cfg.V, cfg.K + 1
-    total = args.warmup + 2 * args.steps
+    total = args.warmup + 3 * args.steps
     t_setup = time.perf_counter()
     gt_h = synth.token_streams(cfg, total)
     gt = torch.as_tensor(gt_h, device=dev)
@@ -141,32 +141,70 @@ def main():
     booster = harness.Booster(gt, np.full(B, H, np.int32), R, V, RING,
                               cfg.boost, ssl.DTYPE_F32)
     ws = ssl.verify_workspace(B, K, V, dev)
-    draft = torch.empty((B, K), dtype=torch.int32, device=dev)
+    drafts = [torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2)]
     mlen = torch.empty(B, dtype=torch.int32, device=dev)
-    dl_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    dl_hist = torch.zeros((total + 1, B), dtype=torch.int32, device=dev)
     nem_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
     out = torch.empty((B, R), dtype=torch.int32, device=dev)
     pd = torch.empty((B, K), dtype=torch.float32, device=dev)
     status = torch.zeros(B, dtype=torch.int32, device=dev)
+    st.draft(K, drafts[0], dl_hist[0], mlen)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    def step(s, evs=None):
-        """One step. With evs (5 events), events are recorded between the
-        kernels so each call's GPU duration can be read back."""
+    # Direct C calls with precomputed device addresses: the timed loop does
+    # argument marshalling only (the checked wrappers cost as much host time
+    # as a whole GPU step).
+    L = ssl.lib()
+    H_ = harness.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    ring_p = [t.data_ptr() for t in ring]
+    draft_p = [t.data_ptr() for t in drafts]
+    dl0, nem0, u0 = dl_hist.data_ptr(), nem_hist.data_ptr(), u_all.data_ptr()
+    rowB, rowU = B * 4, B * R * 4
+    temp_p, st_p, out_p, pd_p = temp.data_ptr(), st.buf.data_ptr(), out.data_ptr(), pd.data_ptr()
+    status_p, mlen_p, ws_p, ws_n = status.data_ptr(), mlen.data_ptr(), ws.data_ptr(), ws.numel()
+    gt_p, gt_ld = booster.gt.data_ptr(), booster.gt.shape[1]
+    nc_p = [t.data_ptr() for t in booster.ncommit]
+    sp_p = [booster.saved_pos[i].data_ptr() for i in range(RING)]
+    sv_p = [booster.saved_val[i].data_ptr() for i in range(RING)]
+
+    def boost(s):
         slot = s % RING
-        rec = (lambda k: evs[k].record()) if evs is not None else (lambda k: None)
-        rec(0)
-        st.draft(K, draft, dl_hist[s], mlen)
-        rec(1)
-        booster.step(ring[slot], slot, nem_hist[s - 1] if s > 0 else None)
-        rec(2)
-        ssl.spec_verify(ring[slot], draft, dl_hist[s], temp, u_all[s],
-                        workspace=ws, out_tokens=out, num_emitted=nem_hist[s],
-                        p_draft=pd, status=status)
-        rec(3)
-        st.extend(out, nem_hist[s])
-        rec(4)
+        rc = H_.hs_boost_step(ring_p[slot], 0, B, R, V, gt_p, gt_ld, nc_p[s % 2],
+                              nc_p[(s + 1) % 2], nem0 + (s - 1) * rowB if s else None,
+                              sp_p[slot], sv_p[slot], None, float(cfg.boost), stream)
+        if rc:
+            raise RuntimeError("hs_boost_step failed")
+
+    def fused(s):
+        rc = L.spec_step(ring_p[s % RING], 0, B, K, V, draft_p[s % 2], dl0 + s * rowB,
+                         temp_p, u0 + s * rowU, st_p, max_len, out_p, nem0 + s * rowB,
+                         pd_p, status_p, draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB,
+                         mlen_p, ws_p, ws_n, stream)
+        if rc:
+            raise RuntimeError("spec_step failed: " + L.ss_last_error_string().decode())
+
+    def separate(s):
+        # The same step as three calls: verify, extend + next draft.
+        rc = L.spec_verify(ring_p[s % RING], 0, B, K, V, draft_p[s % 2], dl0 + s * rowB,
+                           None, temp_p, u0 + s * rowU, out_p, nem0 + s * rowB, pd_p,
+                           status_p, ws_p, ws_n, stream)
+        rc |= L.sam_extend_draft(st_p, B, max_len, out_p, R, nem0 + s * rowB, K,
+                                 draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
+                                 stream)
+        if rc:
+            raise RuntimeError("separate step failed: " + L.ss_last_error_string().decode())
+
+    def step(s, evs=None, path=fused):
+        if evs is not None:
+            evs[0].record()
+        boost(s)
+        if evs is not None:
+            evs[1].record()
+        path(s)
+        if evs is not None:
+            evs[2].record()
 
     for s in range(args.warmup):
         step(s)
@@ -181,21 +219,31 @@ def main():
     # Per-call durations from HIP events recorded on the launch stream (a
     # second pass over the next `steps` steps; events add small gaps, so this
     # pass is not the one `value` comes from).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-           for _ in range(args.steps)]
     first_ev = args.warmup + args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.steps)]
     for i in range(args.steps):
         step(first_ev + i, evs[i])
     torch.cuda.synchronize()
-    dur = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs])
-    draft_us, harness_us, verify_us, extend_us = (1e3 * dur.mean(axis=0)).tolist()
+    dur = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in evs])
+    harness_us, step_kernel_us = (1e3 * dur.mean(axis=0)).tolist()
+
+    # The same steps issued as separate library calls (verify, then extend +
+    # draft), for comparison.
+    first_sep = first_ev + args.steps
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(first_sep + i, path=separate)
+    torch.cuda.synchronize()
+    separate_steps_s = args.steps / (time.perf_counter() - t1)
 
     ms_per_step = elapsed * 1e3 / args.steps
-    dl = dl_hist[first_ev:].cpu().numpy()
+    dl = dl_hist[first_ev:first_ev + args.steps].cpu().numpy()
     nem = nem_hist[args.warmup:first_ev].cpu().numpy()
     rows_per_launch = float((dl + 1).sum(axis=1).mean())
     bytes_per_launch = rows_per_launch * V * 4
-    achieved = bytes_per_launch / (verify_us * 1e-6) / 1e9
+    achieved = bytes_per_launch / (step_kernel_us * 1e-6) / 1e9
     if int(status.cpu().abs().sum()) != 0 or int(st.status().abs().sum()) != 0:
         print("status words are non-zero: the run is invalid", file=sys.stderr)
         sys.exit(1)
@@ -232,11 +280,11 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": _traffic_from_profile(rows_per_launch, V)},
         "cpu_baseline": cpu,
-        "verify_avg_us": verify_us,
-        "sam_draft_avg_us": draft_us,
-        "sam_extend_avg_us": extend_us,
+        "path": "spec_step (one kernel per step: verify + SAM extend + next draft)",
+        "step_kernel_avg_us": step_kernel_us,
         "harness_boost_avg_us": harness_us,
-        "verify_rows_per_launch": rows_per_launch,
+        "separate_calls_steps_per_s": separate_steps_s,
+        "verified_rows_per_launch": rows_per_launch,
         "verify_bytes_per_launch": bytes_per_launch,
         "mean_tokens_per_step": float(nem.mean()),
         "hbm_read_probe_GBps": probe,

@@ -76,9 +76,10 @@ const char* ss_last_error_string(void);
  * Verification ([P2] §2.2, [P3] "贪婪采样" / "拒绝采样", [P1] §1.1, §3.1.2)
  * ========================================================================= */
 
-/* Bytes of workspace spec_verify needs for (B, K, V); 0 if unsupported.
- * The workspace is scratch owned by the caller: no initialisation is needed
- * and its contents between calls do not matter. */
+/* Bytes of workspace spec_verify / spec_step need for (B, K, V); 0 if
+ * unsupported. The workspace is scratch owned by the caller (256-byte
+ * aligned): it needs no initialisation, its contents between calls do not
+ * matter, and one buffer serves any call whose size fits. */
 size_t ss_verify_workspace_bytes(int B, int K, int V);
 
 /*
@@ -114,7 +115,7 @@ size_t ss_verify_workspace_bytes(int B, int K, int V);
  *   p_draft     [B, K] float or NULL: p_j(x_j) for j < num_emitted and j < d
  *               at T > 0; -1 elsewhere.
  *   status      [B] int32, OR-ed with SS_ST_* bits.
- *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), 16-byte
+ *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), 256-byte
  *               aligned.
  * Limits: 1 <= B, 1 <= K <= SS_MAX_K, 1 <= V <= 2^21. A temperature that is
  * positive but below the smallest normal float is reported as
@@ -127,6 +128,29 @@ int spec_verify(const void* logits, int dtype, int B, int K, int V,
                 int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
                 int32_t* status, void* workspace, size_t ws_bytes,
                 void* stream);
+
+/*
+ * spec_step — one whole speculative step in one pass over the logits:
+ * spec_verify with one-hot drafts (q = NULL), then, for each sequence, the
+ * emitted tokens extend its automaton (sam_extend) and the next draft is
+ * taken from it (sam_draft) — [P1] §1.1: the dynamic SAM is updated after each
+ * verified token and drafts from its link walk.
+ *   draft, draft_len    this step's drafts (from sam_draft or the previous
+ *                       spec_step).
+ *   sam_state, max_len  the automata (see below).
+ *   next_draft [B, K], next_draft_len [B], next_match_len [B]: the drafts for
+ *                       the next step; must not alias draft / draft_len.
+ * Other arguments as spec_verify. A sequence flagged in this call is not
+ * extended; its next draft comes from its unchanged automaton. Status bits of
+ * the automaton itself go to the automaton's own status word (sam_status).
+ */
+int spec_step(const void* logits, int dtype, int B, int K, int V,
+              const int32_t* draft, const int32_t* draft_len,
+              const float* temperature, const float* uniforms, void* sam_state,
+              int max_len, int32_t* out_tokens, int32_t* num_emitted,
+              float* p_draft, int32_t* status, int32_t* next_draft,
+              int32_t* next_draft_len, int32_t* next_match_len,
+              void* workspace, size_t ws_bytes, void* stream);
 
 /* ========================================================================= *
  * Dynamic suffix automaton ([P1] §1.1, [P4] §3)
@@ -169,6 +193,12 @@ int sam_extend(void* state, int B, int max_len, const int32_t* tokens,
  */
 int sam_draft(const void* state, int B, int max_len, int K, int32_t* draft,
               int32_t* draft_len, int32_t* match_len, void* stream);
+
+/* sam_extend followed by sam_draft in one launch (per-step use). */
+int sam_extend_draft(void* state, int B, int max_len, const int32_t* tokens,
+                     int ld_tokens, const int32_t* counts, int K,
+                     int32_t* draft, int32_t* draft_len, int32_t* match_len,
+                     void* stream);
 
 /* Copies the sticky per-sequence status words to status_out [B] int32. */
 int sam_status(const void* state, int B, int max_len, int32_t* status_out,

@@ -56,6 +56,11 @@ def lib():
     L.spec_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                               P, sz, P]
     L.spec_verify.restype = i32
+    L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, P,
+                            P, P, P, P, P, sz, P]
+    L.spec_step.restype = i32
+    L.sam_extend_draft.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P]
+    L.sam_extend_draft.restype = i32
     L.sam_state_bytes.argtypes = [i32, i32]
     L.sam_state_bytes.restype = sz
     L.sam_hash_slots.argtypes = [i32]
@@ -105,7 +110,8 @@ def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
 
 
 def verify_workspace(B: int, K: int, V: int, device=None):
-    """A workspace tensor (uint8) for spec_verify."""
+    """A workspace tensor (uint8) for spec_verify / spec_step calls of this
+    size (or smaller)."""
     n = ss_verify_workspace_bytes(B, K, V)
     if n == 0:
         raise SpecSamError(f"unsupported sizes B={B} K={K} V={V}")
@@ -158,6 +164,63 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
     return out_tokens, num_emitted, p_draft, status
 
 
+def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
+              workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
+              status=None, next_draft=None, next_draft_len=None,
+              next_match_len=None, stream=None):
+    """One fused step (see include/specsam.h): verify the drafts, extend each
+    automaton of `state` (a SamState) with the emitted tokens, and draft for
+    the next step. Returns (out_tokens, num_emitted, p_draft, status,
+    next_draft, next_draft_len, next_match_len)."""
+    if logits.dim() != 3:
+        raise SpecSamError("logits must be [B, K+1, V]")
+    B, R, V = logits.shape
+    K = R - 1
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(logits.dtype)
+    if dt is None:
+        raise SpecSamError("logits must be float32 or bfloat16")
+    if state.B != B:
+        raise SpecSamError("state holds a different number of sequences")
+    dev = logits.device
+    i32 = torch.int32
+    if workspace is None:
+        workspace = verify_workspace(B, K, V, dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, R), dtype=i32, device=dev)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=i32, device=dev)
+    if p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.zeros(B, dtype=i32, device=dev)
+    if next_draft is None:
+        next_draft = torch.empty((B, K), dtype=i32, device=dev)
+    if next_draft_len is None:
+        next_draft_len = torch.empty(B, dtype=i32, device=dev)
+    if next_match_len is None:
+        next_match_len = torch.empty(B, dtype=i32, device=dev)
+    args = (
+        _dev(logits, "logits"), dt, B, K, V,
+        _dev(draft, "draft", i32, (B, K)),
+        _dev(draft_len, "draft_len", i32, (B,)),
+        _dev(temperature, "temperature", torch.float32, (B,)),
+        None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
+                                           (B, R)),
+        _dev(state.buf, "state", torch.uint8), state.max_len,
+        _dev(out_tokens, "out_tokens", i32, (B, R)),
+        _dev(num_emitted, "num_emitted", i32, (B,)),
+        _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _dev(status, "status", i32, (B,)),
+        _dev(next_draft, "next_draft", i32, (B, K)),
+        _dev(next_draft_len, "next_draft_len", i32, (B,)),
+        _dev(next_match_len, "next_match_len", i32, (B,)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream))
+    _check(lib().spec_step(*args), "spec_step")
+    return (out_tokens, num_emitted, p_draft, status, next_draft,
+            next_draft_len, next_match_len)
+
+
 # ------------------------------------------------------- suffix automaton ----
 def sam_state_bytes(B: int, max_len: int) -> int:
     return int(lib().sam_state_bytes(B, max_len))
@@ -196,6 +259,28 @@ def sam_draft(state, B: int, max_len: int, K: int, draft=None, draft_len=None,
                            _dev(draft_len, "draft_len", torch.int32, (B,)),
                            _dev(match_len, "match_len", torch.int32, (B,)),
                            _stream(stream)), "sam_draft")
+    return draft, draft_len, match_len
+
+
+def sam_extend_draft(state, B: int, max_len: int, tokens, counts, K: int,
+                     draft=None, draft_len=None, match_len=None, stream=None):
+    dev = state.device
+    if tokens.dim() != 2 or tokens.shape[0] != B:
+        raise SpecSamError("tokens must be [B, ld]")
+    if draft is None:
+        draft = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if draft_len is None:
+        draft_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if match_len is None:
+        match_len = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(lib().sam_extend_draft(
+        _dev(state, "state", torch.uint8), B, max_len,
+        _dev(tokens, "tokens", torch.int32), int(tokens.shape[1]),
+        _dev(counts, "counts", torch.int32, (B,)), K,
+        _dev(draft, "draft", torch.int32, (B, K)),
+        _dev(draft_len, "draft_len", torch.int32, (B,)),
+        _dev(match_len, "match_len", torch.int32, (B,)), _stream(stream)),
+        "sam_extend_draft")
     return draft, draft_len, match_len
 
 
@@ -253,6 +338,11 @@ class SamState:
               stream=None):
         return sam_draft(self.buf, self.B, self.max_len, K, draft, draft_len,
                          match_len, stream)
+
+    def extend_draft(self, tokens, counts, K: int, draft=None, draft_len=None,
+                     match_len=None, stream=None):
+        return sam_extend_draft(self.buf, self.B, self.max_len, tokens, counts,
+                                K, draft, draft_len, match_len, stream)
 
     def status(self, out=None, stream=None):
         return sam_status(self.buf, self.B, self.max_len, out, stream)

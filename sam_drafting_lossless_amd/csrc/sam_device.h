@@ -1,0 +1,264 @@
+// Device-side suffix automaton: layout, Blumer extension and drafting, shared
+// by the stand-alone automaton kernels (sam.hip) and the fused step kernel
+// (verify.hip).
+//
+// Method ([P1] cann-recipes-train article §1.1 "SAM 原理"; [P4] SAM-Decoding
+// summary §3 "Suffix Automaton Construction", "Drafting with Suffix
+// Automaton", "Update of Suffix Automaton"): states are endpos classes with
+// len, link and min_endpos (first end position of the state's strings); every
+// verified token extends the automaton by Blumer's online construction; the
+// draft follows suffix links from the state of the whole text to the first
+// state with an outgoing transition and copies the tokens that followed that
+// state's first occurrence.
+//
+// Layout (one contiguous block per sequence, 256-byte aligned):
+//   header  int32[16]: n, last, num_states, num_edges, status, max_len, V,
+//           hash_slots, magic, ...
+//   states  int4[2*max_len]: (len, link, min_endpos, first_edge); one 16-byte
+//           load brings every field a step of the construction reads.
+//   text    int32[max_len]: committed tokens (the draft source).
+//   hash    int4[hash_slots]: (src, token, dst, next) open-addressing table
+//           keyed by (src, token), in 128-byte buckets of 8 rows probed
+//           linearly; `next` chains a state's transitions so a clone can copy
+//           them. hash_slots = next power of two >= 6*max_len keeps the load
+//           at most 1/2 for the at most 3*max_len transitions.
+//
+// Execution: one wavefront per sequence. The construction is a chain of
+// dependent loads, so lanes do not split it; they cooperate on each hash
+// probe (8 lanes read a whole bucket in one request, a ballot finds the key or
+// the first empty row), and the next state record is loaded alongside each
+// probe. Every lane performs the same stores with the same values, so each
+// lane reads its own writes (no cross-lane ordering through memory is
+// assumed).
+#pragma once
+
+#include "internal.h"
+
+namespace specsam {
+
+constexpr int kBucket = 8;  // rows per 128-byte bucket
+constexpr int kSamMagic = 0x53414d31;
+
+struct SamLayout {
+  size_t states, text, slots, block;
+  int hash_slots;
+};
+
+__host__ __device__ inline size_t sam_al256(size_t x) {
+  return (x + 255) & ~(size_t)255;
+}
+
+__host__ __device__ inline SamLayout sam_layout(int max_len) {
+  SamLayout L;
+  const size_t want = (size_t)6 * (size_t)max_len;
+  size_t h = 64;
+  while (h < want) h <<= 1;
+  L.hash_slots = (int)h;
+  L.states = 64;
+  L.text = L.states + (size_t)2 * max_len * 16;
+  L.slots = sam_al256(L.text + (size_t)max_len * 4);
+  L.block = sam_al256(L.slots + h * 16);
+  return L;
+}
+
+enum SamHdr { H_N = 0, H_LAST, H_STATES, H_EDGES, H_STATUS, H_MAXLEN, H_V,
+              H_SLOTS, H_MAGIC };
+
+struct SamSeq {
+  int* hdr;
+  i32x4* st;
+  int* text;
+  i32x4* slots;
+};
+
+__device__ __forceinline__ SamSeq sam_seq(unsigned char* base, int b,
+                                          const SamLayout& L) {
+  unsigned char* p = base + (size_t)b * L.block;
+  return SamSeq{reinterpret_cast<int*>(p), reinterpret_cast<i32x4*>(p + L.states),
+                reinterpret_cast<int*>(p + L.text),
+                reinterpret_cast<i32x4*>(p + L.slots)};
+}
+
+__device__ __forceinline__ unsigned sam_bucket(int s, int c, unsigned bmask) {
+  unsigned long long k = ((unsigned long long)(unsigned)s << 32) | (unsigned)c;
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return (unsigned)k & bmask;
+}
+
+struct SamProbe {
+  int slot;  // row of (s, c), or the first empty row in probe order; -1 if full
+  bool found;
+  int dst;
+};
+
+// Wave-cooperative lookup of (s, c). Uniform in, uniform out.
+__device__ __forceinline__ SamProbe sam_probe(const i32x4* slots, unsigned bmask,
+                                              int s, int c) {
+  const int l = lane_id();
+  unsigned bk = sam_bucket(s, c, bmask);
+  for (unsigned it = 0; it <= bmask; ++it) {
+    i32x4 v = i32x4{-2, -2, -2, -2};
+    if (l < kBucket) v = slots[(size_t)bk * kBucket + l];
+    const bool m = (l < kBucket) && v.x == s && v.y == c;
+    const bool e = (l < kBucket) && v.x == -1;
+    const unsigned long long bal = __ballot(m || e);
+    if (bal) {
+      const int f = __ffsll((unsigned long long)bal) - 1;
+      SamProbe r;
+      r.slot = (int)(bk * kBucket) + f;
+      r.found = (__ballot(m) >> f) & 1ull;
+      r.dst = __shfl(v.z, f, kWave);
+      return r;
+    }
+    bk = (bk + 1) & bmask;
+  }
+  return SamProbe{-1, false, -1};
+}
+
+struct SamHdrRegs {
+  int n, last, nstates, nedges, status, max_len, V, slots;
+};
+
+__device__ __forceinline__ SamHdrRegs sam_load_header(const SamSeq& S) {
+  const i32x4 h0 = reinterpret_cast<const i32x4*>(S.hdr)[0];
+  const i32x4 h1 = reinterpret_cast<const i32x4*>(S.hdr)[1];
+  return SamHdrRegs{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+}
+
+__device__ __forceinline__ void sam_store_header(const SamSeq& S,
+                                                 const SamHdrRegs& h) {
+  reinterpret_cast<i32x4*>(S.hdr)[0] = i32x4{h.n, h.last, h.nstates, h.nedges};
+  S.hdr[H_STATUS] = h.status;
+}
+
+// Appends token c at position n (Blumer's online extension; `cur` is numbered
+// before `clone`). Returns false if a bound check trips.
+__device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
+                                      unsigned bmask) {
+  const int i = h.n;
+  const int cur = h.nstates++;
+  i32x4 rp = S.st[h.last];
+  S.st[cur] = i32x4{rp.x + 1, -1, i, -1};
+  int p = h.last;
+  SamProbe pr;
+  int guard = 0;
+  // Walk suffix links from last, adding (p, c) -> cur until (p, c) exists.
+  while (true) {
+    const int nxt = rp.y;
+    i32x4 rn = i32x4{0, -1, -1, -1};
+    if (nxt != -1) rn = S.st[nxt];  // in flight together with the probe
+    pr = sam_probe(S.slots, bmask, p, c);
+    if (pr.slot < 0) return false;
+    if (pr.found) break;
+    S.slots[pr.slot] = i32x4{p, c, cur, rp.w};
+    reinterpret_cast<int*>(&S.st[p])[3] = pr.slot;
+    h.nedges++;
+    p = nxt;
+    if (p == -1) break;
+    rp = rn;
+    if (++guard > h.nstates) return false;
+  }
+  if (p == -1) {
+    reinterpret_cast<int*>(&S.st[cur])[1] = 0;
+  } else {
+    const int q = pr.dst;
+    const i32x4 rq = S.st[q];
+    if (rp.x + 1 == rq.x) {
+      reinterpret_cast<int*>(&S.st[cur])[1] = q;
+    } else {
+      const int clone = h.nstates++;
+      // Copy q's transitions into the clone.
+      int first = -1, e = rq.w, g2 = 0;
+      while (e != -1) {
+        const i32x4 se = S.slots[e];
+        const SamProbe pc = sam_probe(S.slots, bmask, clone, se.y);
+        if (pc.slot < 0 || pc.found) return false;
+        S.slots[pc.slot] = i32x4{clone, se.y, se.z, first};
+        first = pc.slot;
+        h.nedges++;
+        e = se.w;
+        if (++g2 > h.nedges) return false;
+      }
+      S.st[clone] = i32x4{rp.x + 1, rq.y, rq.z, first};
+      // Redirect (p', c) -> q to the clone along the suffix path from p.
+      int sl = pr.slot;
+      i32x4 rr = rp;
+      int g3 = 0;
+      while (true) {
+        reinterpret_cast<int*>(&S.slots[sl])[2] = clone;
+        const int pp = rr.y;
+        if (pp == -1) break;
+        rr = S.st[pp];
+        const SamProbe p3 = sam_probe(S.slots, bmask, pp, c);
+        if (p3.slot < 0 || !p3.found || p3.dst != q) break;
+        sl = p3.slot;
+        if (++g3 > h.nstates) return false;
+      }
+      reinterpret_cast<int*>(&S.st[q])[1] = clone;
+      reinterpret_cast<int*>(&S.st[cur])[1] = clone;
+    }
+  }
+  h.last = cur;
+  S.text[i] = c;
+  h.n = i + 1;
+  return true;
+}
+
+// Appends tokens tk[0..cnt) (wave-uniform) to one sequence, stopping at the
+// first token that is out of range or would exceed capacity. A sequence whose
+// status is already non-zero is left alone. Executed by one whole wavefront.
+__device__ inline void sam_extend_seq(const SamSeq& S, const int32_t* tk,
+                                      int cnt, int ld, int max_len) {
+  SamHdrRegs h = sam_load_header(S);
+  if (h.status != 0) return;
+  const unsigned bmask = (unsigned)(h.slots / kBucket) - 1u;
+  int st = 0;
+  if (cnt < 0 || cnt > ld) {
+    st = SS_ST_COUNT;
+  } else {
+    for (int t = 0; t < cnt; ++t) {
+      const int c = tk[t];
+      if (c < 0 || c >= h.V) {
+        st = SS_ST_TOKEN_RANGE;
+        break;
+      }
+      if (h.n >= max_len || h.nstates + 2 > 2 * max_len ||
+          !sam_extend_one(S, h, c, bmask)) {
+        st = SS_ST_SAM_CAPACITY;
+        break;
+      }
+    }
+  }
+  h.status |= st;
+  sam_store_header(S, h);
+}
+
+// Draft for one sequence: link walk from last to the first state with an
+// outgoing transition, then lanes j < K gather text[p + 1 + j]. Executed by
+// one whole wavefront (the walk is uniform across lanes).
+__device__ inline void sam_draft_seq(const SamSeq& S, int K, int32_t* draft,
+                                     int32_t* draft_len, int32_t* match_len) {
+  const i32x4 h0 = reinterpret_cast<const i32x4*>(S.hdr)[0];
+  const int n = h0.x, nstates = h0.z;
+  int s = h0.y;
+  i32x4 rs = S.st[s];
+  for (int g = 0; s > 0 && rs.w == -1 && g < nstates; ++g) {
+    s = rs.y;
+    rs = S.st[s < 0 ? 0 : s];
+  }
+  const int Lm = (s < 0) ? 0 : rs.x;
+  const int p = rs.z;
+  const int d = (Lm == 0) ? 0 : min(K, n - 1 - p);
+  const int l = lane_id();
+  if (l < K) draft[l] = (l < d) ? S.text[p + 1 + l] : -1;
+  if (l == 0) {
+    *draft_len = d;
+    *match_len = Lm;
+  }
+}
+
+}  // namespace specsam

@@ -8,29 +8,37 @@
 // max(0, p - q) normalised (p with x_j removed for one-hot drafts); if every
 // draft passes, a bonus token comes from the last row.
 //
-// Design for gfx950 (the hot path is one HBM stream over the needed rows):
-//   stats     grid over (sequence, row group, 32 KiB chunk). Each 256-thread
+// Design for gfx950: two kernels per step (three more when draft
+// probabilities q are given), ordered by the stream they are launched on.
+//   stream    grid over (sequence, row group, 32 KiB chunk). Each 256-thread
 //             workgroup streams its chunk of every row j <= draft_len in its
 //             group with non-temporal 16-byte loads (8 in flight per lane)
 //             and writes one partial per row: (max, lowest argmax) at T = 0,
-//             or (max, sum exp2((l - max) * log2e / T)) at T > 0. Rows past
-//             draft_len are never read. Row groups are sized on the host so
-//             the grid has enough workgroups to fill 256 CUs.
-//   finalize  one workgroup per sequence: combines the chunk partials of
-//             each row, judges the drafts with one wavefront (lane j judges
-//             draft j; a ballot finds the first rejection), writes the
-//             outputs and, for one-hot drafts or the bonus, draws the token:
-//             the chunk is picked from the rescaled partials and only that
-//             chunk is re-read.
+//             or the online (max, sum exp2((l - max) * log2e / T)) folded one
+//             16-byte vector at a time, plus the logit of the draft token when
+//             it falls in the chunk. Rows past draft_len are never read. Row
+//             groups are sized on the host so the grid has enough workgroups
+//             to fill 256 CUs. Nothing but loads, arithmetic and one store per
+//             row: 75 VGPRs, 6 resident workgroups per CU.
+//   finalize  one workgroup per sequence: combines the chunk partials of each
+//             row, judges the drafts with one wavefront (lane j judges draft
+//             j; a ballot finds the first rejection), writes the outputs and,
+//             for one-hot drafts or the bonus, draws the token (the chunk is
+//             picked from the rescaled partials and only that chunk is
+//             re-read). In the fused step it then extends the sequence's
+//             automaton with the emitted tokens and writes the next draft.
 //   residual  only when q is given: chunk sums of max(0, p - q) over the
-//             rejected row (grid over sequence x chunk), then one workgroup
-//             per sequence picks the chunk and re-reads it for the draw.
-// Kernel boundaries order the passes; no workgroup waits on another.
+//             rejected row (sequence x chunk), then one workgroup per
+//             sequence draws from them.
+// A design that let the last workgroup of each sequence finalize inside the
+// stream kernel (agent-scope atomic hand-off) was measured slower: the
+// finalize code raises the stream kernel's register count and its latency
+// lands in the kernel's tail.
 #include <algorithm>
 #include <climits>
 #include <cmath>
 
-#include "internal.h"
+#include "sam_device.h"
 
 namespace specsam {
 namespace {
@@ -83,23 +91,23 @@ __device__ __forceinline__ float load_one(const unsigned char* base, int64_t i) 
   }
 }
 
-// Index (within the row) of element k of load `it` of lane `tid`. Each lane
-// sees its elements in increasing index order (it, then k), which the argmax
-// relies on for its lowest-index tie rule.
-//   VP (vector path): load it of lane tid covers kVec consecutive elements at
-//                     cstart + (it*256 + tid)*kVec: one coalesced 4 KiB wave
-//                     request per load.
-//   scalar path:      element e = it*kVec + k sits at cstart + e*256 + tid.
+// Index (within the row) of element k of load `it` of lane `tid`: load it of
+// lane tid covers kVec consecutive elements at cstart + (it*256 + tid)*kVec,
+// so one wavefront's load is one contiguous 1 KiB request. Token order in a
+// chunk is therefore (it, lane, k); each lane sees its elements in increasing
+// index order, which the argmax relies on for its lowest-index tie rule and
+// the draw for its scan. The scalar path (rows not 16-byte aligned) uses the
+// same layout with element-wise loads.
 template <int DT, bool VP>
 __device__ __forceinline__ int elem_index(int cstart, int tid, int it, int k) {
-  if constexpr (VP)
-    return cstart + (it * kThreads + tid) * kVec<DT> + k;
-  else
-    return cstart + (it * kVec<DT> + k) * kThreads + tid;
+  return cstart + (it * kThreads + tid) * kVec<DT> + k;
 }
 
 // Loads one chunk of a row into registers. Elements past V read as -inf.
-template <int DT, bool VP>
+// NT: non-temporal loads for the streaming pass (measured faster there);
+// the draw's single-chunk re-read uses ordinary loads, which can still find
+// the chunk in the memory-side cache.
+template <int DT, bool VP, bool NT = true>
 __device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
                                            int V, int tid, u32x4 (&raw)[kLoads]) {
   constexpr unsigned kNegInfWord =
@@ -111,13 +119,15 @@ __device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
     if (rem >= kChunk<DT>) {
 #pragma unroll
       for (int it = 0; it < kLoads; ++it)
-        raw[it] = __builtin_nontemporal_load(p + it * kThreads + tid);
+        raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
+                     : p[it * kThreads + tid];
     } else {
 #pragma unroll
       for (int it = 0; it < kLoads; ++it) {
         const int e = (it * kThreads + tid) * kVec<DT>;
         if (e < rem)
-          raw[it] = __builtin_nontemporal_load(p + it * kThreads + tid);
+          raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
+                       : p[it * kThreads + tid];
         else
           raw[it] = u32x4{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
       }
@@ -159,9 +169,16 @@ struct Args {
   int32_t* nem;
   float* p_draft;
   int32_t* status;
-  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, -, argidx)
+  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
   i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
   float* rpart;     // [B*nchunks] residual chunk sums
+  // Fused automaton step (sam == nullptr when only verifying).
+  unsigned char* sam;
+  int max_len;
+  SamLayout sl;
+  int32_t* next_draft;
+  int32_t* next_draft_len;
+  int32_t* next_match_len;
 };
 
 // Per-sequence checks that need device data.
@@ -195,90 +212,14 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os
   m = M;
 }
 
-// ---------------------------------------------------------------------------
-// stats: one partial per (row, chunk).
-// ---------------------------------------------------------------------------
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void verify_stats(Args a) {
-  __shared__ f32x4 red[kWaves];
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1;
-  const int c = blockIdx.x % a.nchunks;
-  const int bg = blockIdx.x / a.nchunks;
-  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
-  int d;
-  float T;
-  if (seq_check(a, b, &d, &T)) return;  // reported by finalize
-  const int j0 = g * a.rows_per_wg;
-  const int j1 = min(j0 + a.rows_per_wg, d + 1);
-  const bool greedy = (T == 0.0f);
-  const float kk = greedy ? 0.0f : kLog2e / T;
-  const int cstart = c * kChunk<DT>;
-  for (int j = j0; j < j1; ++j) {
-    const int64_t row = (int64_t)b * R + j;
-    const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
-    u32x4 raw[kLoads];
-    load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
-    if (greedy) {
-      float bv = kNegInf;
-      int bi = INT_MAX, nan = 0;
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) {
-          const float v = elem<DT>(raw[it], k);
-          if (v > bv) {
-            bv = v;
-            bi = elem_index<DT, VP>(cstart, tid, it, k);
-          }
-          nan |= (v != v);
-        }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-        argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
-      nan = wave_or(nan);
-      if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
-      __syncthreads();
-      if (tid == 0) {
-        float pv = red[0].x, pn = red[0].y;
-        int pi = __float_as_int(red[0].w);
-        for (int i = 1; i < kWaves; ++i) {
-          argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
-          pn = fmaxf(pn, red[i].y);
-        }
-        a.partials[row * a.nchunks + c] = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
-      }
-    } else {
-      float mx = kNegInf;
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) mx = fmaxf(mx, elem<DT>(raw[it], k));
-      const float base = (mx == kNegInf) ? 0.0f : mx;
-      float s = 0.0f;
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k)
-          s += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-        lse_merge(mx, s, __shfl_xor(mx, o, kWave), __shfl_xor(s, o, kWave), kk);
-      if (l == 0) red[w] = f32x4{mx, s, 0.0f, 0.0f};
-      __syncthreads();
-      if (tid == 0) {
-        float pm = red[0].x, ps = red[0].y;
-        for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
-        a.partials[row * a.nchunks + c] = f32x4{pm, ps, 0.0f, 0.0f};
-      }
-    }
-    __syncthreads();  // red[] is reused by the next row
-  }
-}
+// Partials and residual sums are written by one kernel and read by the next
+// one on the same stream; plain accesses suffice.
+__device__ __forceinline__ f32x4 load_partial(const f32x4* p) { return *p; }
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
 
 // ---------------------------------------------------------------------------
-// Draw from one row. Weights are exp2((l - m) * kk) with token `excl`
-// removed (one-hot residual, or none for the bonus), or, for RESIDUAL,
+// Draw from one row. Weights are exp2((l - m) * kk) with token `excl` (weight
+// wx) removed (one-hot residual; excl < 0 for the bonus), or, for RESIDUAL,
 // max(0, exp2((l - m) * kk) / S - q).
 //
 // Step 1 (wave 0): inclusive scan of the chunk weights in chunk order; take
@@ -287,70 +228,60 @@ __global__ __launch_bounds__(kThreads) void verify_stats(Args a) {
 // workgroup): re-read that chunk as 256 contiguous 128-byte segments held in
 // registers, scan the lane sums, and let the lane whose interval holds the
 // target find the first token whose running sum exceeds it. A rounding miss
-// falls back to the chunk's last positive weight.
+// falls back to the last positive weight.
 // ---------------------------------------------------------------------------
 struct DrawShared {
   float W[kMaxChunks];
   float cum[kMaxChunks];
-  float wsum[kWaves];
+  float cell[kLoads * kWaves];  // (load, wave) sums in token order
   int wlast[kWaves];
   float t_in;
+  float t_cell;
   int chunk;
+  int cell_sel;
   int result;
 };
 
-// Loads lane tid's segment of chunk c (kSeg elements) into registers.
+// Weight of element k of raw vector `it` (token index i).
+template <int DT, bool RESIDUAL>
+__device__ __forceinline__ float draw_weight(float l, int i, int excl, float m,
+                                             float kk, float invS, float qi) {
+  if constexpr (RESIDUAL)
+    return fmaxf(0.0f, fast_exp2((l - m) * kk) * invS - qi);
+  else
+    return (i == excl) ? 0.0f : fast_exp2((l - m) * kk);
+}
+
+// q values for the kVec elements of one raw vector (RESIDUAL only).
 template <int DT, bool VP>
-__device__ __forceinline__ void load_segment(const unsigned char* row, int s0,
-                                             int V, float (&x)[kSeg<DT>]) {
-  if constexpr (VP) {
-    constexpr int kVecs = kSeg<DT> / kVec<DT>;  // 8 loads of 16 bytes
-    const u32x4* p =
-        reinterpret_cast<const u32x4*>(row + (int64_t)s0 * Dt<DT>::kBytes);
+__device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int tid,
+                                           int it, int V, float (&qv)[kVec<DT>]) {
 #pragma unroll
-    for (int v = 0; v < kVecs; ++v) {
-      if (s0 + v * kVec<DT> < V) {
-        const u32x4 r = p[v];
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) x[v * kVec<DT> + k] = elem<DT>(r, k);
-      } else {
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) x[v * kVec<DT> + k] = kNegInf;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kSeg<DT>; ++k)
-      x[k] = (s0 + k < V) ? load_one<DT>(row, s0 + k) : kNegInf;
+  for (int k = 0; k < kVec<DT>; ++k) {
+    const int i = elem_index<DT, VP>(cstart, tid, it, k);
+    qv[k] = i < V ? qrow[i] : 0.0f;
   }
 }
 
-template <int DT, bool VP>
-__device__ __forceinline__ void load_q_segment(const float* qrow, int s0, int V,
-                                               float (&x)[kSeg<DT>]) {
-  if constexpr (VP) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(qrow + s0);
-#pragma unroll
-    for (int v = 0; v < kSeg<DT> / 4; ++v) {
-      if (s0 + v * 4 < V) {
-        const f32x4 r = p[v];
-        x[4 * v] = r.x;
-        x[4 * v + 1] = r.y;
-        x[4 * v + 2] = r.z;
-        x[4 * v + 3] = r.w;
-      } else {
-        x[4 * v] = x[4 * v + 1] = x[4 * v + 2] = x[4 * v + 3] = 0.0f;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kSeg<DT>; ++k) x[k] = (s0 + k < V) ? qrow[s0 + k] : 0.0f;
-  }
-}
-
+// Draw from one row. Weights are exp2((l - m) * kk) with token `excl` (weight
+// wx) removed (one-hot residual; excl < 0 for the bonus), or, for RESIDUAL,
+// max(0, exp2((l - m) * kk) / S - q).
+//
+// Step 1 (wave 0): inclusive scan of the chunk weights in chunk order; take
+// the first chunk whose running sum exceeds u * total (strict), or the last
+// chunk with positive weight if rounding leaves none. Step 2: re-read that
+// chunk with the same coalesced layout as the stream pass, where token order
+// is (load, lane, element). Each lane sums the weights of each of its 8
+// vectors; 32 (load, wavefront) cells are scanned in token order to find the
+// cell, a wavefront scan inside the cell finds the lane, and that lane scans
+// its vector. The cell totals and the lane scan come from the same inclusive
+// scan, so the search is consistent; a target beyond the chunk's total (a
+// rounding difference with the chunk partials) takes the last positive
+// weight of the chunk.
 template <int DT, bool VP, bool RESIDUAL>
-__device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
-                        float m, float S, float kk, float u) {
+__device__ int draw_row(const Args& a, DrawShared& sh, int b, int r,
+                        const f32x4* Pr, int excl, float wx, float m, float S,
+                        float kk, float u) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int R = a.K + 1, nc = a.nchunks;
   const unsigned char* row =
@@ -358,21 +289,16 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
   const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const float invS = RESIDUAL ? 1.0f / S : 0.0f;
   if (w == 0) {
-    float wx = 0.0f;
-    int cx = -1;
-    if (!RESIDUAL && excl >= 0) {
-      wx = fast_exp2((load_one<DT>(row, excl) - m) * kk);
-      cx = excl / kChunk<DT>;
-    }
+    const int cx = (!RESIDUAL && excl >= 0) ? excl / kChunk<DT> : -1;
     float carry = 0.0f;
     for (int g0 = 0; g0 < nc; g0 += kWave) {
       const int c = g0 + l;
       float W = 0.0f;
       if (c < nc) {
         if constexpr (RESIDUAL) {
-          W = a.rpart[(int64_t)b * nc + c];
+          W = load_f32(a.rpart + (int64_t)b * nc + c);
         } else {
-          const f32x4 P = a.partials[((int64_t)b * R + r) * nc + c];
+          const f32x4 P = Pr[c];
           W = P.y * fast_exp2((P.x - m) * kk);
           if (c == cx) W = fmaxf(0.0f, W - wx);
         }
@@ -408,99 +334,155 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r, int excl,
   const int c = sh.chunk;
   if (c < 0) return -1;
   const float t_in = sh.t_in;
-  const int s0 = c * kChunk<DT> + tid * kSeg<DT>;
-  float x[kSeg<DT>];
-  load_segment<DT, VP>(row, s0, a.V, x);
-  if constexpr (RESIDUAL) {
-    float qv[kSeg<DT>];
-    load_q_segment<DT, VP>(qrow, s0, a.V, qv);
-#pragma unroll
-    for (int k = 0; k < kSeg<DT>; ++k)
-      x[k] = fmaxf(0.0f, fast_exp2((x[k] - m) * kk) * invS - qv[k]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < kSeg<DT>; ++k)
-      x[k] = (s0 + k == excl) ? 0.0f : fast_exp2((x[k] - m) * kk);
-  }
-  float tsum = 0.0f;
+  const int cstart = c * kChunk<DT>;
+  u32x4 raw[kLoads];
+  load_chunk<DT, VP, false>(row, cstart, a.V, tid, raw);
+  float vs[kLoads];
   int tlast = -1;
 #pragma unroll
-  for (int k = 0; k < kSeg<DT>; ++k) {
-    tsum += x[k];
-    if (x[k] > 0.0f) tlast = s0 + k;
+  for (int it = 0; it < kLoads; ++it) {
+    float qv[kVec<DT>];
+    if constexpr (RESIDUAL) load_q_vec<DT, VP>(qrow, cstart, tid, it, a.V, qv);
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k) {
+      const int i = elem_index<DT, VP>(cstart, tid, it, k);
+      const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
+                                                 kk, invS, RESIDUAL ? qv[k] : 0.0f);
+      acc += wk;
+      if (wk > 0.0f) tlast = max(tlast, i);
+    }
+    vs[it] = acc;
   }
-  // Block-wide inclusive scan of the lane sums.
-  float inc = wave_inclusive_sum(tsum);
-  if (l == kWave - 1) sh.wsum[w] = inc;
+  // Cell (it, wave) totals: the last lane of each wavefront's inclusive scan.
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const float inc = wave_inclusive_sum(vs[it]);
+    if (l == kWave - 1) sh.cell[it * kWaves + w] = inc;
+  }
   int wl = tlast;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
   if (l == 0) sh.wlast[w] = wl;
   __syncthreads();
-  float wbase = 0.0f;
-  for (int i = 0; i < w; ++i) wbase += sh.wsum[i];
-  inc += wbase;
-  float exc = __shfl_up(inc, 1, kWave);
-  if (l == 0) exc = wbase;
-  if (tid == 0) {
-    int cl = -1;
-    for (int i = 0; i < kWaves; ++i) cl = max(cl, sh.wlast[i]);
-    sh.result = cl;  // default: the chunk's last positive weight
+  if (w == 0) {
+    const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
+    const float inc = wave_inclusive_sum(cv);
+    float exc = __shfl_up(inc, 1, kWave);
+    if (l == 0) exc = 0.0f;
+    const unsigned long long hit =
+        __ballot(l < kLoads * kWaves && exc <= t_in && t_in < inc);
+    if (l == 0) {
+      int cl = -1;
+      for (int i = 0; i < kWaves; ++i) cl = max(cl, sh.wlast[i]);
+      sh.result = cl;  // default: the chunk's last positive weight
+      sh.cell_sel = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+    }
+    if (hit && l == __ffsll((unsigned long long)hit) - 1) sh.t_cell = t_in - exc;
   }
   __syncthreads();
-  if (exc <= t_in && t_in < inc) {  // at most one lane's interval holds t_in
-    const float tl = t_in - exc;
-    float run = 0.0f;
-    int found = -1;
+  const int cell = sh.cell_sel;
+  if (cell >= 0 && w == cell % kWaves) {
+    const int its = cell / kWaves;
+    float v = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kSeg<DT>; ++k) {
-      run += x[k];
-      if (found < 0 && run > tl) found = s0 + k;
+    for (int it = 0; it < kLoads; ++it)
+      if (it == its) v = vs[it];
+    const float inc = wave_inclusive_sum(v);
+    float exc = __shfl_up(inc, 1, kWave);
+    if (l == 0) exc = 0.0f;
+    const float tc = sh.t_cell;
+    if (exc <= tc && tc < inc) {  // exactly one lane: same scan as the cell total
+      const float tl = tc - exc;
+      u32x4 rv = raw[0];
+#pragma unroll
+      for (int it = 1; it < kLoads; ++it)
+        if (it == its) rv = raw[it];
+      float qv[kVec<DT>];
+      if constexpr (RESIDUAL) {
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) {
+          const int i = elem_index<DT, VP>(cstart, tid, its, k);
+          qv[k] = i < a.V ? qrow[i] : 0.0f;
+        }
+      }
+      float run = 0.0f;
+      int found = -1, lastp = -1;
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const int i = elem_index<DT, VP>(cstart, tid, its, k);
+        const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(rv, k), i, excl, m, kk,
+                                                   invS, RESIDUAL ? qv[k] : 0.0f);
+        run += wk;
+        if (wk > 0.0f) lastp = i;
+        if (found < 0 && run > tl) found = i;
+      }
+      sh.result = found >= 0 ? found : lastp;
     }
-    sh.result = found >= 0 ? found : tlast;
   }
   __syncthreads();
   return sh.result;
 }
 
-// ---------------------------------------------------------------------------
-// finalize: one workgroup per sequence.
-// ---------------------------------------------------------------------------
+// Chunk partials of all K+1 rows are cached in LDS when they fit.
+constexpr int kPartialCache = 1024;
+
 struct FinalShared {
+  f32x4 pc[kPartialCache];
   float m[kMaxRows];
   float s[kMaxRows];
+  float lx[kMaxRows];
+  float u[kMaxRows];
   int idx[kMaxRows];
   int bad[kMaxRows];
+  int x[kMaxRows];
+  int tok[kMaxRows];
   int acc_len;
   int st;
   DrawShared draw;
 };
 
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
+template <int DT, bool VP, bool SAM>
+__global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   __shared__ FinalShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int b = blockIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
+  // Everything that does not depend on another load is requested at once:
+  // the sequence's parameters, drafts, coins and the partials of every row.
+  const bool cached = R * nc <= kPartialCache;
+  const f32x4* Pb = a.partials + (int64_t)b * R * nc;
+  if (cached)
+    for (int e = tid; e < R * nc; e += kThreads) sh.pc[e] = Pb[e];
+  if (tid < a.K) sh.x[tid] = a.draft[(int64_t)b * a.K + tid];
+  if (tid < R && a.uniforms) sh.u[tid] = a.uniforms[(int64_t)b * R + tid];
   int d;
   float T;
   const int st0 = seq_check(a, b, &d, &T);
+  __syncthreads();
   if (st0) {
+    // Reported once; the automaton (if any) is left unchanged and the next
+    // draft is taken from it as it is.
     if (tid == 0) {
       atomicOr(&a.status[b], st0);
       a.seqinfo[b] = i32x4{0, 0, 0, 0};
+    }
+    if constexpr (SAM) {
+      if (w == 0)
+        sam_draft_seq(sam_seq(a.sam, b, a.sl), a.K, a.next_draft + (int64_t)b * a.K,
+                      a.next_draft_len + b, a.next_match_len + b);
     }
     return;
   }
   const bool greedy = (T == 0.0f);
   const float kk = greedy ? 0.0f : kLog2e / T;
   for (int j = w; j <= d; j += kWaves) {
-    const f32x4* P = a.partials + ((int64_t)b * R + j) * nc;
+    const f32x4* P = cached ? sh.pc + j * nc : Pb + (int64_t)j * nc;
     if (greedy) {
       float bv = kNegInf;
       int bi = INT_MAX, nan = 0;
       for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = P[c];
+        const f32x4 p = load_partial(P + c);
         argmax_merge(bv, bi, p.x, __float_as_int(p.w));
         nan |= (p.y != 0.0f);
       }
@@ -514,17 +496,27 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
         sh.bad[j] = nan || bv == INFINITY || bv == kNegInf;
       }
     } else {
-      float m = kNegInf, s = 0.0f;
+      const int xj = (j < d) ? sh.x[j] : -1;
+      const int cx = (xj >= 0 && xj < a.V) ? xj / kChunk<DT> : -1;
+      float m = kNegInf, s = 0.0f, lxv = 0.0f;
+      bool has = false;
       for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = P[c];
+        const f32x4 p = load_partial(P + c);
         lse_merge(m, s, p.x, p.y, kk);
+        if (c == cx) {
+          lxv = p.z;
+          has = true;
+        }
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1)
         lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
+      const unsigned long long hb = __ballot(has);
+      if (hb) lxv = __shfl(lxv, __ffsll((unsigned long long)hb) - 1, kWave);
       if (l == 0) {
         sh.m[j] = m;
         sh.s[j] = s;
+        sh.lx[j] = lxv;
         sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
       }
     }
@@ -533,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
   if (w == 0) {
     int st = 0, x = -1;
     if (l < d) {
-      x = a.draft[(int64_t)b * a.K + l];
+      x = sh.x[l];
       if (x < 0 || x >= a.V) st |= SS_ST_TOKEN_RANGE;
     }
     if (l <= d && sh.bad[l]) st |= SS_ST_NONFINITE;
@@ -551,24 +543,22 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
         if (greedy) {
           acc = (x == sh.idx[l]);
         } else {
-          const unsigned char* row =
-              a.logits + ((int64_t)b * R + l) * a.V * Dt<DT>::kBytes;
-          px = fast_exp2((load_one<DT>(row, x) - sh.m[l]) * kk) / sh.s[l];
+          px = fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l];
           const float qx = a.q ? a.q[((int64_t)b * a.K + l) * a.V + x] : 1.0f;
-          const float u = a.uniforms[(int64_t)b * R + l];
-          acc = (qx > 0.0f) ? (u <= px / qx) : (px > 0.0f);
+          acc = (qx > 0.0f) ? (sh.u[l] <= px / qx) : (px > 0.0f);
         }
       }
       // Wavefront scan of the accept flags: the first rejection ends the run.
       const unsigned long long rej = __ballot(!acc);
       const int al = rej ? __ffsll((unsigned long long)rej) - 1 : d;
       if (l < R) {
+        int tok = -1;
         if (l < al)
-          a.out[(int64_t)b * R + l] = x;
+          tok = x;
         else if (l == al && greedy)
-          a.out[(int64_t)b * R + l] = sh.idx[l];
-        else if (l > al)
-          a.out[(int64_t)b * R + l] = -1;
+          tok = sh.idx[l];
+        if (!(l == al && !greedy)) a.out[(int64_t)b * R + l] = tok;
+        sh.tok[l] = tok;
       }
       if (a.p_draft && l < a.K)
         a.p_draft[(int64_t)b * a.K + l] =
@@ -588,11 +578,130 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
                                     __float_as_int(sh.s[al]), __float_as_int(kk)}
                             : i32x4{0, 0, 0, 0};
   if (sh.st == 0 && !greedy && !residual) {
-    const int excl = (al < d) ? a.draft[(int64_t)b * a.K + al] : -1;
-    const float u = a.uniforms[(int64_t)b * R + a.K];
-    const int tok = draw_row<DT, VP, false>(a, sh.draw, b, al, excl, sh.m[al],
-                                            sh.s[al], kk, u);
-    if (tid == 0) a.out[(int64_t)b * R + al] = tok;
+    const int excl = (al < d) ? sh.x[al] : -1;
+    const float wx = (al < d) ? fast_exp2((sh.lx[al] - sh.m[al]) * kk) : 0.0f;
+    const f32x4* Pr = cached ? sh.pc + al * nc : Pb + (int64_t)al * nc;
+    const int tok = draw_row<DT, VP, false>(a, sh.draw, b, al, Pr, excl, wx,
+                                            sh.m[al], sh.s[al], kk, sh.u[a.K]);
+    if (tid == 0) {
+      a.out[(int64_t)b * R + al] = tok;
+      sh.tok[al] = tok;
+    }
+    __syncthreads();
+  }
+  if constexpr (SAM) {
+    if (w == 0) {
+      const SamSeq S = sam_seq(a.sam, b, a.sl);
+      if (sh.st == 0) sam_extend_seq(S, sh.tok, al + 1, R, a.max_len);
+      sam_draft_seq(S, a.K, a.next_draft + (int64_t)b * a.K, a.next_draft_len + b,
+                    a.next_match_len + b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// stream: one partial per (row, chunk).
+// ---------------------------------------------------------------------------
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
+  __shared__ f32x4 red[kWaves];
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int R = a.K + 1, nc = a.nchunks;
+  const int c = blockIdx.x % nc;
+  const int bg = blockIdx.x / nc;
+  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
+  const int j0 = g * a.rows_per_wg;
+  const int cstart = c * kChunk<DT>;
+  // The sequence's parameters and the draft token of row j0 are requested
+  // first; row 0, which every valid sequence needs, is requested before they
+  // return.
+  int d;
+  float T;
+  const int st = seq_check(a, b, &d, &T);  // reported by finalize
+  int x0 = -1;
+  if (tid == 0 && j0 < a.K) x0 = a.draft[(int64_t)b * a.K + j0];
+  u32x4 raw[kLoads];
+  if (j0 == 0)
+    load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
+                       a.V, tid, raw);
+  if (st) return;
+  const int j1 = min(j0 + a.rows_per_wg, d + 1);
+  if (j0 >= j1) return;
+  const bool greedy = (T == 0.0f);
+  const float kk = greedy ? 0.0f : kLog2e / T;
+  for (int j = j0; j < j1; ++j) {
+    const int64_t row = (int64_t)b * R + j;
+    const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
+    if (j != 0) load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
+    int x = x0;
+    if (j != j0) x = (tid == 0 && j < a.K) ? a.draft[(int64_t)b * a.K + j] : -1;
+    // The logit of the draft token, when it lies in this chunk, is requested
+    // before the chunk is consumed.
+    float lx = 0.0f;
+    if (!greedy && j < d && tid == 0 && x >= cstart && x < cstart + kChunk<DT> &&
+        x < a.V)
+      lx = load_one<DT>(rowp, x);
+    f32x4 part;
+    if (greedy) {
+      // Position within the lane's elements (it*kVec + k) is a compile-time
+      // constant per element; the row index is formed once at the end.
+      float bv = kNegInf;
+      int bp = -1, nan = 0;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) {
+          const float v = elem<DT>(raw[it], k);
+          if (v > bv) {
+            bv = v;
+            bp = it * kVec<DT> + k;
+          }
+          nan |= (v != v);
+        }
+      int bi = bp < 0 ? INT_MAX
+                      : elem_index<DT, VP>(cstart, tid, bp / kVec<DT>, bp % kVec<DT>);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+      nan = wave_or(nan);
+      if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
+      __syncthreads();
+      float pv = red[0].x, pn = red[0].y;
+      int pi = __float_as_int(red[0].w);
+      for (int i = 1; i < kWaves; ++i) {
+        argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
+        pn = fmaxf(pn, red[i].y);
+      }
+      part = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
+    } else {
+      // Online (max, sum exp2) folded one 16-byte vector at a time, in the
+      // order the loads return, so only the raw vectors stay live.
+      float m = kNegInf, s = 0.0f;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) {
+        float vm = kNegInf;
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
+        const float mn = fmaxf(m, vm);
+        const float base = (mn == kNegInf) ? 0.0f : mn;
+        float t = s * fast_exp2((m - base) * kk);
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k)
+          t += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
+        s = t;
+        m = mn;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
+      if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
+      __syncthreads();
+      float pm = red[0].x, ps = red[0].y;
+      for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
+      part = f32x4{pm, ps, lx, 0.0f};
+    }
+    if (tid == 0) a.partials[row * nc + c] = part;
+    __syncthreads();  // red[] is reused by the next row
   }
 }
 
@@ -658,29 +767,33 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
 
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
-  __shared__ DrawShared sh;
   __shared__ float total_sh;
+  __shared__ DrawShared dsh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int b = blockIdx.x;
   const int nc = a.nchunks;
+  const int b = blockIdx.x;
   const i32x4 info = a.seqinfo[b];
   if (info.x == 0) return;
   const int r = info.x - 1;
   const float m = __int_as_float(info.y), S = __int_as_float(info.z);
   const float kk = __int_as_float(info.w);
+  const int R = a.K + 1;
   if (w == 0) {
     float tot = 0.0f;
-    for (int c = l; c < nc; c += kWave) tot += a.rpart[(int64_t)b * nc + c];
+    for (int cc = l; cc < nc; cc += kWave) tot += a.rpart[(int64_t)b * nc + cc];
     tot = wave_sum(tot);
     if (l == 0) total_sh = tot;
   }
   __syncthreads();
-  const float u = a.uniforms[(int64_t)b * (a.K + 1) + a.K];
+  const float u = a.uniforms[(int64_t)b * R + a.K];
   // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
   const int tok = total_sh > 0.0f
-                      ? draw_row<DT, VP, true>(a, sh, b, r, -1, m, S, kk, u)
-                      : draw_row<DT, VP, false>(a, sh, b, r, -1, m, S, kk, u);
-  if (tid == 0) a.out[(int64_t)b * (a.K + 1) + r] = tok;
+                      ? draw_row<DT, VP, true>(a, dsh, b, r, nullptr, -1, 0.0f, m,
+                                               S, kk, u)
+                      : draw_row<DT, VP, false>(a, dsh, b, r,
+                                                a.partials + ((int64_t)b * R + r) * nc,
+                                                -1, 0.0f, m, S, kk, u);
+  if (tid == 0) a.out[(int64_t)b * R + r] = tok;
 }
 
 // ---------------------------------------------------------------------------
@@ -711,25 +824,25 @@ WsLayout ws_layout(int B, int K, int V) {
   return L;
 }
 
-// Workgroups the stats grid aims for: enough to keep every CU busy with
+// Workgroups the stream grid aims for: enough to keep every CU busy with
 // several resident workgroups.
 constexpr int64_t kTargetWorkgroups = 4096;
 
-template <int DT, bool VP>
+template <int DT, bool VP, bool SAM>
 int launch(Args a, hipStream_t s) {
   const int R = a.K + 1;
   const int64_t base = (int64_t)a.B * a.nchunks;
-  int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
+  const int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
   a.rows_per_wg = (R + ngroups - 1) / ngroups;
   a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
   const int64_t grid1 = base * a.ngroups;
   if (grid1 > INT_MAX) return set_error(SS_EINVAL, "spec_verify: grid too large");
-  hipLaunchKernelGGL((verify_stats<DT, VP>), dim3((unsigned)grid1), dim3(kThreads),
-                     0, s, a);
-  int rc = check_launch("spec_verify stats");
+  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid1),
+                     dim3(kThreads), 0, s, a);
+  int rc = check_launch("spec_verify stream pass");
   if (rc != SS_OK) return rc;
-  hipLaunchKernelGGL((verify_finalize<DT, VP>), dim3((unsigned)a.B), dim3(kThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM>), dim3((unsigned)a.B),
+                     dim3(kThreads), 0, s, a);
   rc = check_launch("spec_verify finalize");
   if (rc != SS_OK || a.q == nullptr) return rc;
   hipLaunchKernelGGL((verify_residual_sums<DT, VP>), dim3((unsigned)base),
@@ -741,37 +854,28 @@ int launch(Args a, hipStream_t s) {
   return check_launch("spec_verify residual draw");
 }
 
-}  // namespace
-}  // namespace specsam
-
-using namespace specsam;
-
-extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
-  if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV) return 0;
-  return ws_layout(B, K, V).total;
-}
-
-extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
-                           const int32_t* draft, const int32_t* draft_len,
-                           const float* q, const float* temperature,
-                           const float* uniforms, int32_t* out_tokens,
-                           int32_t* num_emitted, float* p_draft, int32_t* status,
-                           void* workspace, size_t ws_bytes, void* stream) {
+int run(const void* logits, int dtype, int B, int K, int V, const int32_t* draft,
+        const int32_t* draft_len, const float* q, const float* temperature,
+        const float* uniforms, int32_t* out_tokens, int32_t* num_emitted,
+        float* p_draft, int32_t* status, void* workspace, size_t ws_bytes,
+        void* sam_state, int max_len, int32_t* next_draft,
+        int32_t* next_draft_len, int32_t* next_match_len, void* stream,
+        const char* fn) {
   if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV)
     return set_error(SS_EINVAL,
-                     "spec_verify: need B >= 1, 1 <= K <= %d, 1 <= V <= %d "
+                     "%s: need B >= 1, 1 <= K <= %d, 1 <= V <= %d "
                      "(got B=%d K=%d V=%d)",
-                     SS_MAX_K, kMaxV, B, K, V);
+                     fn, SS_MAX_K, kMaxV, B, K, V);
   if (dtype != SS_DTYPE_F32 && dtype != SS_DTYPE_BF16)
-    return set_error(SS_EINVAL, "spec_verify: unknown dtype %d", dtype);
+    return set_error(SS_EINVAL, "%s: unknown dtype %d", fn, dtype);
   if (!logits || !draft || !draft_len || !temperature || !out_tokens ||
       !num_emitted || !status || !workspace)
-    return set_error(SS_EINVAL, "spec_verify: a required pointer is NULL");
-  if ((uintptr_t)workspace & 15)
-    return set_error(SS_EINVAL, "spec_verify: workspace must be 16-byte aligned");
+    return set_error(SS_EINVAL, "%s: a required pointer is NULL", fn);
+  if ((uintptr_t)workspace & 255)
+    return set_error(SS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
   const WsLayout L = ws_layout(B, K, V);
   if (ws_bytes < L.total)
-    return set_error(SS_EWORKSPACE, "spec_verify: workspace %zu < %zu bytes",
+    return set_error(SS_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn,
                      ws_bytes, L.total);
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   Args a;
@@ -794,11 +898,70 @@ extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
+  a.sam = reinterpret_cast<unsigned char*>(sam_state);
+  a.max_len = max_len;
+  a.sl = sam_layout(max_len > 0 ? max_len : 1);
+  a.next_draft = next_draft;
+  a.next_draft_len = next_draft_len;
+  a.next_match_len = next_match_len;
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
   const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0) &&
                   (q == nullptr || ((uintptr_t)q & 15) == 0);
   hipStream_t s = as_stream(stream);
+  if (sam_state) {
+    if (dtype == SS_DTYPE_F32)
+      return vp ? launch<SS_DTYPE_F32, true, true>(a, s)
+                : launch<SS_DTYPE_F32, false, true>(a, s);
+    return vp ? launch<SS_DTYPE_BF16, true, true>(a, s)
+              : launch<SS_DTYPE_BF16, false, true>(a, s);
+  }
   if (dtype == SS_DTYPE_F32)
-    return vp ? launch<SS_DTYPE_F32, true>(a, s) : launch<SS_DTYPE_F32, false>(a, s);
-  return vp ? launch<SS_DTYPE_BF16, true>(a, s) : launch<SS_DTYPE_BF16, false>(a, s);
+    return vp ? launch<SS_DTYPE_F32, true, false>(a, s)
+              : launch<SS_DTYPE_F32, false, false>(a, s);
+  return vp ? launch<SS_DTYPE_BF16, true, false>(a, s)
+            : launch<SS_DTYPE_BF16, false, false>(a, s);
+}
+
+}  // namespace
+}  // namespace specsam
+
+using namespace specsam;
+
+extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
+  if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV) return 0;
+  return ws_layout(B, K, V).total;
+}
+
+extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
+                           const int32_t* draft, const int32_t* draft_len,
+                           const float* q, const float* temperature,
+                           const float* uniforms, int32_t* out_tokens,
+                           int32_t* num_emitted, float* p_draft, int32_t* status,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  return run(logits, dtype, B, K, V, draft, draft_len, q, temperature, uniforms,
+             out_tokens, num_emitted, p_draft, status, workspace, ws_bytes,
+             nullptr, 0, nullptr, nullptr, nullptr, stream, "spec_verify");
+}
+
+extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
+                         const int32_t* draft, const int32_t* draft_len,
+                         const float* temperature, const float* uniforms,
+                         void* sam_state, int max_len, int32_t* out_tokens,
+                         int32_t* num_emitted, float* p_draft, int32_t* status,
+                         int32_t* next_draft, int32_t* next_draft_len,
+                         int32_t* next_match_len, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  if (!sam_state || ((uintptr_t)sam_state & 255) || max_len < 1 ||
+      max_len > SS_MAX_LEN)
+    return set_error(SS_EINVAL, "spec_step: state must be non-null and 256-byte "
+                                "aligned, 1 <= max_len <= %d", SS_MAX_LEN);
+  if (!next_draft || !next_draft_len || !next_match_len)
+    return set_error(SS_EINVAL, "spec_step: next-draft outputs must be non-null");
+  if (next_draft == draft || next_draft_len == draft_len)
+    return set_error(SS_EINVAL, "spec_step: next-draft outputs must not alias "
+                                "the drafts being verified");
+  return run(logits, dtype, B, K, V, draft, draft_len, nullptr, temperature,
+             uniforms, out_tokens, num_emitted, p_draft, status, workspace,
+             ws_bytes, sam_state, max_len, next_draft, next_draft_len,
+             next_match_len, stream, "spec_step");
 }

@@ -131,3 +131,23 @@ def test_zero_counts_and_empty_drafts():
     d, dl, ml = st.draft(4)
     assert dl.cpu().tolist() == [0, 0, 1] and ml.cpu().tolist() == [0, 0, 1]
     assert d.cpu()[2].tolist() == [0, -1, -1, -1]
+
+
+def test_extend_draft_matches_separate_calls():
+    say("[gpu] sam_extend_draft")
+    rng = np.random.default_rng(44)
+    B, max_len, K, ld = 8, 400, 4, 5
+    a = ssl.SamState(B, max_len, 6, "cuda")
+    bst = ssl.SamState(B, max_len, 6, "cuda")
+    for _ in range(60):
+        cnt = rng.integers(0, ld + 1, B).astype(np.int32)
+        tok = rng.integers(0, 6, (B, ld)).astype(np.int32)
+        a.extend(dev(tok), dev(cnt))
+        d1, l1, m1 = a.draft(K)
+        d2, l2, m2 = bst.extend_draft(dev(tok), dev(cnt), K)
+        torch.cuda.synchronize()
+        assert torch.equal(d1, d2) and torch.equal(l1, l2) and torch.equal(m1, m2)
+    for b in range(B):
+        ea, eb = a.export(b), bst.export(b)
+        for k in ("len", "link", "min_endpos", "edges", "text"):
+            np.testing.assert_array_equal(ea[k], eb[k])

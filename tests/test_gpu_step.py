@@ -98,3 +98,98 @@ def test_c5_draft_model_full_size():
                           nthreads=8)
         compare_verify(*g, r, T, u, tally, what=f"c5 step {s}")
     say(f"    {tally}")
+
+
+def _run_fused_workload(c, steps, **over):
+    """Same as the separate-call run, but each step is one spec_step call
+    (verify + extend + next draft), with drafts ping-ponging between two
+    buffers; compared against the oracle every step."""
+    cfg = synth.config(c, **over)
+    say(f"[gpu] fused steps {cfg.name} B={cfg.B} steps={steps}")
+    gt = synth.token_streams(cfg, steps)
+    H = cfg.hist_len
+    n = np.full(cfg.B, H, np.int32)
+    st = ssl.SamState(cfg.B, cfg.stream_len(steps), cfg.V, "cuda")
+    st.extend(dev(gt[:, :H]), dev(np.full(cfg.B, H, np.int32)))
+    sams = [oracle.SAM(gt[b, :H]) for b in range(cfg.B)]
+    T = np.full(cfg.B, cfg.T, np.float32)
+    Td = dev(T)
+    ws = ssl.verify_workspace(cfg.B, cfg.K, cfg.V)
+    bufs = [st.draft(cfg.K), tuple(torch.empty_like(t) for t in st.draft(cfg.K))]
+    tally = Tally()
+    for s in range(steps):
+        d, dl, ml = bufs[s % 2]
+        nd, ndl, nml = bufs[(s + 1) % 2]
+        x = synth.target_logits(cfg, s, gt, n, device="cuda")
+        u = synth.uniforms(cfg, s)
+        out, nem, pd, status, *_ = ssl.spec_step(
+            x, d, dl, Td, dev(u), st, workspace=ws, next_draft=nd,
+            next_draft_len=ndl, next_match_len=nml)
+        torch.cuda.synchronize()
+        dh, dlh, mlh = d.cpu().numpy(), dl.cpu().numpy(), ml.cpu().numpy()
+        for b in range(cfg.B):
+            od, odl, oml = sams[b].draft(cfg.K)
+            assert (od == dh[b]).all() and odl == dlh[b] and oml == mlh[b], (s, b)
+        g = (out.cpu().numpy(), nem.cpu().numpy(), pd.cpu().numpy(),
+             status.cpu().numpy())
+        r = oracle.verify(to_host_logits(x), dh, dlh, T, u, nthreads=8)
+        compare_verify(*g, r, T, u, tally, what=f"fused {cfg.name} step {s}")
+        for b in range(cfg.B):
+            sams[b].extend(g[0][b, :g[1][b]])
+        n = n + g[1]
+    nd, ndl, nml = bufs[steps % 2]
+    ndh = nd.cpu().numpy()
+    for b in range(cfg.B):
+        od, odl, oml = sams[b].draft(cfg.K)
+        assert (od == ndh[b]).all() and odl == int(ndl[b]) and oml == int(nml[b])
+    for b in range(min(cfg.B, 4)):
+        e, o = st.export(b), sams[b].export()
+        np.testing.assert_array_equal(e["len"], o["len"])
+        np.testing.assert_array_equal(e["link"], o["link"])
+        np.testing.assert_array_equal(e["min_endpos"], o["min_endpos"])
+        np.testing.assert_array_equal(e["edges"], o["edges"])
+    assert (st.status().cpu().numpy() == 0).all()
+    say(f"    {tally}")
+
+
+def test_fused_c1_tiny_greedy():
+    _run_fused_workload(1, 300)
+
+
+def test_fused_c2_greedy_full_size():
+    _run_fused_workload(2, 5)
+
+
+def test_fused_c3_one_hot_full_size():
+    _run_fused_workload(3, 4)
+
+
+def test_fused_c3_shape_high_acceptance():
+    _run_fused_workload(3, 8, B=48, boost=12.0)
+
+
+def test_fused_c4_bf16_long_history():
+    _run_fused_workload(4, 3)
+
+
+def test_fused_step_flagged_sequence_keeps_automaton():
+    """A sequence whose draft_len is invalid is reported, not extended, and
+    still gets a next draft from its unchanged automaton."""
+    say("[gpu] fused step with a flagged sequence")
+    cfg = synth.config(1, B=3, V=50, hist_len=40)
+    gt = synth.token_streams(cfg, 2)
+    st = ssl.SamState(3, 100, cfg.V, "cuda")
+    st.extend(dev(gt[:, :40]), dev(np.full(3, 40, np.int32)))
+    d, dl, ml = st.draft(cfg.K)
+    dl_bad = dl.clone()
+    dl_bad[1] = cfg.K + 2
+    x = torch.zeros((3, cfg.K + 1, cfg.V), device="cuda")
+    out, nem, pd, status, nd, ndl, nml = ssl.spec_step(
+        x, d, dl_bad, dev(np.zeros(3, np.float32)), None, st)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [0, ssl.ST_DRAFT_LEN, 0]
+    e = st.export(1)
+    assert e["n"] == 40
+    o = oracle.SAM(gt[1, :40])
+    od, odl, oml = o.draft(cfg.K)
+    assert nd[1].cpu().tolist() == od.tolist() and int(ndl[1]) == odl

@@ -251,3 +251,27 @@ def test_full_size_draft_model_q():
     tally = Tally()
     compare_verify(*g, r, T, u, tally, what=cfg.name)
     say(f"    {tally}  mean tokens/step {g[1].mean():.3f}")
+
+
+def test_one_workspace_serves_every_shape_that_fits():
+    """The workspace is scratch: one buffer, with whatever the previous call
+    left in it, serves calls of any shape whose size fits."""
+    say("[gpu] workspace reuse across shapes")
+    ws = ssl.verify_workspace(40, 6, 40000)
+    ws.fill_(0xA5)
+    rng = np.random.default_rng(3)
+    for (B, K, V, T) in [(40, 6, 40000, 1.0), (40, 6, 40000, 0.0),
+                         (7, 2, 9000, 0.0), (33, 5, 12345, 0.8),
+                         (40, 6, 40000, 0.5), (1, 1, 17, 1.3), (1, 1, 17, 0.0)]:
+        x = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(np.float32)
+        dl = rng.integers(0, K + 1, B).astype(np.int32)
+        draft = _drafts_near_argmax(rng, x, K, dl, flip=0.5)
+        Ta = np.full(B, T, np.float32)
+        u = rng.random((B, K + 1)).astype(np.float32)
+        st = dev(np.zeros(B, np.int32))
+        g = ssl.spec_verify(torch.from_numpy(x).cuda(), dev(draft), dev(dl),
+                            dev(Ta), dev(u), workspace=ws, status=st)
+        torch.cuda.synchronize()
+        g = tuple(t.cpu().numpy() for t in g)
+        r = oracle.verify(x, draft, dl, Ta, u, nthreads=8)
+        compare_verify(*g, r, Ta, u, Tally(), what=f"reuse B={B} K={K} V={V}")
