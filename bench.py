@@ -1,6 +1,8 @@
 """Benchmark: batched spec-verify + SAM-draft steps on one MI355X.
 
-One step = sam_draft -> spec_verify -> sam_extend over the whole batch, on
+One step = verify the current drafts, extend every automaton with the
+emitted tokens and draft for the next step, over the whole batch (one
+spec_step call: the HBM stream pass, then the per-sequence finish pass), on
 the workload B=256, V=151936, K=3, T=1.0 with one-hot SAM drafts and 8,192-
 token histories (copy process, p_copy 0.6, span mean 8). Target logits are
 fp32 N(0, 2) noise from a ring of 4 device-resident slots (2.5 GB, far beyond
@@ -10,8 +12,10 @@ target model and sits inside the timed loop, so the reported rate is
 conservative). Inputs are resident in HBM when timing starts.
 
 Prints one JSON line (see the keys below). `roofline` is for the dominant
-kernel (verify pass 1): algorithmic bytes = rows verified x V x 4, timed with
-HIP events recorded on the launch stream around every verify call.
+kernel (the stream pass): algorithmic bytes = rows verified x V x 4, timed
+with HIP events recorded on the launch stream in a second pass that issues
+the same steps as spec_stream + spec_finish, around back-to-back batches of
+stream launches (per-launch time = event interval / batch size).
 `cpu_baseline` is the oracle (C++, double precision, std::map automata) on the
 host cores, on a bounded sample of the same workload.
 """
@@ -32,7 +36,7 @@ METRIC = ("spec-verify+SAM-draft steps/s at B=256,V=152k,K=3; "
           "achieved HBM GB/s")
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 RING = 4
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_pass1_c3_traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "spec_stream_c3_traffic.json")
 
 
 def _verify_source_hash() -> str:
@@ -97,6 +101,84 @@ def hbm_read_probe(torch, harness, nbytes=4 << 30, iters=5):
     return best
 
 
+def sam_stats_report(steps: int):
+    """Automaton work per appended token (hash lookups, 128-byte bucket reads,
+    suffix-link steps, clones) and time per extend call, for prefill and for
+    the per-step append, on the c3 and c4 histories and on a c3-shaped run
+    with a +12 boost (long accepted drafts)."""
+    import numpy as np
+    import torch
+
+    import sam_drafting_lossless_amd as ssl
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for c, over in [(3, {}), (4, {}), (3, {"boost": 12.0, "B": 256})]:
+        cfg = synth.config(c, **over)
+        gt_h = synth.token_streams(cfg, steps)
+        gt = torch.as_tensor(gt_h, device=dev)
+        H = cfg.hist_len
+        st = ssl.SamState(cfg.B, cfg.stream_len(steps), cfg.V, dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pre = st.extend_stats(gt[:, :H].contiguous(),
+                              torch.full((cfg.B,), H, dtype=torch.int32, device=dev))
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms = e0.elapsed_time(e1)
+        pre = pre.cpu().numpy()
+        # Per-step appends: the tokens the verifier emits, from the real step.
+        T = torch.full((cfg.B,), cfg.T, dtype=torch.float32, device=dev)
+        ws = ssl.verify_workspace(cfg.B, cfg.K, cfg.V, dev)
+        stats = torch.zeros(len(ssl.SAM_STATS), dtype=torch.int64, device=dev)
+        n = np.full(cfg.B, H, np.int32)
+        ext_us = []
+        for s in range(steps):
+            d, dl, ml = st.draft(cfg.K)
+            x = synth.target_logits(cfg, s, gt_h, n, device=dev)
+            u = torch.as_tensor(synth.uniforms(cfg, s), device=dev)
+            out, nem, _, _ = ssl.spec_verify(x, d, dl, T, u, workspace=ws)
+            e0.record()
+            st.extend_stats(out, nem, stats)
+            e1.record()
+            torch.cuda.synchronize()
+            ext_us.append(1e3 * e0.elapsed_time(e1))
+            n = n + nem.cpu().numpy()
+        per = stats.cpu().numpy()
+        names = ssl.SAM_STATS
+
+        def norm(v):
+            return {k: round(float(v[i]) / max(float(v[0]), 1.0), 4)
+                    for i, k in enumerate(names) if i > 0}
+        print(json.dumps({
+            "workload": cfg.name + ("" if not over else "_boost12"),
+            "B": cfg.B, "history": H,
+            "prefill": {"tokens": int(pre[0]), "ms": round(prefill_ms, 3),
+                        "tokens_per_s": round(float(pre[0]) / (prefill_ms * 1e-3)),
+                        "per_token": norm(pre)},
+            "steps": {"steps": steps, "tokens": int(per[0]),
+                      "tokens_per_step_per_seq": round(float(per[0]) / (steps * cfg.B), 3),
+                      "extend_us_median": round(float(np.median(ext_us)), 2),
+                      "per_token": norm(per)},
+            "status_ok": bool(int(st.status().abs().sum()) == 0)}), flush=True)
+
+
+def copy_probe(nbytes: int, iters: int = 5):
+    """A copy kernel of known size (the reference for hardware byte
+    counters): reads and writes `nbytes` per launch."""
+    import torch
+
+    from sam_drafting_lossless_amd import harness
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        harness.copy(dst, src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": iters}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,12 +187,23 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--sam-stats", action="store_true",
+                    help="report automaton work per token instead")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (the step shards by sequence with no exchange; see "
               "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sam_stats:
+        sam_stats_report(args.steps)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import numpy as np
     import torch
@@ -196,15 +289,36 @@ def main():
         if rc:
             raise RuntimeError("separate step failed: " + L.ss_last_error_string().decode())
 
-    def step(s, evs=None, path=fused):
-        if evs is not None:
-            evs[0].record()
+    STREAM_BATCH = 2 * RING
+
+    def timed_step(s, evs):
+        # The same step as spec_stream + spec_finish. The stream pass is
+        # launched STREAM_BATCH times back to back between two events, over
+        # every ring slot in turn (650 MB of distinct rows per cycle, so the
+        # re-reads do not come from the 256 MB Infinity Cache), ending with
+        # this step's slot so the workspace holds its statistics; one event
+        # pair per launch would add the event's own dispatch gap to each.
         boost(s)
-        if evs is not None:
-            evs[1].record()
+        evs[0].record()
+        rc = 0
+        for r in range(STREAM_BATCH):
+            slot = (s + 1 + r) % RING
+            rc |= L.spec_stream(ring_p[slot], 0, B, K, V, draft_p[s % 2],
+                                dl0 + s * rowB, temp_p, u0 + s * rowU, ws_p, ws_n,
+                                stream)
+        evs[1].record()
+        rc |= L.spec_finish(ring_p[s % RING], 0, B, K, V, draft_p[s % 2],
+                            dl0 + s * rowB, None, temp_p, u0 + s * rowU, out_p,
+                            nem0 + s * rowB, pd_p, status_p, st_p, max_len,
+                            draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
+                            ws_p, ws_n, stream)
+        evs[2].record()
+        if rc:
+            raise RuntimeError("two-pass step failed: " + L.ss_last_error_string().decode())
+
+    def step(s, path=fused):
+        boost(s)
         path(s)
-        if evs is not None:
-            evs[2].record()
 
     for s in range(args.warmup):
         step(s)
@@ -223,10 +337,11 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
            for _ in range(args.steps)]
     for i in range(args.steps):
-        step(first_ev + i, evs[i])
+        timed_step(first_ev + i, evs[i])
     torch.cuda.synchronize()
     dur = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in evs])
-    harness_us, step_kernel_us = (1e3 * dur.mean(axis=0)).tolist()
+    stream_us = 1e3 * dur[:, 0].mean() / STREAM_BATCH
+    finish_us = 1e3 * dur[:, 1].mean()
 
     # The same steps issued as separate library calls (verify, then extend +
     # draft), for comparison.
@@ -243,7 +358,7 @@ def main():
     nem = nem_hist[args.warmup:first_ev].cpu().numpy()
     rows_per_launch = float((dl + 1).sum(axis=1).mean())
     bytes_per_launch = rows_per_launch * V * 4
-    achieved = bytes_per_launch / (step_kernel_us * 1e-6) / 1e9
+    achieved = bytes_per_launch / (stream_us * 1e-6) / 1e9
     if int(status.cpu().abs().sum()) != 0 or int(st.status().abs().sum()) != 0:
         print("status words are non-zero: the run is invalid", file=sys.stderr)
         sys.exit(1)
@@ -280,9 +395,11 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": _traffic_from_profile(rows_per_launch, V)},
         "cpu_baseline": cpu,
-        "path": "spec_step (one kernel per step: verify + SAM extend + next draft)",
-        "step_kernel_avg_us": step_kernel_us,
-        "harness_boost_avg_us": harness_us,
+        "path": "spec_step (stream pass, then finish pass: decisions, draws, "
+                "SAM extend, next draft)",
+        "stream_pass_avg_us": stream_us,
+        "finish_pass_event_us": finish_us,
+        "stream_launches_per_event_pair": STREAM_BATCH,
         "separate_calls_steps_per_s": separate_steps_s,
         "verified_rows_per_launch": rows_per_launch,
         "verify_bytes_per_launch": bytes_per_launch,

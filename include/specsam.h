@@ -152,6 +152,32 @@ int spec_step(const void* logits, int dtype, int B, int K, int V,
               int32_t* next_draft_len, int32_t* next_match_len,
               void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * The two passes of spec_verify / spec_step as separate calls, for callers
+ * that schedule them (and for timing the HBM pass alone):
+ *   spec_stream  reads the logit rows j <= draft_len once and leaves per-row
+ *                statistics in the workspace.
+ *   spec_finish  judges the drafts, draws the recovered / bonus tokens (with
+ *                the residual pass when q is given) and, when sam_state is
+ *                non-NULL, updates the automata and writes the next drafts
+ *                (then q must be NULL and the next-draft outputs non-NULL).
+ * spec_finish must follow spec_stream on the same stream with the same
+ * logits, sizes, drafts, temperatures, uniforms and workspace.
+ */
+int spec_stream(const void* logits, int dtype, int B, int K, int V,
+                const int32_t* draft, const int32_t* draft_len,
+                const float* temperature, const float* uniforms,
+                void* workspace, size_t ws_bytes, void* stream);
+
+int spec_finish(const void* logits, int dtype, int B, int K, int V,
+                const int32_t* draft, const int32_t* draft_len, const float* q,
+                const float* temperature, const float* uniforms,
+                int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
+                int32_t* status, void* sam_state, int max_len,
+                int32_t* next_draft, int32_t* next_draft_len,
+                int32_t* next_match_len, void* workspace, size_t ws_bytes,
+                void* stream);
+
 /* ========================================================================= *
  * Dynamic suffix automaton ([P1] §1.1, [P4] §3)
  *
@@ -199,6 +225,15 @@ int sam_extend_draft(void* state, int B, int max_len, const int32_t* tokens,
                      int ld_tokens, const int32_t* counts, int K,
                      int32_t* draft, int32_t* draft_len, int32_t* match_len,
                      void* stream);
+
+/* Measurement: sam_extend with work counters. Adds, over all sequences, to
+ * stats[7] (uint64, device): tokens appended, hash lookups, 128-byte buckets
+ * read by them, suffix-link steps that inserted a transition, clones,
+ * transitions copied into clones, transitions redirected to clones. The
+ * automaton ends up exactly as after sam_extend. */
+int sam_extend_stats(void* state, int B, int max_len, const int32_t* tokens,
+                     int ld_tokens, const int32_t* counts,
+                     unsigned long long* stats, void* stream);
 
 /* Copies the sticky per-sequence status words to status_out [B] int32. */
 int sam_status(const void* state, int B, int max_len, int32_t* status_out,

@@ -59,6 +59,11 @@ def lib():
     L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, P,
                             P, P, P, P, P, sz, P]
     L.spec_step.restype = i32
+    L.spec_stream.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.spec_stream.restype = i32
+    L.spec_finish.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                              P, i32, P, P, P, P, sz, P]
+    L.spec_finish.restype = i32
     L.sam_extend_draft.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P]
     L.sam_extend_draft.restype = i32
     L.sam_state_bytes.argtypes = [i32, i32]
@@ -71,6 +76,8 @@ def lib():
     L.sam_extend.restype = i32
     L.sam_draft.argtypes = [P, i32, i32, i32, P, P, P, P]
     L.sam_draft.restype = i32
+    L.sam_extend_stats.argtypes = [P, i32, i32, P, i32, P, P, P]
+    L.sam_extend_stats.restype = i32
     L.sam_status.argtypes = [P, i32, i32, P, P]
     L.sam_status.restype = i32
     L.sam_export.argtypes = [P, i32, i32, i32, P, P, P, P, P]
@@ -221,6 +228,88 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
             next_draft_len, next_match_len)
 
 
+def _shape(logits):
+    if logits.dim() != 3:
+        raise SpecSamError("logits must be [B, K+1, V]")
+    B, R, V = logits.shape
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(logits.dtype)
+    if dt is None:
+        raise SpecSamError("logits must be float32 or bfloat16")
+    return B, R - 1, V, dt
+
+
+def spec_stream(logits, draft, draft_len, temperature, uniforms, workspace, *,
+                stream=None):
+    """First pass of a verification (see include/specsam.h): read the logit
+    rows once and leave per-row statistics in `workspace`."""
+    B, K, V, dt = _shape(logits)
+    i32 = torch.int32
+    _check(lib().spec_stream(
+        _dev(logits, "logits"), dt, B, K, V,
+        _dev(draft, "draft", i32, (B, K)),
+        _dev(draft_len, "draft_len", i32, (B,)),
+        _dev(temperature, "temperature", torch.float32, (B,)),
+        None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
+                                           (B, K + 1)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "spec_stream")
+
+
+def spec_finish(logits, draft, draft_len, temperature, uniforms, workspace,
+                q=None, state=None, *, out_tokens=None, num_emitted=None,
+                p_draft=None, status=None, next_draft=None, next_draft_len=None,
+                next_match_len=None, stream=None):
+    """Second pass (see include/specsam.h), after spec_stream with the same
+    arguments and workspace. Returns (out_tokens, num_emitted, p_draft,
+    status), followed by (next_draft, next_draft_len, next_match_len) when
+    `state` (a SamState) is given."""
+    B, K, V, dt = _shape(logits)
+    R = K + 1
+    dev = logits.device
+    i32 = torch.int32
+    if out_tokens is None:
+        out_tokens = torch.empty((B, R), dtype=i32, device=dev)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=i32, device=dev)
+    if p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.zeros(B, dtype=i32, device=dev)
+    if state is not None:
+        if state.B != B:
+            raise SpecSamError("state holds a different number of sequences")
+        if next_draft is None:
+            next_draft = torch.empty((B, K), dtype=i32, device=dev)
+        if next_draft_len is None:
+            next_draft_len = torch.empty(B, dtype=i32, device=dev)
+        if next_match_len is None:
+            next_match_len = torch.empty(B, dtype=i32, device=dev)
+    opt = lambda t, name, shape: None if t is None else _dev(t, name, i32, shape)
+    _check(lib().spec_finish(
+        _dev(logits, "logits"), dt, B, K, V,
+        _dev(draft, "draft", i32, (B, K)),
+        _dev(draft_len, "draft_len", i32, (B,)),
+        None if q is None else _dev(q, "q", torch.float32, (B, K, V)),
+        _dev(temperature, "temperature", torch.float32, (B,)),
+        None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
+                                           (B, R)),
+        _dev(out_tokens, "out_tokens", i32, (B, R)),
+        _dev(num_emitted, "num_emitted", i32, (B,)),
+        _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _dev(status, "status", i32, (B,)),
+        None if state is None else _dev(state.buf, "state", torch.uint8),
+        0 if state is None else state.max_len,
+        opt(next_draft, "next_draft", (B, K)),
+        opt(next_draft_len, "next_draft_len", (B,)),
+        opt(next_match_len, "next_match_len", (B,)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "spec_finish")
+    res = (out_tokens, num_emitted, p_draft, status)
+    if state is not None:
+        res += (next_draft, next_draft_len, next_match_len)
+    return res
+
+
 # ------------------------------------------------------- suffix automaton ----
 def sam_state_bytes(B: int, max_len: int) -> int:
     return int(lib().sam_state_bytes(B, max_len))
@@ -284,6 +373,27 @@ def sam_extend_draft(state, B: int, max_len: int, tokens, counts, K: int,
     return draft, draft_len, match_len
 
 
+SAM_STATS = ("tokens", "probes", "buckets", "walk_steps", "clones",
+             "copied", "redirects")
+
+
+def sam_extend_stats(state, B: int, max_len: int, tokens, counts, stats=None,
+                     stream=None):
+    """sam_extend with work counters; returns the uint64 stats tensor [7]
+    (accumulated into `stats` if given)."""
+    if stats is None:
+        stats = torch.zeros(len(SAM_STATS), dtype=torch.int64, device=state.device)
+    if tokens.dim() != 2 or tokens.shape[0] != B:
+        raise SpecSamError("tokens must be [B, ld]")
+    _check(lib().sam_extend_stats(
+        _dev(state, "state", torch.uint8), B, max_len,
+        _dev(tokens, "tokens", torch.int32), int(tokens.shape[1]),
+        _dev(counts, "counts", torch.int32, (B,)),
+        _dev(stats, "stats", torch.int64, (len(SAM_STATS),)), _stream(stream)),
+        "sam_extend_stats")
+    return stats
+
+
 def sam_status(state, B: int, max_len: int, out=None, stream=None):
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=state.device)
@@ -343,6 +453,10 @@ class SamState:
                      match_len=None, stream=None):
         return sam_extend_draft(self.buf, self.B, self.max_len, tokens, counts,
                                 K, draft, draft_len, match_len, stream)
+
+    def extend_stats(self, tokens, counts, stats=None, stream=None):
+        return sam_extend_stats(self.buf, self.B, self.max_len, tokens, counts,
+                                stats, stream)
 
     def status(self, out=None, stream=None):
         return sam_status(self.buf, self.B, self.max_len, out, stream)

@@ -20,6 +20,23 @@ __global__ __launch_bounds__(kWave) void sam_extend_kernel(
                  max_len);
 }
 
+// The same extension with work counters, summed into stats[SS_STAT_COUNT].
+__global__ __launch_bounds__(kWave) void sam_extend_stats_kernel(
+    unsigned char* base, int max_len, SamLayout L, const int32_t* tokens,
+    int ld, const int32_t* counts, unsigned long long* stats) {
+  const int b = blockIdx.x;
+  SamCounters ctr = {};
+  sam_extend_seq<true>(sam_seq(base, b, L), tokens + (int64_t)b * ld, counts[b],
+                       ld, max_len, &ctr);
+  if (lane_id() < SS_STAT_COUNT) {
+    unsigned long long v = 0;
+#pragma unroll
+    for (int k = 0; k < SS_STAT_COUNT; ++k)
+      if (lane_id() == k) v = ctr.v[k];
+    atomicAdd(stats + lane_id(), v);
+  }
+}
+
 // One wavefront per sequence.
 __global__ __launch_bounds__(kWave) void sam_draft_kernel(
     const unsigned char* base, SamLayout L, int K, int32_t* draft,
@@ -115,6 +132,21 @@ extern "C" int sam_extend(void* state, int B, int max_len, const int32_t* tokens
                      as_stream(stream), reinterpret_cast<unsigned char*>(state),
                      max_len, L, tokens, ld_tokens, counts);
   return check_launch("sam_extend");
+}
+
+extern "C" int sam_extend_stats(void* state, int B, int max_len,
+                                const int32_t* tokens, int ld_tokens,
+                                const int32_t* counts, unsigned long long* stats,
+                                void* stream) {
+  int rc = check_dims("sam_extend_stats", state, B, max_len);
+  if (rc) return rc;
+  if (!tokens || !counts || ld_tokens < 0 || !stats)
+    return set_error(SS_EINVAL, "sam_extend_stats: null pointer or ld < 0");
+  const SamLayout L = sam_layout(max_len);
+  hipLaunchKernelGGL(sam_extend_stats_kernel, dim3((unsigned)B), dim3(kWave), 0,
+                     as_stream(stream), reinterpret_cast<unsigned char*>(state),
+                     max_len, L, tokens, ld_tokens, counts, stats);
+  return check_launch("sam_extend_stats");
 }
 
 extern "C" int sam_draft(const void* state, int B, int max_len, int K,

@@ -93,6 +93,24 @@ struct SamProbe {
   int slot;  // row of (s, c), or the first empty row in probe order; -1 if full
   bool found;
   int dst;
+  int buckets;  // 128-byte buckets read
+};
+
+// Work counters of the extension (measurement builds of the kernels only;
+// the counting template parameter is false on the normal path).
+enum SamStat {
+  SS_STAT_TOKENS = 0,    // tokens appended
+  SS_STAT_PROBES,        // hash lookups (each one or more bucket reads)
+  SS_STAT_BUCKETS,       // 128-byte buckets read by those lookups
+  SS_STAT_WALK,          // suffix-link steps that inserted a transition
+  SS_STAT_CLONES,        // states cloned
+  SS_STAT_COPIED,        // transitions copied into clones
+  SS_STAT_REDIRECTS,     // transitions redirected to clones
+  SS_STAT_COUNT
+};
+
+struct SamCounters {
+  unsigned long long v[SS_STAT_COUNT];
 };
 
 // Wave-cooperative lookup of (s, c). Uniform in, uniform out.
@@ -112,11 +130,12 @@ __device__ __forceinline__ SamProbe sam_probe(const i32x4* slots, unsigned bmask
       r.slot = (int)(bk * kBucket) + f;
       r.found = (__ballot(m) >> f) & 1ull;
       r.dst = __shfl(v.z, f, kWave);
+      r.buckets = (int)it + 1;
       return r;
     }
     bk = (bk + 1) & bmask;
   }
-  return SamProbe{-1, false, -1};
+  return SamProbe{-1, false, -1, (int)bmask + 1};
 }
 
 struct SamHdrRegs {
@@ -137,8 +156,13 @@ __device__ __forceinline__ void sam_store_header(const SamSeq& S,
 
 // Appends token c at position n (Blumer's online extension; `cur` is numbered
 // before `clone`). Returns false if a bound check trips.
+template <bool COUNT = false>
 __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
-                                      unsigned bmask) {
+                                      unsigned bmask, SamCounters* ctr = nullptr) {
+  auto tally = [&](int k, int n) {
+    if constexpr (COUNT) ctr->v[k] += (unsigned long long)n;
+  };
+  tally(SS_STAT_TOKENS, 1);
   const int i = h.n;
   const int cur = h.nstates++;
   i32x4 rp = S.st[h.last];
@@ -152,8 +176,11 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
     i32x4 rn = i32x4{0, -1, -1, -1};
     if (nxt != -1) rn = S.st[nxt];  // in flight together with the probe
     pr = sam_probe(S.slots, bmask, p, c);
+    tally(SS_STAT_PROBES, 1);
+    tally(SS_STAT_BUCKETS, pr.buckets);
     if (pr.slot < 0) return false;
     if (pr.found) break;
+    tally(SS_STAT_WALK, 1);
     S.slots[pr.slot] = i32x4{p, c, cur, rp.w};
     reinterpret_cast<int*>(&S.st[p])[3] = pr.slot;
     h.nedges++;
@@ -171,11 +198,15 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
       reinterpret_cast<int*>(&S.st[cur])[1] = q;
     } else {
       const int clone = h.nstates++;
+      tally(SS_STAT_CLONES, 1);
       // Copy q's transitions into the clone.
       int first = -1, e = rq.w, g2 = 0;
       while (e != -1) {
         const i32x4 se = S.slots[e];
         const SamProbe pc = sam_probe(S.slots, bmask, clone, se.y);
+        tally(SS_STAT_PROBES, 1);
+        tally(SS_STAT_BUCKETS, pc.buckets);
+        tally(SS_STAT_COPIED, 1);
         if (pc.slot < 0 || pc.found) return false;
         S.slots[pc.slot] = i32x4{clone, se.y, se.z, first};
         first = pc.slot;
@@ -190,10 +221,13 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
       int g3 = 0;
       while (true) {
         reinterpret_cast<int*>(&S.slots[sl])[2] = clone;
+        tally(SS_STAT_REDIRECTS, 1);
         const int pp = rr.y;
         if (pp == -1) break;
         rr = S.st[pp];
         const SamProbe p3 = sam_probe(S.slots, bmask, pp, c);
+        tally(SS_STAT_PROBES, 1);
+        tally(SS_STAT_BUCKETS, p3.buckets);
         if (p3.slot < 0 || !p3.found || p3.dst != q) break;
         sl = p3.slot;
         if (++g3 > h.nstates) return false;
@@ -211,8 +245,10 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
 // Appends tokens tk[0..cnt) (wave-uniform) to one sequence, stopping at the
 // first token that is out of range or would exceed capacity. A sequence whose
 // status is already non-zero is left alone. Executed by one whole wavefront.
+template <bool COUNT = false>
 __device__ inline void sam_extend_seq(const SamSeq& S, const int32_t* tk,
-                                      int cnt, int ld, int max_len) {
+                                      int cnt, int ld, int max_len,
+                                      SamCounters* ctr = nullptr) {
   SamHdrRegs h = sam_load_header(S);
   if (h.status != 0) return;
   const unsigned bmask = (unsigned)(h.slots / kBucket) - 1u;
@@ -227,7 +263,7 @@ __device__ inline void sam_extend_seq(const SamSeq& S, const int32_t* tk,
         break;
       }
       if (h.n >= max_len || h.nstates + 2 > 2 * max_len ||
-          !sam_extend_one(S, h, c, bmask)) {
+          !sam_extend_one<COUNT>(S, h, c, bmask, ctr)) {
         st = SS_ST_SAM_CAPACITY;
         break;
       }

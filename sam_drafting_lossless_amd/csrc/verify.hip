@@ -828,37 +828,48 @@ WsLayout ws_layout(int B, int K, int V) {
 // several resident workgroups.
 constexpr int64_t kTargetWorkgroups = 4096;
 
-template <int DT, bool VP, bool SAM>
-int launch(Args a, hipStream_t s) {
+// Grid of the stream pass: (sequence, row group, chunk).
+inline void set_row_groups(Args& a) {
   const int R = a.K + 1;
   const int64_t base = (int64_t)a.B * a.nchunks;
   const int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
   a.rows_per_wg = (R + ngroups - 1) / ngroups;
   a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
-  const int64_t grid1 = base * a.ngroups;
-  if (grid1 > INT_MAX) return set_error(SS_EINVAL, "spec_verify: grid too large");
-  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid1),
+}
+
+template <int DT, bool VP>
+int launch_stream(const Args& a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.B * a.nchunks * a.ngroups;
+  if (grid > INT_MAX) return set_error(SS_EINVAL, "spec_stream: grid too large");
+  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid),
                      dim3(kThreads), 0, s, a);
-  int rc = check_launch("spec_verify stream pass");
-  if (rc != SS_OK) return rc;
+  return check_launch("spec_stream");
+}
+
+template <int DT, bool VP, bool SAM>
+int launch_finish(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM>), dim3((unsigned)a.B),
                      dim3(kThreads), 0, s, a);
-  rc = check_launch("spec_verify finalize");
+  int rc = check_launch("spec_finish");
   if (rc != SS_OK || a.q == nullptr) return rc;
-  hipLaunchKernelGGL((verify_residual_sums<DT, VP>), dim3((unsigned)base),
-                     dim3(kThreads), 0, s, a);
-  rc = check_launch("spec_verify residual sums");
+  hipLaunchKernelGGL((verify_residual_sums<DT, VP>),
+                     dim3((unsigned)((int64_t)a.B * a.nchunks)), dim3(kThreads), 0, s,
+                     a);
+  rc = check_launch("spec_finish residual sums");
   if (rc != SS_OK) return rc;
   hipLaunchKernelGGL((verify_residual_draw<DT, VP>), dim3((unsigned)a.B),
                      dim3(kThreads), 0, s, a);
-  return check_launch("spec_verify residual draw");
+  return check_launch("spec_finish residual draw");
 }
 
-int run(const void* logits, int dtype, int B, int K, int V, const int32_t* draft,
-        const int32_t* draft_len, const float* q, const float* temperature,
-        const float* uniforms, int32_t* out_tokens, int32_t* num_emitted,
-        float* p_draft, int32_t* status, void* workspace, size_t ws_bytes,
-        void* sam_state, int max_len, int32_t* next_draft,
+// Which passes to launch.
+enum Passes { kStream = 1, kFinish = 2 };
+
+int run(int passes, const void* logits, int dtype, int B, int K, int V,
+        const int32_t* draft, const int32_t* draft_len, const float* q,
+        const float* temperature, const float* uniforms, int32_t* out_tokens,
+        int32_t* num_emitted, float* p_draft, int32_t* status, void* workspace,
+        size_t ws_bytes, void* sam_state, int max_len, int32_t* next_draft,
         int32_t* next_draft_len, int32_t* next_match_len, void* stream,
         const char* fn) {
   if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV)
@@ -868,11 +879,25 @@ int run(const void* logits, int dtype, int B, int K, int V, const int32_t* draft
                      fn, SS_MAX_K, kMaxV, B, K, V);
   if (dtype != SS_DTYPE_F32 && dtype != SS_DTYPE_BF16)
     return set_error(SS_EINVAL, "%s: unknown dtype %d", fn, dtype);
-  if (!logits || !draft || !draft_len || !temperature || !out_tokens ||
-      !num_emitted || !status || !workspace)
+  if (!logits || !draft || !draft_len || !temperature || !workspace)
     return set_error(SS_EINVAL, "%s: a required pointer is NULL", fn);
+  if ((passes & kFinish) && (!out_tokens || !num_emitted || !status))
+    return set_error(SS_EINVAL, "%s: an output pointer is NULL", fn);
   if ((uintptr_t)workspace & 255)
     return set_error(SS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (sam_state) {
+    if (((uintptr_t)sam_state & 255) || max_len < 1 || max_len > SS_MAX_LEN)
+      return set_error(SS_EINVAL, "%s: state must be 256-byte aligned and "
+                                  "1 <= max_len <= %d", fn, SS_MAX_LEN);
+    if (q)
+      return set_error(SS_EINVAL, "%s: the automaton step takes one-hot drafts "
+                                  "(q must be NULL)", fn);
+    if (!next_draft || !next_draft_len || !next_match_len)
+      return set_error(SS_EINVAL, "%s: next-draft outputs must be non-null", fn);
+    if (next_draft == draft || next_draft_len == draft_len)
+      return set_error(SS_EINVAL, "%s: next-draft outputs must not alias the "
+                                  "drafts being verified", fn);
+  }
   const WsLayout L = ws_layout(B, K, V);
   if (ws_bytes < L.total)
     return set_error(SS_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn,
@@ -884,8 +909,6 @@ int run(const void* logits, int dtype, int B, int K, int V, const int32_t* draft
   a.K = K;
   a.V = V;
   a.nchunks = nchunks_for(V, dtype);
-  a.rows_per_wg = 1;
-  a.ngroups = K + 1;
   a.draft = draft;
   a.draft_len = draft_len;
   a.q = q;
@@ -904,22 +927,33 @@ int run(const void* logits, int dtype, int B, int K, int V, const int32_t* draft
   a.next_draft = next_draft;
   a.next_draft_len = next_draft_len;
   a.next_match_len = next_match_len;
+  set_row_groups(a);
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
   const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0) &&
                   (q == nullptr || ((uintptr_t)q & 15) == 0);
   hipStream_t s = as_stream(stream);
-  if (sam_state) {
-    if (dtype == SS_DTYPE_F32)
-      return vp ? launch<SS_DTYPE_F32, true, true>(a, s)
-                : launch<SS_DTYPE_F32, false, true>(a, s);
-    return vp ? launch<SS_DTYPE_BF16, true, true>(a, s)
-              : launch<SS_DTYPE_BF16, false, true>(a, s);
+  const bool f32 = dtype == SS_DTYPE_F32;
+  int rc = SS_OK;
+  if (passes & kStream) {
+    rc = f32 ? (vp ? launch_stream<SS_DTYPE_F32, true>(a, s)
+                   : launch_stream<SS_DTYPE_F32, false>(a, s))
+             : (vp ? launch_stream<SS_DTYPE_BF16, true>(a, s)
+                   : launch_stream<SS_DTYPE_BF16, false>(a, s));
+    if (rc != SS_OK) return rc;
   }
-  if (dtype == SS_DTYPE_F32)
-    return vp ? launch<SS_DTYPE_F32, true, false>(a, s)
-              : launch<SS_DTYPE_F32, false, false>(a, s);
-  return vp ? launch<SS_DTYPE_BF16, true, false>(a, s)
-            : launch<SS_DTYPE_BF16, false, false>(a, s);
+  if (passes & kFinish) {
+    if (sam_state)
+      rc = f32 ? (vp ? launch_finish<SS_DTYPE_F32, true, true>(a, s)
+                     : launch_finish<SS_DTYPE_F32, false, true>(a, s))
+               : (vp ? launch_finish<SS_DTYPE_BF16, true, true>(a, s)
+                     : launch_finish<SS_DTYPE_BF16, false, true>(a, s));
+    else
+      rc = f32 ? (vp ? launch_finish<SS_DTYPE_F32, true, false>(a, s)
+                     : launch_finish<SS_DTYPE_F32, false, false>(a, s))
+               : (vp ? launch_finish<SS_DTYPE_BF16, true, false>(a, s)
+                     : launch_finish<SS_DTYPE_BF16, false, false>(a, s));
+  }
+  return rc;
 }
 
 }  // namespace
@@ -938,9 +972,10 @@ extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
                            const float* uniforms, int32_t* out_tokens,
                            int32_t* num_emitted, float* p_draft, int32_t* status,
                            void* workspace, size_t ws_bytes, void* stream) {
-  return run(logits, dtype, B, K, V, draft, draft_len, q, temperature, uniforms,
-             out_tokens, num_emitted, p_draft, status, workspace, ws_bytes,
-             nullptr, 0, nullptr, nullptr, nullptr, stream, "spec_verify");
+  return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len, q,
+             temperature, uniforms, out_tokens, num_emitted, p_draft, status,
+             workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
+             "spec_verify");
 }
 
 extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
@@ -951,17 +986,34 @@ extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
                          int32_t* next_draft, int32_t* next_draft_len,
                          int32_t* next_match_len, void* workspace,
                          size_t ws_bytes, void* stream) {
-  if (!sam_state || ((uintptr_t)sam_state & 255) || max_len < 1 ||
-      max_len > SS_MAX_LEN)
-    return set_error(SS_EINVAL, "spec_step: state must be non-null and 256-byte "
-                                "aligned, 1 <= max_len <= %d", SS_MAX_LEN);
-  if (!next_draft || !next_draft_len || !next_match_len)
-    return set_error(SS_EINVAL, "spec_step: next-draft outputs must be non-null");
-  if (next_draft == draft || next_draft_len == draft_len)
-    return set_error(SS_EINVAL, "spec_step: next-draft outputs must not alias "
-                                "the drafts being verified");
-  return run(logits, dtype, B, K, V, draft, draft_len, nullptr, temperature,
+  if (!sam_state)
+    return set_error(SS_EINVAL, "spec_step: state is NULL");
+  return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len,
+             nullptr, temperature, uniforms, out_tokens, num_emitted, p_draft,
+             status, workspace, ws_bytes, sam_state, max_len, next_draft,
+             next_draft_len, next_match_len, stream, "spec_step");
+}
+
+extern "C" int spec_stream(const void* logits, int dtype, int B, int K, int V,
+                           const int32_t* draft, const int32_t* draft_len,
+                           const float* temperature, const float* uniforms,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  return run(kStream, logits, dtype, B, K, V, draft, draft_len, nullptr,
+             temperature, uniforms, nullptr, nullptr, nullptr, nullptr, workspace,
+             ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
+             "spec_stream");
+}
+
+extern "C" int spec_finish(const void* logits, int dtype, int B, int K, int V,
+                           const int32_t* draft, const int32_t* draft_len,
+                           const float* q, const float* temperature,
+                           const float* uniforms, int32_t* out_tokens,
+                           int32_t* num_emitted, float* p_draft, int32_t* status,
+                           void* sam_state, int max_len, int32_t* next_draft,
+                           int32_t* next_draft_len, int32_t* next_match_len,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  return run(kFinish, logits, dtype, B, K, V, draft, draft_len, q, temperature,
              uniforms, out_tokens, num_emitted, p_draft, status, workspace,
              ws_bytes, sam_state, max_len, next_draft, next_draft_len,
-             next_match_len, stream, "spec_step");
+             next_match_len, stream, "spec_finish");
 }

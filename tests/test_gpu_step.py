@@ -193,3 +193,51 @@ def test_fused_step_flagged_sequence_keeps_automaton():
     o = oracle.SAM(gt[1, :40])
     od, odl, oml = o.draft(cfg.K)
     assert nd[1].cpu().tolist() == od.tolist() and int(ndl[1]) == odl
+
+
+def test_two_pass_calls_match_one_call_forms():
+    """spec_stream followed by spec_finish gives bit-identical results to
+    spec_step (automaton update) and to spec_verify (given q, residual pass),
+    and the automata end up identical."""
+    cfg = synth.config(3, B=48, boost=12.0)
+    say("[gpu] two-pass calls vs one-call forms")
+    steps = 4
+    gt = synth.token_streams(cfg, steps)
+    H = cfg.hist_len
+    n = np.full(cfg.B, H, np.int32)
+    ml_cap = cfg.stream_len(steps)
+    sts = [ssl.SamState(cfg.B, ml_cap, cfg.V, "cuda") for _ in range(2)]
+    for st in sts:
+        st.extend(dev(gt[:, :H]), dev(np.full(cfg.B, H, np.int32)))
+    Td = dev(np.full(cfg.B, cfg.T, np.float32))
+    ws = [ssl.verify_workspace(cfg.B, cfg.K, cfg.V) for _ in range(2)]
+    d, dl, ml = sts[0].draft(cfg.K)
+    for s in range(steps):
+        x = synth.target_logits(cfg, s, gt, n, device="cuda")
+        u = dev(synth.uniforms(cfg, s))
+        a = ssl.spec_step(x, d, dl, Td, u, sts[0], workspace=ws[0])
+        ssl.spec_stream(x, d, dl, Td, u, ws[1])
+        b = ssl.spec_finish(x, d, dl, Td, u, ws[1], state=sts[1])
+        torch.cuda.synchronize()
+        for ta, tb in zip(a, b):
+            assert torch.equal(ta, tb), s
+        n = n + a[1].cpu().numpy()
+        d, dl, ml = a[4], a[5], a[6]
+    for bq in range(cfg.B):
+        ea, eb = sts[0].export(bq), sts[1].export(bq)
+        for k in ("len", "link", "min_endpos", "edges"):
+            np.testing.assert_array_equal(ea[k], eb[k])
+    c5 = synth.config(5, B=16)
+    x = synth.noise(c5, 0, "cuda")
+    q, draft = synth.draft_model_inputs(c5, 0, x, "cuda")
+    u = dev(synth.uniforms(c5, 0))
+    T = dev(np.full(c5.B, c5.T, np.float32))
+    dl = dev(np.full(c5.B, c5.K, np.int32))
+    dd = dev(draft)
+    a = ssl.spec_verify(x, dd, dl, T, u, q)
+    w = ssl.verify_workspace(c5.B, c5.K, c5.V)
+    ssl.spec_stream(x, dd, dl, T, u, w)
+    b = ssl.spec_finish(x, dd, dl, T, u, w, q)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)

@@ -168,6 +168,13 @@ def test_host_argument_errors():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(ssl.SpecSamError, match="workspace"):
         ssl.spec_verify(x, i, d, T, workspace=ws)
+    with pytest.raises(ssl.SpecSamError, match="workspace"):
+        ssl.spec_stream(x, i, d, T, None, ws)
+    st = ssl.SamState(2, 16, 8, "cuda")
+    q = torch.full((2, 3, 8), 0.125, device="cuda")
+    w = ssl.verify_workspace(2, 3, 8)
+    with pytest.raises(ssl.SpecSamError, match="one-hot"):
+        ssl.spec_finish(x, i, d, T, None, w, q, st)
 
 
 @pytest.mark.parametrize("mode", ["onehot", "given_q"])
