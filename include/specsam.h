@@ -79,7 +79,8 @@ const char* ss_last_error_string(void);
 /* Bytes of workspace spec_verify / spec_step need for (B, K, V); 0 if
  * unsupported. The workspace is scratch owned by the caller (256-byte
  * aligned): it needs no initialisation, its contents between calls do not
- * matter, and one buffer serves any call whose size fits. */
+ * matter, and one buffer serves any call whose size fits. A workspace must
+ * not serve two calls that may run concurrently. */
 size_t ss_verify_workspace_bytes(int B, int K, int V);
 
 /*

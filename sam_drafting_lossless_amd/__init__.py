@@ -118,7 +118,7 @@ def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
 
 def verify_workspace(B: int, K: int, V: int, device=None):
     """A workspace tensor (uint8) for spec_verify / spec_step calls of this
-    size (or smaller)."""
+    size (or smaller); it needs no initialisation."""
     n = ss_verify_workspace_bytes(B, K, V)
     if n == 0:
         raise SpecSamError(f"unsupported sizes B={B} K={K} V={V}")

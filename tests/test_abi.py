@@ -58,3 +58,20 @@ def test_library_loads_and_answers_size_queries():
     assert rc == -1
     L.ss_last_error_string.restype = ctypes.c_char_p
     assert b"B >= 1" in L.ss_last_error_string()
+
+
+def test_binding_constants_match_the_header():
+    import sam_drafting_lossless_amd as ssl
+    src = open(HEADER).read()
+    defs = {k: v.strip() for k, v in
+            re.findall(r"#define\s+(SS_\w+)[ \t]+([-() <0-9x]+)", src)}
+
+    def val(name):  # integer literals and shifts only
+        assert re.fullmatch(r"[-() <0-9x]+", defs[name])
+        return eval(defs[name], {"__builtins__": {}})
+
+    assert val("SS_DTYPE_F32") == ssl.DTYPE_F32
+    assert val("SS_DTYPE_BF16") == ssl.DTYPE_BF16
+    for n in ("SAM_CAPACITY", "TOKEN_RANGE", "DRAFT_LEN", "NONFINITE",
+              "TEMPERATURE", "NO_UNIFORMS"):
+        assert val("SS_ST_" + n) == getattr(ssl, "ST_" + n), n

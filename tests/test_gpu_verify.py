@@ -282,3 +282,27 @@ def test_one_workspace_serves_every_shape_that_fits():
         g = tuple(t.cpu().numpy() for t in g)
         r = oracle.verify(x, draft, dl, Ta, u, nthreads=8)
         compare_verify(*g, r, Ta, u, Tally(), what=f"reuse B={B} K={K} V={V}")
+
+
+@pytest.mark.parametrize("B", [2048, 2049])
+@pytest.mark.parametrize("lengths", ["empty", "full", "mixed"])
+def test_row_balancing_across_batch_sizes(B, lengths):
+    """The stream pass deals (row, chunk) items round-robin to a resident grid
+    up to B = 2048 and streams rows per sequence above it; both give the oracle's
+    results for all-empty, all-full and mixed draft lengths (with invalid
+    lengths mixed in, which are reported and need no rows)."""
+    say(f"[gpu] row balancing B={B} {lengths}")
+    rng = np.random.default_rng(B + len(lengths))
+    K, V = 3, 9000  # two chunks, the second ragged
+    x = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(np.float32)
+    if lengths == "empty":
+        dl = np.zeros(B, np.int32)
+    elif lengths == "full":
+        dl = np.full(B, K, np.int32)
+    else:
+        dl = rng.choice([0, 0, 0, 1, 2, 3, -1, 4], B).astype(np.int32)
+    draft = _drafts_near_argmax(rng, x, K, np.clip(dl, 0, K), flip=0.5)
+    T = np.where(rng.random(B) < 0.5, 0.0, 0.9).astype(np.float32)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
+    compare_verify(*g, r, T, u, Tally(), what=f"balance B={B} {lengths}")
