@@ -39,21 +39,30 @@ RING = 4
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "spec_stream_c3_traffic.json")
 
 
-def _verify_source_hash() -> str:
-    p = os.path.join(ROOT, "sam_drafting_lossless_amd", "csrc", "verify.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+STREAM_SOURCES = ("stream.hip", "verify_common.h", "internal.h")
 
 
-def _traffic_from_profile(rows_per_launch: float, V: int):
-    """HBM bytes per verify launch from the committed rocprofv3 counter
-    summary, if it was taken on the current verify source."""
+def stream_source_hash() -> str:
+    """Digest of the sources the stream kernel is written in; a traffic
+    record taken on other sources is stale."""
+    h = hashlib.sha256()
+    for name in STREAM_SOURCES:
+        p = os.path.join(ROOT, "sam_drafting_lossless_amd", "csrc", name)
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(rows_per_launch: float):
+    """HBM bytes per stream launch from the committed rocprofv3 counter
+    record, scaled from the rows of the profiled launches to the rows of this
+    run's launches; None if the record was taken on other stream sources."""
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None
-    if rec.get("verify_hip_sha256_16") != _verify_source_hash():
+    if rec.get("stream_sources_sha256_16") != stream_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec["hbm_bytes_per_row"] * rows_per_launch
 
 
 def cpu_baseline(slot_host, gt, cfg, nthreads: int, budget_s: float = 15.0):
@@ -357,6 +366,12 @@ def main():
     dl = dl_hist[first_ev:first_ev + args.steps].cpu().numpy()
     nem = nem_hist[args.warmup:first_ev].cpu().numpy()
     rows_per_launch = float((dl + 1).sum(axis=1).mean())
+    # Rows of every stream launch this run made (warmup, timed pass, event
+    # pass x STREAM_BATCH, separate-call pass), for the traffic record.
+    rows_all = (dl_hist[:total].cpu().numpy() + 1).sum(axis=1).astype(np.float64)
+    w = np.ones(total)
+    w[first_ev:first_ev + args.steps] = STREAM_BATCH
+    stream_launch_rows_mean = float((rows_all * w).sum() / w.sum())
     bytes_per_launch = rows_per_launch * V * 4
     achieved = bytes_per_launch / (stream_us * 1e-6) / 1e9
     if int(status.cpu().abs().sum()) != 0 or int(st.status().abs().sum()) != 0:
@@ -393,7 +408,7 @@ def main():
                    "ring_slots": RING},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": _traffic_from_profile(rows_per_launch, V)},
+                     "traffic": _traffic_from_profile(rows_per_launch)},
         "cpu_baseline": cpu,
         "path": "spec_step (stream pass, then finish pass: decisions, draws, "
                 "SAM extend, next draft)",
@@ -402,6 +417,7 @@ def main():
         "stream_launches_per_event_pair": STREAM_BATCH,
         "separate_calls_steps_per_s": separate_steps_s,
         "verified_rows_per_launch": rows_per_launch,
+        "stream_launch_rows_mean": stream_launch_rows_mean,
         "verify_bytes_per_launch": bytes_per_launch,
         "mean_tokens_per_step": float(nem.mean()),
         "hbm_read_probe_GBps": probe,

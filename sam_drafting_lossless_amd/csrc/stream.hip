@@ -1,0 +1,299 @@
+// Stream pass of the batched verification: reads every logit row a sequence
+// needs once, in 32 KiB chunks, and leaves one partial per (row, chunk).
+//
+// Method ([P2] m.nxbn.cn guide §2.2; [P3] gogongxt notes "贪婪采样",
+// "拒绝采样"): row j of sequence b is needed iff j <= draft_len[b] (rows past
+// the drafts are never read). At T = 0 a partial is (max, lowest index of the
+// max, NaN flag); at T > 0 it is the online (max m, sum of exp2((l - m) *
+// log2e / T)) plus the logit of the draft token x_j when x_j falls in the
+// chunk. The finish pass combines them.
+//
+// Design for gfx950: 256-thread workgroups each hold one chunk in registers
+// (8 non-temporal 16-byte loads in flight per lane, each wavefront load one
+// contiguous 1 KiB request) and write one 16-byte partial per row: nothing
+// but loads, arithmetic and one store. The balanced kernel (batches up to
+// 2048 sequences) gives every (sequence, chunk) of row 0 its own workgroup
+// and deals the chunks of rows 1..draft_len round-robin to the same
+// workgroups, so that the ones with extra work are dispatched first; larger
+// batches use a (sequence, row group, chunk) grid.
+#include <algorithm>
+
+#include "verify_common.h"
+
+namespace specsam {
+namespace {
+
+// ---------------------------------------------------------------------------
+// stream: one partial per (row, chunk).
+// ---------------------------------------------------------------------------
+
+// Reduces one loaded chunk of row j of sequence b into its partial. `raw`
+// holds the chunk; `mid` runs once every element has been consumed, before
+// the workgroup reduction (the balanced kernel issues its next item's loads
+// into `raw` there). Ends with a barrier, so `red` may be reused at once.
+template <int DT, bool VP, typename Mid>
+__device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
+                                           float T, int c, u32x4 (&raw)[kLoads],
+                                           f32x4* red, Mid mid) {
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int R = a.K + 1, nc = a.nchunks;
+  const int cstart = c * kChunk<DT>;
+  const int64_t row = (int64_t)b * R + j;
+  const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
+  const bool greedy = (T == 0.0f);
+  const float kk = greedy ? 0.0f : kLog2e / T;
+  // The logit of the draft token, when it lies in this chunk.
+  float lx = 0.0f;
+  if (!greedy && j < d && tid == 0) {
+    const int x = a.draft[(int64_t)b * a.K + j];
+    if (x >= cstart && x < cstart + kChunk<DT> && x < a.V) lx = load_one<DT>(rowp, x);
+  }
+  f32x4 part;
+  if (greedy) {
+    // Position within the lane's elements (it*kVec + k) is a compile-time
+    // constant per element; the row index is formed once at the end.
+    float bv = kNegInf;
+    int bp = -1, nan = 0;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const float v = elem<DT>(raw[it], k);
+        if (v > bv) {
+          bv = v;
+          bp = it * kVec<DT> + k;
+        }
+        nan |= (v != v);
+      }
+    mid();
+    int bi = bp < 0 ? INT_MAX
+                    : elem_index<DT, VP>(cstart, tid, bp / kVec<DT>, bp % kVec<DT>);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+    nan = wave_or(nan);
+    if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
+    __syncthreads();
+    float pv = red[0].x, pn = red[0].y;
+    int pi = __float_as_int(red[0].w);
+    for (int i = 1; i < kWaves; ++i) {
+      argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
+      pn = fmaxf(pn, red[i].y);
+    }
+    part = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
+  } else {
+    // Online (max, sum exp2) folded one 16-byte vector at a time, in the
+    // order the loads return, so only the raw vectors stay live.
+    float m = kNegInf, s = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      float vm = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
+      const float mn = fmaxf(m, vm);
+      const float base = (mn == kNegInf) ? 0.0f : mn;
+      float t = s * fast_exp2((m - base) * kk);
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k)
+        t += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
+      s = t;
+      m = mn;
+    }
+    mid();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
+    if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
+    __syncthreads();
+    float pm = red[0].x, ps = red[0].y;
+    for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
+    part = f32x4{pm, ps, lx, 0.0f};
+  }
+  if (tid == 0) a.partials[row * nc + c] = part;
+  __syncthreads();  // red[] is reused by the next row
+}
+
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+// Static grid over (sequence, row group, chunk), for batches too large for
+// the balanced kernel's plan: each workgroup streams its chunk of every row
+// j <= draft_len in its group, one row after another.
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
+  __shared__ f32x4 red[kWaves];
+  const int tid = threadIdx.x;
+  const int R = a.K + 1, nc = a.nchunks;
+  const int c = blockIdx.x % nc;
+  const int bg = blockIdx.x / nc;
+  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
+  const int j0 = g * a.rows_per_wg;
+  const int cstart = c * kChunk<DT>;
+  // Row 0, which every valid sequence needs, is requested before the
+  // sequence's parameters return.
+  int d;
+  float T;
+  const int st = seq_check(a, b, &d, &T);  // reported by finalize
+  u32x4 raw[kLoads];
+  if (j0 == 0)
+    load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
+                       a.V, tid, raw);
+  if (st) return;
+  const int j1 = min(j0 + a.rows_per_wg, d + 1);
+  for (int j = j0; j < j1; ++j) {
+    if (j != 0)
+      load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
+                         cstart, a.V, tid, raw);
+    stream_row<DT, VP>(a, b, j, d, T, c, raw, red, NoMid{});
+  }
+}
+
+constexpr int kPlanMaxB = 2048;  // sequences whose plan fits in LDS
+constexpr int kPlanPer = kPlanMaxB / kThreads;
+
+// Balanced stream: one workgroup per (sequence, chunk) of row 0, which every
+// valid sequence needs, in (sequence, chunk) order. The items of rows
+// 1..draft_len, (row, chunk) pairs in (sequence, row, chunk) order, are dealt
+// round-robin to the same workgroups: workgroup g also takes extra items g,
+// g + n0, g + 2 n0, ... (n0 = B x nchunks). The workgroups with extra work are
+// therefore the first ones dispatched, and a sequence with several rows is
+// spread over many workgroups instead of being streamed row after row by
+// one. Every workgroup learns the number of extra rows E from the draft
+// lengths (loaded while its row-0 chunk is in flight); only
+// those with extra items build the exclusive prefix of draft lengths in LDS
+// that maps an item to its sequence and row. (A persistent grid that deals
+// every item round-robin runs its workgroups in lock-step rounds and was
+// measured slower; so was handing items out with atomic counters.)
+struct Item {
+  int b, j, c;
+};
+
+// Item x of rows >= 1: the largest b with pre[b] <= x / nc.
+__device__ __forceinline__ Item decode_extra(int x, int nc, int B, const int* pre) {
+  Item t;
+  const int r = x / nc;
+  t.c = x - r * nc;
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int m = (lo + hi + 1) >> 1;
+    if (pre[m] <= r) lo = m;
+    else hi = m - 1;
+  }
+  t.b = lo;
+  t.j = r - pre[lo] + 1;
+  return t;
+}
+
+// Extra rows of one sequence: draft_len when it is in [1, K], else 0
+// (invalid lengths are reported by finalize and need no rows).
+__device__ __forceinline__ int extra_rows(const Args& a, int b) {
+  const int v = a.draft_len[b];
+  return (v >= 1 && v <= a.K) ? v : 0;
+}
+
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads, DT == SS_DTYPE_F32 ? 6 : 4) void
+spec_stream_balanced_kernel(Args a) {
+  __shared__ f32x4 red[kWaves];
+  __shared__ int pre[kPlanMaxB + 1];
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int B = a.B, R = a.K + 1, nc = a.nchunks;
+  const int n0 = B * nc;
+  const int g = blockIdx.x;
+  const int b0 = g / nc, c0 = g - b0 * nc;
+  u32x4 raw[kLoads];
+  load_chunk<DT, VP>(a.logits + (int64_t)b0 * R * a.V * Dt<DT>::kBytes,
+                     c0 * kChunk<DT>, a.V, tid, raw);
+  int d;
+  float T;
+  int st = seq_check(a, b0, &d, &T);  // reported by finalize
+  int part = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPer; ++i) {
+    const int b = tid + i * kThreads;
+    if (b < B) part += extra_rows(a, b);
+  }
+  if (st == 0) stream_row<DT, VP>(a, b0, 0, d, T, c0, raw, red, NoMid{});
+  part = (int)wave_sum((float)part);  // exact: < 2^24
+  if (l == 0) wsum[w] = part;
+  __syncthreads();
+  int E = 0;
+  for (int i = 0; i < kWaves; ++i) E += wsum[i];
+  const int nx = E * nc;  // extra items
+  if (g >= nx) return;
+  // Exclusive prefix of extra rows, kPlanPer consecutive sequences a thread.
+  int tsum = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPer; ++i) {
+    const int b = tid * kPlanPer + i;
+    if (b < B) {
+      const int v = extra_rows(a, b);
+      pre[b] = v;
+      tsum += v;
+    }
+  }
+  const int incl = (int)wave_inclusive_sum((float)tsum);
+  __syncthreads();  // wsum[0] has been read
+  if (l == kWave - 1) wsum[w] = incl;
+  __syncthreads();
+  int base = incl - tsum;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+#pragma unroll
+  for (int i = 0; i < kPlanPer; ++i) {
+    const int b = tid * kPlanPer + i;
+    if (b < B) {
+      const int v = pre[b];
+      pre[b] = base;
+      base += v;
+    }
+  }
+  __syncthreads();
+  for (int x = g; x < nx; x += n0) {
+    const Item t = decode_extra(x, nc, B, pre);
+    load_chunk<DT, VP>(a.logits + ((int64_t)t.b * R + t.j) * a.V * Dt<DT>::kBytes,
+                       t.c * kChunk<DT>, a.V, tid, raw);
+    st = seq_check(a, t.b, &d, &T);
+    if (st == 0) stream_row<DT, VP>(a, t.b, t.j, d, T, t.c, raw, red, NoMid{});
+  }
+}
+
+// Workgroups the stream grid aims for: enough to keep every CU busy with
+// several resident workgroups.
+constexpr int64_t kTargetWorkgroups = 4096;
+
+// Grid of the stream pass: (sequence, row group, chunk).
+inline void set_row_groups(Args& a) {
+  const int R = a.K + 1;
+  const int64_t base = (int64_t)a.B * a.nchunks;
+  const int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
+  a.rows_per_wg = (R + ngroups - 1) / ngroups;
+  a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
+}
+
+template <int DT, bool VP>
+int launch_stream_t(const Args& a, hipStream_t s) {
+  if (a.B <= kPlanMaxB) {
+    hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP>),
+                       dim3((unsigned)(a.B * a.nchunks)), dim3(kThreads), 0, s, a);
+    return check_launch("spec_stream");
+  }
+  const int64_t grid = (int64_t)a.B * a.nchunks * a.ngroups;
+  if (grid > INT_MAX) return set_error(SS_EINVAL, "spec_stream: grid too large");
+  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, a);
+  return check_launch("spec_stream");
+}
+
+}  // namespace
+
+int launch_stream(Args a, bool f32, bool vp, hipStream_t s) {
+  set_row_groups(a);
+  return f32 ? (vp ? launch_stream_t<SS_DTYPE_F32, true>(a, s)
+                   : launch_stream_t<SS_DTYPE_F32, false>(a, s))
+             : (vp ? launch_stream_t<SS_DTYPE_BF16, true>(a, s)
+                   : launch_stream_t<SS_DTYPE_BF16, false>(a, s));
+}
+
+}  // namespace specsam

@@ -8,18 +8,10 @@
 // max(0, p - q) normalised (p with x_j removed for one-hot drafts); if every
 // draft passes, a bonus token comes from the last row.
 //
-// Design for gfx950: two kernels per step (three more when draft
+// Design for gfx950: two kernels per step (two more when draft
 // probabilities q are given), ordered by the stream they are launched on.
-//   stream    grid over (sequence, row group, 32 KiB chunk). Each 256-thread
-//             workgroup streams its chunk of every row j <= draft_len in its
-//             group with non-temporal 16-byte loads (8 in flight per lane)
-//             and writes one partial per row: (max, lowest argmax) at T = 0,
-//             or the online (max, sum exp2((l - max) * log2e / T)) folded one
-//             16-byte vector at a time, plus the logit of the draft token when
-//             it falls in the chunk. Rows past draft_len are never read. Row
-//             groups are sized on the host so the grid has enough workgroups
-//             to fill 256 CUs. Nothing but loads, arithmetic and one store per
-//             row: 75 VGPRs, 6 resident workgroups per CU.
+//   stream    (stream.hip) reads each needed logit row once and leaves one
+//             partial per (row, 32 KiB chunk) in the workspace.
 //   finalize  one workgroup per sequence: combines the chunk partials of each
 //             row, judges the drafts with one wavefront (lane j judges draft
 //             j; a ballot finds the first rejection), writes the outputs and,
@@ -35,187 +27,11 @@
 // finalize code raises the stream kernel's register count and its latency
 // lands in the kernel's tail.
 #include <algorithm>
-#include <climits>
-#include <cmath>
 
-#include "sam_device.h"
+#include "verify_common.h"
 
 namespace specsam {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kLoads = 8;  // 16-byte loads in flight per lane
-constexpr int kChunkBytes = kThreads * kLoads * 16;  // 32 KiB per workgroup
-constexpr int kMaxRows = SS_MAX_K + 1;
-constexpr int kMaxV = 1 << 21;
-constexpr int kMaxChunks = kMaxV / (kChunkBytes / 4);  // 256 (fp32 chunks)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -INFINITY;
-
-template <int DT>
-struct Dt;
-template <>
-struct Dt<SS_DTYPE_F32> {
-  static constexpr int kBytes = 4;
-};
-template <>
-struct Dt<SS_DTYPE_BF16> {
-  static constexpr int kBytes = 2;
-};
-template <int DT>
-constexpr int kVec = 16 / Dt<DT>::kBytes;  // elements per 16-byte load
-template <int DT>
-constexpr int kChunk = kChunkBytes / Dt<DT>::kBytes;  // elements per chunk
-template <int DT>
-constexpr int kSeg = kChunk<DT> / kThreads;  // elements per lane in a re-read
-
-// Element k of a 16-byte vector, widened to float (bf16 exactly).
-template <int DT>
-__device__ __forceinline__ float elem(const u32x4& r, int k) {
-  if constexpr (DT == SS_DTYPE_F32) {
-    return __uint_as_float(r[k]);
-  } else {
-    const unsigned w = r[k >> 1];
-    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ float load_one(const unsigned char* base, int64_t i) {
-  if constexpr (DT == SS_DTYPE_F32) {
-    return reinterpret_cast<const float*>(base)[i];
-  } else {
-    const unsigned short h = reinterpret_cast<const unsigned short*>(base)[i];
-    return __uint_as_float((unsigned)h << 16);
-  }
-}
-
-// Index (within the row) of element k of load `it` of lane `tid`: load it of
-// lane tid covers kVec consecutive elements at cstart + (it*256 + tid)*kVec,
-// so one wavefront's load is one contiguous 1 KiB request. Token order in a
-// chunk is therefore (it, lane, k); each lane sees its elements in increasing
-// index order, which the argmax relies on for its lowest-index tie rule and
-// the draw for its scan. The scalar path (rows not 16-byte aligned) uses the
-// same layout with element-wise loads.
-template <int DT, bool VP>
-__device__ __forceinline__ int elem_index(int cstart, int tid, int it, int k) {
-  return cstart + (it * kThreads + tid) * kVec<DT> + k;
-}
-
-// Loads one chunk of a row into registers. Elements past V read as -inf.
-// NT: non-temporal loads for the streaming pass (measured faster there);
-// the draw's single-chunk re-read uses ordinary loads, which can still find
-// the chunk in the memory-side cache.
-template <int DT, bool VP, bool NT = true>
-__device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
-                                           int V, int tid, u32x4 (&raw)[kLoads]) {
-  constexpr unsigned kNegInfWord =
-      DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
-  if constexpr (VP) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(
-        row + (int64_t)cstart * Dt<DT>::kBytes);
-    const int rem = V - cstart;
-    if (rem >= kChunk<DT>) {
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-        raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
-                     : p[it * kThreads + tid];
-    } else {
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it) {
-        const int e = (it * kThreads + tid) * kVec<DT>;
-        if (e < rem)
-          raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
-                       : p[it * kThreads + tid];
-        else
-          raw[it] = u32x4{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
-      }
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      unsigned w[4] = {kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const int i = elem_index<DT, false>(cstart, tid, it, k);
-        if (i < V) {
-          if constexpr (DT == SS_DTYPE_F32) {
-            w[k] = __builtin_nontemporal_load(
-                reinterpret_cast<const unsigned*>(row) + i);
-          } else {
-            const unsigned h = __builtin_nontemporal_load(
-                reinterpret_cast<const unsigned short*>(row) + i);
-            w[k >> 1] = (k & 1) ? ((w[k >> 1] & 0xffffu) | (h << 16))
-                                : ((w[k >> 1] & 0xffff0000u) | h);
-          }
-        }
-      }
-      raw[it] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  }
-}
-
-
-struct Args {
-  const unsigned char* logits;
-  int B, K, V, nchunks, rows_per_wg, ngroups;
-  const int32_t* draft;
-  const int32_t* draft_len;
-  const float* q;
-  const float* temperature;
-  const float* uniforms;
-  int32_t* out;
-  int32_t* nem;
-  float* p_draft;
-  int32_t* status;
-  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
-  i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
-  float* rpart;     // [B*nchunks] residual chunk sums
-  // Fused automaton step (sam == nullptr when only verifying).
-  unsigned char* sam;
-  int max_len;
-  SamLayout sl;
-  int32_t* next_draft;
-  int32_t* next_draft_len;
-  int32_t* next_match_len;
-};
-
-// Per-sequence checks that need device data.
-__device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T) {
-  *d = a.draft_len[b];
-  *T = a.temperature[b];
-  int st = 0;
-  if (*d < 0 || *d > a.K) st |= SS_ST_DRAFT_LEN;
-  // T = 0 is greedy; otherwise T must be a finite normal positive float so
-  // that log2(e)/T stays finite.
-  if (!(*T == 0.0f || (*T >= 1.17549435e-38f && isfinite(*T))))
-    st |= SS_ST_TEMPERATURE;
-  if (*T > 0.0f && a.uniforms == nullptr) st |= SS_ST_NO_UNIFORMS;
-  return st;
-}
-
-// (value, index) merge: larger value wins, the lower index on equal values.
-__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// Online-softmax merge of (max, sum exp2((x-max)*kk)) pairs.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os,
-                                          float kk) {
-  const float M = fmaxf(m, om);
-  const float Mb = (M == kNegInf) ? 0.0f : M;
-  s = s * fast_exp2((m - Mb) * kk) + os * fast_exp2((om - Mb) * kk);
-  m = M;
-}
-
-// Partials and residual sums are written by one kernel and read by the next
-// one on the same stream; plain accesses suffice.
-__device__ __forceinline__ f32x4 load_partial(const f32x4* p) { return *p; }
-__device__ __forceinline__ float load_f32(const float* p) { return *p; }
 
 // ---------------------------------------------------------------------------
 // Draw from one row. Weights are exp2((l - m) * kk) with token `excl` (weight
@@ -599,242 +415,6 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// stream: one partial per (row, chunk).
-// ---------------------------------------------------------------------------
-
-// Reduces one loaded chunk of row j of sequence b into its partial. `raw`
-// holds the chunk; `mid` runs once every element has been consumed, before
-// the workgroup reduction (the balanced kernel issues its next item's loads
-// into `raw` there). Ends with a barrier, so `red` may be reused at once.
-template <int DT, bool VP, typename Mid>
-__device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
-                                           float T, int c, u32x4 (&raw)[kLoads],
-                                           f32x4* red, Mid mid) {
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1, nc = a.nchunks;
-  const int cstart = c * kChunk<DT>;
-  const int64_t row = (int64_t)b * R + j;
-  const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
-  const bool greedy = (T == 0.0f);
-  const float kk = greedy ? 0.0f : kLog2e / T;
-  // The logit of the draft token, when it lies in this chunk.
-  float lx = 0.0f;
-  if (!greedy && j < d && tid == 0) {
-    const int x = a.draft[(int64_t)b * a.K + j];
-    if (x >= cstart && x < cstart + kChunk<DT> && x < a.V) lx = load_one<DT>(rowp, x);
-  }
-  f32x4 part;
-  if (greedy) {
-    // Position within the lane's elements (it*kVec + k) is a compile-time
-    // constant per element; the row index is formed once at the end.
-    float bv = kNegInf;
-    int bp = -1, nan = 0;
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const float v = elem<DT>(raw[it], k);
-        if (v > bv) {
-          bv = v;
-          bp = it * kVec<DT> + k;
-        }
-        nan |= (v != v);
-      }
-    mid();
-    int bi = bp < 0 ? INT_MAX
-                    : elem_index<DT, VP>(cstart, tid, bp / kVec<DT>, bp % kVec<DT>);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
-    nan = wave_or(nan);
-    if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
-    __syncthreads();
-    float pv = red[0].x, pn = red[0].y;
-    int pi = __float_as_int(red[0].w);
-    for (int i = 1; i < kWaves; ++i) {
-      argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
-      pn = fmaxf(pn, red[i].y);
-    }
-    part = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
-  } else {
-    // Online (max, sum exp2) folded one 16-byte vector at a time, in the
-    // order the loads return, so only the raw vectors stay live.
-    float m = kNegInf, s = 0.0f;
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      float vm = kNegInf;
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
-      const float mn = fmaxf(m, vm);
-      const float base = (mn == kNegInf) ? 0.0f : mn;
-      float t = s * fast_exp2((m - base) * kk);
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k)
-        t += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
-      s = t;
-      m = mn;
-    }
-    mid();
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
-    if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
-    __syncthreads();
-    float pm = red[0].x, ps = red[0].y;
-    for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
-    part = f32x4{pm, ps, lx, 0.0f};
-  }
-  if (tid == 0) a.partials[row * nc + c] = part;
-  __syncthreads();  // red[] is reused by the next row
-}
-
-struct NoMid {
-  __device__ void operator()() const {}
-};
-
-// Static grid over (sequence, row group, chunk), for batches too large for
-// the balanced kernel's plan: each workgroup streams its chunk of every row
-// j <= draft_len in its group, one row after another.
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
-  __shared__ f32x4 red[kWaves];
-  const int tid = threadIdx.x;
-  const int R = a.K + 1, nc = a.nchunks;
-  const int c = blockIdx.x % nc;
-  const int bg = blockIdx.x / nc;
-  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
-  const int j0 = g * a.rows_per_wg;
-  const int cstart = c * kChunk<DT>;
-  // Row 0, which every valid sequence needs, is requested before the
-  // sequence's parameters return.
-  int d;
-  float T;
-  const int st = seq_check(a, b, &d, &T);  // reported by finalize
-  u32x4 raw[kLoads];
-  if (j0 == 0)
-    load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
-                       a.V, tid, raw);
-  if (st) return;
-  const int j1 = min(j0 + a.rows_per_wg, d + 1);
-  for (int j = j0; j < j1; ++j) {
-    if (j != 0)
-      load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
-                         cstart, a.V, tid, raw);
-    stream_row<DT, VP>(a, b, j, d, T, c, raw, red, NoMid{});
-  }
-}
-
-constexpr int kPlanMaxB = 2048;  // sequences whose plan fits in LDS
-constexpr int kPlanPer = kPlanMaxB / kThreads;
-
-// Balanced stream: one workgroup per (sequence, chunk) of row 0, which every
-// valid sequence needs, in (sequence, chunk) order. The items of rows
-// 1..draft_len, (row, chunk) pairs in (sequence, row, chunk) order, are dealt
-// round-robin to the same workgroups: workgroup g also takes extra items g,
-// g + n0, g + 2 n0, ... (n0 = B x nchunks). The workgroups with extra work are
-// therefore the first ones dispatched, and a sequence with several rows is
-// spread over many workgroups instead of being streamed row after row by
-// one. Every workgroup learns the number of extra rows E from the draft
-// lengths (loaded while its row-0 chunk is in flight); only
-// those with extra items build the exclusive prefix of draft lengths in LDS
-// that maps an item to its sequence and row. (A persistent grid that deals
-// every item round-robin runs its workgroups in lock-step rounds and was
-// measured slower; so was handing items out with atomic counters.)
-struct Item {
-  int b, j, c;
-};
-
-// Item x of rows >= 1: the largest b with pre[b] <= x / nc.
-__device__ __forceinline__ Item decode_extra(int x, int nc, int B, const int* pre) {
-  Item t;
-  const int r = x / nc;
-  t.c = x - r * nc;
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int m = (lo + hi + 1) >> 1;
-    if (pre[m] <= r) lo = m;
-    else hi = m - 1;
-  }
-  t.b = lo;
-  t.j = r - pre[lo] + 1;
-  return t;
-}
-
-// Extra rows of one sequence: draft_len when it is in [1, K], else 0
-// (invalid lengths are reported by finalize and need no rows).
-__device__ __forceinline__ int extra_rows(const Args& a, int b) {
-  const int v = a.draft_len[b];
-  return (v >= 1 && v <= a.K) ? v : 0;
-}
-
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads, DT == SS_DTYPE_F32 ? 6 : 4) void
-spec_stream_balanced_kernel(Args a) {
-  __shared__ f32x4 red[kWaves];
-  __shared__ int pre[kPlanMaxB + 1];
-  __shared__ int wsum[kWaves];
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int B = a.B, R = a.K + 1, nc = a.nchunks;
-  const int n0 = B * nc;
-  const int g = blockIdx.x;
-  const int b0 = g / nc, c0 = g - b0 * nc;
-  u32x4 raw[kLoads];
-  load_chunk<DT, VP>(a.logits + (int64_t)b0 * R * a.V * Dt<DT>::kBytes,
-                     c0 * kChunk<DT>, a.V, tid, raw);
-  int d;
-  float T;
-  int st = seq_check(a, b0, &d, &T);  // reported by finalize
-  int part = 0;
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid + i * kThreads;
-    if (b < B) part += extra_rows(a, b);
-  }
-  if (st == 0) stream_row<DT, VP>(a, b0, 0, d, T, c0, raw, red, NoMid{});
-  part = (int)wave_sum((float)part);  // exact: < 2^24
-  if (l == 0) wsum[w] = part;
-  __syncthreads();
-  int E = 0;
-  for (int i = 0; i < kWaves; ++i) E += wsum[i];
-  const int nx = E * nc;  // extra items
-  if (g >= nx) return;
-  // Exclusive prefix of extra rows, kPlanPer consecutive sequences a thread.
-  int tsum = 0;
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid * kPlanPer + i;
-    if (b < B) {
-      const int v = extra_rows(a, b);
-      pre[b] = v;
-      tsum += v;
-    }
-  }
-  const int incl = (int)wave_inclusive_sum((float)tsum);
-  __syncthreads();  // wsum[0] has been read
-  if (l == kWave - 1) wsum[w] = incl;
-  __syncthreads();
-  int base = incl - tsum;
-  for (int i = 0; i < w; ++i) base += wsum[i];
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid * kPlanPer + i;
-    if (b < B) {
-      const int v = pre[b];
-      pre[b] = base;
-      base += v;
-    }
-  }
-  __syncthreads();
-  for (int x = g; x < nx; x += n0) {
-    const Item t = decode_extra(x, nc, B, pre);
-    load_chunk<DT, VP>(a.logits + ((int64_t)t.b * R + t.j) * a.V * Dt<DT>::kBytes,
-                       t.c * kChunk<DT>, a.V, tid, raw);
-    st = seq_check(a, t.b, &d, &T);
-    if (st == 0) stream_row<DT, VP>(a, t.b, t.j, d, T, t.c, raw, red, NoMid{});
-  }
-}
-
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
   __shared__ float red[kWaves];
@@ -950,33 +530,6 @@ WsLayout ws_layout(int B, int K, int V) {
   return L;
 }
 
-// Workgroups the stream grid aims for: enough to keep every CU busy with
-// several resident workgroups.
-constexpr int64_t kTargetWorkgroups = 4096;
-
-// Grid of the stream pass: (sequence, row group, chunk).
-inline void set_row_groups(Args& a) {
-  const int R = a.K + 1;
-  const int64_t base = (int64_t)a.B * a.nchunks;
-  const int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
-  a.rows_per_wg = (R + ngroups - 1) / ngroups;
-  a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
-}
-
-template <int DT, bool VP>
-int launch_stream(const Args& a, hipStream_t s) {
-  if (a.B <= kPlanMaxB) {
-    hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP>),
-                       dim3((unsigned)(a.B * a.nchunks)), dim3(kThreads), 0, s, a);
-    return check_launch("spec_stream");
-  }
-  const int64_t grid = (int64_t)a.B * a.nchunks * a.ngroups;
-  if (grid > INT_MAX) return set_error(SS_EINVAL, "spec_stream: grid too large");
-  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, s, a);
-  return check_launch("spec_stream");
-}
-
 template <int DT, bool VP, bool SAM>
 int launch_finish(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM>), dim3((unsigned)a.B),
@@ -1058,7 +611,6 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.next_draft = next_draft;
   a.next_draft_len = next_draft_len;
   a.next_match_len = next_match_len;
-  set_row_groups(a);
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
   const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0) &&
                   (q == nullptr || ((uintptr_t)q & 15) == 0);
@@ -1066,10 +618,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   const bool f32 = dtype == SS_DTYPE_F32;
   int rc = SS_OK;
   if (passes & kStream) {
-    rc = f32 ? (vp ? launch_stream<SS_DTYPE_F32, true>(a, s)
-                   : launch_stream<SS_DTYPE_F32, false>(a, s))
-             : (vp ? launch_stream<SS_DTYPE_BF16, true>(a, s)
-                   : launch_stream<SS_DTYPE_BF16, false>(a, s));
+    rc = launch_stream(a, f32, vp, s);
     if (rc != SS_OK) return rc;
   }
   if (passes & kFinish) {

@@ -1,0 +1,192 @@
+// Definitions shared by the verification kernels (stream.hip, verify.hip):
+// sizes, the 16-byte load layout of a chunk, the kernel argument block and
+// the per-sequence checks.
+#pragma once
+
+#include <climits>
+#include <cmath>
+
+#include "sam_device.h"
+
+namespace specsam {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kLoads = 8;  // 16-byte loads in flight per lane
+constexpr int kChunkBytes = kThreads * kLoads * 16;  // 32 KiB per workgroup
+constexpr int kMaxRows = SS_MAX_K + 1;
+constexpr int kMaxV = 1 << 21;
+constexpr int kMaxChunks = kMaxV / (kChunkBytes / 4);  // 256 (fp32 chunks)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -INFINITY;
+
+template <int DT>
+struct Dt;
+template <>
+struct Dt<SS_DTYPE_F32> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct Dt<SS_DTYPE_BF16> {
+  static constexpr int kBytes = 2;
+};
+template <int DT>
+constexpr int kVec = 16 / Dt<DT>::kBytes;  // elements per 16-byte load
+template <int DT>
+constexpr int kChunk = kChunkBytes / Dt<DT>::kBytes;  // elements per chunk
+template <int DT>
+constexpr int kSeg = kChunk<DT> / kThreads;  // elements per lane in a re-read
+
+// Element k of a 16-byte vector, widened to float (bf16 exactly).
+template <int DT>
+__device__ __forceinline__ float elem(const u32x4& r, int k) {
+  if constexpr (DT == SS_DTYPE_F32) {
+    return __uint_as_float(r[k]);
+  } else {
+    const unsigned w = r[k >> 1];
+    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const unsigned char* base, int64_t i) {
+  if constexpr (DT == SS_DTYPE_F32) {
+    return reinterpret_cast<const float*>(base)[i];
+  } else {
+    const unsigned short h = reinterpret_cast<const unsigned short*>(base)[i];
+    return __uint_as_float((unsigned)h << 16);
+  }
+}
+
+// Index (within the row) of element k of load `it` of lane `tid`: load it of
+// lane tid covers kVec consecutive elements at cstart + (it*256 + tid)*kVec,
+// so one wavefront's load is one contiguous 1 KiB request. Token order in a
+// chunk is therefore (it, lane, k); each lane sees its elements in increasing
+// index order, which the argmax relies on for its lowest-index tie rule and
+// the draw for its scan. The scalar path (rows not 16-byte aligned) uses the
+// same layout with element-wise loads.
+template <int DT, bool VP>
+__device__ __forceinline__ int elem_index(int cstart, int tid, int it, int k) {
+  return cstart + (it * kThreads + tid) * kVec<DT> + k;
+}
+
+// Loads one chunk of a row into registers. Elements past V read as -inf.
+// NT: non-temporal loads for the streaming pass (measured faster there);
+// the draw's single-chunk re-read uses ordinary loads, which can still find
+// the chunk in the memory-side cache.
+template <int DT, bool VP, bool NT = true>
+__device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
+                                           int V, int tid, u32x4 (&raw)[kLoads]) {
+  constexpr unsigned kNegInfWord =
+      DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
+  if constexpr (VP) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(
+        row + (int64_t)cstart * Dt<DT>::kBytes);
+    const int rem = V - cstart;
+    if (rem >= kChunk<DT>) {
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+        raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
+                     : p[it * kThreads + tid];
+    } else {
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) {
+        const int e = (it * kThreads + tid) * kVec<DT>;
+        if (e < rem)
+          raw[it] = NT ? __builtin_nontemporal_load(p + it * kThreads + tid)
+                       : p[it * kThreads + tid];
+        else
+          raw[it] = u32x4{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      unsigned w[4] = {kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const int i = elem_index<DT, false>(cstart, tid, it, k);
+        if (i < V) {
+          if constexpr (DT == SS_DTYPE_F32) {
+            w[k] = __builtin_nontemporal_load(
+                reinterpret_cast<const unsigned*>(row) + i);
+          } else {
+            const unsigned h = __builtin_nontemporal_load(
+                reinterpret_cast<const unsigned short*>(row) + i);
+            w[k >> 1] = (k & 1) ? ((w[k >> 1] & 0xffffu) | (h << 16))
+                                : ((w[k >> 1] & 0xffff0000u) | h);
+          }
+        }
+      }
+      raw[it] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+
+struct Args {
+  const unsigned char* logits;
+  int B, K, V, nchunks, rows_per_wg, ngroups;
+  const int32_t* draft;
+  const int32_t* draft_len;
+  const float* q;
+  const float* temperature;
+  const float* uniforms;
+  int32_t* out;
+  int32_t* nem;
+  float* p_draft;
+  int32_t* status;
+  f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
+  i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
+  float* rpart;     // [B*nchunks] residual chunk sums
+  // Fused automaton step (sam == nullptr when only verifying).
+  unsigned char* sam;
+  int max_len;
+  SamLayout sl;
+  int32_t* next_draft;
+  int32_t* next_draft_len;
+  int32_t* next_match_len;
+};
+
+// Per-sequence checks that need device data.
+__device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T) {
+  *d = a.draft_len[b];
+  *T = a.temperature[b];
+  int st = 0;
+  if (*d < 0 || *d > a.K) st |= SS_ST_DRAFT_LEN;
+  // T = 0 is greedy; otherwise T must be a finite normal positive float so
+  // that log2(e)/T stays finite.
+  if (!(*T == 0.0f || (*T >= 1.17549435e-38f && isfinite(*T))))
+    st |= SS_ST_TEMPERATURE;
+  if (*T > 0.0f && a.uniforms == nullptr) st |= SS_ST_NO_UNIFORMS;
+  return st;
+}
+
+// (value, index) merge: larger value wins, the lower index on equal values.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Online-softmax merge of (max, sum exp2((x-max)*kk)) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os,
+                                          float kk) {
+  const float M = fmaxf(m, om);
+  const float Mb = (M == kNegInf) ? 0.0f : M;
+  s = s * fast_exp2((m - Mb) * kk) + os * fast_exp2((om - Mb) * kk);
+  m = M;
+}
+
+// Partials and residual sums are written by one kernel and read by the next
+// one on the same stream; plain accesses suffice.
+__device__ __forceinline__ f32x4 load_partial(const f32x4* p) { return *p; }
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+
+// Launches the stream pass (stream.hip): one partial per (row, chunk) of the
+// rows each sequence needs. f32 selects fp32 logits (else bf16); vp the
+// 16-byte vector path (rows 16-byte aligned and V a multiple of the vector).
+int launch_stream(Args a, bool f32, bool vp, hipStream_t s);
+
+}  // namespace specsam
