@@ -2,7 +2,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "specsam.h"
 
@@ -24,35 +28,104 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// Wave-wide reductions over 64 lanes (butterfly through cross-lane shuffles;
-// every lane ends with the result).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Cross-lane moves through DPP (the GFX9 encodings gfx950 keeps), for code
+// in which all 64 lanes of the wavefront are active. A lane whose source
+// lies outside its 16-lane row (or the wavefront), or whose row is masked
+// off, receives `id`. Unlike shuffles through ds_bpermute these stay in the
+// vector ALU.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int id, int v) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float id, float v) {
+  return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(id), __float_as_int(v)));
+}
+
+__device__ __forceinline__ float lane63(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+// Inclusive scan of an associative, commutative operation with identity id:
+// shifts by 1, 2, 4 and 8 inside each row, then the row broadcasts of lanes
+// 15 and 31.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan(T v, T id, Op op) {
+  if constexpr (std::is_same<T, int>::value) {
+    v = op(v, dpp_i<kDppRowShr1>(id, v));
+    v = op(v, dpp_i<kDppRowShr2>(id, v));
+    v = op(v, dpp_i<kDppRowShr4>(id, v));
+    v = op(v, dpp_i<kDppRowShr8>(id, v));
+    v = op(v, dpp_i<kDppRowBcast15, 0xa>(id, v));
+    v = op(v, dpp_i<kDppRowBcast31, 0xc>(id, v));
+  } else {
+    v = op(v, dpp_f<kDppRowShr1>(id, v));
+    v = op(v, dpp_f<kDppRowShr2>(id, v));
+    v = op(v, dpp_f<kDppRowShr4>(id, v));
+    v = op(v, dpp_f<kDppRowShr8>(id, v));
+    v = op(v, dpp_f<kDppRowBcast15, 0xa>(id, v));
+    v = op(v, dpp_f<kDppRowBcast31, 0xc>(id, v));
+  }
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Inclusive prefix sum across the wavefront.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  return wave_scan(v, 0.0f, [](float x, float y) { return x + y; });
+}
+
+// The value of the previous lane (0 in lane 0): an inclusive scan's
+// exclusive counterpart, bit for bit.
+__device__ __forceinline__ float wave_shift_up1(float v) {
+  return dpp_f<kDppWaveShr1>(0.0f, v);
+}
+
+// Wavefront reductions; every lane ends with the result.
+__device__ __forceinline__ float wave_sum(float v) { return lane63(wave_inclusive_sum(v)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  return lane63(wave_scan(v, -INFINITY, [](float x, float y) { return fmaxf(x, y); }));
 }
 
 __device__ __forceinline__ int wave_or(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+  return lane63(wave_scan(v, 0, [](int x, int y) { return x | y; }));
 }
 
-// Inclusive prefix sum across the wave (Hillis-Steele through shuffles).
-__device__ __forceinline__ float wave_inclusive_sum(float v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    float t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
+__device__ __forceinline__ int wave_max_i(int v) {
+  return lane63(wave_scan(v, INT_MIN, [](int x, int y) { return x > y ? x : y; }));
+}
+
+// Reduces (x, y) pairs with merge(x, y, ox, oy), an associative and
+// commutative update of (x, y) by (ox, oy) with identity (idx, idy); y is
+// carried as raw 32-bit bits. Every lane ends with the result.
+template <typename Merge>
+__device__ __forceinline__ void wave_reduce2(float& x, float& y, float idx, float idy,
+                                             Merge merge) {
+#define SPECSAM_DPP2(C, M)                                        \
+  {                                                               \
+    const float ox = dpp_f<C, M>(idx, x), oy = dpp_f<C, M>(idy, y); \
+    merge(x, y, ox, oy);                                          \
   }
-  return v;
+  SPECSAM_DPP2(kDppRowShr1, 0xf)
+  SPECSAM_DPP2(kDppRowShr2, 0xf)
+  SPECSAM_DPP2(kDppRowShr4, 0xf)
+  SPECSAM_DPP2(kDppRowShr8, 0xf)
+  SPECSAM_DPP2(kDppRowBcast15, 0xa)
+  SPECSAM_DPP2(kDppRowBcast31, 0xc)
+#undef SPECSAM_DPP2
+  x = lane63(x);
+  y = lane63(y);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {

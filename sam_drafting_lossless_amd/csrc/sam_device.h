@@ -129,7 +129,7 @@ __device__ __forceinline__ SamProbe sam_probe(const i32x4* slots, unsigned bmask
       SamProbe r;
       r.slot = (int)(bk * kBucket) + f;
       r.found = (__ballot(m) >> f) & 1ull;
-      r.dst = __shfl(v.z, f, kWave);
+      r.dst = __builtin_amdgcn_readlane(v.z, f);
       r.buckets = (int)it + 1;
       return r;
     }

@@ -68,9 +68,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     mid();
     int bi = bp < 0 ? INT_MAX
                     : elem_index<DT, VP>(cstart, tid, bp / kVec<DT>, bp % kVec<DT>);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+    wave_argmax(bv, bi);
     nan = wave_or(nan);
     if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
     __syncthreads();
@@ -100,9 +98,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
       m = mn;
     }
     mid();
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
+    wave_lse(m, s, kk);
     if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
     __syncthreads();
     float pm = red[0].x, ps = red[0].y;

@@ -34,27 +34,76 @@ namespace specsam {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Draw from one row. Weights are exp2((l - m) * kk) with token `excl` (weight
-// wx) removed (one-hot residual; excl < 0 for the bonus), or, for RESIDUAL,
-// max(0, exp2((l - m) * kk) / S - q).
+// Draw from one row by inverse CDF in ascending token order: the first token
+// whose running weight exceeds u * total (strict, so zero weights are never
+// chosen). Weights are exp2((l - m) * kk) with token `excl` removed (one-hot
+// residual; excl < 0 for the bonus), or, for RESIDUAL, max(0, exp2((l - m) *
+// kk) / S - q).
 //
-// Step 1 (wave 0): inclusive scan of the chunk weights in chunk order; take
-// the first chunk whose running sum exceeds u * total (strict), or the last
-// chunk with positive weight if rounding leaves none. Step 2 (whole
-// workgroup): re-read that chunk as 256 contiguous 128-byte segments held in
-// registers, scan the lane sums, and let the lane whose interval holds the
-// target find the first token whose running sum exceeds it. A rounding miss
-// falls back to the last positive weight.
+// pick_chunk (one wavefront): the chunk weights, from the stream pass's
+// partials, are scanned in chunk order and the first chunk whose running sum
+// exceeds u * total is taken, with the target left inside it; if rounding
+// leaves none, the last chunk with positive weight (its last positive token
+// is then drawn). draw_in_chunk (whole workgroup): that chunk is re-read with
+// the stream pass's layout, in which token order is (load, lane, element).
+// Each lane sums its 8 vectors; the 32 (load, wavefront) cell totals are
+// scanned in token order to find the cell, a wavefront scan inside the cell
+// finds the lane, and that lane scans its vector. The cell totals and the
+// lane scan come from the same inclusive scan, so the search is consistent;
+// a target beyond the chunk's re-read total (a rounding difference with the
+// partials) takes the chunk's last positive weight.
 // ---------------------------------------------------------------------------
+struct ChunkPick {
+  int chunk;   // -1: every weight is 0
+  float t_in;  // target left inside the chunk; +inf: take its last positive
+};
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// One wavefront, all lanes active; weight(c) is called for c < nc.
+template <typename WeightFn>
+__device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight) {
+  constexpr int kGroups = kMaxChunks / kWave;
+  const int l = lane_id();
+  float W[kGroups], cum[kGroups];
+  float carry = 0.0f;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    W[g] = 0.0f;
+    cum[g] = carry;
+    if (g * kWave < nc) {
+      const int c = g * kWave + l;
+      W[g] = c < nc ? weight(c) : 0.0f;
+      cum[g] = wave_inclusive_sum(W[g]) + carry;
+      carry = lane63(cum[g]);
+    }
+  }
+  const float t = u * carry;
+  ChunkPick r{-1, INFINITY};
+  int lastpos = -1;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    if (g * kWave < nc) {
+      const int c = g * kWave + l;
+      const unsigned long long hit = __ballot(c < nc && cum[g] > t);
+      const unsigned long long pos = __ballot(c < nc && W[g] > 0.0f);
+      if (hit && r.chunk < 0) {
+        const int ln = __ffsll((unsigned long long)hit) - 1;
+        r.chunk = g * kWave + ln;
+        r.t_in = t - (readlane_f(cum[g], ln) - readlane_f(W[g], ln));
+      }
+      if (pos) lastpos = g * kWave + 63 - __clzll((unsigned long long)pos);
+    }
+  }
+  if (r.chunk < 0) r.chunk = lastpos;
+  return r;
+}
+
 struct DrawShared {
-  float W[kMaxChunks];
-  float cum[kMaxChunks];
-  float cell[kLoads * kWaves];  // (load, wave) sums in token order
+  float cell[kLoads * kWaves];  // (load, wave) totals in token order
   int wlast[kWaves];
-  float t_in;
-  float t_cell;
-  int chunk;
-  int cell_sel;
   int result;
 };
 
@@ -79,78 +128,18 @@ __device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int ti
   }
 }
 
-// Draw from one row. Weights are exp2((l - m) * kk) with token `excl` (weight
-// wx) removed (one-hot residual; excl < 0 for the bonus), or, for RESIDUAL,
-// max(0, exp2((l - m) * kk) / S - q).
-//
-// Step 1 (wave 0): inclusive scan of the chunk weights in chunk order; take
-// the first chunk whose running sum exceeds u * total (strict), or the last
-// chunk with positive weight if rounding leaves none. Step 2: re-read that
-// chunk with the same coalesced layout as the stream pass, where token order
-// is (load, lane, element). Each lane sums the weights of each of its 8
-// vectors; 32 (load, wavefront) cells are scanned in token order to find the
-// cell, a wavefront scan inside the cell finds the lane, and that lane scans
-// its vector. The cell totals and the lane scan come from the same inclusive
-// scan, so the search is consistent; a target beyond the chunk's total (a
-// rounding difference with the chunk partials) takes the last positive
-// weight of the chunk.
+// Whole workgroup; `pk` must be the same in every thread.
 template <int DT, bool VP, bool RESIDUAL>
-__device__ int draw_row(const Args& a, DrawShared& sh, int b, int r,
-                        const f32x4* Pr, int excl, float wx, float m, float S,
-                        float kk, float u) {
+__device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
+                             ChunkPick pk, int excl, float m, float kk,
+                             float invS) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1, nc = a.nchunks;
+  const int R = a.K + 1;
+  if (pk.chunk < 0) return -1;
   const unsigned char* row =
       a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
   const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
-  const float invS = RESIDUAL ? 1.0f / S : 0.0f;
-  if (w == 0) {
-    const int cx = (!RESIDUAL && excl >= 0) ? excl / kChunk<DT> : -1;
-    float carry = 0.0f;
-    for (int g0 = 0; g0 < nc; g0 += kWave) {
-      const int c = g0 + l;
-      float W = 0.0f;
-      if (c < nc) {
-        if constexpr (RESIDUAL) {
-          W = load_f32(a.rpart + (int64_t)b * nc + c);
-        } else {
-          const f32x4 P = Pr[c];
-          W = P.y * fast_exp2((P.x - m) * kk);
-          if (c == cx) W = fmaxf(0.0f, W - wx);
-        }
-      }
-      const float inc = wave_inclusive_sum(W) + carry;
-      if (c < nc) {
-        sh.W[c] = W;
-        sh.cum[c] = inc;
-      }
-      carry = __shfl(inc, kWave - 1, kWave);
-    }
-    const float t = u * carry;
-    int chosen = -1, lastpos = -1;
-    for (int g0 = 0; g0 < nc && chosen < 0; g0 += kWave) {
-      const int c = g0 + l;
-      const bool ok = c < nc;
-      const unsigned long long hit = __ballot(ok && sh.cum[c] > t);
-      const unsigned long long pos = __ballot(ok && sh.W[c] > 0.0f);
-      if (hit) chosen = g0 + __ffsll((unsigned long long)hit) - 1;
-      if (pos) lastpos = g0 + 63 - __clzll((unsigned long long)pos);
-    }
-    if (l == 0) {
-      if (chosen >= 0) {
-        sh.chunk = chosen;
-        sh.t_in = t - (sh.cum[chosen] - sh.W[chosen]);
-      } else {
-        sh.chunk = lastpos;  // rounding: take the last positive weight
-        sh.t_in = INFINITY;
-      }
-    }
-  }
-  __syncthreads();
-  const int c = sh.chunk;
-  if (c < 0) return -1;
-  const float t_in = sh.t_in;
-  const int cstart = c * kChunk<DT>;
+  const int cstart = pk.chunk * kChunk<DT>;
   u32x4 raw[kLoads];
   load_chunk<DT, VP, false>(row, cstart, a.V, tid, raw);
   float vs[kLoads];
@@ -170,46 +159,43 @@ __device__ int draw_row(const Args& a, DrawShared& sh, int b, int r,
     }
     vs[it] = acc;
   }
-  // Cell (it, wave) totals: the last lane of each wavefront's inclusive scan.
+  // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
+  float tot[kLoads];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) {
-    const float inc = wave_inclusive_sum(vs[it]);
-    if (l == kWave - 1) sh.cell[it * kWaves + w] = inc;
-  }
-  int wl = tlast;
+  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum(vs[it]);
+  const int wl = wave_max_i(tlast);
+  if (l == 0) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wl = max(wl, __shfl_xor(wl, o, kWave));
-  if (l == 0) sh.wlast[w] = wl;
-  __syncthreads();
-  if (w == 0) {
-    const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
-    const float inc = wave_inclusive_sum(cv);
-    float exc = __shfl_up(inc, 1, kWave);
-    if (l == 0) exc = 0.0f;
-    const unsigned long long hit =
-        __ballot(l < kLoads * kWaves && exc <= t_in && t_in < inc);
-    if (l == 0) {
-      int cl = -1;
-      for (int i = 0; i < kWaves; ++i) cl = max(cl, sh.wlast[i]);
-      sh.result = cl;  // default: the chunk's last positive weight
-      sh.cell_sel = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
-    }
-    if (hit && l == __ffsll((unsigned long long)hit) - 1) sh.t_cell = t_in - exc;
+    for (int it = 0; it < kLoads; ++it) sh.cell[it * kWaves + w] = tot[it];
+    sh.wlast[w] = wl;
   }
   __syncthreads();
-  const int cell = sh.cell_sel;
-  if (cell >= 0 && w == cell % kWaves) {
+  // Every wavefront finds the cell (the same scan gives the same answer).
+  const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
+  const float inc = wave_inclusive_sum(cv);
+  const float exc = wave_shift_up1(inc);
+  const unsigned long long hit =
+      __ballot(l < kLoads * kWaves && exc <= pk.t_in && pk.t_in < inc);
+  int clast = sh.wlast[0];
+  for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
+  const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+  if (cell < 0) {
+    if (tid == 0) sh.result = clast;  // the chunk's last positive weight
+  } else if (w == cell % kWaves) {
     const int its = cell / kWaves;
-    float v = 0.0f;
+    float v = vs[0];
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it)
+    for (int it = 1; it < kLoads; ++it)
       if (it == its) v = vs[it];
-    const float inc = wave_inclusive_sum(v);
-    float exc = __shfl_up(inc, 1, kWave);
-    if (l == 0) exc = 0.0f;
-    const float tc = sh.t_cell;
-    if (exc <= tc && tc < inc) {  // exactly one lane: same scan as the cell total
-      const float tl = tc - exc;
+    const float tc = pk.t_in - readlane_f(exc, cell);
+    const float inc2 = wave_inclusive_sum(v);
+    const float exc2 = wave_shift_up1(inc2);
+    const bool mine = exc2 <= tc && tc < inc2;
+    const unsigned long long who = __ballot(mine);
+    if (!who) {
+      if (l == 0) sh.result = clast;
+    } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
+      const float tl = tc - exc2;
       u32x4 rv = raw[0];
 #pragma unroll
       for (int it = 1; it < kLoads; ++it)
@@ -253,6 +239,7 @@ struct FinalShared {
   int bad[kMaxRows];
   int x[kMaxRows];
   int tok[kMaxRows];
+  ChunkPick pick[kMaxRows];  // chunk choice of a draw at each row (T > 0)
   int acc_len;
   int st;
   DrawShared draw;
@@ -302,9 +289,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         argmax_merge(bv, bi, p.x, __float_as_int(p.w));
         nan |= (p.y != 0.0f);
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-        argmax_merge(bv, bi, __shfl_xor(bv, o, kWave), __shfl_xor(bi, o, kWave));
+      wave_argmax(bv, bi);
       nan = wave_or(nan);
       if (l == 0) {
         sh.m[j] = bv;
@@ -324,16 +309,25 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
           has = true;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-        lse_merge(m, s, __shfl_xor(m, o, kWave), __shfl_xor(s, o, kWave), kk);
+      wave_lse(m, s, kk);
       const unsigned long long hb = __ballot(has);
-      if (hb) lxv = __shfl(lxv, __ffsll((unsigned long long)hb) - 1, kWave);
+      if (hb) lxv = readlane_f(lxv, __ffsll((unsigned long long)hb) - 1);
+      // Where a draw at this row would land: x_j (j < d) is removed from its
+      // chunk's weight for the one-hot residual; row d is the bonus.
+      const float wx = (j < d && hb) ? fast_exp2((lxv - m) * kk) : 0.0f;
+      const int cxw = (j < d) ? cx : -1;
+      const float uK = sh.u[a.K];
+      const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
+        const f32x4 p = load_partial(P + c);
+        const float W = p.y * fast_exp2((p.x - m) * kk);
+        return c == cxw ? fmaxf(0.0f, W - wx) : W;
+      });
       if (l == 0) {
         sh.m[j] = m;
         sh.s[j] = s;
         sh.lx[j] = lxv;
         sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
+        sh.pick[j] = pk;
       }
     }
   }
@@ -395,10 +389,8 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
                             : i32x4{0, 0, 0, 0};
   if (sh.st == 0 && !greedy && !residual) {
     const int excl = (al < d) ? sh.x[al] : -1;
-    const float wx = (al < d) ? fast_exp2((sh.lx[al] - sh.m[al]) * kk) : 0.0f;
-    const f32x4* Pr = cached ? sh.pc + al * nc : Pb + (int64_t)al * nc;
-    const int tok = draw_row<DT, VP, false>(a, sh.draw, b, al, Pr, excl, wx,
-                                            sh.m[al], sh.s[al], kk, sh.u[a.K]);
+    const int tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, sh.pick[al],
+                                                 excl, sh.m[al], kk, 0.0f);
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
@@ -473,7 +465,8 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
 
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
-  __shared__ float total_sh;
+  __shared__ ChunkPick pick_sh;
+  __shared__ int from_p;
   __shared__ DrawShared dsh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int nc = a.nchunks;
@@ -485,20 +478,28 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   const float kk = __int_as_float(info.w);
   const int R = a.K + 1;
   if (w == 0) {
-    float tot = 0.0f;
-    for (int cc = l; cc < nc; cc += kWave) tot += a.rpart[(int64_t)b * nc + cc];
-    tot = wave_sum(tot);
-    if (l == 0) total_sh = tot;
+    const float u = a.uniforms[(int64_t)b * R + a.K];
+    const float* rp = a.rpart + (int64_t)b * nc;
+    ChunkPick pk = pick_chunk(nc, u, [&](int c) { return load_f32(rp + c); });
+    // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
+    const bool fallback = pk.chunk < 0;
+    if (fallback) {
+      const f32x4* Pr = a.partials + ((int64_t)b * R + r) * nc;
+      pk = pick_chunk(nc, u, [&](int c) {
+        const f32x4 p = load_partial(Pr + c);
+        return p.y * fast_exp2((p.x - m) * kk);
+      });
+    }
+    if (l == 0) {
+      pick_sh = pk;
+      from_p = fallback;
+    }
   }
   __syncthreads();
-  const float u = a.uniforms[(int64_t)b * R + a.K];
-  // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
-  const int tok = total_sh > 0.0f
-                      ? draw_row<DT, VP, true>(a, dsh, b, r, nullptr, -1, 0.0f, m,
-                                               S, kk, u)
-                      : draw_row<DT, VP, false>(a, dsh, b, r,
-                                                a.partials + ((int64_t)b * R + r) * nc,
-                                                -1, 0.0f, m, S, kk, u);
+  const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, -1, m,
+                                                        kk, 0.0f)
+                         : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, -1, m,
+                                                       kk, 1.0f / S);
   if (tid == 0) a.out[(int64_t)b * R + r] = tok;
 }
 

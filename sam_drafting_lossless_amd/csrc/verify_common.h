@@ -179,6 +179,25 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float om, float os
   m = M;
 }
 
+// Wavefront reductions of (value, index) by argmax_merge and of (max, sum)
+// by lse_merge; every lane ends with the result.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  float fi = __int_as_float(i);
+  wave_reduce2(v, fi, kNegInf, __int_as_float(INT_MAX),
+               [](float& x, float& y, float ox, float oy) {
+                 int iy = __float_as_int(y);
+                 argmax_merge(x, iy, ox, __float_as_int(oy));
+                 y = __int_as_float(iy);
+               });
+  i = __float_as_int(fi);
+}
+
+__device__ __forceinline__ void wave_lse(float& m, float& s, float kk) {
+  wave_reduce2(m, s, kNegInf, 0.0f, [kk](float& x, float& y, float ox, float oy) {
+    lse_merge(x, y, ox, oy, kk);
+  });
+}
+
 // Partials and residual sums are written by one kernel and read by the next
 // one on the same stream; plain accesses suffice.
 __device__ __forceinline__ f32x4 load_partial(const f32x4* p) { return *p; }
