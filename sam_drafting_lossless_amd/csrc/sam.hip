@@ -16,8 +16,9 @@ __global__ __launch_bounds__(kWave) void sam_extend_kernel(
     unsigned char* base, int max_len, SamLayout L, const int32_t* tokens,
     int ld, const int32_t* counts) {
   const int b = blockIdx.x;
-  sam_extend_seq(sam_seq(base, b, L), tokens + (int64_t)b * ld, counts[b], ld,
-                 max_len);
+  const SamSeq S = sam_seq(base, b, L);
+  SamCursor cs = sam_open(S);
+  sam_append(S, cs, tokens + (int64_t)b * ld, counts[b], ld, max_len);
 }
 
 // The same extension with work counters, summed into stats[SS_STAT_COUNT].
@@ -26,8 +27,9 @@ __global__ __launch_bounds__(kWave) void sam_extend_stats_kernel(
     int ld, const int32_t* counts, unsigned long long* stats) {
   const int b = blockIdx.x;
   SamCounters ctr = {};
-  sam_extend_seq<true>(sam_seq(base, b, L), tokens + (int64_t)b * ld, counts[b],
-                       ld, max_len, &ctr);
+  const SamSeq S = sam_seq(base, b, L);
+  SamCursor cs = sam_open(S);
+  sam_append<true>(S, cs, tokens + (int64_t)b * ld, counts[b], ld, max_len, &ctr);
   if (lane_id() < SS_STAT_COUNT) {
     unsigned long long v = 0;
 #pragma unroll
@@ -53,8 +55,11 @@ __global__ __launch_bounds__(kWave) void sam_extend_draft_kernel(
     int32_t* match_len) {
   const int b = blockIdx.x;
   const SamSeq S = sam_seq(base, b, L);
-  sam_extend_seq(S, tokens + (int64_t)b * ld, counts[b], ld, max_len);
-  sam_draft_seq(S, K, draft + (int64_t)b * K, draft_len + b, match_len + b);
+  SamCursor cs = sam_open(S);
+  if (sam_append(S, cs, tokens + (int64_t)b * ld, counts[b], ld, max_len))
+    sam_draft_cursor(S, cs, K, draft + (int64_t)b * K, draft_len + b, match_len + b);
+  else
+    sam_draft_seq(S, K, draft + (int64_t)b * K, draft_len + b, match_len + b);
 }
 
 __global__ void sam_init_kernel(unsigned char* base, int max_len, int V,

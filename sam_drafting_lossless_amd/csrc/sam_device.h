@@ -154,20 +154,59 @@ __device__ __forceinline__ void sam_store_header(const SamSeq& S,
   S.hdr[H_STATUS] = h.status;
 }
 
+// What a wavefront keeps in registers while it works on one sequence: the
+// header, the record of the last state and, after an extension, the link of
+// the last state with its record. Every record here is exact: each one is
+// either loaded after the stores that could change it or is what was just
+// stored.
+struct SamCursor {
+  SamHdrRegs h;
+  i32x4 rlast;      // record of h.last
+  int link;         // link(h.last), or -1 if not carried
+  i32x4 rlink;      // its record
+};
+
+// Loads the header, then the record of the last state.
+__device__ __forceinline__ SamCursor sam_open(const SamSeq& S) {
+  SamCursor cs;
+  cs.h = sam_load_header(S);
+  cs.rlast = S.st[cs.h.last];
+  cs.link = -1;
+  return cs;
+}
+
+// A cursor assembled from values fetched one dword per lane: lane k of hv
+// holds header word k (k < 8), lane k of rv word k of the last state's record
+// (k < 4). Wave-uniform result.
+__device__ __forceinline__ SamCursor cursor_from_lanes(int hv, int rv) {
+  SamCursor cs;
+  cs.h = SamHdrRegs{__builtin_amdgcn_readlane(hv, 0), __builtin_amdgcn_readlane(hv, 1),
+                    __builtin_amdgcn_readlane(hv, 2), __builtin_amdgcn_readlane(hv, 3),
+                    __builtin_amdgcn_readlane(hv, 4), __builtin_amdgcn_readlane(hv, 5),
+                    __builtin_amdgcn_readlane(hv, 6), __builtin_amdgcn_readlane(hv, 7)};
+  cs.rlast = i32x4{__builtin_amdgcn_readlane(rv, 0), __builtin_amdgcn_readlane(rv, 1),
+                   __builtin_amdgcn_readlane(rv, 2), __builtin_amdgcn_readlane(rv, 3)};
+  cs.link = -1;
+  return cs;
+}
+
 // Appends token c at position n (Blumer's online extension; `cur` is numbered
-// before `clone`). Returns false if a bound check trips.
+// before `clone`) and moves the cursor to cur. Returns false if a bound check
+// trips.
 template <bool COUNT = false>
-__device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
+__device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
                                       unsigned bmask, SamCounters* ctr = nullptr) {
   auto tally = [&](int k, int n) {
     if constexpr (COUNT) ctr->v[k] += (unsigned long long)n;
   };
+  SamHdrRegs& h = cs.h;
   tally(SS_STAT_TOKENS, 1);
   const int i = h.n;
   const int cur = h.nstates++;
-  i32x4 rp = S.st[h.last];
-  S.st[cur] = i32x4{rp.x + 1, -1, i, -1};
+  const int lencur = cs.rlast.x + 1;
+  S.st[cur] = i32x4{lencur, -1, i, -1};
   int p = h.last;
+  i32x4 rp = cs.rlast;
   SamProbe pr;
   int guard = 0;
   // Walk suffix links from last, adding (p, c) -> cur until (p, c) exists.
@@ -189,13 +228,17 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
     rp = rn;
     if (++guard > h.nstates) return false;
   }
+  int link;
+  i32x4 rlink;
   if (p == -1) {
-    reinterpret_cast<int*>(&S.st[cur])[1] = 0;
+    link = 0;
+    rlink = i32x4{0, -1, 0, 0};  // only the root's len (0) is read from it
   } else {
     const int q = pr.dst;
     const i32x4 rq = S.st[q];
     if (rp.x + 1 == rq.x) {
-      reinterpret_cast<int*>(&S.st[cur])[1] = q;
+      link = q;
+      rlink = rq;  // loaded after the walk's stores; nothing below changes it
     } else {
       const int clone = h.nstates++;
       tally(SS_STAT_CLONES, 1);
@@ -214,7 +257,8 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
         e = se.w;
         if (++g2 > h.nedges) return false;
       }
-      S.st[clone] = i32x4{rp.x + 1, rq.y, rq.z, first};
+      const i32x4 rc = i32x4{rp.x + 1, rq.y, rq.z, first};
+      S.st[clone] = rc;
       // Redirect (p', c) -> q to the clone along the suffix path from p.
       int sl = pr.slot;
       i32x4 rr = rp;
@@ -233,26 +277,34 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamHdrRegs& h, int c,
         if (++g3 > h.nstates) return false;
       }
       reinterpret_cast<int*>(&S.st[q])[1] = clone;
-      reinterpret_cast<int*>(&S.st[cur])[1] = clone;
+      link = clone;
+      rlink = rc;
     }
   }
+  reinterpret_cast<int*>(&S.st[cur])[1] = link;
   h.last = cur;
   S.text[i] = c;
   h.n = i + 1;
+  cs.rlast = i32x4{lencur, link, i, -1};
+  cs.link = link;
+  cs.rlink = rlink;
   return true;
 }
 
 // Appends tokens tk[0..cnt) (wave-uniform) to one sequence, stopping at the
 // first token that is out of range or would exceed capacity. A sequence whose
-// status is already non-zero is left alone. Executed by one whole wavefront.
+// status is already non-zero is left alone. Returns false if the cursor no
+// longer describes the sequence (an extension stopped part-way). Executed by
+// one whole wavefront.
 template <bool COUNT = false>
-__device__ inline void sam_extend_seq(const SamSeq& S, const int32_t* tk,
-                                      int cnt, int ld, int max_len,
-                                      SamCounters* ctr = nullptr) {
-  SamHdrRegs h = sam_load_header(S);
-  if (h.status != 0) return;
+__device__ inline bool sam_append(const SamSeq& S, SamCursor& cs, const int32_t* tk,
+                                  int cnt, int ld, int max_len,
+                                  SamCounters* ctr = nullptr) {
+  SamHdrRegs& h = cs.h;
+  if (h.status != 0) return true;
   const unsigned bmask = (unsigned)(h.slots / kBucket) - 1u;
   int st = 0;
+  bool whole = true;
   if (cnt < 0 || cnt > ld) {
     st = SS_ST_COUNT;
   } else {
@@ -262,26 +314,28 @@ __device__ inline void sam_extend_seq(const SamSeq& S, const int32_t* tk,
         st = SS_ST_TOKEN_RANGE;
         break;
       }
-      if (h.n >= max_len || h.nstates + 2 > 2 * max_len ||
-          !sam_extend_one<COUNT>(S, h, c, bmask, ctr)) {
+      if (h.n >= max_len || h.nstates + 2 > 2 * max_len) {
         st = SS_ST_SAM_CAPACITY;
+        break;
+      }
+      if (!sam_extend_one<COUNT>(S, cs, c, bmask, ctr)) {
+        st = SS_ST_SAM_CAPACITY;
+        whole = false;
         break;
       }
     }
   }
   h.status |= st;
   sam_store_header(S, h);
+  return whole;
 }
 
-// Draft for one sequence: link walk from last to the first state with an
-// outgoing transition, then lanes j < K gather text[p + 1 + j]. Executed by
-// one whole wavefront (the walk is uniform across lanes).
-__device__ inline void sam_draft_seq(const SamSeq& S, int K, int32_t* draft,
-                                     int32_t* draft_len, int32_t* match_len) {
-  const i32x4 h0 = reinterpret_cast<const i32x4*>(S.hdr)[0];
-  const int n = h0.x, nstates = h0.z;
-  int s = h0.y;
-  i32x4 rs = S.st[s];
+// Draft from state s with record rs: follow suffix links while the state has
+// no outgoing transition, then lanes j < K gather text[p + 1 + j] where p is
+// the min_endpos of the state reached. Executed by one whole wavefront.
+__device__ inline void sam_draft_from(const SamSeq& S, int n, int nstates, int s,
+                                      i32x4 rs, int K, int32_t* draft,
+                                      int32_t* draft_len, int32_t* match_len) {
   for (int g = 0; s > 0 && rs.w == -1 && g < nstates; ++g) {
     s = rs.y;
     rs = S.st[s < 0 ? 0 : s];
@@ -295,6 +349,29 @@ __device__ inline void sam_draft_seq(const SamSeq& S, int K, int32_t* draft,
     *draft_len = d;
     *match_len = Lm;
   }
+}
+
+// Draft for one sequence from its stored header (the link walk starts at the
+// last state).
+__device__ inline void sam_draft_seq(const SamSeq& S, int K, int32_t* draft,
+                                     int32_t* draft_len, int32_t* match_len) {
+  const SamCursor cs = sam_open(S);
+  sam_draft_from(S, cs.h.n, cs.h.nstates, cs.h.last, cs.rlast, K, draft, draft_len,
+                 match_len);
+}
+
+// Draft from a cursor: after an extension the last state is the newest one,
+// which has no outgoing transition, so the walk starts at its link, whose
+// record the extension carried.
+__device__ inline void sam_draft_cursor(const SamSeq& S, const SamCursor& cs, int K,
+                                        int32_t* draft, int32_t* draft_len,
+                                        int32_t* match_len) {
+  if (cs.link >= 0 && cs.rlast.w == -1)
+    sam_draft_from(S, cs.h.n, cs.h.nstates, cs.link, cs.rlink, K, draft, draft_len,
+                   match_len);
+  else
+    sam_draft_from(S, cs.h.n, cs.h.nstates, cs.h.last, cs.rlast, K, draft,
+                   draft_len, match_len);
 }
 
 }  // namespace specsam

@@ -128,20 +128,34 @@ __device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int ti
   }
 }
 
-// Whole workgroup; `pk` must be the same in every thread.
-template <int DT, bool VP, bool RESIDUAL>
+struct NoDuring {
+  __device__ void operator()() const {}
+};
+
+// Requests the chosen chunk of row r (nothing if every weight is 0).
+template <int DT, bool VP>
+__device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick pk,
+                                          u32x4 (&raw)[kLoads]) {
+  if (pk.chunk < 0) return;
+  const unsigned char* row =
+      a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes;
+  load_chunk<DT, VP, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
+}
+
+// Whole workgroup; `pk` must be the same in every thread and `raw` hold the
+// chunk draw_load requested. `during` runs first, while that chunk is still
+// in flight (the fused step appends the accepted drafts to the automaton
+// there).
+template <int DT, bool VP, bool RESIDUAL, typename During = NoDuring>
 __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
                              ChunkPick pk, int excl, float m, float kk,
-                             float invS) {
+                             float invS, const u32x4 (&raw)[kLoads],
+                             During during = During{}) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int R = a.K + 1;
+  during();
   if (pk.chunk < 0) return -1;
-  const unsigned char* row =
-      a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
   const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const int cstart = pk.chunk * kChunk<DT>;
-  u32x4 raw[kLoads];
-  load_chunk<DT, VP, false>(row, cstart, a.V, tid, raw);
   float vs[kLoads];
   int tlast = -1;
 #pragma unroll
@@ -239,13 +253,15 @@ struct FinalShared {
   int bad[kMaxRows];
   int x[kMaxRows];
   int tok[kMaxRows];
+  float qx[kMaxRows];        // q at the draft token of each row
   ChunkPick pick[kMaxRows];  // chunk choice of a draw at each row (T > 0)
   int acc_len;
   int st;
   DrawShared draw;
 };
 
-template <int DT, bool VP, bool SAM>
+// Q: draft probabilities q are given (then SAM is false).
+template <int DT, bool VP, bool SAM, bool Q>
 __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   __shared__ FinalShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
@@ -253,15 +269,35 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   const int R = a.K + 1, nc = a.nchunks;
   // Everything that does not depend on another load is requested at once:
   // the sequence's parameters, drafts, coins and the partials of every row.
-  const bool cached = R * nc <= kPartialCache;
-  const f32x4* Pb = a.partials + (int64_t)b * R * nc;
-  if (cached)
-    for (int e = tid; e < R * nc; e += kThreads) sh.pc[e] = Pb[e];
-  if (tid < a.K) sh.x[tid] = a.draft[(int64_t)b * a.K + tid];
-  if (tid < R && a.uniforms) sh.u[tid] = a.uniforms[(int64_t)b * R + tid];
+  // The automaton step's header and last-state record are requested in the
+  // following phases, so that no barrier waits for them and both are in
+  // registers when the step needs them.
   int d;
   float T;
   const int st0 = seq_check(a, b, &d, &T);
+  SamSeq S;
+  SamCursor cs;
+  if constexpr (SAM) S = sam_seq(a.sam, b, a.sl);
+  const bool cached = R * nc <= kPartialCache;
+  const f32x4* Pb = a.partials + (int64_t)b * R * nc;
+  // All loads are issued before the first LDS store, so that they share one
+  // round trip.
+  // (The common case has at most one partial per thread; more go through a
+  // plain loop.)
+  const bool one = cached && R * nc <= kThreads;  // uniform
+  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (one) {
+    pv = Pb[min(tid, R * nc - 1)];
+  } else if (cached) {
+    for (int e = tid; e < R * nc; e += kThreads) sh.pc[e] = Pb[e];
+  }
+  int xv = -1;
+  float uv = 0.0f;
+  if (tid < a.K) xv = a.draft[(int64_t)b * a.K + tid];
+  if (tid < R && a.uniforms) uv = a.uniforms[(int64_t)b * R + tid];
+  if (one && tid < R * nc) sh.pc[tid] = pv;
+  if (tid < a.K) sh.x[tid] = xv;
+  if (tid < R) sh.u[tid] = uv;
   __syncthreads();
   if (st0) {
     // Reported once; the automaton (if any) is left unchanged and the next
@@ -277,61 +313,94 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     }
     return;
   }
+  // The header is fetched one dword per lane: a lane-varying value is not
+  // moved to scalar registers, so nothing waits for it before the step reads
+  // it with readlane.
+  int hv = 0, rv = 0;
+  if constexpr (SAM) {
+    if (w == 0 && l < 8) hv = S.hdr[l];
+  }
   const bool greedy = (T == 0.0f);
   const float kk = greedy ? 0.0f : kLog2e / T;
-  for (int j = w; j <= d; j += kWaves) {
-    const f32x4* P = cached ? sh.pc + j * nc : Pb + (int64_t)j * nc;
-    if (greedy) {
-      float bv = kNegInf;
-      int bi = INT_MAX, nan = 0;
-      for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = load_partial(P + c);
-        argmax_merge(bv, bi, p.x, __float_as_int(p.w));
-        nan |= (p.y != 0.0f);
-      }
-      wave_argmax(bv, bi);
-      nan = wave_or(nan);
-      if (l == 0) {
-        sh.m[j] = bv;
-        sh.idx[j] = bi;
-        sh.bad[j] = nan || bv == INFINITY || bv == kNegInf;
-      }
-    } else {
-      const int xj = (j < d) ? sh.x[j] : -1;
-      const int cx = (xj >= 0 && xj < a.V) ? xj / kChunk<DT> : -1;
-      float m = kNegInf, s = 0.0f, lxv = 0.0f;
-      bool has = false;
-      for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = load_partial(P + c);
-        lse_merge(m, s, p.x, p.y, kk);
-        if (c == cx) {
-          lxv = p.z;
-          has = true;
-        }
-      }
-      wave_lse(m, s, kk);
-      const unsigned long long hb = __ballot(has);
-      if (hb) lxv = readlane_f(lxv, __ffsll((unsigned long long)hb) - 1);
-      // Where a draw at this row would land: x_j (j < d) is removed from its
-      // chunk's weight for the one-hot residual; row d is the bonus.
-      const float wx = (j < d && hb) ? fast_exp2((lxv - m) * kk) : 0.0f;
-      const int cxw = (j < d) ? cx : -1;
-      const float uK = sh.u[a.K];
-      const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
-        const f32x4 p = load_partial(P + c);
-        const float W = p.y * fast_exp2((p.x - m) * kk);
-        return c == cxw ? fmaxf(0.0f, W - wx) : W;
-      });
-      if (l == 0) {
-        sh.m[j] = m;
-        sh.s[j] = s;
-        sh.lx[j] = lxv;
-        sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
-        sh.pick[j] = pk;
-      }
+  // q at each draft token (1 for one-hot drafts), gathered while the rows
+  // are combined so that the accept scan reads only LDS.
+  if constexpr (Q) {
+    if (!greedy && tid < d) {
+      const int x = sh.x[tid];
+      sh.qx[tid] = (x >= 0 && x < a.V) ? a.q[((int64_t)b * a.K + tid) * a.V + x] : 1.0f;
     }
   }
+  // Row j's partials come from LDS when cached, else from the workspace. The
+  // two sources are separate instantiations, so that LDS reads never wait
+  // for global loads still in flight (a generic pointer, or a per-access
+  // choice, would make them).
+  auto combine_rows = [&](auto part) {
+    for (int j = w; j <= d; j += kWaves) {
+      if (greedy) {
+        float bv = kNegInf;
+        int bi = INT_MAX, nan = 0;
+        for (int c = l; c < nc; c += kWave) {
+          const f32x4 p = part(j, c);
+          argmax_merge(bv, bi, p.x, __float_as_int(p.w));
+          nan |= (p.y != 0.0f);
+        }
+        wave_argmax(bv, bi);
+        nan = wave_or(nan);
+        if (l == 0) {
+          sh.m[j] = bv;
+          sh.idx[j] = bi;
+          sh.bad[j] = nan || bv == INFINITY || bv == kNegInf;
+        }
+      } else {
+        const int xj = (j < d) ? sh.x[j] : -1;
+        const int cx = (xj >= 0 && xj < a.V) ? xj / kChunk<DT> : -1;
+        float m = kNegInf, s = 0.0f, lxv = 0.0f;
+        bool has = false;
+        for (int c = l; c < nc; c += kWave) {
+          const f32x4 p = part(j, c);
+          lse_merge(m, s, p.x, p.y, kk);
+          if (c == cx) {
+            lxv = p.z;
+            has = true;
+          }
+        }
+        wave_lse(m, s, kk);
+        const unsigned long long hb = __ballot(has);
+        if (hb) lxv = readlane_f(lxv, __ffsll((unsigned long long)hb) - 1);
+        // Where a draw at this row would land: x_j (j < d) is removed from
+        // its chunk's weight for the one-hot residual; row d is the bonus.
+        const float wx = (j < d && hb) ? fast_exp2((lxv - m) * kk) : 0.0f;
+        const int cxw = (j < d) ? cx : -1;
+        const float uK = sh.u[a.K];
+        const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
+          const f32x4 p = part(j, c);
+          const float W = p.y * fast_exp2((p.x - m) * kk);
+          return c == cxw ? fmaxf(0.0f, W - wx) : W;
+        });
+        if (l == 0) {
+          sh.m[j] = m;
+          sh.s[j] = s;
+          sh.lx[j] = lxv;
+          sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
+          sh.pick[j] = pk;
+        }
+      }
+    }
+  };
+  if (cached)
+    combine_rows([&](int j, int c) { return sh.pc[j * nc + c]; });
+  else
+    combine_rows([&](int j, int c) { return load_partial(Pb + (int64_t)j * nc + c); });
   __syncthreads();
+  if constexpr (SAM) {
+    if (w == 0 && l < 4)
+      rv = reinterpret_cast<const int*>(S.st)[__builtin_amdgcn_readlane(hv, H_LAST) * 4 + l];
+  }
+  // The bonus row's chosen chunk is requested before the accept scan: row d
+  // is the draw row whenever every draft is accepted, and always when d = 0.
+  u32x4 raw[kLoads];
+  const bool spec = !greedy && sh.pick[d].chunk >= 0;
+  if (spec) draw_load<DT, VP>(a, b, d, sh.pick[d], raw);
   if (w == 0) {
     int st = 0, x = -1;
     if (l < d) {
@@ -354,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
           acc = (x == sh.idx[l]);
         } else {
           px = fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l];
-          const float qx = a.q ? a.q[((int64_t)b * a.K + l) * a.V + x] : 1.0f;
+          const float qx = Q ? sh.qx[l] : 1.0f;
           acc = (qx > 0.0f) ? (sh.u[l] <= px / qx) : (px > 0.0f);
         }
       }
@@ -382,15 +451,33 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   }
   __syncthreads();
   const int al = sh.acc_len;
-  const bool residual = sh.st == 0 && !greedy && al < d && a.q != nullptr;
+  const bool residual = Q && sh.st == 0 && !greedy && al < d;
   if (tid == 0)
     a.seqinfo[b] = residual ? i32x4{al + 1, __float_as_int(sh.m[al]),
                                     __float_as_int(sh.s[al]), __float_as_int(kk)}
                             : i32x4{0, 0, 0, 0};
-  if (sh.st == 0 && !greedy && !residual) {
+  // Automaton step (wavefront 0): the emitted tokens sh.tok[0..al] are
+  // appended in order; when a token is drawn, the accepted drafts before it
+  // are appended while the draw's chunk is in flight.
+  bool whole = true, cs_ready = false;
+  int appended = 0;
+  const bool drawn = sh.st == 0 && !greedy && !residual;
+  if (drawn) {
     const int excl = (al < d) ? sh.x[al] : -1;
+    if (!spec || al != d) draw_load<DT, VP>(a, b, al, sh.pick[al], raw);
+    auto during = [&]() {
+      if constexpr (SAM) {
+        if (w == 0 && al > 0) {
+          cs = cursor_from_lanes(hv, rv);
+          cs_ready = true;
+          whole = sam_append(S, cs, sh.tok, al, R, a.max_len);
+          appended = al;
+        }
+      }
+    };
     const int tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, sh.pick[al],
-                                                 excl, sh.m[al], kk, 0.0f);
+                                                 excl, sh.m[al], kk, 0.0f, raw,
+                                                 during);
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
@@ -399,10 +486,14 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   }
   if constexpr (SAM) {
     if (w == 0) {
-      const SamSeq S = sam_seq(a.sam, b, a.sl);
-      if (sh.st == 0) sam_extend_seq(S, sh.tok, al + 1, R, a.max_len);
-      sam_draft_seq(S, a.K, a.next_draft + (int64_t)b * a.K, a.next_draft_len + b,
-                    a.next_match_len + b);
+      int32_t* nd = a.next_draft + (int64_t)b * a.K;
+      if (!cs_ready) cs = cursor_from_lanes(hv, rv);
+      if (sh.st == 0 && whole)
+        whole = sam_append(S, cs, sh.tok + appended, al + 1 - appended, R, a.max_len);
+      if (whole)
+        sam_draft_cursor(S, cs, a.K, nd, a.next_draft_len + b, a.next_match_len + b);
+      else
+        sam_draft_seq(S, a.K, nd, a.next_draft_len + b, a.next_match_len + b);
     }
   }
 }
@@ -496,10 +587,12 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
     }
   }
   __syncthreads();
+  u32x4 raw[kLoads];
+  draw_load<DT, VP>(a, b, r, pick_sh, raw);
   const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, -1, m,
-                                                        kk, 0.0f)
+                                                        kk, 0.0f, raw)
                          : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, -1, m,
-                                                       kk, 1.0f / S);
+                                                       kk, 1.0f / S, raw);
   if (tid == 0) a.out[(int64_t)b * R + r] = tok;
 }
 
@@ -533,8 +626,12 @@ WsLayout ws_layout(int B, int K, int V) {
 
 template <int DT, bool VP, bool SAM>
 int launch_finish(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM>), dim3((unsigned)a.B),
-                     dim3(kThreads), 0, s, a);
+  if (a.q)
+    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, false, true>), dim3((unsigned)a.B),
+                       dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM, false>), dim3((unsigned)a.B),
+                       dim3(kThreads), 0, s, a);
   int rc = check_launch("spec_finish");
   if (rc != SS_OK || a.q == nullptr) return rc;
   hipLaunchKernelGGL((verify_residual_sums<DT, VP>),
