@@ -65,31 +65,67 @@ def _traffic_from_profile(rows_per_launch: float):
     return rec["hbm_bytes_per_row"] * rows_per_launch
 
 
-def cpu_baseline(slot_host, gt, cfg, nthreads: int, budget_s: float = 15.0):
+def cpu_baseline(slot_host, gt, cfg, nthreads: int, budget_s: float = 10.0):
     """Times the oracle's whole step (draft, verify, extend) over all B
-    sequences on one host copy of a boosted logit slot."""
+    sequences on one host copy of a boosted logit slot, with `nthreads`
+    threads over sequences for about budget_s seconds; then a shorter
+    single-thread run, and a split of one step's time between verification
+    and the automata. Returns (baseline line, detail)."""
     import numpy as np
 
     import oracle
-    H = cfg.hist_len
-    sams = [oracle.SAM(gt[b, :H]) for b in range(cfg.B)]
-    T = np.full(cfg.B, cfg.T, np.float32)
     import synth
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        u = synth.uniforms(cfg, 10_000 + steps)
-        oracle.step(sams, slot_host, T, u, nthreads=nthreads)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 200:
-            break
-    return {"value": steps / el, "unit": "steps/s", "cores": nthreads,
+    H = cfg.hist_len
+    T = np.full(cfg.B, cfg.T, np.float32)
+
+    def run(nthreads, budget, cap):
+        sams = [oracle.SAM(gt[b, :H]) for b in range(cfg.B)]
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            u = synth.uniforms(cfg, 10_000 + steps)
+            oracle.step(sams, slot_host, T, u, nthreads=nthreads)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or steps >= cap:
+                return steps, el, sams
+
+    steps, el, sams = run(nthreads, budget_s, 5000)
+    steps1, el1, _ = run(1, budget_s / 4, 5000)
+    # Split: drafts from the automata, verification, then the extension, on
+    # the automata the main run left behind.
+    t_sam = t_ver = 0.0
+    nsplit = 10
+    for i in range(nsplit):
+        t0 = time.perf_counter()
+        dr = [s.draft(cfg.K) for s in sams]
+        t1 = time.perf_counter()
+        d = np.stack([x[0] for x in dr]).astype(np.int32)
+        dl = np.array([x[1] for x in dr], np.int32)
+        u = synth.uniforms(cfg, 20_000 + i)
+        r = oracle.verify(slot_host, d, dl, T, u, nthreads=nthreads)
+        t2 = time.perf_counter()
+        for b, s in enumerate(sams):
+            s.extend(r.out_tokens[b, :r.num_emitted[b]])
+        t3 = time.perf_counter()
+        t_sam += (t1 - t0) + (t3 - t2)
+        t_ver += t2 - t1
+    line = {"value": steps / el, "unit": "steps/s", "cores": nthreads,
             "kind": "oracle",
             "sample": (f"{steps} whole steps (draft+verify+extend) of all "
                        f"{cfg.B} sequences on one host copy of a boosted "
                        f"logit slot [{cfg.B},{cfg.K + 1},{cfg.V}] fp32, "
                        f"{nthreads} threads over sequences, {el:.1f} s")}
+    detail = {"single_thread_steps_per_s": steps1 / el1,
+              "single_thread_sample": f"{steps1} steps, {el1:.1f} s",
+              "verify_ms_per_step": 1e3 * t_ver / nsplit,
+              "verify_threads": nthreads,
+              "automata_ms_per_step": 1e3 * t_sam / nsplit,
+              "automata_threads": 1,
+              "split_sample": (f"{nsplit} steps: drafts and extends through the "
+                               f"oracle's per-sequence calls, verification "
+                               f"over all sequences")}
+    return line, detail
 
 
 def hbm_read_probe(torch, harness, nbytes=4 << 30, iters=5):
@@ -113,8 +149,9 @@ def hbm_read_probe(torch, harness, nbytes=4 << 30, iters=5):
 def sam_stats_report(steps: int):
     """Automaton work per appended token (hash lookups, 128-byte bucket reads,
     suffix-link steps, clones) and time per extend call, for prefill and for
-    the per-step append, on the c3 and c4 histories and on a c3-shaped run
-    with a +12 boost (long accepted drafts)."""
+    the per-step append, on the c2 (1,024 tokens), c3 (8,192) and c4
+    (32,768) histories and on a c3-shaped run with a +12 boost (long accepted
+    drafts)."""
     import numpy as np
     import torch
 
@@ -122,7 +159,7 @@ def sam_stats_report(steps: int):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    for c, over in [(3, {}), (4, {}), (3, {"boost": 12.0, "B": 256})]:
+    for c, over in [(2, {}), (3, {}), (4, {}), (3, {"boost": 12.0, "B": 256})]:
         cfg = synth.config(c, **over)
         gt_h = synth.token_streams(cfg, steps)
         gt = torch.as_tensor(gt_h, device=dev)
@@ -193,7 +230,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--sam-stats", action="store_true",
@@ -225,7 +262,7 @@ def main():
     torch.cuda.set_device(dev)
     cfg = synth.config(3)
     B, K, V, R = cfg.B, cfg.K, cfg.V, cfg.K + 1
-    total = args.warmup + 3 * args.steps
+    total = args.warmup + 4 * args.steps
     t_setup = time.perf_counter()
     gt_h = synth.token_streams(cfg, total)
     gt = torch.as_tensor(gt_h, device=dev)
@@ -362,9 +399,25 @@ def main():
     torch.cuda.synchronize()
     separate_steps_s = args.steps / (time.perf_counter() - t1)
 
+    # Per-step library time (harness excluded): events around each spec_step
+    # call of a fourth pass. The event pair adds its own dispatch gap to each
+    # sample, so these are upper bounds.
+    first_ps = first_sep + args.steps
+    evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        boost(first_ps + i)
+        evp[i][0].record()
+        fused(first_ps + i)
+        evp[i][1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([1e3 * a.elapsed_time(b) for a, b in evp])
+
     ms_per_step = elapsed * 1e3 / args.steps
     dl = dl_hist[first_ev:first_ev + args.steps].cpu().numpy()
     nem = nem_hist[args.warmup:first_ev].cpu().numpy()
+    accept_hist = np.bincount(nem.ravel() - 1, minlength=R)[:R]
+    needed_bytes = float(nem.sum(axis=1).mean()) * V * 4
     rows_per_launch = float((dl + 1).sum(axis=1).mean())
     # Rows of every stream launch this run made (warmup, timed pass, event
     # pass x STREAM_BATCH, separate-call pass), for the traffic record.
@@ -379,14 +432,15 @@ def main():
         sys.exit(1)
 
     probe = None if args.no_probe else hbm_read_probe(torch, harness)
-    cpu = None
+    cpu = cpu_detail = None
     if args.cpu_budget > 0:
         slot_h = ring[(total - 1) % RING].cpu().numpy()
         try:
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:
             ncpu = os.cpu_count() or 1
-        cpu = cpu_baseline(slot_h, gt_h, cfg, min(ncpu, 16), args.cpu_budget)
+        cpu, cpu_detail = cpu_baseline(slot_h, gt_h, cfg, min(ncpu, 16),
+                                       args.cpu_budget)
 
     res = {
         "metric": METRIC,
@@ -410,6 +464,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": _traffic_from_profile(rows_per_launch)},
         "cpu_baseline": cpu,
+        "cpu_baseline_detail": cpu_detail,
         "path": "spec_step (stream pass, then finish pass: decisions, draws, "
                 "SAM extend, next draft)",
         "stream_pass_avg_us": stream_us,
@@ -420,6 +475,10 @@ def main():
         "stream_launch_rows_mean": stream_launch_rows_mean,
         "verify_bytes_per_launch": bytes_per_launch,
         "mean_tokens_per_step": float(nem.mean()),
+        "accepted_drafts_histogram": {str(k): int(c) for k, c in enumerate(accept_hist)},
+        "needed_rows_bytes_per_step": needed_bytes,
+        "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
+                                      np.percentile(step_us, [10, 50, 90])],
         "hbm_read_probe_GBps": probe,
         "setup_s": setup_s,
     }
