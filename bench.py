@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 METRIC = ("spec-verify+SAM-draft steps/s at B=256,V=152k,K=3; "
           "achieved HBM GB/s")
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-RING = 4
+INFINITY_CACHE_BYTES = 256 << 20
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "spec_stream_c3_traffic.json")
 
 
@@ -225,32 +225,11 @@ def copy_probe(nbytes: int, iters: int = 5):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": iters}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle work for cpu_baseline (0 = skip)")
-    ap.add_argument("--no-probe", action="store_true")
-    ap.add_argument("--sam-stats", action="store_true",
-                    help="report automaton work per token instead")
-    ap.add_argument("--copy-probe", type=int, default=0,
-                    help="run a copy kernel of this many bytes instead")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the step shards by sequence with no exchange; see "
-              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.sam_stats:
-        sam_stats_report(args.steps)
-        return
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
-
+def measure_sam_workload(cfg, steps: int, warmup: int):
+    """Runs the one-call step (harness boost, then spec_step) over `steps`
+    timed steps after `warmup`, then the event, separate-call and per-step
+    passes described in the module docstring. Inputs are resident before
+    timing starts."""
     import numpy as np
     import torch
 
@@ -259,10 +238,12 @@ def main():
     from sam_drafting_lossless_amd import harness
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = synth.config(3)
     B, K, V, R = cfg.B, cfg.K, cfg.V, cfg.K + 1
-    total = args.warmup + 4 * args.steps
+    dt = ssl.DTYPE_BF16 if cfg.dtype == "bf16" else ssl.DTYPE_F32
+    # Ring slots: at least 4, and together at least twice the 256 MB
+    # Infinity Cache, so that re-reading a slot comes from HBM.
+    RING = max(4, -(-(2 * INFINITY_CACHE_BYTES) // (B * R * V * cfg.elem_bytes)))
+    total = warmup + 4 * steps
     t_setup = time.perf_counter()
     gt_h = synth.token_streams(cfg, total)
     gt = torch.as_tensor(gt_h, device=dev)
@@ -271,6 +252,8 @@ def main():
 
     # Resident inputs: noise ring, uniforms for every step, automata.
     ring = [synth.noise(cfg, s, dev) for s in range(RING)]
+    if dt == ssl.DTYPE_BF16:
+        ring = [x.to(torch.bfloat16) for x in ring]
     u_all = torch.as_tensor(
         np.stack([synth.uniforms(cfg, s) for s in range(total)]), device=dev)
     temp = torch.full((B,), cfg.T, dtype=torch.float32, device=dev)
@@ -278,7 +261,7 @@ def main():
     st.extend(gt[:, :H].contiguous(),
               torch.full((B,), H, dtype=torch.int32, device=dev))
     booster = harness.Booster(gt, np.full(B, H, np.int32), R, V, RING,
-                              cfg.boost, ssl.DTYPE_F32)
+                              cfg.boost, dt)
     ws = ssl.verify_workspace(B, K, V, dev)
     drafts = [torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2)]
     mlen = torch.empty(B, dtype=torch.int32, device=dev)
@@ -310,14 +293,14 @@ def main():
 
     def boost(s):
         slot = s % RING
-        rc = H_.hs_boost_step(ring_p[slot], 0, B, R, V, gt_p, gt_ld, nc_p[s % 2],
+        rc = H_.hs_boost_step(ring_p[slot], dt, B, R, V, gt_p, gt_ld, nc_p[s % 2],
                               nc_p[(s + 1) % 2], nem0 + (s - 1) * rowB if s else None,
                               sp_p[slot], sv_p[slot], None, float(cfg.boost), stream)
         if rc:
             raise RuntimeError("hs_boost_step failed")
 
     def fused(s):
-        rc = L.spec_step(ring_p[s % RING], 0, B, K, V, draft_p[s % 2], dl0 + s * rowB,
+        rc = L.spec_step(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
                          temp_p, u0 + s * rowU, st_p, max_len, out_p, nem0 + s * rowB,
                          pd_p, status_p, draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB,
                          mlen_p, ws_p, ws_n, stream)
@@ -326,7 +309,7 @@ def main():
 
     def separate(s):
         # The same step as three calls: verify, extend + next draft.
-        rc = L.spec_verify(ring_p[s % RING], 0, B, K, V, draft_p[s % 2], dl0 + s * rowB,
+        rc = L.spec_verify(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
                            None, temp_p, u0 + s * rowU, out_p, nem0 + s * rowB, pd_p,
                            status_p, ws_p, ws_n, stream)
         rc |= L.sam_extend_draft(st_p, B, max_len, out_p, R, nem0 + s * rowB, K,
@@ -349,11 +332,11 @@ def main():
         rc = 0
         for r in range(STREAM_BATCH):
             slot = (s + 1 + r) % RING
-            rc |= L.spec_stream(ring_p[slot], 0, B, K, V, draft_p[s % 2],
+            rc |= L.spec_stream(ring_p[slot], dt, B, K, V, draft_p[s % 2],
                                 dl0 + s * rowB, temp_p, u0 + s * rowU, ws_p, ws_n,
                                 stream)
         evs[1].record()
-        rc |= L.spec_finish(ring_p[s % RING], 0, B, K, V, draft_p[s % 2],
+        rc |= L.spec_finish(ring_p[s % RING], dt, B, K, V, draft_p[s % 2],
                             dl0 + s * rowB, None, temp_p, u0 + s * rowU, out_p,
                             nem0 + s * rowB, pd_p, status_p, st_p, max_len,
                             draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
@@ -366,23 +349,23 @@ def main():
         boost(s)
         path(s)
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
     # Timed region: exactly `steps` steps, synchronised on both sides.
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     # Per-call durations from HIP events recorded on the launch stream (a
     # second pass over the next `steps` steps; events add small gaps, so this
     # pass is not the one `value` comes from).
-    first_ev = args.warmup + args.steps
+    first_ev = warmup + steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
+           for _ in range(steps)]
+    for i in range(steps):
         timed_step(first_ev + i, evs[i])
     torch.cuda.synchronize()
     dur = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in evs])
@@ -391,21 +374,21 @@ def main():
 
     # The same steps issued as separate library calls (verify, then extend +
     # draft), for comparison.
-    first_sep = first_ev + args.steps
+    first_sep = first_ev + steps
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(first_sep + i, path=separate)
     torch.cuda.synchronize()
-    separate_steps_s = args.steps / (time.perf_counter() - t1)
+    separate_steps_s = steps / (time.perf_counter() - t1)
 
     # Per-step library time (harness excluded): events around each spec_step
     # call of a fourth pass. The event pair adds its own dispatch gap to each
     # sample, so these are upper bounds.
-    first_ps = first_sep + args.steps
+    first_ps = first_sep + steps
     evp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
+           for _ in range(steps)]
+    for i in range(steps):
         boost(first_ps + i)
         evp[i][0].record()
         fused(first_ps + i)
@@ -413,23 +396,221 @@ def main():
     torch.cuda.synchronize()
     step_us = np.array([1e3 * a.elapsed_time(b) for a, b in evp])
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    dl = dl_hist[first_ev:first_ev + args.steps].cpu().numpy()
-    nem = nem_hist[args.warmup:first_ev].cpu().numpy()
+    ms_per_step = elapsed * 1e3 / steps
+    dl = dl_hist[first_ev:first_ev + steps].cpu().numpy()
+    nem = nem_hist[warmup:first_ev].cpu().numpy()
     accept_hist = np.bincount(nem.ravel() - 1, minlength=R)[:R]
-    needed_bytes = float(nem.sum(axis=1).mean()) * V * 4
+    needed_bytes = float(nem.sum(axis=1).mean()) * V * cfg.elem_bytes
     rows_per_launch = float((dl + 1).sum(axis=1).mean())
     # Rows of every stream launch this run made (warmup, timed pass, event
     # pass x STREAM_BATCH, separate-call pass), for the traffic record.
     rows_all = (dl_hist[:total].cpu().numpy() + 1).sum(axis=1).astype(np.float64)
     w = np.ones(total)
-    w[first_ev:first_ev + args.steps] = STREAM_BATCH
+    w[first_ev:first_ev + steps] = STREAM_BATCH
     stream_launch_rows_mean = float((rows_all * w).sum() / w.sum())
-    bytes_per_launch = rows_per_launch * V * 4
+    bytes_per_launch = rows_per_launch * V * cfg.elem_bytes
     achieved = bytes_per_launch / (stream_us * 1e-6) / 1e9
     if int(status.cpu().abs().sum()) != 0 or int(st.status().abs().sum()) != 0:
-        print("status words are non-zero: the run is invalid", file=sys.stderr)
-        sys.exit(1)
+        raise RuntimeError("status words are non-zero: the run is invalid")
+    return {
+        "elapsed": elapsed, "setup_s": setup_s, "ring": ring, "gt_h": gt_h,
+        "total": total, "RING": RING, "STREAM_BATCH": STREAM_BATCH,
+        "stream_us": stream_us, "finish_us": finish_us, "step_us": step_us,
+        "separate_steps_s": separate_steps_s, "rows_per_launch": rows_per_launch,
+        "stream_launch_rows_mean": stream_launch_rows_mean,
+        "bytes_per_launch": bytes_per_launch, "achieved": achieved, "nem": nem,
+        "accept_hist": accept_hist, "needed_bytes": needed_bytes,
+    }
+
+
+
+def _sam_workload_line(cfg, m, steps: int) -> dict:
+    import numpy as np
+    return {
+        "workload": cfg.name, "dtype": cfg.dtype, "B": cfg.B, "V": cfg.V,
+        "K": cfg.K, "T": cfg.T, "steps": steps,
+        "steps_per_s": steps / m["elapsed"],
+        "us_per_step": m["elapsed"] * 1e6 / steps,
+        "stream_pass_avg_us": m["stream_us"],
+        "verified_rows_per_launch": m["rows_per_launch"],
+        "stream_bytes_per_launch": m["bytes_per_launch"],
+        "stream_GBps": m["achieved"],
+        "stream_frac_of_8TBps": m["achieved"] / PEAK_HBM_GBPS,
+        "finish_pass_event_us": m["finish_us"],
+        "mean_tokens_per_step": float(m["nem"].mean()),
+        "accepted_drafts_histogram": {str(k): int(c) for k, c in
+                                      enumerate(m["accept_hist"])},
+        "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
+                                      np.percentile(m["step_us"], [10, 50, 90])],
+        "ring_slots": m["RING"],
+    }
+
+
+def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
+    """Verification with given draft probabilities q (no automaton): each
+    step is one spec_verify call (stream pass, finish pass, residual chunk
+    sums over the rejected row, residual draw), all drafts of length K, on
+    two resident slots of target logits, q and drafts (1.7 GB). The stream
+    pass is timed as in the main bench (events around back-to-back batches
+    alternating the two slots)."""
+    import numpy as np
+    import torch
+
+    import sam_drafting_lossless_amd as ssl
+    import synth
+    dev = torch.device("cuda:0")
+    B, K, V, R = cfg.B, cfg.K, cfg.V, cfg.K + 1
+    nslots = 2
+    slots = []
+    for i in range(nslots):
+        x = synth.noise(cfg, i, dev)
+        q, draft = synth.draft_model_inputs(cfg, i, x, dev)
+        slots.append((x, q, torch.as_tensor(draft, device=dev)))
+    total = warmup + 2 * steps
+    u_all = torch.as_tensor(
+        np.stack([synth.uniforms(cfg, s) for s in range(total)]), device=dev)
+    temp = torch.full((B,), cfg.T, dtype=torch.float32, device=dev)
+    dl = torch.full((B,), K, dtype=torch.int32, device=dev)
+    out = torch.empty((B, R), dtype=torch.int32, device=dev)
+    nem_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    pd = torch.empty((B, K), dtype=torch.float32, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = ssl.verify_workspace(B, K, V, dev)
+    torch.cuda.synchronize()
+    L = ssl.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    xp = [t[0].data_ptr() for t in slots]
+    qp = [t[1].data_ptr() for t in slots]
+    dp = [t[2].data_ptr() for t in slots]
+    u0, nem0, rowU, rowB = u_all.data_ptr(), nem_hist.data_ptr(), B * R * 4, B * 4
+
+    def call(s):
+        k = s % nslots
+        rc = L.spec_verify(xp[k], 0, B, K, V, dp[k], dl.data_ptr(), qp[k],
+                           temp.data_ptr(), u0 + s * rowU, out.data_ptr(),
+                           nem0 + s * rowB, pd.data_ptr(), status.data_ptr(),
+                           ws.data_ptr(), ws.numel(), stream)
+        if rc:
+            raise RuntimeError("spec_verify failed: " + L.ss_last_error_string().decode())
+
+    for s in range(warmup):
+        call(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    batch = 2 * nslots
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(steps)]
+    for i in range(steps):
+        s = warmup + steps + i
+        k = s % nslots
+        evs[i][0].record()
+        rc = 0
+        for r in range(batch):
+            kk = (s + 1 + r) % nslots
+            rc |= L.spec_stream(xp[kk], 0, B, K, V, dp[k], dl.data_ptr(),
+                                temp.data_ptr(), u0 + s * rowU, ws.data_ptr(),
+                                ws.numel(), stream)
+        evs[i][1].record()
+        rc |= L.spec_finish(xp[k], 0, B, K, V, dp[k], dl.data_ptr(), qp[k],
+                            temp.data_ptr(), u0 + s * rowU, out.data_ptr(),
+                            nem0 + s * rowB, pd.data_ptr(), status.data_ptr(), None,
+                            0, None, None, None, ws.data_ptr(), ws.numel(), stream)
+        evs[i][2].record()
+        if rc:
+            raise RuntimeError("two-pass call failed: " + L.ss_last_error_string().decode())
+    torch.cuda.synchronize()
+    if int(status.cpu().abs().sum()) != 0:
+        raise RuntimeError("status words are non-zero: the run is invalid")
+    dur = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(2)] for e in evs])
+    stream_us = 1e3 * dur[:, 0].mean() / batch
+    finish_us = 1e3 * dur[:, 1].mean()
+    nem = nem_hist[warmup:warmup + steps].cpu().numpy()
+    stream_bytes = B * R * V * 4
+    rejected = float((nem <= K).sum(axis=1).mean())
+    return {
+        "workload": cfg.name, "dtype": cfg.dtype, "B": B, "V": V, "K": K, "T": cfg.T,
+        "steps": steps, "steps_per_s": steps / elapsed,
+        "us_per_step": elapsed * 1e6 / steps,
+        "stream_pass_avg_us": stream_us,
+        "verified_rows_per_launch": B * R,
+        "stream_bytes_per_launch": stream_bytes,
+        "stream_GBps": stream_bytes / (stream_us * 1e-6) / 1e9,
+        "stream_frac_of_8TBps": stream_bytes / (stream_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "finish_pass_event_us": finish_us,
+        "finish_pass_contents": "finish kernel, residual chunk sums, residual draw",
+        "rejected_sequences_per_step": rejected,
+        "residual_bytes_per_step": rejected * V * 8,
+        "mean_tokens_per_step": float(nem.mean()),
+        "accepted_drafts_histogram": {str(k): int(c) for k, c in
+                                      enumerate(np.bincount(nem.ravel() - 1,
+                                                            minlength=R)[:R])},
+        "slots": nslots,
+    }
+
+
+def workloads_report(steps: int, warmup: int):
+    """One JSON line per workload: c2 (greedy), c4 (bf16 logits, long
+    histories) through the automaton step, c5 through given q."""
+    import synth
+    for c in (2, 4):
+        cfg = synth.config(c)
+        print(json.dumps(_sam_workload_line(cfg, measure_sam_workload(cfg, steps,
+                                                                       warmup),
+                                            steps)), flush=True)
+    print(json.dumps(measure_draft_model_workload(synth.config(5), steps, warmup)),
+          flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--sam-stats", action="store_true",
+                    help="report automaton work per token instead")
+    ap.add_argument("--workloads", action="store_true",
+                    help="measure the c2, c4 and c5 workloads instead")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="run a copy kernel of this many bytes instead")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (the step shards by sequence with no exchange; see "
+              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.sam_stats:
+        sam_stats_report(args.steps)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sam_drafting_lossless_amd import harness
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    if args.workloads:
+        workloads_report(args.steps, args.warmup)
+        return
+    cfg = synth.config(3)
+    B, K, V = cfg.B, cfg.K, cfg.V
+    m = measure_sam_workload(cfg, args.steps, args.warmup)
+    elapsed, ring, total, RING = m["elapsed"], m["ring"], m["total"], m["RING"]
+    ms_per_step = elapsed * 1e3 / args.steps
+    rows_per_launch, achieved = m["rows_per_launch"], m["achieved"]
+    nem, step_us, H = m["nem"], m["step_us"], cfg.hist_len
+    gt_h = m["gt_h"]
 
     probe = None if args.no_probe else hbm_read_probe(torch, harness)
     cpu = cpu_detail = None
@@ -467,20 +648,20 @@ def main():
         "cpu_baseline_detail": cpu_detail,
         "path": "spec_step (stream pass, then finish pass: decisions, draws, "
                 "SAM extend, next draft)",
-        "stream_pass_avg_us": stream_us,
-        "finish_pass_event_us": finish_us,
-        "stream_launches_per_event_pair": STREAM_BATCH,
-        "separate_calls_steps_per_s": separate_steps_s,
+        "stream_pass_avg_us": m["stream_us"],
+        "finish_pass_event_us": m["finish_us"],
+        "stream_launches_per_event_pair": m["STREAM_BATCH"],
+        "separate_calls_steps_per_s": m["separate_steps_s"],
         "verified_rows_per_launch": rows_per_launch,
-        "stream_launch_rows_mean": stream_launch_rows_mean,
-        "verify_bytes_per_launch": bytes_per_launch,
+        "stream_launch_rows_mean": m["stream_launch_rows_mean"],
+        "verify_bytes_per_launch": m["bytes_per_launch"],
         "mean_tokens_per_step": float(nem.mean()),
-        "accepted_drafts_histogram": {str(k): int(c) for k, c in enumerate(accept_hist)},
-        "needed_rows_bytes_per_step": needed_bytes,
+        "accepted_drafts_histogram": {str(k): int(c) for k, c in enumerate(m["accept_hist"])},
+        "needed_rows_bytes_per_step": m["needed_bytes"],
         "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
                                       np.percentile(step_us, [10, 50, 90])],
         "hbm_read_probe_GBps": probe,
-        "setup_s": setup_s,
+        "setup_s": m["setup_s"],
     }
     print(json.dumps(res), flush=True)
 
