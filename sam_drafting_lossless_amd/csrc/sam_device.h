@@ -242,10 +242,17 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
     } else {
       const int clone = h.nstates++;
       tally(SS_STAT_CLONES, 1);
-      // Copy q's transitions into the clone.
+      // Copy q's transitions into the clone. The next row of q's chain is
+      // requested together with each probe (a probe ends at an empty row,
+      // never at a row of the chain, so the read is not overtaken by the
+      // store that follows).
       int first = -1, e = rq.w, g2 = 0;
+      i32x4 se = i32x4{-1, -1, -1, -1};
+      if (e != -1) se = S.slots[e];
       while (e != -1) {
-        const i32x4 se = S.slots[e];
+        const int en = se.w;
+        i32x4 sn = i32x4{-1, -1, -1, -1};
+        if (en != -1) sn = S.slots[en];
         const SamProbe pc = sam_probe(S.slots, bmask, clone, se.y);
         tally(SS_STAT_PROBES, 1);
         tally(SS_STAT_BUCKETS, pc.buckets);
@@ -254,7 +261,8 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
         S.slots[pc.slot] = i32x4{clone, se.y, se.z, first};
         first = pc.slot;
         h.nedges++;
-        e = se.w;
+        e = en;
+        se = sn;
         if (++g2 > h.nedges) return false;
       }
       const i32x4 rc = i32x4{rp.x + 1, rq.y, rq.z, first};
