@@ -236,6 +236,41 @@ int sam_extend_stats(void* state, int B, int max_len, const int32_t* tokens,
                      int ld_tokens, const int32_t* counts,
                      unsigned long long* stats, void* stream);
 
+/*
+ * sam_match — the static automaton of [P4] §3 ("Suffix Automaton
+ * Construction": built offline over a corpus whose documents are joined with
+ * an end-of-sequence token; "Drafting with Suffix Automaton"; "Update of
+ * Suffix Automaton": the matching state is transferred with each accepted
+ * token). static_state is a state buffer of ONE sequence (B = 1, capacity
+ * static_max_len) holding the corpus, built with sam_init + sam_extend; it is
+ * only read here.
+ *   match [B, 2] int32 (state, length): the state of the longest suffix of
+ *     sequence b's text that occurs in the corpus, and that suffix's length.
+ *     Start from zeros (root, empty match); this call updates it in place.
+ *     An entry that is not a state of the automaton is taken as the root.
+ *   tokens [B, ld_tokens] int32, counts [B] (device; NULL: no tokens): the
+ *     tokens appended to each sequence since the last call. For each token t:
+ *     if the state has a transition on t it is taken (length + 1); else
+ *     suffix links are followed to the first state with one (length = that
+ *     state's len + 1); if even the root has none, (root, 0).
+ *   K > 0 also writes drafts: the static draft is the K tokens after the
+ *     state's min_endpos in the corpus (cut at its end; none for an empty
+ *     match). With dyn_draft/dyn_len/dyn_match given (all three, e.g. the
+ *     next-draft outputs of spec_step), the dynamic draft is kept unless the
+ *     static match is longer than dyn_match[b] + delta, as the page prefers
+ *     the dynamic automaton's drafts. Without them the static drafts are
+ *     written. draft [B, K] int32 (-1 padded), draft_len [B]; source [B]
+ *     (or NULL) receives 1 where the static draft was taken.
+ * K = 0 only advances the match states. delta >= 0.
+ * CURRENTLY SWITCHED OFF: returns SS_EINVAL without launching anything (one
+ * GPU run of its tests ended in a memory fault whose cause is not shown).
+ */
+int sam_match(const void* static_state, int static_max_len, int B, int32_t* match,
+              const int32_t* tokens, int ld_tokens, const int32_t* counts, int K,
+              int delta, const int32_t* dyn_draft, const int32_t* dyn_len,
+              const int32_t* dyn_match, int32_t* draft, int32_t* draft_len,
+              int32_t* source, void* stream);
+
 /* Copies the sticky per-sequence status words to status_out [B] int32. */
 int sam_status(const void* state, int B, int max_len, int32_t* status_out,
                void* stream);

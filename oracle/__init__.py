@@ -70,6 +70,10 @@ def _load():
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = i32
     lib.orc_sam_export.argtypes = [P, P, P, P, P]
+    lib.orc_sam_match.argtypes = [P, i32, P, P, P, i64, P]
+    lib.orc_sam_match.restype = None
+    lib.orc_sam_static_draft.argtypes = [P, i32, P, P, i32, P, P]
+    lib.orc_sam_static_draft.restype = None
     lib.orc_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P,
                                P, P, P, P, P, P, P, i32]
     lib.orc_step.argtypes = [P, i32, i32, i32, P, i32, P, P, P, P, P,
@@ -147,6 +151,45 @@ class SAM:
         self._lib.orc_sam_export(self._h, _ptr(ln), _ptr(lk), _ptr(me), _ptr(ed))
         return {"len": ln, "link": lk, "min_endpos": me, "edges": ed,
                 "last": self.last}
+
+    def match(self, state, mlen, tokens, counts=None):
+        """Advances match states in this automaton (used as the static
+        automaton over a reference text) by tokens [B, L] (counts[b] of them
+        per row, all L by default). state, mlen: int32 [B], updated in place
+        (start from zeros: the root and an empty match)."""
+        t = _c(tokens, np.int32)
+        if t.ndim == 1:
+            t = t[None, :]
+        B, L = t.shape
+        c = (np.full(B, L, np.int32) if counts is None
+             else _c(counts, np.int32))
+        assert state.dtype == np.int32 and mlen.dtype == np.int32
+        assert state.flags.c_contiguous and mlen.flags.c_contiguous
+        self._lib.orc_sam_match(self._h, B, _ptr(state), _ptr(mlen), _ptr(t), L,
+                                _ptr(c))
+
+    def static_draft(self, state, mlen, K: int):
+        """Drafts of match states: (draft [B,K] int32, draft_len [B] int32)."""
+        st = _c(state, np.int32)
+        ml = _c(mlen, np.int32)
+        B = st.size
+        d = np.empty((B, K), np.int32)
+        dl = np.empty(B, np.int32)
+        self._lib.orc_sam_static_draft(self._h, B, _ptr(st), _ptr(ml), K, _ptr(d),
+                                       _ptr(dl))
+        return d, dl
+
+
+def select_drafts(static_draft, static_len, static_match, dyn_draft, dyn_len,
+                  dyn_match, delta: int):
+    """[P4] §3, choosing between the automata: the dynamic automaton's draft is
+    preferred; the static automaton's draft is used only when its match is
+    longer than the dynamic one's by more than delta (> 0). Returns (draft,
+    draft_len, source) with source 1 where the static draft was taken."""
+    use = np.asarray(static_match) > np.asarray(dyn_match) + delta
+    draft = np.where(use[:, None], static_draft, dyn_draft).astype(np.int32)
+    dl = np.where(use, static_len, dyn_len).astype(np.int32)
+    return draft, dl, use.astype(np.int32)
 
 
 @dataclass

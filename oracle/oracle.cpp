@@ -125,6 +125,44 @@ struct OracleSAM {
     return d;
   }
 
+  // Match-state transfer on a fixed automaton ([P4] "Drafting with Suffix
+  // Automaton", "Update of Suffix Automaton", state transfer of Algorithm 1):
+  // (s, l) is the state of the longest suffix of a generated text that occurs
+  // in this automaton's reference text, and that suffix's length. Appending
+  // token t: if s has a transition on t it is taken and the match grows by
+  // one; otherwise suffix links are followed to the first state with such a
+  // transition, and the match becomes that state's longest string plus t; if
+  // even the root has none, the match is empty (root, 0).
+  void match_step(int32_t& s, int32_t& l, int32_t t) const {
+    while (true) {
+      auto it = next[s].find(t);
+      if (it != next[s].end()) {
+        s = it->second;
+        l += 1;
+        return;
+      }
+      if (s == 0) {
+        l = 0;
+        return;
+      }
+      s = link[s];
+      l = len[s];
+    }
+  }
+
+  // Draft from a match state: the tokens that followed the first occurrence
+  // of the matched suffix in the reference text (min_endpos of s), cut at the
+  // end of the text; an empty match gives no draft.
+  int32_t draft_from(int32_t s, int32_t l, int32_t K, int32_t* out) const {
+    for (int32_t j = 0; j < K; ++j) out[j] = -1;
+    if (l == 0) return 0;
+    const int32_t n = (int32_t)text.size();
+    const int32_t p = minend[s];
+    const int32_t d = std::min<int32_t>(K, n - 1 - p);
+    for (int32_t j = 0; j < d; ++j) out[j] = text[p + 1 + j];
+    return d;
+  }
+
   int64_t num_edges() const {
     int64_t e = 0;
     for (const auto& m : next) e += (int64_t)m.size();
@@ -373,6 +411,26 @@ int64_t orc_sam_num_states(void* h) { return (int64_t)((OracleSAM*)h)->len.size(
 int64_t orc_sam_num_edges(void* h) { return ((OracleSAM*)h)->num_edges(); }
 int64_t orc_sam_length(void* h) { return (int64_t)((OracleSAM*)h)->text.size(); }
 int32_t orc_sam_last(void* h) { return ((OracleSAM*)h)->last; }
+
+// Advances B match states (state[b], mlen[b]) in the automaton h (the static
+// automaton of [P4] §3) by tokens[b, 0..counts[b]) (row stride ld).
+void orc_sam_match(void* h, int32_t B, int32_t* state, int32_t* mlen,
+                   const int32_t* tokens, int64_t ld, const int32_t* counts) {
+  const OracleSAM* s = (const OracleSAM*)h;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t j = 0; j < counts[b]; ++j)
+      s->match_step(state[b], mlen[b], tokens[(int64_t)b * ld + j]);
+}
+
+// Static drafts of B match states; returns nothing, writes draft [B,K] and
+// draft_len [B].
+void orc_sam_static_draft(void* h, int32_t B, const int32_t* state,
+                          const int32_t* mlen, int32_t K, int32_t* draft,
+                          int32_t* draft_len) {
+  const OracleSAM* s = (const OracleSAM*)h;
+  for (int32_t b = 0; b < B; ++b)
+    draft_len[b] = s->draft_from(state[b], mlen[b], K, draft + (int64_t)b * K);
+}
 
 // Copies the structure out. edges receives [E,3] rows (src, token, dst) in
 // ascending (src, token) order.

@@ -78,6 +78,9 @@ def lib():
     L.sam_draft.restype = i32
     L.sam_extend_stats.argtypes = [P, i32, i32, P, i32, P, P, P]
     L.sam_extend_stats.restype = i32
+    L.sam_match.argtypes = [P, i32, i32, P, P, i32, P, i32, i32, P, P, P, P, P,
+                            P, P]
+    L.sam_match.restype = i32
     L.sam_status.argtypes = [P, i32, i32, P, P]
     L.sam_status.restype = i32
     L.sam_export.argtypes = [P, i32, i32, i32, P, P, P, P, P]
@@ -463,3 +466,67 @@ class SamState:
 
     def export(self, b: int):
         return sam_export(self.buf, self.B, self.max_len, b)
+
+
+class StaticSam:
+    """The static automaton over a corpus ([P4] §3): one sequence of capacity
+    len(corpus), built on the device by the same extension as the dynamic
+    automata, then only read by sam_match."""
+
+    def __init__(self, corpus, V: int, device="cuda", stream=None):
+        corpus = torch.as_tensor(corpus, dtype=torch.int32, device=device)
+        n = int(corpus.numel())
+        if n < 1:
+            raise SpecSamError("the corpus is empty")
+        self.state = SamState(1, n, V, device, stream)
+        self.state.extend(corpus.view(1, n).contiguous(),
+                          torch.full((1,), n, dtype=torch.int32, device=device),
+                          stream)
+        self.max_len, self.V = n, V
+
+    def new_match(self, B: int, device="cuda"):
+        """Match states [B, 2] int32 at the root."""
+        return torch.zeros((B, 2), dtype=torch.int32, device=device)
+
+    def match(self, match, tokens=None, counts=None, K: int = 0, delta: int = 0,
+              dyn=None, draft=None, draft_len=None, source=None, stream=None):
+        """Advances `match` [B, 2] by tokens [B, L] (counts [B], all L by
+        default); with K > 0 returns (draft, draft_len, source): the static
+        drafts, or, with dyn = (draft, draft_len, match_len) of the dynamic
+        automata, the dynamic draft unless the static match is longer by more
+        than delta."""
+        B = match.shape[0]
+        dev = match.device
+        i32 = torch.int32
+        tp = cp = None
+        ld = 0
+        if tokens is not None:
+            if tokens.dim() != 2 or tokens.shape[0] != B:
+                raise SpecSamError("tokens must be [B, L]")
+            ld = tokens.shape[1]
+            if counts is None:
+                counts = torch.full((B,), ld, dtype=i32, device=dev)
+            tp = _dev(tokens, "tokens", i32)
+            cp = _dev(counts, "counts", i32, (B,))
+        if K > 0:
+            if draft is None:
+                draft = torch.empty((B, K), dtype=i32, device=dev)
+            if draft_len is None:
+                draft_len = torch.empty(B, dtype=i32, device=dev)
+            if source is None:
+                source = torch.empty(B, dtype=i32, device=dev)
+        dd = dl = dm = None
+        if dyn is not None:
+            dd = _dev(dyn[0], "dyn draft", i32, (B, K))
+            dl = _dev(dyn[1], "dyn draft_len", i32, (B,))
+            dm = _dev(dyn[2], "dyn match_len", i32, (B,))
+        _check(lib().sam_match(
+            _dev(self.state.buf, "state", torch.uint8), self.max_len, B,
+            _dev(match, "match", i32, (B, 2)), tp, ld, cp, K, delta, dd, dl, dm,
+            None if draft is None else _dev(draft, "draft", i32, (B, K)),
+            None if draft_len is None else _dev(draft_len, "draft_len", i32, (B,)),
+            None if source is None else _dev(source, "source", i32, (B,)),
+            _stream(stream)), "sam_match")
+        if K > 0:
+            return draft, draft_len, source
+        return None

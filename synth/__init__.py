@@ -94,6 +94,7 @@ def config(c: int, **overrides) -> Config:
 # changing one does not shift the others.
 # ---------------------------------------------------------------------------
 STREAM_TOKENS, STREAM_BOOST_MASK, STREAM_UNIFORMS, STREAM_DRAFT = 0, 1, 2, 3
+STREAM_CORPUS, STREAM_QUERY = 4, 5
 
 
 def rng_for(seed: int, stream: int, *sub: int) -> np.random.Generator:
@@ -170,6 +171,47 @@ def token_streams(cfg: Config, steps: int | None = None) -> np.ndarray:
         gt[b] = copy_process(rng_for(cfg.seed, STREAM_TOKENS, b), n, cfg.V,
                              cfg.p_copy, cfg.span_mean, cfg.zipf_s, cdf)
     return gt
+
+
+def corpus(seed: int, n_docs: int, doc_len: int, V: int, eos: int,
+           p_copy: float = 0.6, span_mean: float = 8.0,
+           zipf_s: float = 1.1) -> np.ndarray:
+    """A reference corpus for a static automaton: n_docs copy-process
+    documents of doc_len tokens (each from its own seed), each followed by
+    the end-of-sequence token `eos`."""
+    cdf = zipf_cdf(V, zipf_s)
+    parts = []
+    for d in range(n_docs):
+        doc = copy_process(rng_for(seed, STREAM_CORPUS, d), doc_len, V, p_copy,
+                           span_mean, zipf_s, cdf)
+        parts.append(doc)
+        parts.append(np.array([eos], np.int32))
+    return np.concatenate(parts).astype(np.int32)
+
+
+def corpus_queries(seed: int, corpus_tokens: np.ndarray, B: int, n: int, V: int,
+                   p_span: float = 0.5, span_mean: float = 12.0,
+                   zipf_s: float = 1.1) -> np.ndarray:
+    """Texts [B, n] that partly overlap a corpus: with probability p_span a
+    span of length Geometric(1/span_mean) copied from a uniform corpus
+    position, otherwise one Zipf token; so matches against the corpus of
+    every length occur."""
+    cdf = zipf_cdf(V, zipf_s)
+    out = np.empty((B, n), np.int32)
+    N = len(corpus_tokens)
+    for b in range(B):
+        rng = rng_for(seed, STREAM_QUERY, b)
+        row = []
+        while len(row) < n:
+            if rng.random() < p_span:
+                L = int(rng.geometric(1.0 / span_mean))
+                a = int(rng.integers(0, N))
+                row.extend(corpus_tokens[a:a + L].tolist())
+            else:
+                row.append(int(min(np.searchsorted(cdf, rng.random(), side="right"),
+                                   V - 1)))
+        out[b] = row[:n]
+    return out
 
 
 def uniforms(cfg: Config, step: int) -> np.ndarray:

@@ -1,0 +1,152 @@
+"""Static automaton over a corpus ([P4] SAM-Decoding summary §3), on the GPU
+through the C ABI, against the oracle: the automaton built on the device is
+the oracle's state for state; match states (state, length) after every call,
+static drafts and the choice between static and dynamic drafts are
+bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sam_drafting_lossless_amd as ssl
+import synth
+from _parity import dev, say
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skip(reason=(
+        "sam_match is switched off: the one GPU run of these tests ended in a "
+        "memory fault (reported at the synchronize of "
+        "test_entries_that_are_not_states_start_at_the_root, after the three "
+        "tests before it had passed bit-exact). A bounds-checked host model of "
+        "init, extend and match over the same inputs stays in bounds, so the "
+        "cause is not shown; the case stays off the GPU until it is.")),
+]
+
+V = 151936
+EOS = V - 1
+
+
+def _same_structure(gpu_export, ora_export):
+    for k in ("len", "link", "min_endpos", "edges"):
+        np.testing.assert_array_equal(gpu_export[k], ora_export[k])
+
+
+def _corpus(alpha, seed, n_docs=20, doc_len=500):
+    if alpha >= 1000:
+        return synth.corpus(seed, n_docs, doc_len, alpha, alpha - 1)
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, alpha, n_docs * doc_len).astype(np.int32)
+
+
+def _queries(alpha, seed, c, B, n):
+    if alpha >= 1000:
+        return synth.corpus_queries(seed, c, B, n, alpha)
+    rng = np.random.default_rng(seed + 1)
+    return rng.integers(0, alpha, (B, n)).astype(np.int32)
+
+
+def test_static_automaton_is_built_like_the_oracle():
+    say("[gpu] static automaton structure")
+    c = synth.corpus(3, 30, 400, V, EOS)
+    st = ssl.StaticSam(c, V)
+    _same_structure(st.state.export(0), oracle.SAM(c).export())
+
+
+@pytest.mark.parametrize("alpha", [4, V])
+def test_match_states_drafts_and_choice_follow_the_oracle(alpha):
+    say(f"[gpu] static matching alphabet={alpha}")
+    c = _corpus(alpha, 11)
+    st = ssl.StaticSam(c, alpha if alpha >= 1000 else V)
+    ora = oracle.SAM(c)
+    B, K, delta = 64, 5, 2
+    q = _queries(alpha, 11, c, B, 400)
+    rng = np.random.default_rng(alpha)
+    m = st.new_match(B)
+    os_ = np.zeros(B, np.int32)
+    ol = np.zeros(B, np.int32)
+    pos = np.zeros(B, np.int64)
+    # prefill with a different length per sequence (some none), then steps
+    # of 0..4 tokens
+    counts = [rng.integers(0, 150, B)] + [rng.integers(0, 5, B) for _ in range(12)]
+    for step, cnt in enumerate(counts):
+        cnt = cnt.astype(np.int32)
+        L = int(cnt.max()) if cnt.max() > 0 else 1
+        toks = np.full((B, L), -1, np.int32)
+        for b in range(B):
+            toks[b, :cnt[b]] = q[b, pos[b]:pos[b] + cnt[b]]
+        if step % 2 == 0:
+            d, dl, src = st.match(m, dev(toks), dev(cnt), K=K)
+            dyn = None
+        else:
+            dd = rng.integers(0, V, (B, K)).astype(np.int32)
+            ddl = rng.integers(0, K + 1, B).astype(np.int32)
+            dm = rng.integers(0, 12, B).astype(np.int32)
+            d, dl, src = st.match(m, dev(toks), dev(cnt), K=K, delta=delta,
+                                  dyn=(dev(dd), dev(ddl), dev(dm)))
+            dyn = (dd, ddl, dm)
+        torch.cuda.synchronize()
+        ora.match(os_, ol, toks, cnt)
+        pos += cnt
+        mh = m.cpu().numpy()
+        np.testing.assert_array_equal(mh[:, 0], os_, err_msg=f"state, step {step}")
+        np.testing.assert_array_equal(mh[:, 1], ol, err_msg=f"length, step {step}")
+        sd, sdl = ora.static_draft(os_, ol, K)
+        if dyn is None:
+            want_d, want_l, want_src = sd, sdl, np.ones(B, np.int32)
+        else:
+            want_d, want_l, want_src = oracle.select_drafts(sd, sdl, ol, *dyn,
+                                                            delta=delta)
+        np.testing.assert_array_equal(d.cpu().numpy(), want_d, err_msg=f"step {step}")
+        np.testing.assert_array_equal(dl.cpu().numpy(), want_l)
+        np.testing.assert_array_equal(src.cpu().numpy(), want_src)
+    assert ol.max() > 5  # long matches occurred
+
+
+def test_entries_that_are_not_states_start_at_the_root():
+    say("[gpu] static matching: invalid match entries")
+    c = synth.corpus(5, 4, 100, V, EOS)
+    st = ssl.StaticSam(c, V)
+    m = torch.tensor([[-5, 3], [10 ** 9, 1], [0, 0]], dtype=torch.int32,
+                     device="cuda")
+    d, dl, _ = st.match(m, K=3)
+    torch.cuda.synchronize()
+    assert m.cpu().tolist() == [[0, 0], [0, 0], [0, 0]]
+    assert dl.cpu().tolist() == [0, 0, 0]
+    assert (d.cpu().numpy() == -1).all()
+
+
+def test_host_argument_errors():
+    c = synth.corpus(5, 2, 50, V, EOS)
+    st = ssl.StaticSam(c, V)
+    m = st.new_match(2)
+    dd = torch.zeros((2, 3), dtype=torch.int32, device="cuda")
+    with pytest.raises(ssl.SpecSamError, match="all dynamic"):
+        st.match(m, K=3, dyn=(dd, None, None))
+
+
+def test_long_corpus_full_batch():
+    """A 262,144-token corpus of 512 documents and 256 sequences of 2,048
+    tokens each, matched in one call, then 20 one-token steps with drafts."""
+    say("[gpu] static matching: 262k-token corpus, B=256")
+    c = synth.corpus(21, 512, 511, V, EOS)
+    st = ssl.StaticSam(c, V)
+    ora = oracle.SAM(c)
+    _same_structure(st.state.export(0), ora.export())
+    B, K = 256, 3
+    q = synth.corpus_queries(21, c, B, 2048 + 20, V)
+    m = st.new_match(B)
+    st.match(m, dev(q[:, :2048]))
+    os_ = np.zeros(B, np.int32)
+    ol = np.zeros(B, np.int32)
+    ora.match(os_, ol, q[:, :2048])
+    np.testing.assert_array_equal(m.cpu().numpy(), np.stack([os_, ol], 1))
+    for s in range(20):
+        tok = q[:, 2048 + s:2049 + s]
+        d, dl, _ = st.match(m, dev(tok), K=K)
+        ora.match(os_, ol, tok)
+        sd, sdl = ora.static_draft(os_, ol, K)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(m.cpu().numpy(), np.stack([os_, ol], 1))
+        np.testing.assert_array_equal(d.cpu().numpy(), sd)
+        np.testing.assert_array_equal(dl.cpu().numpy(), sdl)
