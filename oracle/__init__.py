@@ -70,6 +70,8 @@ def _load():
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = i32
     lib.orc_sam_export.argtypes = [P, P, P, P, P]
+    lib.orc_logprobs.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+    lib.orc_logprobs.restype = None
     lib.orc_sam_match.argtypes = [P, i32, P, P, P, i64, P]
     lib.orc_sam_match.restype = None
     lib.orc_sam_static_draft.argtypes = [P, i32, P, P, i32, P, P]
@@ -80,6 +82,18 @@ def _load():
                              P, P, P, P, P, P, P, i32]
     _lib = lib
     return lib
+
+
+def _logits_arg(logits):
+    """(contiguous array, dtype code): float32 is 0, bfloat16 bit patterns
+    held as uint16 are 1."""
+    if logits.dtype == np.float32:
+        dtype = 0
+    elif logits.dtype == np.uint16:
+        dtype = 1
+    else:
+        raise TypeError("logits must be float32 or uint16 (bfloat16 bits)")
+    return np.ascontiguousarray(logits), dtype
 
 
 def _ptr(a: np.ndarray | None):
@@ -180,6 +194,23 @@ class SAM:
         return d, dl
 
 
+def logprobs(logits, out_tokens, num_emitted, temperature):
+    """[B, K+1] float64: log softmax(l_j / T)[out[b, j]] for j < num_emitted
+    (T = 1 for greedy sequences), NaN elsewhere."""
+    x, dt = _logits_arg(logits)
+    B, R, V = x.shape
+    out_tokens = np.asarray(out_tokens).reshape(B, R)
+    num_emitted = np.asarray(num_emitted).reshape(B)
+    temperature = np.asarray(temperature).reshape(B)
+    out = _c(out_tokens, np.int32)
+    nem = _c(num_emitted, np.int32)
+    T = _c(temperature, np.float32)
+    lp = np.empty((B, R), np.float64)
+    _load().orc_logprobs(_ptr(x), dt, B, R - 1, V, _ptr(out), _ptr(nem), _ptr(T),
+                         _ptr(lp))
+    return lp
+
+
 def select_drafts(static_draft, static_len, static_match, dyn_draft, dyn_len,
                   dyn_match, delta: int):
     """[P4] §3, choosing between the automata: the dynamic automaton's draft is
@@ -212,13 +243,7 @@ def verify(logits, draft, draft_len, temperature, uniforms=None, q=None,
     uniforms: [B,K+1] float32 or None; q: [B,K,V] float32 or None (one-hot).
     """
     lib = _load()
-    if logits.dtype == np.float32:
-        dtype = 0
-    elif logits.dtype == np.uint16:
-        dtype = 1
-    else:
-        raise TypeError("logits must be float32 or uint16 (bfloat16 bits)")
-    logits = np.ascontiguousarray(logits)
+    logits, dtype = _logits_arg(logits)
     B, R, V = logits.shape
     K = R - 1
     draft = _c(draft, np.int32).reshape(B, K)

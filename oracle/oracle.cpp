@@ -453,6 +453,34 @@ void orc_sam_export(void* h, int32_t* len, int32_t* link, int32_t* minend,
 
 // Verification of a batch. Sequences are independent; nthreads > 1 splits them
 // over std::threads (the arithmetic of each sequence is unchanged).
+// Log-probabilities of emitted tokens (for RL rollouts; [P1] §2.1 compares
+// draft-token logprobs between decoding paths): for j < num_emitted[b],
+// logprob[b, j] = log softmax(l_{b,j} / T)[out[b, j]] with T the sequence's
+// temperature, or T = 1 for a greedy sequence (T = 0): the model's own
+// log-probability. Entries past num_emitted are NaN.
+void orc_logprobs(const void* logits, int32_t dtype, int32_t B, int32_t K,
+                  int32_t V, const int32_t* out_tokens, const int32_t* num_emitted,
+                  const float* temperature, double* logprob) {
+  const int32_t R = K + 1;
+  std::vector<double> row;
+  for (int32_t b = 0; b < B; ++b) {
+    const double T = temperature[b] > 0.0f ? (double)temperature[b] : 1.0;
+    for (int32_t j = 0; j < R; ++j) {
+      double& o = logprob[(int64_t)b * R + j];
+      o = std::numeric_limits<double>::quiet_NaN();
+      if (j >= num_emitted[b]) continue;
+      const int32_t x = out_tokens[(int64_t)b * R + j];
+      if (x < 0 || x >= V) continue;
+      load_row(logits, dtype, (int64_t)b * R + j, V, row);
+      double m = -std::numeric_limits<double>::infinity();
+      for (int32_t i = 0; i < V; ++i) m = std::max(m, row[i] / T);
+      double z = 0.0;
+      for (int32_t i = 0; i < V; ++i) z += std::exp(row[i] / T - m);
+      o = row[x] / T - m - std::log(z);
+    }
+  }
+}
+
 void orc_verify(const void* logits, int32_t dtype, int32_t B, int32_t K,
                 int32_t V, const int32_t* draft, const int32_t* draft_len,
                 const float* q, const float* temperature, const float* uniforms,
