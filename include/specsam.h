@@ -115,6 +115,11 @@ size_t ss_verify_workspace_bytes(int B, int K, int V);
  *   num_emitted [B] int32 = accepted drafts + 1.
  *   p_draft     [B, K] float or NULL: p_j(x_j) for j < num_emitted and j < d
  *               at T > 0; -1 elsewhere.
+ *   logprobs    [B, K+1] float or NULL: for j < num_emitted, the natural log
+ *               of softmax(l_j / T)[out_tokens[b, j]] — the target's own
+ *               log-probability of each emitted token (accepted, corrected or
+ *               bonus), with T = 1 for greedy sequences ([P1] §2.1 compares
+ *               these between decoding paths); NaN after num_emitted.
  *   status      [B] int32, OR-ed with SS_ST_* bits.
  *   workspace   ws_bytes >= ss_verify_workspace_bytes(B, K, V), 256-byte
  *               aligned.
@@ -127,8 +132,8 @@ int spec_verify(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len, const float* q,
                 const float* temperature, const float* uniforms,
                 int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
-                int32_t* status, void* workspace, size_t ws_bytes,
-                void* stream);
+                float* logprobs, int32_t* status, void* workspace,
+                size_t ws_bytes, void* stream);
 
 /*
  * spec_step — one whole speculative step in one pass over the logits:
@@ -149,7 +154,8 @@ int spec_step(const void* logits, int dtype, int B, int K, int V,
               const int32_t* draft, const int32_t* draft_len,
               const float* temperature, const float* uniforms, void* sam_state,
               int max_len, int32_t* out_tokens, int32_t* num_emitted,
-              float* p_draft, int32_t* status, int32_t* next_draft,
+              float* p_draft, float* logprobs, int32_t* status,
+              int32_t* next_draft,
               int32_t* next_draft_len, int32_t* next_match_len,
               void* workspace, size_t ws_bytes, void* stream);
 
@@ -174,7 +180,7 @@ int spec_finish(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len, const float* q,
                 const float* temperature, const float* uniforms,
                 int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
-                int32_t* status, void* sam_state, int max_len,
+                float* logprobs, int32_t* status, void* sam_state, int max_len,
                 int32_t* next_draft, int32_t* next_draft_len,
                 int32_t* next_match_len, void* workspace, size_t ws_bytes,
                 void* stream);

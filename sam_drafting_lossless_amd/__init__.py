@@ -54,15 +54,15 @@ def lib():
     L.ss_verify_workspace_bytes.argtypes = [i32, i32, i32]
     L.ss_verify_workspace_bytes.restype = sz
     L.spec_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                              P, sz, P]
+                              P, P, sz, P]
     L.spec_verify.restype = i32
     L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, P,
-                            P, P, P, P, P, sz, P]
+                            P, P, P, P, P, P, sz, P]
     L.spec_step.restype = i32
     L.spec_stream.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     L.spec_stream.restype = i32
     L.spec_finish.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                              P, i32, P, P, P, P, sz, P]
+                              P, P, i32, P, P, P, P, sz, P]
     L.spec_finish.restype = i32
     L.sam_extend_draft.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P]
     L.sam_extend_draft.restype = i32
@@ -114,6 +114,10 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
     return t.data_ptr()
 
 
+def _opt_f32(t, name, shape):
+    return None if t is None else _dev(t, name, torch.float32, shape)
+
+
 # ------------------------------------------------------------- verification --
 def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
     return int(lib().ss_verify_workspace_bytes(B, K, V))
@@ -130,10 +134,11 @@ def verify_workspace(B: int, K: int, V: int, device=None):
 
 def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
                 workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
-                status=None, stream=None):
+                status=None, logprobs=None, stream=None):
     """Verify one batch (see include/specsam.h). Returns
     (out_tokens [B,K+1] int32, num_emitted [B] int32, p_draft [B,K] float32,
-    status [B] int32)."""
+    status [B] int32). `logprobs`, a [B,K+1] float32 tensor, receives the
+    log-probabilities of the emitted tokens when given."""
     if logits.dim() != 3:
         raise SpecSamError("logits must be [B, K+1, V]")
     B, R, V = logits.shape
@@ -167,6 +172,7 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
         _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _opt_f32(logprobs, "logprobs", (B, R)),
         _dev(status, "status", i32, (B,)),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream))
@@ -177,11 +183,11 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
 def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
               workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
               status=None, next_draft=None, next_draft_len=None,
-              next_match_len=None, stream=None):
+              next_match_len=None, logprobs=None, stream=None):
     """One fused step (see include/specsam.h): verify the drafts, extend each
     automaton of `state` (a SamState) with the emitted tokens, and draft for
     the next step. Returns (out_tokens, num_emitted, p_draft, status,
-    next_draft, next_draft_len, next_match_len)."""
+    next_draft, next_draft_len, next_match_len); `logprobs` as spec_verify."""
     if logits.dim() != 3:
         raise SpecSamError("logits must be [B, K+1, V]")
     B, R, V = logits.shape
@@ -220,6 +226,7 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
         _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _opt_f32(logprobs, "logprobs", (B, R)),
         _dev(status, "status", i32, (B,)),
         _dev(next_draft, "next_draft", i32, (B, K)),
         _dev(next_draft_len, "next_draft_len", i32, (B,)),
@@ -261,11 +268,11 @@ def spec_stream(logits, draft, draft_len, temperature, uniforms, workspace, *,
 def spec_finish(logits, draft, draft_len, temperature, uniforms, workspace,
                 q=None, state=None, *, out_tokens=None, num_emitted=None,
                 p_draft=None, status=None, next_draft=None, next_draft_len=None,
-                next_match_len=None, stream=None):
+                next_match_len=None, logprobs=None, stream=None):
     """Second pass (see include/specsam.h), after spec_stream with the same
     arguments and workspace. Returns (out_tokens, num_emitted, p_draft,
     status), followed by (next_draft, next_draft_len, next_match_len) when
-    `state` (a SamState) is given."""
+    `state` (a SamState) is given; `logprobs` as spec_verify."""
     B, K, V, dt = _shape(logits)
     R = K + 1
     dev = logits.device
@@ -299,6 +306,7 @@ def spec_finish(logits, draft, draft_len, temperature, uniforms, workspace,
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
         _dev(p_draft, "p_draft", torch.float32, (B, K)),
+        _opt_f32(logprobs, "logprobs", (B, R)),
         _dev(status, "status", i32, (B,)),
         None if state is None else _dev(state.buf, "state", torch.uint8),
         0 if state is None else state.max_len,

@@ -50,10 +50,13 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
   }
   f32x4 part;
   if (greedy) {
-    // Position within the lane's elements (it*kVec + k) is a compile-time
-    // constant per element; the row index is formed once at the end.
-    float bv = kNegInf;
-    int bp = -1, nan = 0;
+    // Argmax with the lowest index on ties; position within the lane's
+    // elements (it*kVec + k) is a compile-time constant per element, the row
+    // index is formed once at the end. Alongside, the online sum of
+    // exp(l - max) at temperature 1 (for the log-probabilities of emitted
+    // tokens); a NaN anywhere in the chunk makes the sum NaN.
+    float bv = kNegInf, s = 0.0f;
+    int bp = -1;
 #pragma unroll
     for (int it = 0; it < kLoads; ++it)
 #pragma unroll
@@ -63,22 +66,38 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
           bv = v;
           bp = it * kVec<DT> + k;
         }
-        nan |= (v != v);
       }
+    float m = kNegInf;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      float vm = kNegInf;
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
+      const float mn = fmaxf(m, vm);
+      const float base = (mn == kNegInf) ? 0.0f : mn;
+      float t = s * fast_exp2((m - base) * kLog2e);
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k)
+        t += fast_exp2((elem<DT>(raw[it], k) - base) * kLog2e);
+      s = t;
+      m = mn;
+    }
     mid();
     int bi = bp < 0 ? INT_MAX
                     : elem_index<DT, VP>(cstart, tid, bp / kVec<DT>, bp % kVec<DT>);
     wave_argmax(bv, bi);
-    nan = wave_or(nan);
-    if (l == 0) red[w] = f32x4{bv, nan ? 1.0f : 0.0f, 0.0f, __int_as_float(bi)};
+    wave_lse(m, s, kLog2e);
+    if (l == 0) red[w] = f32x4{bv, s, m, __int_as_float(bi)};
     __syncthreads();
-    float pv = red[0].x, pn = red[0].y;
+    float pv = red[0].x, pm = red[0].z, ps = red[0].y;
     int pi = __float_as_int(red[0].w);
     for (int i = 1; i < kWaves; ++i) {
       argmax_merge(pv, pi, red[i].x, __float_as_int(red[i].w));
-      pn = fmaxf(pn, red[i].y);
+      lse_merge(pm, ps, red[i].z, red[i].y, kLog2e);
     }
-    part = f32x4{pv, pn, 0.0f, __int_as_float(pi)};
+    // The sum is relative to the chunk max pm, which equals pv except when
+    // the chunk holds NaN (then the sum is NaN and the row is reported).
+    part = f32x4{pv, ps, 0.0f, __int_as_float(pi)};
   } else {
     // Online (max, sum exp2) folded one 16-byte vector at a time, in the
     // order the loads return, so only the raw vectors stay live.

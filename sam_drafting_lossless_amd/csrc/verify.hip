@@ -105,6 +105,7 @@ struct DrawShared {
   float cell[kLoads * kWaves];  // (load, wave) totals in token order
   int wlast[kWaves];
   int result;
+  float result_l;  // the drawn token's logit (NaN if the draw did not see it)
 };
 
 // Weight of element k of raw vector `it` (token index i).
@@ -126,6 +127,21 @@ __device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int ti
     const int i = elem_index<DT, VP>(cstart, tid, it, k);
     qv[k] = i < V ? qrow[i] : 0.0f;
   }
+}
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Log-probability of token `tok` drawn from row r: (l - m) / T - log S with
+// the row's (m, S) at scale kk = log2(e) / T. lt is the token's logit as the
+// draw saw it; NaN (a rounding fallback) reads it from the row.
+template <int DT>
+__device__ __forceinline__ float drawn_logprob(const Args& a, int b, int r, int tok,
+                                               float lt, float m, float S, float kk) {
+  if (tok < 0) return NAN;
+  if (lt != lt)
+    lt = load_one<DT>(a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes,
+                      tok);
+  return ((lt - m) * kk - log2f(S)) * kLn2;
 }
 
 struct NoDuring {
@@ -194,7 +210,10 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
   for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
   const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
   if (cell < 0) {
-    if (tid == 0) sh.result = clast;  // the chunk's last positive weight
+    if (tid == 0) {
+      sh.result = clast;  // the chunk's last positive weight
+      sh.result_l = NAN;
+    }
   } else if (w == cell % kWaves) {
     const int its = cell / kWaves;
     float v = vs[0];
@@ -207,7 +226,10 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
     const bool mine = exc2 <= tc && tc < inc2;
     const unsigned long long who = __ballot(mine);
     if (!who) {
-      if (l == 0) sh.result = clast;
+      if (l == 0) {
+        sh.result = clast;
+        sh.result_l = NAN;
+      }
     } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
       const float tl = tc - exc2;
       u32x4 rv = raw[0];
@@ -222,18 +244,26 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
           qv[k] = i < a.V ? qrow[i] : 0.0f;
         }
       }
-      float run = 0.0f;
+      float run = 0.0f, lfound = NAN, llast = NAN;
       int found = -1, lastp = -1;
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
         const int i = elem_index<DT, VP>(cstart, tid, its, k);
-        const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(rv, k), i, excl, m, kk,
-                                                   invS, RESIDUAL ? qv[k] : 0.0f);
+        const float lk = elem<DT>(rv, k);
+        const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
+                                                   RESIDUAL ? qv[k] : 0.0f);
         run += wk;
-        if (wk > 0.0f) lastp = i;
-        if (found < 0 && run > tl) found = i;
+        if (wk > 0.0f) {
+          lastp = i;
+          llast = lk;
+        }
+        if (found < 0 && run > tl) {
+          found = i;
+          lfound = lk;
+        }
       }
       sh.result = found >= 0 ? found : lastp;
+      sh.result_l = found >= 0 ? lfound : llast;
     }
   }
   __syncthreads();
@@ -337,19 +367,23 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   auto combine_rows = [&](auto part) {
     for (int j = w; j <= d; j += kWaves) {
       if (greedy) {
-        float bv = kNegInf;
-        int bi = INT_MAX, nan = 0;
+        // argmax, and the sum of exp(l - max) at temperature 1 (NaN if the
+        // row holds NaN)
+        float bv = kNegInf, m1 = kNegInf, s1 = 0.0f;
+        int bi = INT_MAX;
         for (int c = l; c < nc; c += kWave) {
           const f32x4 p = part(j, c);
           argmax_merge(bv, bi, p.x, __float_as_int(p.w));
-          nan |= (p.y != 0.0f);
+          lse_merge(m1, s1, p.x, p.y, kLog2e);
         }
         wave_argmax(bv, bi);
-        nan = wave_or(nan);
+        wave_lse(m1, s1, kLog2e);
         if (l == 0) {
           sh.m[j] = bv;
+          sh.s[j] = s1;
           sh.idx[j] = bi;
-          sh.bad[j] = nan || bv == INFINITY || bv == kNegInf;
+          sh.bad[j] = !(s1 > 0.0f) || !isfinite(s1) || bv == INFINITY ||
+                      bv == kNegInf;
         }
       } else {
         const int xj = (j < d) ? sh.x[j] : -1;
@@ -442,6 +476,17 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
       if (a.p_draft && l < a.K)
         a.p_draft[(int64_t)b * a.K + l] =
             (!greedy && l < d && l <= al) ? px : -1.0f;
+      // Log-probabilities: accepted drafts here, a drawn token after its
+      // draw. Greedy rows are at temperature 1 (an accepted draft and the
+      // final token are the row's argmax: log p = -log s).
+      if (a.logprob && l < R) {
+        float lp = NAN;
+        if (greedy && l <= al)
+          lp = -logf(sh.s[l]);
+        else if (!greedy && l < al)
+          lp = ((sh.lx[l] - sh.m[l]) * kk - log2f(sh.s[l])) * kLn2;
+        if (greedy || l != al) a.logprob[(int64_t)b * R + l] = lp;
+      }
       if (l == 0) {
         a.nem[b] = al + 1;
         sh.acc_len = al;
@@ -481,6 +526,9 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
+      if (a.logprob)
+        a.logprob[(int64_t)b * R + al] =
+            drawn_logprob<DT>(a, b, al, tok, sh.draw.result_l, sh.m[al], sh.s[al], kk);
     }
     __syncthreads();
   }
@@ -593,7 +641,11 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
                                                         kk, 0.0f, raw)
                          : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, -1, m,
                                                        kk, 1.0f / S, raw);
-  if (tid == 0) a.out[(int64_t)b * R + r] = tok;
+  if (tid == 0) {
+    a.out[(int64_t)b * R + r] = tok;
+    if (a.logprob)
+      a.logprob[(int64_t)b * R + r] = drawn_logprob<DT>(a, b, r, tok, dsh.result_l, m, S, kk);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -650,8 +702,9 @@ enum Passes { kStream = 1, kFinish = 2 };
 int run(int passes, const void* logits, int dtype, int B, int K, int V,
         const int32_t* draft, const int32_t* draft_len, const float* q,
         const float* temperature, const float* uniforms, int32_t* out_tokens,
-        int32_t* num_emitted, float* p_draft, int32_t* status, void* workspace,
-        size_t ws_bytes, void* sam_state, int max_len, int32_t* next_draft,
+        int32_t* num_emitted, float* p_draft, float* logprob, int32_t* status,
+        void* workspace, size_t ws_bytes, void* sam_state, int max_len,
+        int32_t* next_draft,
         int32_t* next_draft_len, int32_t* next_match_len, void* stream,
         const char* fn) {
   if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV)
@@ -699,6 +752,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.out = out_tokens;
   a.nem = num_emitted;
   a.p_draft = p_draft;
+  a.logprob = logprob;
   a.status = status;
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
@@ -748,27 +802,28 @@ extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
                            const int32_t* draft, const int32_t* draft_len,
                            const float* q, const float* temperature,
                            const float* uniforms, int32_t* out_tokens,
-                           int32_t* num_emitted, float* p_draft, int32_t* status,
-                           void* workspace, size_t ws_bytes, void* stream) {
+                           int32_t* num_emitted, float* p_draft, float* logprobs,
+                           int32_t* status, void* workspace, size_t ws_bytes,
+                           void* stream) {
   return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len, q,
-             temperature, uniforms, out_tokens, num_emitted, p_draft, status,
-             workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
-             "spec_verify");
+             temperature, uniforms, out_tokens, num_emitted, p_draft, logprobs,
+             status, workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr,
+             stream, "spec_verify");
 }
 
 extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
                          const int32_t* draft, const int32_t* draft_len,
                          const float* temperature, const float* uniforms,
                          void* sam_state, int max_len, int32_t* out_tokens,
-                         int32_t* num_emitted, float* p_draft, int32_t* status,
-                         int32_t* next_draft, int32_t* next_draft_len,
-                         int32_t* next_match_len, void* workspace,
-                         size_t ws_bytes, void* stream) {
+                         int32_t* num_emitted, float* p_draft, float* logprobs,
+                         int32_t* status, int32_t* next_draft,
+                         int32_t* next_draft_len, int32_t* next_match_len,
+                         void* workspace, size_t ws_bytes, void* stream) {
   if (!sam_state)
     return set_error(SS_EINVAL, "spec_step: state is NULL");
   return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len,
              nullptr, temperature, uniforms, out_tokens, num_emitted, p_draft,
-             status, workspace, ws_bytes, sam_state, max_len, next_draft,
+             logprobs, status, workspace, ws_bytes, sam_state, max_len, next_draft,
              next_draft_len, next_match_len, stream, "spec_step");
 }
 
@@ -777,8 +832,8 @@ extern "C" int spec_stream(const void* logits, int dtype, int B, int K, int V,
                            const float* temperature, const float* uniforms,
                            void* workspace, size_t ws_bytes, void* stream) {
   return run(kStream, logits, dtype, B, K, V, draft, draft_len, nullptr,
-             temperature, uniforms, nullptr, nullptr, nullptr, nullptr, workspace,
-             ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
+             temperature, uniforms, nullptr, nullptr, nullptr, nullptr, nullptr,
+             workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
              "spec_stream");
 }
 
@@ -786,12 +841,13 @@ extern "C" int spec_finish(const void* logits, int dtype, int B, int K, int V,
                            const int32_t* draft, const int32_t* draft_len,
                            const float* q, const float* temperature,
                            const float* uniforms, int32_t* out_tokens,
-                           int32_t* num_emitted, float* p_draft, int32_t* status,
-                           void* sam_state, int max_len, int32_t* next_draft,
-                           int32_t* next_draft_len, int32_t* next_match_len,
-                           void* workspace, size_t ws_bytes, void* stream) {
+                           int32_t* num_emitted, float* p_draft, float* logprobs,
+                           int32_t* status, void* sam_state, int max_len,
+                           int32_t* next_draft, int32_t* next_draft_len,
+                           int32_t* next_match_len, void* workspace,
+                           size_t ws_bytes, void* stream) {
   return run(kFinish, logits, dtype, B, K, V, draft, draft_len, q, temperature,
-             uniforms, out_tokens, num_emitted, p_draft, status, workspace,
-             ws_bytes, sam_state, max_len, next_draft, next_draft_len,
+             uniforms, out_tokens, num_emitted, p_draft, logprobs, status,
+             workspace, ws_bytes, sam_state, max_len, next_draft, next_draft_len,
              next_match_len, stream, "spec_finish");
 }

@@ -135,6 +135,7 @@ struct Args {
   int32_t* out;
   int32_t* nem;
   float* p_draft;
+  float* logprob;   // [B, K+1] or NULL: log-probabilities of emitted tokens
   int32_t* status;
   f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
   i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)

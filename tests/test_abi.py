@@ -54,7 +54,7 @@ def test_library_loads_and_answers_size_queries():
     assert L.sam_hash_slots(9216) == 65536
     # argument errors are reported without touching a device
     rc = L.spec_verify(None, 0, 0, 3, 10, None, None, None, None, None, None,
-                       None, None, None, None, ctypes.c_size_t(0), None)
+                       None, None, None, None, None, ctypes.c_size_t(0), None)
     assert rc == -1
     L.ss_last_error_string.restype = ctypes.c_char_p
     assert b"B >= 1" in L.ss_last_error_string()
