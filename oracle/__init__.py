@@ -34,6 +34,7 @@ ST_DRAFT_LEN = 1 << 2
 ST_NONFINITE = 1 << 3
 ST_TEMPERATURE = 1 << 4
 ST_NO_UNIFORMS = 1 << 5
+ST_TOP_P = 1 << 6
 
 
 def build() -> str:
@@ -77,7 +78,7 @@ def _load():
     lib.orc_sam_static_draft.argtypes = [P, i32, P, P, i32, P, P]
     lib.orc_sam_static_draft.restype = None
     lib.orc_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P,
-                               P, P, P, P, P, P, P, i32]
+                               P, P, P, P, P, P, P, P, P, P, P, i32]
     lib.orc_step.argtypes = [P, i32, i32, i32, P, i32, P, P, P, P, P,
                              P, P, P, P, P, P, P, i32]
     _lib = lib
@@ -232,15 +233,19 @@ class VerifyResult:
     cdf_lo: np.ndarray       # [B] float64 breakpoints around the final draw
     cdf_hi: np.ndarray       # [B]
     status: np.ndarray       # [B] int32
+    trunc_thr: np.ndarray | None = None     # [B,K+1] threshold logit per row used
+    trunc_margin: np.ndarray | None = None  # [B,K+1] top-p decision margin
 
 
 def verify(logits, draft, draft_len, temperature, uniforms=None, q=None,
-           nthreads: int = 1) -> VerifyResult:
+           nthreads: int = 1, top_k=None, top_p=None) -> VerifyResult:
     """Verify one batch.
 
     logits: [B,K+1,V] float32, or uint16 holding bfloat16 bit patterns.
     draft: [B,K] int32; draft_len: [B] int32; temperature: [B] float32;
     uniforms: [B,K+1] float32 or None; q: [B,K,V] float32 or None (one-hot).
+    top_k: [B] int32 or None; top_p: [B] float32 or None (truncation of the
+    target distribution at T > 0, see ``truncate`` in oracle.cpp).
     """
     lib = _load()
     logits, dtype = _logits_arg(logits)
@@ -260,11 +265,17 @@ def verify(logits, draft, draft_len, temperature, uniforms=None, q=None,
     lo = np.empty(B, np.float64)
     hi = np.empty(B, np.float64)
     st = np.zeros(B, np.int32)
+    if top_k is not None:
+        top_k = _c(top_k, np.int32).reshape(B)
+    if top_p is not None:
+        top_p = _c(top_p, np.float32).reshape(B)
+    thr = np.empty((B, K + 1), np.float64)
+    mg = np.empty((B, K + 1), np.float64)
     lib.orc_verify(_ptr(logits), dtype, B, K, V, _ptr(draft), _ptr(draft_len),
                    _ptr(q), _ptr(temperature), _ptr(uniforms), _ptr(out),
                    _ptr(nem), _ptr(pd), _ptr(al), _ptr(lo), _ptr(hi), _ptr(st),
-                   int(nthreads))
-    return VerifyResult(out, nem, pd, al, lo, hi, st)
+                   _ptr(top_k), _ptr(top_p), _ptr(thr), _ptr(mg), int(nthreads))
+    return VerifyResult(out, nem, pd, al, lo, hi, st, thr, mg)
 
 
 def step(sams, logits, temperature, uniforms, nthreads: int = 1):

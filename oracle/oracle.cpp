@@ -181,6 +181,7 @@ constexpr int32_t ST_DRAFT_LEN = 1 << 2;
 constexpr int32_t ST_NONFINITE = 1 << 3;
 constexpr int32_t ST_TEMPERATURE = 1 << 4;
 constexpr int32_t ST_NO_UNIFORMS = 1 << 5;
+constexpr int32_t ST_TOP_P = 1 << 6;
 
 // bfloat16 is the upper half of an IEEE binary32: widen by appending 16 zero
 // bits.
@@ -261,6 +262,66 @@ bool finite_row(const std::vector<double>& l) {
   return any_above_neg_inf;
 }
 
+// Truncation of a sampling distribution before verification ([P3] "SGLang
+// 的实现": the target probabilities are renormalised by top-k, then by top-p,
+// before the speculative-sampling kernel sees them; one value of each per
+// request, applied to every position of that request). Read as:
+//   top-k (1 <= k < V): keep the tokens whose logit is at least the k-th
+//     largest logit (counted with multiplicity; tokens tied with it are all
+//     kept), drop the rest;
+//   top-p (0 < top_p < 1), on what top-k kept: going down the distinct logit
+//     values, keep every token of each value until the kept probability,
+//     relative to what top-k kept, first reaches top_p (that whole group of
+//     tied tokens included);
+//   then renormalise. k <= 0 or k >= V, and top_p = 1, leave p as it is.
+// p is overwritten with the truncated distribution. Returns the threshold
+// logit (keep l >= threshold; -inf when nothing is dropped). *margin receives
+// how far, relative to the mass top-k kept, the top-p decision was from
+// flipping (the smaller of the gaps to top_p on both sides of the chosen
+// group); NaN when top-p made no decision.
+double truncate(const std::vector<double>& l, std::vector<double>& p, int32_t top_k,
+                double top_p, double* margin) {
+  const int64_t V = (int64_t)l.size();
+  const double ninf = -std::numeric_limits<double>::infinity();
+  *margin = std::numeric_limits<double>::quiet_NaN();
+  const bool use_k = top_k >= 1 && top_k < V;
+  const bool use_p = top_p < 1.0;
+  if (!use_k && !use_p) return ninf;
+  std::vector<int64_t> order((size_t)V);
+  for (int64_t i = 0; i < V; ++i) order[(size_t)i] = i;
+  std::sort(order.begin(), order.end(),
+            [&](int64_t a, int64_t b) { return l[(size_t)a] > l[(size_t)b]; });
+  double thr = ninf;
+  if (use_k) thr = l[(size_t)order[(size_t)(top_k - 1)]];
+  if (use_p) {
+    double Zk = 0.0;
+    for (int64_t i = 0; i < V; ++i)
+      if (l[(size_t)i] >= thr) Zk += p[(size_t)i];
+    const double target = top_p * Zk;
+    double cum = 0.0;
+    int64_t g = 0;
+    while (g < V && l[(size_t)order[(size_t)g]] >= thr) {
+      const double v = l[(size_t)order[(size_t)g]];
+      const double before = cum;
+      int64_t e = g;
+      while (e < V && l[(size_t)order[(size_t)e]] == v) cum += p[(size_t)order[(size_t)e++]];
+      if (cum >= target) {
+        thr = v;
+        *margin = std::min(target - before, cum - target) / Zk;
+        break;
+      }
+      g = e;
+    }
+  }
+  double Z = 0.0;
+  for (int64_t i = 0; i < V; ++i) {
+    if (l[(size_t)i] < thr) p[(size_t)i] = 0.0;
+    Z += p[(size_t)i];
+  }
+  for (double& v : p) v /= Z;
+  return thr;
+}
+
 struct VerifyIO {
   const void* logits;
   int dtype;
@@ -277,6 +338,10 @@ struct VerifyIO {
   double* cdf_lo;         // [B] normalised CDF breakpoints of the final draw
   double* cdf_hi;         // [B]
   int32_t* status;        // [B] (OR-ed)
+  const int32_t* top_k;   // [B] or null (no top-k)
+  const float* top_p;     // [B] or null (no top-p)
+  double* trunc_thr;      // [B,K+1] threshold logit of each row used (NaN unused)
+  double* trunc_margin;   // [B,K+1] top-p decision margin (NaN: none)
 };
 
 // One sequence of the step ([P2] §2.2: K+1 target distributions from one
@@ -295,6 +360,10 @@ void verify_one(const VerifyIO& io, int b) {
     al[j] = std::numeric_limits<double>::quiet_NaN();
   }
   io.cdf_lo[b] = io.cdf_hi[b] = std::numeric_limits<double>::quiet_NaN();
+  if (io.trunc_thr)
+    for (int64_t j = 0; j < R; ++j)
+      io.trunc_thr[(int64_t)b * R + j] = io.trunc_margin[(int64_t)b * R + j] =
+          std::numeric_limits<double>::quiet_NaN();
 
   const int32_t d = io.draft_len[b];
   const double T = (double)io.temperature[b];
@@ -306,6 +375,9 @@ void verify_one(const VerifyIO& io, int b) {
                      std::isfinite(T))))
     st |= ST_TEMPERATURE;
   if (T > 0.0 && io.uniforms == nullptr) st |= ST_NO_UNIFORMS;
+  const int32_t top_k = io.top_k ? io.top_k[b] : 0;
+  const double top_p = io.top_p ? (double)io.top_p[b] : 1.0;
+  if (!(top_p > 0.0 && top_p <= 1.0)) st |= ST_TOP_P;
   if (st == 0) {
     for (int j = 0; j < d; ++j) {
       const int32_t x = io.draft[(int64_t)b * K + j];
@@ -348,9 +420,19 @@ void verify_one(const VerifyIO& io, int b) {
   // when the drafts come with no probabilities, [P3] "SGLang 的实现").
   const float* u = io.uniforms + (int64_t)b * R;
   std::vector<double> p, w;
+  // p_j: softmax(l_j / T), truncated when the request asks for it.
+  auto target = [&](int j) {
+    softmax_T(rows[(size_t)j], T, p);
+    double mg;
+    const double thr = truncate(rows[(size_t)j], p, top_k, top_p, &mg);
+    if (io.trunc_thr) {
+      io.trunc_thr[(int64_t)b * R + j] = thr;
+      io.trunc_margin[(int64_t)b * R + j] = mg;
+    }
+  };
   for (int j = 0; j < d; ++j) {
     const int32_t x = io.draft[(int64_t)b * K + j];
-    softmax_T(rows[(size_t)j], T, p);
+    target(j);
     pd[j] = p[(size_t)x];
     double qx = 1.0;
     if (io.q) qx = (double)io.q[((int64_t)b * K + j) * V + x];
@@ -382,7 +464,7 @@ void verify_one(const VerifyIO& io, int b) {
     return;
   }
   // Every draft accepted: bonus token from the target at row d.
-  softmax_T(rows[(size_t)d], T, p);
+  target(d);
   out[d] = (int32_t)inv_cdf(p, (double)u[K], &io.cdf_lo[b], &io.cdf_hi[b]);
   io.num_emitted[b] = d + 1;
 }
@@ -486,11 +568,13 @@ void orc_verify(const void* logits, int32_t dtype, int32_t B, int32_t K,
                 const float* q, const float* temperature, const float* uniforms,
                 int32_t* out_tokens, int32_t* num_emitted, double* p_draft,
                 double* alpha, double* cdf_lo, double* cdf_hi, int32_t* status,
-                int32_t nthreads) {
+                const int32_t* top_k, const float* top_p, double* trunc_thr,
+                double* trunc_margin, int32_t nthreads) {
   VerifyIO io{logits,      dtype,    B,          K,           V,
               draft,       draft_len, q,         temperature, uniforms,
               out_tokens,  num_emitted, p_draft, alpha,       cdf_lo,
-              cdf_hi,      status};
+              cdf_hi,      status,   top_k,     top_p,       trunc_thr,
+              trunc_margin};
   if (nthreads <= 1) {
     for (int b = 0; b < B; ++b) verify_one(io, b);
     return;
@@ -518,7 +602,7 @@ void orc_step(void** sams, int32_t B, int32_t K, int32_t V, const void* logits,
         ((OracleSAM*)sams[b])->draft(K, draft + (int64_t)b * K, &match_len[b]);
   orc_verify(logits, dtype, B, K, V, draft, draft_len, nullptr, temperature,
              uniforms, out_tokens, num_emitted, p_draft, alpha, cdf_lo, cdf_hi,
-             status, nthreads);
+             status, nullptr, nullptr, nullptr, nullptr, nthreads);
   for (int b = 0; b < B; ++b) {
     if (status[b]) continue;
     OracleSAM* s = (OracleSAM*)sams[b];
