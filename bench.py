@@ -301,7 +301,8 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
 
     def fused(s):
         rc = L.spec_step(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
-                         temp_p, u0 + s * rowU, st_p, max_len, out_p, nem0 + s * rowB,
+                         temp_p, u0 + s * rowU, None, None, st_p, max_len, out_p,
+                         nem0 + s * rowB,
                          pd_p, None, status_p, draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB,
                          mlen_p, ws_p, ws_n, stream)
         if rc:
@@ -310,8 +311,8 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
     def separate(s):
         # The same step as three calls: verify, extend + next draft.
         rc = L.spec_verify(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
-                           None, temp_p, u0 + s * rowU, out_p, nem0 + s * rowB, pd_p,
-                           None, status_p, ws_p, ws_n, stream)
+                           None, temp_p, u0 + s * rowU, None, None, out_p,
+                           nem0 + s * rowB, pd_p, None, status_p, ws_p, ws_n, stream)
         rc |= L.sam_extend_draft(st_p, B, max_len, out_p, R, nem0 + s * rowB, K,
                                  draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
                                  stream)
@@ -333,12 +334,12 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
         for r in range(STREAM_BATCH):
             slot = (s + 1 + r) % RING
             rc |= L.spec_stream(ring_p[slot], dt, B, K, V, draft_p[s % 2],
-                                dl0 + s * rowB, temp_p, u0 + s * rowU, ws_p, ws_n,
-                                stream)
+                                dl0 + s * rowB, temp_p, u0 + s * rowU, None, None,
+                                ws_p, ws_n, stream)
         evs[1].record()
         rc |= L.spec_finish(ring_p[s % RING], dt, B, K, V, draft_p[s % 2],
-                            dl0 + s * rowB, None, temp_p, u0 + s * rowU, out_p,
-                            nem0 + s * rowB, pd_p, None, status_p, st_p, max_len,
+                            dl0 + s * rowB, None, temp_p, u0 + s * rowU, None, None,
+                            out_p, nem0 + s * rowB, pd_p, None, status_p, st_p, max_len,
                             draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
                             ws_p, ws_n, stream)
         evs[2].record()
@@ -487,7 +488,7 @@ def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
     def call(s):
         k = s % nslots
         rc = L.spec_verify(xp[k], 0, B, K, V, dp[k], dl.data_ptr(), qp[k],
-                           temp.data_ptr(), u0 + s * rowU, out.data_ptr(),
+                           temp.data_ptr(), u0 + s * rowU, None, None, out.data_ptr(),
                            nem0 + s * rowB, pd.data_ptr(), None, status.data_ptr(),
                            ws.data_ptr(), ws.numel(), stream)
         if rc:
@@ -512,11 +513,11 @@ def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
         for r in range(batch):
             kk = (s + 1 + r) % nslots
             rc |= L.spec_stream(xp[kk], 0, B, K, V, dp[k], dl.data_ptr(),
-                                temp.data_ptr(), u0 + s * rowU, ws.data_ptr(),
-                                ws.numel(), stream)
+                                temp.data_ptr(), u0 + s * rowU, None, None,
+                                ws.data_ptr(), ws.numel(), stream)
         evs[i][1].record()
         rc |= L.spec_finish(xp[k], 0, B, K, V, dp[k], dl.data_ptr(), qp[k],
-                            temp.data_ptr(), u0 + s * rowU, out.data_ptr(),
+                            temp.data_ptr(), u0 + s * rowU, None, None, out.data_ptr(),
                             nem0 + s * rowB, pd.data_ptr(), None, status.data_ptr(),
                             None, 0, None, None, None, ws.data_ptr(), ws.numel(), stream)
         evs[i][2].record()

@@ -59,6 +59,7 @@ extern "C" {
                                        below the smallest normal float */
 #define SS_ST_NO_UNIFORMS (1 << 5)  /* T > 0 but uniforms == NULL */
 #define SS_ST_COUNT (1 << 6)        /* extend count outside [0, ld_tokens] */
+#define SS_ST_TOP_P (1 << 7)        /* top_p NaN or outside (0, 1] */
 
 #define SS_MAX_K 16            /* largest number of drafted tokens */
 #define SS_MAX_LEN (1 << 24)   /* largest automaton capacity, tokens */
@@ -82,6 +83,14 @@ const char* ss_last_error_string(void);
  * matter, and one buffer serves any call whose size fits. A workspace must
  * not serve two calls that may run concurrently. */
 size_t ss_verify_workspace_bytes(int B, int K, int V);
+
+/* The same with options: flags = 0, or SS_WS_TRUNCATION for calls that pass
+ * top_k or top_p (the truncation passes need per-row histograms, candidate
+ * lists and per-chunk sums: about (K+1) * B * (nchunks * 2 KiB +
+ * min(4096, V) * 8 B), nchunks = ceil(V / 8192)). 0 for unsupported sizes or
+ * flags. */
+#define SS_WS_TRUNCATION 1
+size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);
 
 /*
  * spec_verify — one batched verification step.
@@ -110,6 +119,23 @@ size_t ss_verify_workspace_bytes(int B, int K, int V);
  *   uniforms    [B, K+1] float in [0, 1): columns 0..K-1 are the acceptance
  *               coins, column K the final coin. May be NULL only if every
  *               temperature is 0.
+ *   top_k       [B] int32 or NULL; top_p [B] float or NULL: truncation of the
+ *               target distribution of a sequence at T > 0 before it is used
+ *               anywhere above ([P3] "SGLang 的实现": the target probabilities
+ *               are renormalised by top-k, then top-p, one value of each per
+ *               request, applied to all K+1 positions). p_j is replaced by
+ *               p'_j: top-k (1 <= k < V) keeps every token whose logit is at
+ *               least the k-th largest logit of the row (ties kept); top-p
+ *               (0 < top_p < 1), applied to what top-k kept, keeps whole
+ *               groups of equal logits from the largest down until the kept
+ *               share of what top-k kept reaches top_p; p'_j is p_j on the
+ *               kept tokens, renormalised. k <= 0 or k >= V, and top_p = 1,
+ *               do nothing; top_p NaN or outside (0, 1] sets SS_ST_TOP_P.
+ *               Greedy sequences are not affected. Acceptance, residual,
+ *               bonus and p_draft all use p'_j; logprobs stay those of the
+ *               untruncated p_j. With either pointer non-NULL the workspace
+ *               must come from ss_verify_workspace_bytes_ex(...,
+ *               SS_WS_TRUNCATION).
  *   out_tokens  [B, K+1] int32: accepted drafts then the corrected / bonus
  *               token; -1 after num_emitted.
  *   num_emitted [B] int32 = accepted drafts + 1.
@@ -131,7 +157,7 @@ size_t ss_verify_workspace_bytes(int B, int K, int V);
 int spec_verify(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len, const float* q,
                 const float* temperature, const float* uniforms,
-                int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
+                const int32_t* top_k, const float* top_p, int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
                 float* logprobs, int32_t* status, void* workspace,
                 size_t ws_bytes, void* stream);
 
@@ -152,7 +178,8 @@ int spec_verify(const void* logits, int dtype, int B, int K, int V,
  */
 int spec_step(const void* logits, int dtype, int B, int K, int V,
               const int32_t* draft, const int32_t* draft_len,
-              const float* temperature, const float* uniforms, void* sam_state,
+              const float* temperature, const float* uniforms,
+              const int32_t* top_k, const float* top_p, void* sam_state,
               int max_len, int32_t* out_tokens, int32_t* num_emitted,
               float* p_draft, float* logprobs, int32_t* status,
               int32_t* next_draft,
@@ -169,17 +196,20 @@ int spec_step(const void* logits, int dtype, int B, int K, int V,
  *                non-NULL, updates the automata and writes the next drafts
  *                (then q must be NULL and the next-draft outputs non-NULL).
  * spec_finish must follow spec_stream on the same stream with the same
- * logits, sizes, drafts, temperatures, uniforms and workspace.
+ * logits, sizes, drafts, temperatures, uniforms, top_k, top_p and workspace
+ * (with truncation, spec_finish also runs the truncation passes, which read
+ * each truncated row a second time).
  */
 int spec_stream(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len,
                 const float* temperature, const float* uniforms,
-                void* workspace, size_t ws_bytes, void* stream);
+                const int32_t* top_k, const float* top_p, void* workspace,
+                size_t ws_bytes, void* stream);
 
 int spec_finish(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len, const float* q,
                 const float* temperature, const float* uniforms,
-                int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
+                const int32_t* top_k, const float* top_p, int32_t* out_tokens, int32_t* num_emitted, float* p_draft,
                 float* logprobs, int32_t* status, void* sam_state, int max_len,
                 int32_t* next_draft, int32_t* next_draft_len,
                 int32_t* next_match_len, void* workspace, size_t ws_bytes,

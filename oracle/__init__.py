@@ -34,7 +34,7 @@ ST_DRAFT_LEN = 1 << 2
 ST_NONFINITE = 1 << 3
 ST_TEMPERATURE = 1 << 4
 ST_NO_UNIFORMS = 1 << 5
-ST_TOP_P = 1 << 6
+ST_TOP_P = 1 << 7
 
 
 def build() -> str:

@@ -181,7 +181,7 @@ constexpr int32_t ST_DRAFT_LEN = 1 << 2;
 constexpr int32_t ST_NONFINITE = 1 << 3;
 constexpr int32_t ST_TEMPERATURE = 1 << 4;
 constexpr int32_t ST_NO_UNIFORMS = 1 << 5;
-constexpr int32_t ST_TOP_P = 1 << 6;
+constexpr int32_t ST_TOP_P = 1 << 7;
 
 // bfloat16 is the upper half of an IEEE binary32: widen by appending 16 zero
 // bits.

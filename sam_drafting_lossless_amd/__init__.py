@@ -28,6 +28,7 @@ ST_NONFINITE = 1 << 3
 ST_TEMPERATURE = 1 << 4
 ST_NO_UNIFORMS = 1 << 5
 ST_COUNT = 1 << 6
+ST_TOP_P = 1 << 7
 MAX_K = 16
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
@@ -53,16 +54,18 @@ def lib():
     L.ss_last_error_string.restype = ctypes.c_char_p
     L.ss_verify_workspace_bytes.argtypes = [i32, i32, i32]
     L.ss_verify_workspace_bytes.restype = sz
+    L.ss_verify_workspace_bytes_ex.argtypes = [i32, i32, i32, i32]
+    L.ss_verify_workspace_bytes_ex.restype = sz
     L.spec_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                              P, P, sz, P]
+                              P, P, P, P, sz, P]
     L.spec_verify.restype = i32
-    L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, i32, P, P, P,
-                            P, P, P, P, P, P, sz, P]
+    L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P,
+                            P, P, P, P, P, P, P, P, sz, P]
     L.spec_step.restype = i32
-    L.spec_stream.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.spec_stream.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.spec_stream.restype = i32
     L.spec_finish.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
-                              P, P, i32, P, P, P, P, sz, P]
+                              P, P, P, P, i32, P, P, P, P, sz, P]
     L.spec_finish.restype = i32
     L.sam_extend_draft.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P]
     L.sam_extend_draft.restype = i32
@@ -118,27 +121,39 @@ def _opt_f32(t, name, shape):
     return None if t is None else _dev(t, name, torch.float32, shape)
 
 
+def _trunc_args(top_k, top_p, B):
+    return (None if top_k is None else _dev(top_k, "top_k", torch.int32, (B,)),
+            _opt_f32(top_p, "top_p", (B,)))
+
+
 # ------------------------------------------------------------- verification --
-def ss_verify_workspace_bytes(B: int, K: int, V: int) -> int:
-    return int(lib().ss_verify_workspace_bytes(B, K, V))
+WS_TRUNCATION = 1
 
 
-def verify_workspace(B: int, K: int, V: int, device=None):
+def ss_verify_workspace_bytes(B: int, K: int, V: int, truncation: bool = False) -> int:
+    return int(lib().ss_verify_workspace_bytes_ex(B, K, V,
+                                                  WS_TRUNCATION if truncation else 0))
+
+
+def verify_workspace(B: int, K: int, V: int, device=None, truncation: bool = False):
     """A workspace tensor (uint8) for spec_verify / spec_step calls of this
-    size (or smaller); it needs no initialisation."""
-    n = ss_verify_workspace_bytes(B, K, V)
+    size (or smaller); it needs no initialisation. `truncation`: room for
+    calls that pass top_k / top_p."""
+    n = ss_verify_workspace_bytes(B, K, V, truncation)
     if n == 0:
         raise SpecSamError(f"unsupported sizes B={B} K={K} V={V}")
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
 def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
-                workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
-                status=None, logprobs=None, stream=None):
+                top_k=None, top_p=None, workspace=None, out_tokens=None,
+                num_emitted=None, p_draft=None, status=None, logprobs=None,
+                stream=None):
     """Verify one batch (see include/specsam.h). Returns
     (out_tokens [B,K+1] int32, num_emitted [B] int32, p_draft [B,K] float32,
     status [B] int32). `logprobs`, a [B,K+1] float32 tensor, receives the
-    log-probabilities of the emitted tokens when given."""
+    log-probabilities of the emitted tokens when given. `top_k` ([B] int32)
+    and `top_p` ([B] float32) truncate the target at T > 0."""
     if logits.dim() != 3:
         raise SpecSamError("logits must be [B, K+1, V]")
     B, R, V = logits.shape
@@ -151,8 +166,9 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
         raise SpecSamError("logits must be float32 or bfloat16")
     dev = logits.device
     i32 = torch.int32
+    trunc = top_k is not None or top_p is not None
     if workspace is None:
-        workspace = verify_workspace(B, K, V, dev)
+        workspace = verify_workspace(B, K, V, dev, truncation=trunc)
     if out_tokens is None:
         out_tokens = torch.empty((B, R), dtype=i32, device=dev)
     if num_emitted is None:
@@ -169,6 +185,7 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
         _dev(temperature, "temperature", torch.float32, (B,)),
         None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
                                            (B, R)),
+        *_trunc_args(top_k, top_p, B),
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
         _dev(p_draft, "p_draft", torch.float32, (B, K)),
@@ -183,7 +200,8 @@ def spec_verify(logits, draft, draft_len, temperature, uniforms=None, q=None, *,
 def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
               workspace=None, out_tokens=None, num_emitted=None, p_draft=None,
               status=None, next_draft=None, next_draft_len=None,
-              next_match_len=None, logprobs=None, stream=None):
+              next_match_len=None, logprobs=None, top_k=None, top_p=None,
+              stream=None):
     """One fused step (see include/specsam.h): verify the drafts, extend each
     automaton of `state` (a SamState) with the emitted tokens, and draft for
     the next step. Returns (out_tokens, num_emitted, p_draft, status,
@@ -200,7 +218,8 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
     dev = logits.device
     i32 = torch.int32
     if workspace is None:
-        workspace = verify_workspace(B, K, V, dev)
+        workspace = verify_workspace(B, K, V, dev, truncation=(
+            top_k is not None or top_p is not None))
     if out_tokens is None:
         out_tokens = torch.empty((B, R), dtype=i32, device=dev)
     if num_emitted is None:
@@ -222,6 +241,7 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
         _dev(temperature, "temperature", torch.float32, (B,)),
         None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
                                            (B, R)),
+        *_trunc_args(top_k, top_p, B),
         _dev(state.buf, "state", torch.uint8), state.max_len,
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
@@ -249,7 +269,7 @@ def _shape(logits):
 
 
 def spec_stream(logits, draft, draft_len, temperature, uniforms, workspace, *,
-                stream=None):
+                top_k=None, top_p=None, stream=None):
     """First pass of a verification (see include/specsam.h): read the logit
     rows once and leave per-row statistics in `workspace`."""
     B, K, V, dt = _shape(logits)
@@ -261,6 +281,7 @@ def spec_stream(logits, draft, draft_len, temperature, uniforms, workspace, *,
         _dev(temperature, "temperature", torch.float32, (B,)),
         None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
                                            (B, K + 1)),
+        *_trunc_args(top_k, top_p, B),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)), "spec_stream")
 
@@ -268,7 +289,8 @@ def spec_stream(logits, draft, draft_len, temperature, uniforms, workspace, *,
 def spec_finish(logits, draft, draft_len, temperature, uniforms, workspace,
                 q=None, state=None, *, out_tokens=None, num_emitted=None,
                 p_draft=None, status=None, next_draft=None, next_draft_len=None,
-                next_match_len=None, logprobs=None, stream=None):
+                next_match_len=None, logprobs=None, top_k=None, top_p=None,
+                stream=None):
     """Second pass (see include/specsam.h), after spec_stream with the same
     arguments and workspace. Returns (out_tokens, num_emitted, p_draft,
     status), followed by (next_draft, next_draft_len, next_match_len) when
@@ -303,6 +325,7 @@ def spec_finish(logits, draft, draft_len, temperature, uniforms, workspace,
         _dev(temperature, "temperature", torch.float32, (B,)),
         None if uniforms is None else _dev(uniforms, "uniforms", torch.float32,
                                            (B, R)),
+        *_trunc_args(top_k, top_p, B),
         _dev(out_tokens, "out_tokens", i32, (B, R)),
         _dev(num_emitted, "num_emitted", i32, (B,)),
         _dev(p_draft, "p_draft", torch.float32, (B, K)),

@@ -6,7 +6,9 @@
 // the drafts are never read). At T = 0 a partial is (max, lowest index of the
 // max, NaN flag); at T > 0 it is the online (max m, sum of exp2((l - m) *
 // log2e / T)) plus the logit of the draft token x_j when x_j falls in the
-// chunk. The finish pass combines them.
+// chunk. The finish pass combines them. When the request truncates its
+// target (top-k / top-p), each chunk of a row at T > 0 also leaves a window
+// histogram of its logits for the truncation passes (trunc.hip).
 //
 // Design for gfx950: 256-thread workgroups each hold one chunk in registers
 // (8 non-temporal 16-byte loads in flight per lane, each wavefront load one
@@ -27,14 +29,56 @@ namespace {
 // stream: one partial per (row, chunk).
 // ---------------------------------------------------------------------------
 
+// Window histogram of one chunk of a truncated row (see kHistBins): `raw`
+// still holds the chunk, pm is the chunk max. hs (LDS, kHistBins + 1 words)
+// was cleared before the barrier that published pm.
+static_assert(kHistBins == kThreads, "one histogram bin per thread");
+
+template <int DT>
+__device__ __forceinline__ void chunk_histogram(const Args& a, int64_t row, int c,
+                                                float pm, float kk,
+                                                const u32x4 (&raw)[kLoads],
+                                                unsigned long long* hs) {
+  const int tid = threadIdx.x;
+  const int a0 = abs_bin(pm, kk);
+  unsigned long long rest = 0;
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k) {
+      const float v = elem<DT>(raw[it], k);
+      if (v > kNegInf) {  // -inf (probability 0) and NaN are not counted
+        const int jb = abs_bin(v, kk) - a0;
+        const float w = fast_exp2((v - pm) * kk);
+        const unsigned long long word =
+            kCountOne | (unsigned long long)(unsigned)(w * kFixScale);
+        if (jb >= 0 && jb < kHistBins)
+          atomicAdd(&hs[jb], word);
+        else
+          rest += word;
+      }
+    }
+  if (rest) atomicAdd(&hs[kHistBins], rest);
+  __syncthreads();
+  const int64_t hc = row * a.nchunks + c;
+  a.hist[hc * kHistBins + tid] = hs[tid];
+  if (tid == 0) {
+    const unsigned long long r = hs[kHistBins];
+    a.hhdr[hc] = i32x4{a0, (int)(unsigned)(r >> 32), (int)(unsigned)r, 0};
+  }
+}
+
 // Reduces one loaded chunk of row j of sequence b into its partial. `raw`
 // holds the chunk; `mid` runs once every element has been consumed, before
 // the workgroup reduction (the balanced kernel issues its next item's loads
-// into `raw` there). Ends with a barrier, so `red` may be reused at once.
-template <int DT, bool VP, typename Mid>
+// into `raw` there). With TR, a truncated row also leaves its chunk's window
+// histogram (hs is the LDS histogram). Ends with a barrier, so `red` and `hs`
+// may be reused at once.
+template <int DT, bool VP, bool TR, typename Mid>
 __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
                                            float T, int c, u32x4 (&raw)[kLoads],
-                                           f32x4* red, Mid mid) {
+                                           f32x4* red, unsigned long long* hs,
+                                           Mid mid) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int R = a.K + 1, nc = a.nchunks;
   const int cstart = c * kChunk<DT>;
@@ -117,12 +161,23 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
       m = mn;
     }
     mid();
+    bool tr = false;
+    if constexpr (TR) {
+      tr = trunc_active(a, b, T);
+      if (tr) {
+        hs[tid] = 0;
+        if (tid == 0) hs[kHistBins] = 0;
+      }
+    }
     wave_lse(m, s, kk);
     if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
     __syncthreads();
     float pm = red[0].x, ps = red[0].y;
     for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
     part = f32x4{pm, ps, lx, 0.0f};
+    if constexpr (TR) {
+      if (tr) chunk_histogram<DT>(a, row, c, pm, kk, raw, hs);
+    }
   }
   if (tid == 0) a.partials[row * nc + c] = part;
   __syncthreads();  // red[] is reused by the next row
@@ -135,9 +190,10 @@ struct NoMid {
 // Static grid over (sequence, row group, chunk), for batches too large for
 // the balanced kernel's plan: each workgroup streams its chunk of every row
 // j <= draft_len in its group, one row after another.
-template <int DT, bool VP>
+template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
+  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   const int tid = threadIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
   const int c = blockIdx.x % nc;
@@ -160,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
     if (j != 0)
       load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
                          cstart, a.V, tid, raw);
-    stream_row<DT, VP>(a, b, j, d, T, c, raw, red, NoMid{});
+    stream_row<DT, VP, TR>(a, b, j, d, T, c, raw, red, hs, NoMid{});
   }
 }
 
@@ -207,10 +263,11 @@ __device__ __forceinline__ int extra_rows(const Args& a, int b) {
   return (v >= 1 && v <= a.K) ? v : 0;
 }
 
-template <int DT, bool VP>
+template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, DT == SS_DTYPE_F32 ? 6 : 4) void
 spec_stream_balanced_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
+  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   __shared__ int pre[kPlanMaxB + 1];
   __shared__ int wsum[kWaves];
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
@@ -230,7 +287,7 @@ spec_stream_balanced_kernel(Args a) {
     const int b = tid + i * kThreads;
     if (b < B) part += extra_rows(a, b);
   }
-  if (st == 0) stream_row<DT, VP>(a, b0, 0, d, T, c0, raw, red, NoMid{});
+  if (st == 0) stream_row<DT, VP, TR>(a, b0, 0, d, T, c0, raw, red, hs, NoMid{});
   part = (int)wave_sum((float)part);  // exact: < 2^24
   if (l == 0) wsum[w] = part;
   __syncthreads();
@@ -270,7 +327,7 @@ spec_stream_balanced_kernel(Args a) {
     load_chunk<DT, VP>(a.logits + ((int64_t)t.b * R + t.j) * a.V * Dt<DT>::kBytes,
                        t.c * kChunk<DT>, a.V, tid, raw);
     st = seq_check(a, t.b, &d, &T);
-    if (st == 0) stream_row<DT, VP>(a, t.b, t.j, d, T, t.c, raw, red, NoMid{});
+    if (st == 0) stream_row<DT, VP, TR>(a, t.b, t.j, d, T, t.c, raw, red, hs, NoMid{});
   }
 }
 
@@ -287,28 +344,34 @@ inline void set_row_groups(Args& a) {
   a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
 }
 
-template <int DT, bool VP>
+template <int DT, bool VP, bool TR>
 int launch_stream_t(const Args& a, hipStream_t s) {
   if (a.B <= kPlanMaxB) {
-    hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP>),
+    hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP, TR>),
                        dim3((unsigned)(a.B * a.nchunks)), dim3(kThreads), 0, s, a);
     return check_launch("spec_stream");
   }
   const int64_t grid = (int64_t)a.B * a.nchunks * a.ngroups;
   if (grid > INT_MAX) return set_error(SS_EINVAL, "spec_stream: grid too large");
-  hipLaunchKernelGGL((spec_stream_kernel<DT, VP>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((spec_stream_kernel<DT, VP, TR>), dim3((unsigned)grid),
                      dim3(kThreads), 0, s, a);
   return check_launch("spec_stream");
+}
+
+template <int DT, bool VP>
+int launch_stream_tr(const Args& a, hipStream_t s) {
+  return a.hist ? launch_stream_t<DT, VP, true>(a, s)
+                : launch_stream_t<DT, VP, false>(a, s);
 }
 
 }  // namespace
 
 int launch_stream(Args a, bool f32, bool vp, hipStream_t s) {
   set_row_groups(a);
-  return f32 ? (vp ? launch_stream_t<SS_DTYPE_F32, true>(a, s)
-                   : launch_stream_t<SS_DTYPE_F32, false>(a, s))
-             : (vp ? launch_stream_t<SS_DTYPE_BF16, true>(a, s)
-                   : launch_stream_t<SS_DTYPE_BF16, false>(a, s));
+  return f32 ? (vp ? launch_stream_tr<SS_DTYPE_F32, true>(a, s)
+                   : launch_stream_tr<SS_DTYPE_F32, false>(a, s))
+             : (vp ? launch_stream_tr<SS_DTYPE_BF16, true>(a, s)
+                   : launch_stream_tr<SS_DTYPE_BF16, false>(a, s));
 }
 
 }  // namespace specsam

@@ -1,0 +1,516 @@
+// Truncation of the target distribution before verification: top-k, then
+// top-p on what top-k kept, then renormalisation ([P3] gogongxt notes
+// "SGLang 的实现": the target probabilities pass through a top-k and a top-p
+// renormalisation, with one value of each per request, before the
+// speculative-sampling kernel). Read as: top-k keeps every token whose logit
+// is at least the k-th largest (tied tokens kept); top-p keeps whole groups of
+// equal logits from the top until the kept share of what top-k kept reaches
+// top_p. A row's truncation is then one threshold logit: keep l >= threshold.
+//
+// Design for gfx950. Finding the k-th largest logit, or the logit where the
+// running probability crosses top_p, is a selection over V values per row.
+// Sorting a 152k-entry row, or a radix select that re-reads it once per
+// digit, would cost several passes over HBM. Here the row is read twice:
+//   stream  (stream.hip, truncated rows only) counts each chunk's logits, and
+//           sums their probability, in a 256-bin window histogram on a grid
+//           shared by all chunks of the row (1/8 octave of probability per
+//           bin, 32 octaves below the chunk max);
+//   plan    (one workgroup per row) merges the row's chunk histograms, scans
+//           them from the top and picks the bin range that must hold the
+//           threshold (with a margin for the histogram's rounding);
+//   extract (one workgroup per row chunk) re-reads the chunk, sums the exact
+//           probability of its tokens above the range and appends the tokens
+//           inside the range to the row's candidate list;
+//   select  (one workgroup per row) finds the exact threshold among the
+//           candidates by radix selection on order-preserving keys (8-bit
+//           digits, LDS histograms of counts for top-k and of probability
+//           for top-p), then adds the kept candidates' probability to their
+//           chunks' sums.
+// The finalize kernel then judges and draws with the per-chunk kept sums and
+// the threshold. A row with more than kCandCap candidates (its logits crowd
+// into a few bins; the list holds min(kCandCap, V) per row) is selected by
+// scanning the row itself in each round: exact, but slower.
+#include "verify_common.h"
+
+namespace specsam {
+namespace {
+
+constexpr float kPlanMargin = 1e-4f;  // relative slack for histogram rounding
+constexpr int kKeepAll = INT_MAX;     // range start when nothing is dropped
+
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (l == 0) scratch[w] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < kWaves; ++i) t += scratch[i];
+  return t;
+}
+
+// Row-level activity of truncation; the same test in every kernel.
+struct RowCtx {
+  int b, j, d;
+  float T, kk;
+  bool active;
+};
+
+__device__ __forceinline__ RowCtx row_ctx(const Args& a, int64_t row) {
+  RowCtx r;
+  const int R = a.K + 1;
+  r.b = (int)(row / R);
+  r.j = (int)(row - (int64_t)r.b * R);
+  const int st = seq_check(a, r.b, &r.d, &r.T);
+  r.active = st == 0 && r.j <= r.d && trunc_active(a, r.b, r.T);
+  r.kk = r.active ? kLog2e / r.T : 0.0f;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// plan: one workgroup per row; thread r owns bin r of the row window.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
+  __shared__ int s_a[kMaxChunks];
+  __shared__ float s_pm[kMaxChunks];
+  __shared__ float scratch[kWaves];
+  __shared__ float wtot[2][kWaves];
+  __shared__ int first[3];
+  __shared__ float zval[2];
+  __shared__ int cabove;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int64_t row = blockIdx.x;
+  const RowCtx rc = row_ctx(a, row);
+  if (!rc.active) return;
+  const int nc = a.nchunks;
+  const int64_t h0 = row * nc;
+  for (int c = tid; c < nc; c += kThreads) {
+    s_a[c] = a.hhdr[h0 + c].x;
+    s_pm[c] = a.partials[h0 + c].x;
+  }
+  if (tid < 3) first[tid] = kRestBin;
+  if (tid == 0) cabove = 0;
+  __syncthreads();
+  float m = kNegInf;
+  for (int c = 0; c < nc; ++c) m = fmaxf(m, s_pm[c]);
+  const int a0 = abs_bin(m, rc.kk);
+  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c.
+  float cnt = 0.0f, mass = 0.0f, tcnt = 0.0f, tmass = 0.0f;
+  for (int c = 0; c < nc; ++c) {
+    const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
+    const unsigned long long* hc = a.hist + (h0 + c) * kHistBins;
+    const unsigned long long wt = hc[tid];
+    tcnt += (float)(unsigned)(wt >> 48);
+    tmass += (float)(wt & kMassMask) * sc;
+    const int jb = tid - (s_a[c] - a0);
+    if (jb >= 0 && jb < kHistBins) {
+      const unsigned long long wb = hc[jb];
+      cnt += (float)(unsigned)(wb >> 48);
+      mass += (float)(wb & kMassMask) * sc;
+    }
+    if (tid == 0) {
+      const i32x4 hh = a.hhdr[h0 + c];
+      const unsigned long long r =
+          ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
+      tcnt += (float)(unsigned)(r >> 48);
+      tmass += (float)(r & kMassMask) * sc;
+    }
+  }
+  const float N = block_sum(tcnt, scratch);  // finite tokens (exact: < 2^24)
+  const float Z = block_sum(tmass, scratch);
+  // Inclusive scans of counts and masses from the top bin down.
+  float C = wave_inclusive_sum(cnt), M = wave_inclusive_sum(mass);
+  if (l == kWave - 1) {
+    wtot[0][w] = C;
+    wtot[1][w] = M;
+  }
+  __syncthreads();
+  for (int i = 0; i < w; ++i) {
+    C += wtot[0][i];
+    M += wtot[1][i];
+  }
+  const int k = a.top_k ? a.top_k[rc.b] : 0;
+  const float tp = a.top_p ? a.top_p[rc.b] : 1.0f;
+  const bool kA = k >= 1 && k < a.V && (float)k <= N;
+  const bool pA = tp < 1.0f;
+  if (kA && C >= (float)k) atomicMin(&first[0], tid);
+  __syncthreads();
+  const int bk = kA ? first[0] : kRestBin;
+  // Mass above bin bk (Z_lo) and through it (Z_hi): top-p's share is taken of
+  // what top-k kept, which lies between the two.
+  if (tid == 0) {
+    zval[0] = 0.0f;
+    zval[1] = Z;
+  }
+  __syncthreads();
+  if (kA) {
+    if (tid == bk - 1) zval[0] = M;
+    if (tid == bk) zval[1] = M;
+  } else if (tid == 0) {
+    zval[0] = Z;
+  }
+  __syncthreads();
+  if (pA) {
+    const float tlo = tp * zval[0] * (1.0f - kPlanMargin);
+    const float thi = tp * zval[1] * (1.0f + kPlanMargin);
+    if (M >= tlo) atomicMin(&first[1], tid);
+    if (M >= thi) atomicMin(&first[2], tid);
+  }
+  __syncthreads();
+  // Candidate range [rlo, rhi]. Top-k's own bin is always in it (the k-th
+  // largest logit, and the share top-k keeps, are found among its tokens);
+  // top-p's threshold lies between the bins its two targets reach.
+  int rlo, rhi;
+  if (!kA && !pA) {
+    rlo = rhi = kKeepAll;  // nothing to drop
+  } else if (!pA) {
+    rlo = rhi = bk;
+  } else if (!kA) {
+    rlo = first[1];
+    rhi = first[2];
+  } else {
+    rlo = min(first[1], bk);
+    rhi = bk;
+  }
+  // Tokens above the range: the running count at bin rlo - 1.
+  if (rlo >= 1 && rlo <= kRestBin && tid == rlo - 1) cabove = (int)C;
+  __syncthreads();
+  if (tid == 0) {
+    a.ccount[row] = 0;
+    a.plan[row * 2] = i32x4{a0, rlo, rhi, cabove};
+    a.plan[row * 2 + 1] =
+        i32x4{(kA ? 1 : 0) | (pA ? 2 : 0), k - cabove, __float_as_int(m), 0};
+  }
+}
+
+// Range test of a token's row bin rb against [rlo, rhi] (rhi = kRestBin:
+// unbounded below the window).
+__device__ __forceinline__ bool in_range(int rb, int rlo, int rhi) {
+  return rb >= rlo && (rhi >= kRestBin || rb <= rhi);
+}
+
+// ---------------------------------------------------------------------------
+// extract: one workgroup per (row, chunk).
+// ---------------------------------------------------------------------------
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
+  __shared__ float scratch[kWaves];
+  __shared__ int woff[kWaves + 1];
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int nc = a.nchunks;
+  const int64_t row = blockIdx.x / nc;
+  const int c = (int)(blockIdx.x - row * nc);
+  const RowCtx rc = row_ctx(a, row);
+  if (!rc.active) return;
+  const int cstart = c * kChunk<DT>;
+  u32x4 raw[kLoads];
+  load_chunk<DT, VP, false>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid,
+                            raw);
+  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
+  const int a0 = p0.x, rlo = p0.y, rhi = p0.z;
+  const float m = __int_as_float(p1.z);
+  float above = 0.0f;
+  int n = 0;
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k) {
+      const float v = elem<DT>(raw[it], k);
+      if (v > kNegInf) {
+        const int rb = abs_bin(v, rc.kk) - a0;
+        if (rb < rlo)
+          above += fast_exp2((v - m) * rc.kk);
+        else if (in_range(rb, rlo, rhi))
+          ++n;
+      }
+    }
+  above = block_sum(above, scratch);
+  if (tid == 0) a.tpart[row * nc + c] = above;
+  // Candidates: a block-wide exclusive scan of the per-thread counts, one
+  // atomic per workgroup to reserve room in the row's list.
+  const int inc = (int)wave_inclusive_sum((float)n);
+  if (l == kWave - 1) woff[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      const int v = woff[i];
+      woff[i] = t;
+      t += v;
+    }
+    woff[kWaves] = t ? atomicAdd(&a.ccount[row], t) : 0;
+  }
+  __syncthreads();
+  if (n == 0) return;
+  int pos = woff[kWaves] + woff[w] + inc - n;
+  int2* out = a.cand + row * a.ccap;
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k) {
+      const float v = elem<DT>(raw[it], k);
+      if (v > kNegInf) {
+        const int rb = abs_bin(v, rc.kk) - a0;
+        if (rb >= rlo && in_range(rb, rlo, rhi)) {
+          if (pos < a.ccap)
+            out[pos] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
+          ++pos;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// select: one workgroup per row.
+// ---------------------------------------------------------------------------
+struct SelShared {
+  float cl[kCandCap];
+  int ci[kCandCap];
+  unsigned cnt[256];
+  float mass[256];
+  float csum[kMaxChunks];
+  float scratch[kWaves];
+  int digit;
+  float carry;
+  unsigned minkey;
+};
+
+// Candidates of a row: from LDS when they fit, else by re-reading the row and
+// filtering it by the plan's range (exact, one pass over the row per call).
+template <int DT, bool VP>
+struct CandSource {
+  const Args* a;
+  SelShared* sh;
+  int64_t row;
+  int n, a0, rlo, rhi;
+  float kk;
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+    const int tid = threadIdx.x;
+    if (n <= a->ccap) {
+      for (int i = tid; i < n; i += kThreads) f(sh->cl[i], sh->ci[i]);
+      return;
+    }
+    const unsigned char* rowp = a->logits + row * a->V * Dt<DT>::kBytes;
+    for (int c = 0; c < a->nchunks; ++c) {
+      const int cstart = c * kChunk<DT>;
+      u32x4 raw[kLoads];
+      load_chunk<DT, VP, false>(rowp, cstart, a->V, tid, raw);
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) {
+          const float v = elem<DT>(raw[it], k);
+          if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi))
+            f(v, elem_index<DT, VP>(cstart, tid, it, k));
+        }
+    }
+  }
+};
+
+// Wavefront 0 scans the 256 digit buckets from digit 255 down (lane L holds
+// digits 255-4L .. 252-4L) and returns, in sh.digit, the first digit whose
+// running total reaches t, and in sh.carry the total of the digits above it
+// (-1 when the buckets sum to less than t).
+__device__ __forceinline__ void scan_digits(SelShared& sh, float t, bool by_mass) {
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int dg = 255 - 4 * tid - q;
+      v[q] = by_mass ? sh.mass[dg] : (float)sh.cnt[dg];
+    }
+    const float lane = v[0] + v[1] + v[2] + v[3];
+    const float inc = wave_inclusive_sum(lane);
+    const unsigned long long hit = __ballot(inc >= t);
+    if (hit) {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      if (tid == L) {
+        float run = inc - lane;
+        int q = 0;
+        for (; q < 3; ++q) {
+          if (run + v[q] >= t) break;
+          run += v[q];
+        }
+        sh.digit = 255 - 4 * L - q;
+        sh.carry = run;
+      }
+    } else if (tid == 0) {
+      sh.digit = -1;
+      sh.carry = 0.0f;
+    }
+  }
+  __syncthreads();
+}
+
+// Key of the kth largest candidate (1-based; kth <= the candidate count).
+template <typename Src>
+__device__ unsigned select_kth(const Src& src, SelShared& sh, int kth) {
+  const int tid = threadIdx.x;
+  unsigned prefix = 0, mask = 0;
+  float need = (float)kth;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.cnt[tid] = 0;
+    __syncthreads();
+    src.each([&](float v, int) {
+      const unsigned key = fkey(v);
+      if ((key & mask) == prefix) atomicAdd(&sh.cnt[(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    scan_digits(sh, need, false);
+    const int dg = sh.digit < 0 ? 0 : sh.digit;
+    need -= sh.carry;
+    prefix |= (unsigned)dg << shift;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Largest key K >= kmin such that the candidates with keys in [K, inf) carry
+// at least t of probability; the smallest candidate key >= kmin when rounding
+// leaves the candidates short of t.
+template <typename Src>
+__device__ unsigned select_mass(const Src& src, SelShared& sh, float t, unsigned kmin,
+                                float m, float kk) {
+  const int tid = threadIdx.x;
+  unsigned prefix = 0, mask = 0;
+  bool found = true;
+  for (int shift = 24; shift >= 0 && found; shift -= 8) {
+    sh.mass[tid] = 0.0f;
+    __syncthreads();
+    src.each([&](float v, int) {
+      const unsigned key = fkey(v);
+      if (key >= kmin && (key & mask) == prefix)
+        atomicAdd(&sh.mass[(key >> shift) & 255u], fast_exp2((v - m) * kk));
+    });
+    __syncthreads();
+    scan_digits(sh, t, true);
+    if (sh.digit < 0) {
+      found = false;
+    } else {
+      t -= sh.carry;
+      prefix |= (unsigned)sh.digit << shift;
+      mask |= 255u << shift;
+    }
+    __syncthreads();
+  }
+  if (found) return prefix;
+  if (tid == 0) sh.minkey = 0xffffffffu;
+  __syncthreads();
+  src.each([&](float v, int) {
+    const unsigned key = fkey(v);
+    if (key >= kmin) atomicMin(&sh.minkey, key);
+  });
+  __syncthreads();
+  return sh.minkey;
+}
+
+template <int DT, bool VP>
+__global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const RowCtx rc = row_ctx(a, row);
+  if (!rc.active) return;
+  const int nc = a.nchunks;
+  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
+  const int mode = p1.x, krem = p1.y;
+  const float m = __int_as_float(p1.z);
+  const int n = a.ccount[row];
+  // Probability above the range: every token there is kept.
+  float base = 0.0f;
+  for (int c = tid; c < nc; c += kThreads) base += a.tpart[row * nc + c];
+  base = block_sum(base, sh.scratch);
+  if (mode == 0) {
+    if (tid == 0) a.tinfo[row] = f32x4{kNegInf, base, 1.0f, 0.0f};
+    return;
+  }
+  if (n <= a.ccap) {
+    const int2* in = a.cand + row * a.ccap;
+    for (int i = tid; i < n; i += kThreads) {
+      const int2 e = in[i];
+      sh.cl[i] = __int_as_float(e.x);
+      sh.ci[i] = e.y;
+    }
+  }
+  for (int c = tid; c < nc; c += kThreads) sh.csum[c] = 0.0f;
+  __syncthreads();
+  const CandSource<DT, VP> src{&a, &sh, row, n, p0.x, p0.y, p0.z, rc.kk};
+  unsigned kmin = 0;
+  if (mode & 1) kmin = select_kth(src, sh, krem);
+  unsigned key = kmin;
+  if (mode & 2) {
+    // top-p's share is of what top-k kept: with top-k, base plus the
+    // candidates at or above kmin (everything below the range is below the
+    // k-th largest); without, the whole row (from the stream partials).
+    float zk = 0.0f;
+    if (mode & 1) {
+      src.each([&](float v, int) {
+        if (fkey(v) >= kmin) zk += fast_exp2((v - m) * rc.kk);
+      });
+      zk = base + block_sum(zk, sh.scratch);
+    } else {
+      for (int c = tid; c < nc; c += kThreads) {
+        const f32x4 p = a.partials[row * nc + c];
+        zk += p.y * fast_exp2((p.x - m) * rc.kk);
+      }
+      zk = block_sum(zk, sh.scratch);
+    }
+    const float t = a.top_p[rc.b] * zk - base;
+    if (t > 0.0f) {
+      key = select_mass(src, sh, t, kmin, m, rc.kk);
+    } else {
+      // The range is chosen so that this does not happen (the share above
+      // it stays below top_p); keep the top candidate group if it does.
+      if (tid == 0) sh.minkey = 0;
+      __syncthreads();
+      src.each([&](float v, int) { atomicMax(&sh.minkey, fkey(v)); });
+      __syncthreads();
+      key = sh.minkey;
+    }
+  }
+  // Kept candidates: their probability, per chunk.
+  src.each([&](float v, int i) {
+    if (fkey(v) >= key)
+      atomicAdd(&sh.csum[i / kChunk<DT>], fast_exp2((v - m) * rc.kk));
+  });
+  __syncthreads();
+  float kept = 0.0f;
+  for (int c = tid; c < nc; c += kThreads) {
+    const float t = a.tpart[row * nc + c] + sh.csum[c];
+    a.tpart[row * nc + c] = t;
+    kept += t;
+  }
+  kept = block_sum(kept, sh.scratch);
+  if (tid == 0) a.tinfo[row] = f32x4{fkey_inv(key), kept, 1.0f, 0.0f};
+}
+
+template <int DT, bool VP>
+int launch_t(const Args& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * (a.K + 1);
+  hipLaunchKernelGGL(trunc_plan_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, a);
+  int rc = check_launch("truncation plan");
+  if (rc != SS_OK) return rc;
+  const int64_t grid = rows * a.nchunks;
+  if (grid > INT_MAX) return set_error(SS_EINVAL, "truncation: grid too large");
+  hipLaunchKernelGGL((trunc_extract_kernel<DT, VP>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, a);
+  rc = check_launch("truncation extract");
+  if (rc != SS_OK) return rc;
+  hipLaunchKernelGGL((trunc_select_kernel<DT, VP>), dim3((unsigned)rows),
+                     dim3(kThreads), 0, s, a);
+  return check_launch("truncation select");
+}
+
+}  // namespace
+
+int launch_truncation(const Args& a, bool f32, bool vp, hipStream_t s) {
+  return f32 ? (vp ? launch_t<SS_DTYPE_F32, true>(a, s)
+                   : launch_t<SS_DTYPE_F32, false>(a, s))
+             : (vp ? launch_t<SS_DTYPE_BF16, true>(a, s)
+                   : launch_t<SS_DTYPE_BF16, false>(a, s));
+}
+
+}  // namespace specsam

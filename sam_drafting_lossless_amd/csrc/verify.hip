@@ -108,14 +108,17 @@ struct DrawShared {
   float result_l;  // the drawn token's logit (NaN if the draw did not see it)
 };
 
-// Weight of element k of raw vector `it` (token index i).
+// Weight of a token with logit l (token index i); tokens below the
+// truncation threshold lam have probability 0.
 template <int DT, bool RESIDUAL>
 __device__ __forceinline__ float draw_weight(float l, int i, int excl, float m,
-                                             float kk, float invS, float qi) {
+                                             float kk, float invS, float qi,
+                                             float lam) {
+  const float w = (l >= lam) ? fast_exp2((l - m) * kk) : 0.0f;
   if constexpr (RESIDUAL)
-    return fmaxf(0.0f, fast_exp2((l - m) * kk) * invS - qi);
+    return fmaxf(0.0f, w * invS - qi);
   else
-    return (i == excl) ? 0.0f : fast_exp2((l - m) * kk);
+    return (i == excl) ? 0.0f : w;
 }
 
 // q values for the kVec elements of one raw vector (RESIDUAL only).
@@ -165,7 +168,7 @@ __device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick
 template <int DT, bool VP, bool RESIDUAL, typename During = NoDuring>
 __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
                              ChunkPick pk, int excl, float m, float kk,
-                             float invS, const u32x4 (&raw)[kLoads],
+                             float invS, float lam, const u32x4 (&raw)[kLoads],
                              During during = During{}) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   during();
@@ -183,7 +186,8 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
     for (int k = 0; k < kVec<DT>; ++k) {
       const int i = elem_index<DT, VP>(cstart, tid, it, k);
       const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
-                                                 kk, invS, RESIDUAL ? qv[k] : 0.0f);
+                                                 kk, invS, RESIDUAL ? qv[k] : 0.0f,
+                                                 lam);
       acc += wk;
       if (wk > 0.0f) tlast = max(tlast, i);
     }
@@ -251,7 +255,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
         const int i = elem_index<DT, VP>(cstart, tid, its, k);
         const float lk = elem<DT>(rv, k);
         const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
-                                                   RESIDUAL ? qv[k] : 0.0f);
+                                                   RESIDUAL ? qv[k] : 0.0f, lam);
         run += wk;
         if (wk > 0.0f) {
           lastp = i;
@@ -276,7 +280,9 @@ constexpr int kPartialCache = 1024;
 struct FinalShared {
   f32x4 pc[kPartialCache];
   float m[kMaxRows];
-  float s[kMaxRows];
+  float s[kMaxRows];         // sum of the weights the row's decisions use
+  float su[kMaxRows];        // untruncated sum (log-probabilities)
+  float lam[kMaxRows];       // truncation threshold (-inf: none)
   float lx[kMaxRows];
   float u[kMaxRows];
   int idx[kMaxRows];
@@ -352,6 +358,9 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   }
   const bool greedy = (T == 0.0f);
   const float kk = greedy ? 0.0f : kLog2e / T;
+  // Truncated target (top-k / top-p): the truncation passes left each row's
+  // threshold and its kept probability per chunk.
+  const bool trunc = a.tinfo != nullptr && trunc_active(a, b, T);
   // q at each draft token (1 for one-hot drafts), gathered while the rows
   // are combined so that the accept scan reads only LDS.
   if constexpr (Q) {
@@ -401,19 +410,34 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         wave_lse(m, s, kk);
         const unsigned long long hb = __ballot(has);
         if (hb) lxv = readlane_f(lxv, __ffsll((unsigned long long)hb) - 1);
+        const int64_t rw = (int64_t)b * R + j;
+        float lam = kNegInf, st = s;
+        if (trunc) {
+          lam = a.tinfo[rw].x;
+          st = 0.0f;
+          for (int c = l; c < nc; c += kWave) st += a.tpart[rw * nc + c];
+          st = wave_sum(st);
+        }
         // Where a draw at this row would land: x_j (j < d) is removed from
         // its chunk's weight for the one-hot residual; row d is the bonus.
-        const float wx = (j < d && hb) ? fast_exp2((lxv - m) * kk) : 0.0f;
+        const float wx = (j < d && hb && lxv >= lam) ? fast_exp2((lxv - m) * kk) : 0.0f;
         const int cxw = (j < d) ? cx : -1;
         const float uK = sh.u[a.K];
         const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
-          const f32x4 p = part(j, c);
-          const float W = p.y * fast_exp2((p.x - m) * kk);
+          float W;
+          if (trunc) {
+            W = a.tpart[rw * nc + c];
+          } else {
+            const f32x4 p = part(j, c);
+            W = p.y * fast_exp2((p.x - m) * kk);
+          }
           return c == cxw ? fmaxf(0.0f, W - wx) : W;
         });
         if (l == 0) {
           sh.m[j] = m;
-          sh.s[j] = s;
+          sh.s[j] = st;
+          sh.su[j] = s;
+          sh.lam[j] = lam;
           sh.lx[j] = lxv;
           sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
           sh.pick[j] = pk;
@@ -456,7 +480,9 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         if (greedy) {
           acc = (x == sh.idx[l]);
         } else {
-          px = fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l];
+          px = (sh.lx[l] >= sh.lam[l])
+                   ? fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l]
+                   : 0.0f;
           const float qx = Q ? sh.qx[l] : 1.0f;
           acc = (qx > 0.0f) ? (sh.u[l] <= px / qx) : (px > 0.0f);
         }
@@ -484,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         if (greedy && l <= al)
           lp = -logf(sh.s[l]);
         else if (!greedy && l < al)
-          lp = ((sh.lx[l] - sh.m[l]) * kk - log2f(sh.s[l])) * kLn2;
+          lp = ((sh.lx[l] - sh.m[l]) * kk - log2f(sh.su[l])) * kLn2;
         if (greedy || l != al) a.logprob[(int64_t)b * R + l] = lp;
       }
       if (l == 0) {
@@ -497,10 +523,13 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   __syncthreads();
   const int al = sh.acc_len;
   const bool residual = Q && sh.st == 0 && !greedy && al < d;
-  if (tid == 0)
+  if (tid == 0) {
     a.seqinfo[b] = residual ? i32x4{al + 1, __float_as_int(sh.m[al]),
                                     __float_as_int(sh.s[al]), __float_as_int(kk)}
                             : i32x4{0, 0, 0, 0};
+    if (residual)
+      a.seqinfo2[b] = f32x4{sh.lam[al], sh.su[al], trunc ? 1.0f : 0.0f, 0.0f};
+  }
   // Automaton step (wavefront 0): the emitted tokens sh.tok[0..al] are
   // appended in order; when a token is drawn, the accepted drafts before it
   // are appended while the draw's chunk is in flight.
@@ -521,14 +550,14 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
       }
     };
     const int tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, sh.pick[al],
-                                                 excl, sh.m[al], kk, 0.0f, raw,
-                                                 during);
+                                                 excl, sh.m[al], kk, 0.0f, sh.lam[al],
+                                                 raw, during);
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
       if (a.logprob)
         a.logprob[(int64_t)b * R + al] =
-            drawn_logprob<DT>(a, b, al, tok, sh.draw.result_l, sh.m[al], sh.s[al], kk);
+            drawn_logprob<DT>(a, b, al, tok, sh.draw.result_l, sh.m[al], sh.su[al], kk);
     }
     __syncthreads();
   }
@@ -558,6 +587,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
   const int r = info.x - 1;
   const float m = __int_as_float(info.y), S = __int_as_float(info.z);
   const float kk = __int_as_float(info.w);
+  const float lam = a.seqinfo2[b].x;
   const float invS = 1.0f / S;
   const int R = a.K + 1;
   const int cstart = c * kChunk<DT>;
@@ -577,18 +607,22 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
           const f32x4 qv = __builtin_nontemporal_load(
               reinterpret_cast<const f32x4*>(qrow + i0) + h);
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            s += fmaxf(0.0f, fast_exp2((elem<DT>(raw[it], 4 * h + k) - m) * kk) *
-                                     invS - qv[k]);
+          for (int k = 0; k < 4; ++k) {
+            const float v = elem<DT>(raw[it], 4 * h + k);
+            const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
+            s += fmaxf(0.0f, wv * invS - qv[k]);
+          }
         }
       }
     } else {
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
         const int i = elem_index<DT, false>(cstart, tid, it, k);
-        if (i < a.V)
-          s += fmaxf(0.0f, fast_exp2((elem<DT>(raw[it], k) - m) * kk) * invS -
-                               qrow[i]);
+        if (i < a.V) {
+          const float v = elem<DT>(raw[it], k);
+          const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
+          s += fmaxf(0.0f, wv * invS - qrow[i]);
+        }
       }
     }
   }
@@ -615,6 +649,9 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   const int r = info.x - 1;
   const float m = __int_as_float(info.y), S = __int_as_float(info.z);
   const float kk = __int_as_float(info.w);
+  const f32x4 info2 = a.seqinfo2[b];
+  const float lam = info2.x, Su = info2.y;
+  const bool trunc = info2.z != 0.0f;
   const int R = a.K + 1;
   if (w == 0) {
     const float u = a.uniforms[(int64_t)b * R + a.K];
@@ -623,8 +660,10 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
     // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
     const bool fallback = pk.chunk < 0;
     if (fallback) {
-      const f32x4* Pr = a.partials + ((int64_t)b * R + r) * nc;
+      const int64_t rw = (int64_t)b * R + r;
+      const f32x4* Pr = a.partials + rw * nc;
       pk = pick_chunk(nc, u, [&](int c) {
+        if (trunc) return load_f32(a.tpart + rw * nc + c);
         const f32x4 p = load_partial(Pr + c);
         return p.y * fast_exp2((p.x - m) * kk);
       });
@@ -638,13 +677,14 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   u32x4 raw[kLoads];
   draw_load<DT, VP>(a, b, r, pick_sh, raw);
   const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, -1, m,
-                                                        kk, 0.0f, raw)
+                                                        kk, 0.0f, lam, raw)
                          : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, -1, m,
-                                                       kk, 1.0f / S, raw);
+                                                       kk, 1.0f / S, lam, raw);
   if (tid == 0) {
     a.out[(int64_t)b * R + r] = tok;
     if (a.logprob)
-      a.logprob[(int64_t)b * R + r] = drawn_logprob<DT>(a, b, r, tok, dsh.result_l, m, S, kk);
+      a.logprob[(int64_t)b * R + r] =
+          drawn_logprob<DT>(a, b, r, tok, dsh.result_l, m, Su, kk);
   }
 }
 
@@ -652,7 +692,10 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
 // Workspace layout (bytes, each region 256-byte aligned).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t partials, seqinfo, rpart, total;
+  size_t partials, seqinfo, seqinfo2, rpart;
+  // truncation (top-k / top-p) regions; zero-sized without it
+  size_t hist, hhdr, plan, ccount, cand, tpart, tinfo;
+  size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -662,16 +705,27 @@ inline int nchunks_for(int V, int dtype) {
   return (V + ch - 1) / ch;
 }
 
-WsLayout ws_layout(int B, int K, int V) {
+WsLayout ws_layout(int B, int K, int V, bool trunc) {
   const size_t nc = (size_t)nchunks_for(V, SS_DTYPE_F32);  // the larger count
+  const size_t rows = (size_t)B * (K + 1);
   WsLayout L;
   size_t o = 0;
-  L.partials = o;
-  o = align256(o + (size_t)B * (K + 1) * nc * sizeof(f32x4));
-  L.seqinfo = o;
-  o = align256(o + (size_t)B * sizeof(i32x4));
-  L.rpart = o;
-  o = align256(o + (size_t)B * nc * sizeof(float));
+  auto take = [&](size_t& at, size_t bytes) {
+    at = o;
+    o = align256(o + bytes);
+  };
+  take(L.partials, rows * nc * sizeof(f32x4));
+  take(L.seqinfo, (size_t)B * sizeof(i32x4));
+  take(L.seqinfo2, (size_t)B * sizeof(f32x4));
+  take(L.rpart, (size_t)B * nc * sizeof(float));
+  const size_t t = trunc ? 1 : 0;
+  take(L.hist, t * rows * nc * kHistBins * sizeof(unsigned long long));
+  take(L.hhdr, t * rows * nc * sizeof(i32x4));
+  take(L.plan, t * rows * 2 * sizeof(i32x4));
+  take(L.ccount, t * rows * sizeof(int));
+  take(L.cand, t * rows * std::min(kCandCap, V) * sizeof(int2));
+  take(L.tpart, t * rows * nc * sizeof(float));
+  take(L.tinfo, t * rows * sizeof(f32x4));
   L.total = o;
   return L;
 }
@@ -701,7 +755,8 @@ enum Passes { kStream = 1, kFinish = 2 };
 
 int run(int passes, const void* logits, int dtype, int B, int K, int V,
         const int32_t* draft, const int32_t* draft_len, const float* q,
-        const float* temperature, const float* uniforms, int32_t* out_tokens,
+        const float* temperature, const float* uniforms, const int32_t* top_k,
+        const float* top_p, int32_t* out_tokens,
         int32_t* num_emitted, float* p_draft, float* logprob, int32_t* status,
         void* workspace, size_t ws_bytes, void* sam_state, int max_len,
         int32_t* next_draft,
@@ -733,10 +788,14 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
       return set_error(SS_EINVAL, "%s: next-draft outputs must not alias the "
                                   "drafts being verified", fn);
   }
-  const WsLayout L = ws_layout(B, K, V);
+  const bool trunc = top_k != nullptr || top_p != nullptr;
+  const WsLayout L = ws_layout(B, K, V, trunc);
   if (ws_bytes < L.total)
-    return set_error(SS_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn,
-                     ws_bytes, L.total);
+    return set_error(SS_EWORKSPACE,
+                     "%s: workspace %zu < %zu bytes%s", fn, ws_bytes, L.total,
+                     trunc ? " (top_k / top_p need ss_verify_workspace_bytes_ex "
+                             "with SS_WS_TRUNCATION)"
+                           : "");
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
   Args a;
   a.logits = reinterpret_cast<const unsigned char*>(logits);
@@ -753,10 +812,21 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.nem = num_emitted;
   a.p_draft = p_draft;
   a.logprob = logprob;
+  a.top_k = top_k;
+  a.top_p = top_p;
   a.status = status;
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
+  a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
+  a.hist = trunc ? reinterpret_cast<unsigned long long*>(ws + L.hist) : nullptr;
+  a.hhdr = trunc ? reinterpret_cast<i32x4*>(ws + L.hhdr) : nullptr;
+  a.plan = trunc ? reinterpret_cast<i32x4*>(ws + L.plan) : nullptr;
+  a.ccount = trunc ? reinterpret_cast<int*>(ws + L.ccount) : nullptr;
+  a.cand = trunc ? reinterpret_cast<int2*>(ws + L.cand) : nullptr;
+  a.ccap = std::min(kCandCap, V);
+  a.tpart = trunc ? reinterpret_cast<float*>(ws + L.tpart) : nullptr;
+  a.tinfo = trunc ? reinterpret_cast<f32x4*>(ws + L.tinfo) : nullptr;
   a.sam = reinterpret_cast<unsigned char*>(sam_state);
   a.max_len = max_len;
   a.sl = sam_layout(max_len > 0 ? max_len : 1);
@@ -774,6 +844,10 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
     if (rc != SS_OK) return rc;
   }
   if (passes & kFinish) {
+    if (trunc) {
+      rc = launch_truncation(a, f32, vp, s);
+      if (rc != SS_OK) return rc;
+    }
     if (sam_state)
       rc = f32 ? (vp ? launch_finish<SS_DTYPE_F32, true, true>(a, s)
                      : launch_finish<SS_DTYPE_F32, false, true>(a, s))
@@ -793,27 +867,34 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
 
 using namespace specsam;
 
-extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
+extern "C" size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags) {
   if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV) return 0;
-  return ws_layout(B, K, V).total;
+  if (flags & ~SS_WS_TRUNCATION) return 0;
+  return ws_layout(B, K, V, (flags & SS_WS_TRUNCATION) != 0).total;
+}
+
+extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
+  return ss_verify_workspace_bytes_ex(B, K, V, 0);
 }
 
 extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,
                            const int32_t* draft, const int32_t* draft_len,
                            const float* q, const float* temperature,
-                           const float* uniforms, int32_t* out_tokens,
+                           const float* uniforms, const int32_t* top_k,
+                           const float* top_p, int32_t* out_tokens,
                            int32_t* num_emitted, float* p_draft, float* logprobs,
                            int32_t* status, void* workspace, size_t ws_bytes,
                            void* stream) {
   return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len, q,
-             temperature, uniforms, out_tokens, num_emitted, p_draft, logprobs,
-             status, workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr,
-             stream, "spec_verify");
+             temperature, uniforms, top_k, top_p, out_tokens, num_emitted, p_draft,
+             logprobs, status, workspace, ws_bytes, nullptr, 0, nullptr, nullptr,
+             nullptr, stream, "spec_verify");
 }
 
 extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
                          const int32_t* draft, const int32_t* draft_len,
                          const float* temperature, const float* uniforms,
+                         const int32_t* top_k, const float* top_p,
                          void* sam_state, int max_len, int32_t* out_tokens,
                          int32_t* num_emitted, float* p_draft, float* logprobs,
                          int32_t* status, int32_t* next_draft,
@@ -822,32 +903,34 @@ extern "C" int spec_step(const void* logits, int dtype, int B, int K, int V,
   if (!sam_state)
     return set_error(SS_EINVAL, "spec_step: state is NULL");
   return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len,
-             nullptr, temperature, uniforms, out_tokens, num_emitted, p_draft,
-             logprobs, status, workspace, ws_bytes, sam_state, max_len, next_draft,
-             next_draft_len, next_match_len, stream, "spec_step");
+             nullptr, temperature, uniforms, top_k, top_p, out_tokens, num_emitted,
+             p_draft, logprobs, status, workspace, ws_bytes, sam_state, max_len,
+             next_draft, next_draft_len, next_match_len, stream, "spec_step");
 }
 
 extern "C" int spec_stream(const void* logits, int dtype, int B, int K, int V,
                            const int32_t* draft, const int32_t* draft_len,
                            const float* temperature, const float* uniforms,
+                           const int32_t* top_k, const float* top_p,
                            void* workspace, size_t ws_bytes, void* stream) {
   return run(kStream, logits, dtype, B, K, V, draft, draft_len, nullptr,
-             temperature, uniforms, nullptr, nullptr, nullptr, nullptr, nullptr,
-             workspace, ws_bytes, nullptr, 0, nullptr, nullptr, nullptr, stream,
-             "spec_stream");
+             temperature, uniforms, top_k, top_p, nullptr, nullptr, nullptr,
+             nullptr, nullptr, workspace, ws_bytes, nullptr, 0, nullptr, nullptr,
+             nullptr, stream, "spec_stream");
 }
 
 extern "C" int spec_finish(const void* logits, int dtype, int B, int K, int V,
                            const int32_t* draft, const int32_t* draft_len,
                            const float* q, const float* temperature,
-                           const float* uniforms, int32_t* out_tokens,
+                           const float* uniforms, const int32_t* top_k,
+                           const float* top_p, int32_t* out_tokens,
                            int32_t* num_emitted, float* p_draft, float* logprobs,
                            int32_t* status, void* sam_state, int max_len,
                            int32_t* next_draft, int32_t* next_draft_len,
                            int32_t* next_match_len, void* workspace,
                            size_t ws_bytes, void* stream) {
   return run(kFinish, logits, dtype, B, K, V, draft, draft_len, q, temperature,
-             uniforms, out_tokens, num_emitted, p_draft, logprobs, status,
-             workspace, ws_bytes, sam_state, max_len, next_draft, next_draft_len,
-             next_match_len, stream, "spec_finish");
+             uniforms, top_k, top_p, out_tokens, num_emitted, p_draft, logprobs,
+             status, workspace, ws_bytes, sam_state, max_len, next_draft,
+             next_draft_len, next_match_len, stream, "spec_finish");
 }

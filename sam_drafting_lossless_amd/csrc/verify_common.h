@@ -20,6 +20,22 @@ constexpr int kMaxChunks = kMaxV / (kChunkBytes / 4);  // 256 (fp32 chunks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
 
+// Truncation (top-k / top-p) of the target distribution.
+//   Window histogram: each chunk counts its finite logits, and sums their
+//   probability (relative to the chunk's max, fixed point with 31 fraction
+//   bits), in kHistBins bins of 1/kBinsPerOctave octave of probability,
+//   starting at the bin of the chunk max (32 octaves). Bins lie on one grid
+//   for all chunks of a row: the bin of logit l is floor(-l * log2e/T *
+//   kBinsPerOctave) (abs_bin), so a chunk's window is a shift of the row's.
+//   One bin is a 64-bit word: count in bits 48..63, mass in bits 0..47.
+constexpr int kHistBins = 256;
+constexpr int kBinsPerOctave = 8;
+constexpr int kRestBin = kHistBins;  // "beyond the window"
+constexpr int kCandCap = 4096;       // candidates per row held in LDS
+constexpr float kFixScale = 2147483648.0f;  // 2^31
+constexpr unsigned long long kCountOne = 1ull << 48;
+constexpr unsigned long long kMassMask = kCountOne - 1;
+
 template <int DT>
 struct Dt;
 template <>
@@ -136,10 +152,24 @@ struct Args {
   int32_t* nem;
   float* p_draft;
   float* logprob;   // [B, K+1] or NULL: log-probabilities of emitted tokens
+  const int32_t* top_k;  // [B] or NULL
+  const float* top_p;    // [B] or NULL
   int32_t* status;
   f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
   i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
   float* rpart;     // [B*nchunks] residual chunk sums
+  f32x4* seqinfo2;  // [B]: (truncation threshold, untruncated S, 0, 0)
+  // Truncation workspace (NULL unless top_k or top_p is given), per row
+  // (b*(K+1) + j) and per (row, chunk):
+  unsigned long long* hist;  // [rows*nchunks*kHistBins] window histograms
+  i32x4* hhdr;      // [rows*nchunks]: (window start bin, rest hi, rest lo, 0)
+  i32x4* plan;      // [rows*2]: (row start bin, r_lo, r_hi, count above),
+                    //           (active, 0, 0, 0)
+  int* ccount;      // [rows] candidates found
+  int2* cand;       // [rows*ccap] (logit bits, token)
+  int ccap;         // candidates per row held: min(kCandCap, V)
+  float* tpart;     // [rows*nchunks] kept mass per chunk (relative to row max)
+  f32x4* tinfo;     // [rows]: (threshold logit, kept mass, active, 0)
   // Fused automaton step (sam == nullptr when only verifying).
   unsigned char* sam;
   int max_len;
@@ -160,7 +190,38 @@ __device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T)
   if (!(*T == 0.0f || (*T >= 1.17549435e-38f && isfinite(*T))))
     st |= SS_ST_TEMPERATURE;
   if (*T > 0.0f && a.uniforms == nullptr) st |= SS_ST_NO_UNIFORMS;
+  if (a.top_p) {
+    const float p = a.top_p[b];
+    if (!(p > 0.0f && p <= 1.0f)) st |= SS_ST_TOP_P;
+  }
   return st;
+}
+
+// Whether sequence b's target distribution is truncated: T > 0 and top-k
+// with 1 <= k < V, or top-p below 1.
+__device__ __forceinline__ bool trunc_active(const Args& a, int b, float T) {
+  if (!(T > 0.0f)) return false;
+  const int k = a.top_k ? a.top_k[b] : 0;
+  const float p = a.top_p ? a.top_p[b] : 1.0f;
+  return (k >= 1 && k < a.V) || p < 1.0f;
+}
+
+// Histogram bin of a finite logit on the row's absolute grid (see kHistBins).
+// Every kernel computes it with these same operations, so a token's bin is
+// the same wherever it is computed.
+__device__ __forceinline__ int abs_bin(float l, float kk) {
+  float t = -l * kk * (float)kBinsPerOctave;
+  t = fminf(fmaxf(t, -1.0e9f), 1.0e9f);
+  return (int)floorf(t);
+}
+
+// Order-preserving key of a float (larger float, larger key; -0 as +0).
+__device__ __forceinline__ unsigned fkey(float l) {
+  const unsigned u = __float_as_uint(l == 0.0f ? 0.0f : l);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // (value, index) merge: larger value wins, the lower index on equal values.
@@ -208,5 +269,9 @@ __device__ __forceinline__ float load_f32(const float* p) { return *p; }
 // rows each sequence needs. f32 selects fp32 logits (else bf16); vp the
 // 16-byte vector path (rows 16-byte aligned and V a multiple of the vector).
 int launch_stream(Args a, bool f32, bool vp, hipStream_t s);
+
+// Launches the truncation passes (trunc.hip) after the stream pass: plan,
+// candidate extraction and threshold selection for every truncated row.
+int launch_truncation(const Args& a, bool f32, bool vp, hipStream_t s);
 
 }  // namespace specsam

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ["spec_verify", "sam_extend", "sam_draft", "sam_init",
                  "sam_state_bytes", "ss_verify_workspace_bytes",
-                 "spec_step", "spec_stream", "spec_finish", "sam_extend_draft",
+                 "ss_verify_workspace_bytes_ex", "spec_step", "spec_stream", "spec_finish", "sam_extend_draft",
                  "sam_extend_stats", "sam_match",
                  "sam_status", "sam_export",
                  "sam_hash_slots", "ss_version", "ss_last_error_string"]:
@@ -49,12 +49,20 @@ def test_library_loads_and_answers_size_queries():
     assert L.ss_version() >= 100
     assert L.ss_verify_workspace_bytes(256, 3, 151936) > 256 * 4 * 19 * 16
     assert L.ss_verify_workspace_bytes(256, 17, 151936) == 0  # K > 16
+    ex = L.ss_verify_workspace_bytes_ex
+    ex.restype = ctypes.c_size_t
+    assert ex(256, 3, 151936, 0) == L.ss_verify_workspace_bytes(256, 3, 151936)
+    # truncation: 2 KiB histogram per row chunk and 4096 candidates per row
+    rows = 256 * 4
+    assert ex(256, 3, 151936, 1) > ex(256, 3, 151936, 0) + rows * (19 * 2048 + 4096 * 8)
+    assert ex(256, 3, 151936, 2) == 0  # unknown flag
     assert L.sam_state_bytes(4, 1000) % 256 == 0
     assert L.sam_state_bytes(0, 1000) == 0
     assert L.sam_hash_slots(9216) == 65536
     # argument errors are reported without touching a device
     rc = L.spec_verify(None, 0, 0, 3, 10, None, None, None, None, None, None,
-                       None, None, None, None, None, ctypes.c_size_t(0), None)
+                       None, None, None, None, None, None, None,
+                       ctypes.c_size_t(0), None)
     assert rc == -1
     L.ss_last_error_string.restype = ctypes.c_char_p
     assert b"B >= 1" in L.ss_last_error_string()
