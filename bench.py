@@ -257,12 +257,18 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
     u_all = torch.as_tensor(
         np.stack([synth.uniforms(cfg, s) for s in range(total)]), device=dev)
     temp = torch.full((B,), cfg.T, dtype=torch.float32, device=dev)
+    # Truncation of the target (top-k / top-p), when the workload asks for it.
+    trunc = cfg.top_k != 0 or cfg.top_p < 1.0
+    tk = torch.full((B,), cfg.top_k, dtype=torch.int32, device=dev) if trunc else None
+    tp = torch.full((B,), cfg.top_p, dtype=torch.float32, device=dev) if trunc else None
+    tk_p = tk.data_ptr() if trunc else None
+    tp_p = tp.data_ptr() if trunc else None
     st = ssl.SamState(B, max_len, V, dev)
     st.extend(gt[:, :H].contiguous(),
               torch.full((B,), H, dtype=torch.int32, device=dev))
     booster = harness.Booster(gt, np.full(B, H, np.int32), R, V, RING,
                               cfg.boost, dt)
-    ws = ssl.verify_workspace(B, K, V, dev)
+    ws = ssl.verify_workspace(B, K, V, dev, truncation=trunc)
     drafts = [torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2)]
     mlen = torch.empty(B, dtype=torch.int32, device=dev)
     dl_hist = torch.zeros((total + 1, B), dtype=torch.int32, device=dev)
@@ -301,7 +307,7 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
 
     def fused(s):
         rc = L.spec_step(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
-                         temp_p, u0 + s * rowU, None, None, st_p, max_len, out_p,
+                         temp_p, u0 + s * rowU, tk_p, tp_p, st_p, max_len, out_p,
                          nem0 + s * rowB,
                          pd_p, None, status_p, draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB,
                          mlen_p, ws_p, ws_n, stream)
@@ -311,7 +317,7 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
     def separate(s):
         # The same step as three calls: verify, extend + next draft.
         rc = L.spec_verify(ring_p[s % RING], dt, B, K, V, draft_p[s % 2], dl0 + s * rowB,
-                           None, temp_p, u0 + s * rowU, None, None, out_p,
+                           None, temp_p, u0 + s * rowU, tk_p, tp_p, out_p,
                            nem0 + s * rowB, pd_p, None, status_p, ws_p, ws_n, stream)
         rc |= L.sam_extend_draft(st_p, B, max_len, out_p, R, nem0 + s * rowB, K,
                                  draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
@@ -334,11 +340,11 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
         for r in range(STREAM_BATCH):
             slot = (s + 1 + r) % RING
             rc |= L.spec_stream(ring_p[slot], dt, B, K, V, draft_p[s % 2],
-                                dl0 + s * rowB, temp_p, u0 + s * rowU, None, None,
+                                dl0 + s * rowB, temp_p, u0 + s * rowU, tk_p, tp_p,
                                 ws_p, ws_n, stream)
         evs[1].record()
         rc |= L.spec_finish(ring_p[s % RING], dt, B, K, V, draft_p[s % 2],
-                            dl0 + s * rowB, None, temp_p, u0 + s * rowU, None, None,
+                            dl0 + s * rowB, None, temp_p, u0 + s * rowU, tk_p, tp_p,
                             out_p, nem0 + s * rowB, pd_p, None, status_p, st_p, max_len,
                             draft_p[(s + 1) % 2], dl0 + (s + 1) * rowB, mlen_p,
                             ws_p, ws_n, stream)
@@ -427,7 +433,7 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
 
 def _sam_workload_line(cfg, m, steps: int) -> dict:
     import numpy as np
-    return {
+    line = {
         "workload": cfg.name, "dtype": cfg.dtype, "B": cfg.B, "V": cfg.V,
         "K": cfg.K, "T": cfg.T, "steps": steps,
         "steps_per_s": steps / m["elapsed"],
@@ -445,6 +451,11 @@ def _sam_workload_line(cfg, m, steps: int) -> dict:
                                       np.percentile(m["step_us"], [10, 50, 90])],
         "ring_slots": m["RING"],
     }
+    if cfg.top_k != 0 or cfg.top_p < 1.0:
+        line["top_k"], line["top_p"] = cfg.top_k, cfg.top_p
+        line["finish_pass_contents"] = ("truncation plan, extract (second read of "
+                                        "each verified row), select; finalize")
+    return line
 
 
 def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
@@ -553,17 +564,36 @@ def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
     }
 
 
-def workloads_report(steps: int, warmup: int):
-    """One JSON line per workload: c2 (greedy), c4 (bf16 logits, long
-    histories) through the automaton step, c5 through given q."""
+# Workloads beside the headline one. c3 with truncation takes the pages'
+# sampling setting for their end-to-end throughput figure (T = 0.7,
+# top_p = 0.9), with and without top_k = 50.
+def _workload_configs():
     import synth
-    for c in (2, 4):
-        cfg = synth.config(c)
-        print(json.dumps(_sam_workload_line(cfg, measure_sam_workload(cfg, steps,
-                                                                       warmup),
-                                            steps)), flush=True)
-    print(json.dumps(measure_draft_model_workload(synth.config(5), steps, warmup)),
-          flush=True)
+    return {
+        "c2": synth.config(2),
+        "c4": synth.config(4),
+        "c5": synth.config(5),
+        "c3_topp": synth.config(3, name="c3_b256_v151936_k3_t0.7_topp0.9_onehot",
+                                T=0.7, top_p=0.9),
+        "c3_topk_topp": synth.config(3, name="c3_b256_v151936_k3_t0.7_topk50_topp0.9_onehot",
+                                     T=0.7, top_k=50, top_p=0.9),
+    }
+
+
+def workloads_report(steps: int, warmup: int, names: str = "all"):
+    """One JSON line per workload: c2 (greedy), c4 (bf16 logits, long
+    histories) and the truncated c3 variants through the automaton step, c5
+    through given q."""
+    cfgs = _workload_configs()
+    pick = list(cfgs) if names == "all" else names.split(",")
+    for n in pick:
+        cfg = cfgs[n]
+        if cfg.q_mode == "model":
+            line = measure_draft_model_workload(cfg, steps, warmup)
+        else:
+            line = _sam_workload_line(cfg, measure_sam_workload(cfg, steps, warmup),
+                                      steps)
+        print(json.dumps(line), flush=True)
 
 
 def main():
@@ -576,8 +606,9 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--sam-stats", action="store_true",
                     help="report automaton work per token instead")
-    ap.add_argument("--workloads", action="store_true",
-                    help="measure the c2, c4 and c5 workloads instead")
+    ap.add_argument("--workloads", nargs="?", const="all", default=None,
+                    help="measure other workloads instead: all, or a comma "
+                         "list of c2, c4, c5, c3_topp, c3_topk_topp")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()
@@ -602,7 +633,7 @@ def main():
 
     torch.cuda.set_device(torch.device("cuda:0"))
     if args.workloads:
-        workloads_report(args.steps, args.warmup)
+        workloads_report(args.steps, args.warmup, args.workloads)
         return
     cfg = synth.config(3)
     B, K, V = cfg.B, cfg.K, cfg.V

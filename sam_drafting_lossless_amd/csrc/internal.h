@@ -106,6 +106,10 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return lane63(wave_scan(v, INT_MIN, [](int x, int y) { return x > y ? x : y; }));
 }
 
+__device__ __forceinline__ int wave_min_i(int v) {
+  return lane63(wave_scan(v, INT_MAX, [](int x, int y) { return x < y ? x : y; }));
+}
+
 // Reduces (x, y) pairs with merge(x, y, ox, oy), an associative and
 // commutative update of (x, y) by (ox, oy) with identity (idx, idy); y is
 // carried as raw 32-bit bits. Every lane ends with the result.

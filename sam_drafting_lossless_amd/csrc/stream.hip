@@ -30,9 +30,11 @@ namespace {
 // ---------------------------------------------------------------------------
 
 // Window histogram of one chunk of a truncated row (see kHistBins): `raw`
-// still holds the chunk, pm is the chunk max. hs (LDS, kHistBins + 1 words)
-// was cleared before the barrier that published pm.
+// still holds the chunk, pm is the chunk max. hs (LDS, kHistCopies x
+// kHistBins words, then the rest word) was cleared before the barrier that
+// published pm.
 static_assert(kHistBins == kThreads, "one histogram bin per thread");
+static_assert(kHistCopies == 2 * kWaves, "one copy per wavefront and lane parity");
 
 template <int DT>
 __device__ __forceinline__ void chunk_histogram(const Args& a, int64_t row, int c,
@@ -41,6 +43,8 @@ __device__ __forceinline__ void chunk_histogram(const Args& a, int64_t row, int 
                                                 unsigned long long* hs) {
   const int tid = threadIdx.x;
   const int a0 = abs_bin(pm, kk);
+  unsigned long long* mine =
+      hs + ((tid / kWave) * 2 + (tid & 1)) * kHistBins;  // this lane's copy
   unsigned long long rest = 0;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it)
@@ -53,17 +57,20 @@ __device__ __forceinline__ void chunk_histogram(const Args& a, int64_t row, int 
         const unsigned long long word =
             kCountOne | (unsigned long long)(unsigned)(w * kFixScale);
         if (jb >= 0 && jb < kHistBins)
-          atomicAdd(&hs[jb], word);
+          atomicAdd(&mine[jb], word);
         else
           rest += word;
       }
     }
-  if (rest) atomicAdd(&hs[kHistBins], rest);
+  if (rest) atomicAdd(&hs[kHistCopies * kHistBins], rest);
   __syncthreads();
+  unsigned long long sum = 0;
+#pragma unroll
+  for (int i = 0; i < kHistCopies; ++i) sum += hs[i * kHistBins + tid];
   const int64_t hc = row * a.nchunks + c;
-  a.hist[hc * kHistBins + tid] = hs[tid];
+  a.hist[hc * kHistBins + tid] = sum;
   if (tid == 0) {
-    const unsigned long long r = hs[kHistBins];
+    const unsigned long long r = hs[kHistCopies * kHistBins];
     a.hhdr[hc] = i32x4{a0, (int)(unsigned)(r >> 32), (int)(unsigned)r, 0};
   }
 }
@@ -165,8 +172,9 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     if constexpr (TR) {
       tr = trunc_active(a, b, T);
       if (tr) {
-        hs[tid] = 0;
-        if (tid == 0) hs[kHistBins] = 0;
+#pragma unroll
+        for (int i = 0; i < kHistCopies; ++i) hs[i * kHistBins + tid] = 0;
+        if (tid == 0) hs[kHistCopies * kHistBins] = 0;
       }
     }
     wave_lse(m, s, kk);
@@ -193,7 +201,7 @@ struct NoMid {
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
-  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistCopies * kHistBins + 1 : 1];
   const int tid = threadIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
   const int c = blockIdx.x % nc;
@@ -210,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   if (j0 == 0)
     load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
                        a.V, tid, raw);
+  if (TR && blockIdx.x == 0 && tid == 0) *a.tcount = 0;  // rows the plan lists
   if (st) return;
   const int j1 = min(j0 + a.rows_per_wg, d + 1);
   for (int j = j0; j < j1; ++j) {
@@ -267,7 +276,7 @@ template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, DT == SS_DTYPE_F32 ? 6 : 4) void
 spec_stream_balanced_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
-  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistCopies * kHistBins + 1 : 1];
   __shared__ int pre[kPlanMaxB + 1];
   __shared__ int wsum[kWaves];
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
@@ -278,6 +287,7 @@ spec_stream_balanced_kernel(Args a) {
   u32x4 raw[kLoads];
   load_chunk<DT, VP>(a.logits + (int64_t)b0 * R * a.V * Dt<DT>::kBytes,
                      c0 * kChunk<DT>, a.V, tid, raw);
+  if (TR && g == 0 && tid == 0) *a.tcount = 0;  // rows the plan lists
   int d;
   float T;
   int st = seq_check(a, b0, &d, &T);  // reported by finalize

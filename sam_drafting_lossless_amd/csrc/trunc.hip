@@ -27,9 +27,13 @@
 //           for top-p), then adds the kept candidates' probability to their
 //           chunks' sums.
 // The finalize kernel then judges and draws with the per-chunk kept sums and
-// the threshold. A row with more than kCandCap candidates (its logits crowd
-// into a few bins; the list holds min(kCandCap, V) per row) is selected by
-// scanning the row itself in each round: exact, but slower.
+// the threshold. Selection first finds the bits all candidate keys share and
+// radix-walks only the bits below them, so that no round piles every
+// candidate into one LDS bucket. A row with more than kCandCap candidates
+// (its logits crowd into a few bins; the list holds min(kCandCap, V) per row)
+// is selected by scanning the row itself in each round: exact, but slower.
+#include <algorithm>
+
 #include "verify_common.h"
 
 namespace specsam {
@@ -37,6 +41,7 @@ namespace {
 
 constexpr float kPlanMargin = 1e-4f;  // relative slack for histogram rounding
 constexpr int kKeepAll = INT_MAX;     // range start when nothing is dropped
+constexpr int64_t kExtractGrid = 4096;  // extract workgroups (grid-stride)
 
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
@@ -70,9 +75,12 @@ __device__ __forceinline__ RowCtx row_ctx(const Args& a, int64_t row) {
 // ---------------------------------------------------------------------------
 // plan: one workgroup per row; thread r owns bin r of the row window.
 // ---------------------------------------------------------------------------
+constexpr int kPlanBatch = 24;  // chunk histograms requested at once
+
 __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   __shared__ int s_a[kMaxChunks];
   __shared__ float s_pm[kMaxChunks];
+  __shared__ unsigned long long s_rest[kMaxChunks];
   __shared__ float scratch[kWaves];
   __shared__ float wtot[2][kWaves];
   __shared__ int first[3];
@@ -85,7 +93,9 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   const int nc = a.nchunks;
   const int64_t h0 = row * nc;
   for (int c = tid; c < nc; c += kThreads) {
-    s_a[c] = a.hhdr[h0 + c].x;
+    const i32x4 hh = a.hhdr[h0 + c];
+    s_a[c] = hh.x;
+    s_rest[c] = ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
     s_pm[c] = a.partials[h0 + c].x;
   }
   if (tid < 3) first[tid] = kRestBin;
@@ -94,27 +104,39 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   float m = kNegInf;
   for (int c = 0; c < nc; ++c) m = fmaxf(m, s_pm[c]);
   const int a0 = abs_bin(m, rc.kk);
-  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c.
+  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c. Totals (every
+  // bin of every chunk, and the chunks' rest words) give the finite count N
+  // and the mass Z. The words of kPlanBatch chunks are requested together.
   float cnt = 0.0f, mass = 0.0f, tcnt = 0.0f, tmass = 0.0f;
-  for (int c = 0; c < nc; ++c) {
+  for (int c0 = 0; c0 < nc; c0 += kPlanBatch) {
+    unsigned long long wt[kPlanBatch], wb[kPlanBatch];
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u) {
+      const int c = c0 + u;
+      wt[u] = wb[u] = 0;
+      if (c < nc) {
+        const unsigned long long* hc = a.hist + (h0 + c) * kHistBins;
+        wt[u] = hc[tid];
+        const int jb = tid - (s_a[c] - a0);
+        if (jb >= 0 && jb < kHistBins) wb[u] = hc[jb];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u) {
+      const int c = c0 + u;
+      if (c < nc) {
+        const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
+        tcnt += (float)(unsigned)(wt[u] >> 48);
+        tmass += (float)(wt[u] & kMassMask) * sc;
+        cnt += (float)(unsigned)(wb[u] >> 48);
+        mass += (float)(wb[u] & kMassMask) * sc;
+      }
+    }
+  }
+  for (int c = tid; c < nc; c += kThreads) {
     const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
-    const unsigned long long* hc = a.hist + (h0 + c) * kHistBins;
-    const unsigned long long wt = hc[tid];
-    tcnt += (float)(unsigned)(wt >> 48);
-    tmass += (float)(wt & kMassMask) * sc;
-    const int jb = tid - (s_a[c] - a0);
-    if (jb >= 0 && jb < kHistBins) {
-      const unsigned long long wb = hc[jb];
-      cnt += (float)(unsigned)(wb >> 48);
-      mass += (float)(wb & kMassMask) * sc;
-    }
-    if (tid == 0) {
-      const i32x4 hh = a.hhdr[h0 + c];
-      const unsigned long long r =
-          ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
-      tcnt += (float)(unsigned)(r >> 48);
-      tmass += (float)(r & kMassMask) * sc;
-    }
+    tcnt += (float)(unsigned)(s_rest[c] >> 48);
+    tmass += (float)(s_rest[c] & kMassMask) * sc;
   }
   const float N = block_sum(tcnt, scratch);  // finite tokens (exact: < 2^24)
   const float Z = block_sum(tmass, scratch);
@@ -180,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
     a.plan[row * 2] = i32x4{a0, rlo, rhi, cabove};
     a.plan[row * 2 + 1] =
         i32x4{(kA ? 1 : 0) | (pA ? 2 : 0), k - cabove, __float_as_int(m), 0};
+    a.tlist[atomicAdd(a.tcount, 1)] = (int)row;
   }
 }
 
@@ -189,23 +212,42 @@ __device__ __forceinline__ bool in_range(int rb, int rlo, int rhi) {
   return rb >= rlo && (rhi >= kRestBin || rb <= rhi);
 }
 
+// Row of list entry e of the truncated rows, or -1 past the list's end (the
+// grids of the passes below cover every row; entries past the count exit).
+__device__ __forceinline__ int64_t listed_row(const Args& a, int e) {
+  return e < *a.tcount ? (int64_t)a.tlist[e] : -1;
+}
+
 // ---------------------------------------------------------------------------
-// extract: one workgroup per (row, chunk).
+// extract: (listed row, chunk) items, grid-stride (the grid is sized for the
+// largest list; a workgroup takes items g, g + grid, ... below count x nc).
 // ---------------------------------------------------------------------------
+template <int DT, bool VP>
+__device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
+                                             float* scratch, int* woff);
+
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
   __shared__ float scratch[kWaves];
   __shared__ int woff[kWaves + 1];
+  const int nc = a.nchunks;
+  const int64_t items = (int64_t)*a.tcount * nc;
+  for (int64_t x = blockIdx.x; x < items; x += gridDim.x) {
+    const int e = (int)(x / nc);
+    extract_item<DT, VP>(a, a.tlist[e], (int)(x - (int64_t)e * nc), scratch, woff);
+  }
+}
+
+template <int DT, bool VP>
+__device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
+                                             float* scratch, int* woff) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int nc = a.nchunks;
-  const int64_t row = blockIdx.x / nc;
-  const int c = (int)(blockIdx.x - row * nc);
-  const RowCtx rc = row_ctx(a, row);
-  if (!rc.active) return;
   const int cstart = c * kChunk<DT>;
   u32x4 raw[kLoads];
-  load_chunk<DT, VP, false>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid,
-                            raw);
+  load_chunk<DT, VP>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid, raw);
+  const int b = (int)(row / (a.K + 1));
+  const float kk = kLog2e / a.temperature[b];
   const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
   const int a0 = p0.x, rlo = p0.y, rhi = p0.z;
   const float m = __int_as_float(p1.z);
@@ -217,9 +259,9 @@ __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
     for (int k = 0; k < kVec<DT>; ++k) {
       const float v = elem<DT>(raw[it], k);
       if (v > kNegInf) {
-        const int rb = abs_bin(v, rc.kk) - a0;
+        const int rb = abs_bin(v, kk) - a0;
         if (rb < rlo)
-          above += fast_exp2((v - m) * rc.kk);
+          above += fast_exp2((v - m) * kk);
         else if (in_range(rb, rlo, rhi))
           ++n;
       }
@@ -241,8 +283,9 @@ __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
     woff[kWaves] = t ? atomicAdd(&a.ccount[row], t) : 0;
   }
   __syncthreads();
-  if (n == 0) return;
   int pos = woff[kWaves] + woff[w] + inc - n;
+  __syncthreads();  // woff is reused by the next item
+  if (n == 0) return;
   int2* out = a.cand + row * a.ccap;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it)
@@ -250,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
     for (int k = 0; k < kVec<DT>; ++k) {
       const float v = elem<DT>(raw[it], k);
       if (v > kNegInf) {
-        const int rb = abs_bin(v, rc.kk) - a0;
+        const int rb = abs_bin(v, kk) - a0;
         if (rb >= rlo && in_range(rb, rlo, rhi)) {
           if (pos < a.ccap)
             out[pos] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
@@ -261,22 +304,24 @@ __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// select: one workgroup per row.
+// select: one workgroup per listed row.
 // ---------------------------------------------------------------------------
 struct SelShared {
-  float cl[kCandCap];
-  int ci[kCandCap];
+  unsigned key[kCandCap];  // candidate keys (fkey of the logit)
+  unsigned char chunk[kCandCap];  // the chunk each candidate lies in
   unsigned cnt[256];
   float mass[256];
   float csum[kMaxChunks];
   float scratch[kWaves];
+  int iscr[2][kWaves];
   int digit;
   float carry;
   unsigned minkey;
 };
 
-// Candidates of a row: from LDS when they fit, else by re-reading the row and
-// filtering it by the plan's range (exact, one pass over the row per call).
+// Candidate keys of a row: from LDS when they fit, else by re-reading the row
+// and filtering it by the plan's range (exact, one pass over the row per
+// call). f(key, list position or token index).
 template <int DT, bool VP>
 struct CandSource {
   const Args* a;
@@ -284,11 +329,12 @@ struct CandSource {
   int64_t row;
   int n, a0, rlo, rhi;
   float kk;
+  __device__ __forceinline__ bool in_lds() const { return n <= a->ccap; }
   template <typename F>
   __device__ __forceinline__ void each(F f) const {
     const int tid = threadIdx.x;
-    if (n <= a->ccap) {
-      for (int i = tid; i < n; i += kThreads) f(sh->cl[i], sh->ci[i]);
+    if (in_lds()) {
+      for (int i = tid; i < n; i += kThreads) f(sh->key[i], i);
       return;
     }
     const unsigned char* rowp = a->logits + row * a->V * Dt<DT>::kBytes;
@@ -302,16 +348,16 @@ struct CandSource {
         for (int k = 0; k < kVec<DT>; ++k) {
           const float v = elem<DT>(raw[it], k);
           if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi))
-            f(v, elem_index<DT, VP>(cstart, tid, it, k));
+            f(fkey(v), elem_index<DT, VP>(cstart, tid, it, k));
         }
     }
   }
 };
 
 // Wavefront 0 scans the 256 digit buckets from digit 255 down (lane L holds
-// digits 255-4L .. 252-4L) and returns, in sh.digit, the first digit whose
-// running total reaches t, and in sh.carry the total of the digits above it
-// (-1 when the buckets sum to less than t).
+// digits 255-4L .. 252-4L) and leaves in sh.digit the first digit whose
+// running total reaches t, in sh.carry the total of the digits above it
+// (sh.digit = -1 when the buckets sum to less than t).
 __device__ __forceinline__ void scan_digits(SelShared& sh, float t, bool by_mass) {
   const int tid = threadIdx.x;
   if (tid < kWave) {
@@ -344,25 +390,64 @@ __device__ __forceinline__ void scan_digits(SelShared& sh, float t, bool by_mass
   __syncthreads();
 }
 
+// Radix digits below a common prefix: the candidates' keys agree on their
+// top (32 - nbits) bits (prefix); selection walks the remaining bits in
+// digits of up to 8 bits, so that no round puts every candidate in one
+// bucket.
+struct KeySpan {
+  unsigned prefix;
+  int nbits;
+};
+
+template <typename Src>
+__device__ KeySpan key_span(const Src& src, SelShared& sh) {
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  int lo = INT_MAX, hi = INT_MIN;  // keys as order-preserving signed ints
+  src.each([&](unsigned key, int) {
+    const int s = (int)(key ^ 0x80000000u);
+    lo = min(lo, s);
+    hi = max(hi, s);
+  });
+  lo = wave_min_i(lo);
+  hi = wave_max_i(hi);
+  if (l == 0) {
+    sh.iscr[0][w] = lo;
+    sh.iscr[1][w] = hi;
+  }
+  __syncthreads();
+  for (int i = 0; i < kWaves; ++i) {
+    lo = min(lo, sh.iscr[0][i]);
+    hi = max(hi, sh.iscr[1][i]);
+  }
+  __syncthreads();
+  const unsigned klo = (unsigned)lo ^ 0x80000000u, khi = (unsigned)hi ^ 0x80000000u;
+  KeySpan ks;
+  ks.nbits = (klo == khi) ? 0 : 32 - __clz((int)(klo ^ khi));
+  ks.prefix = ks.nbits == 32 ? 0u : (klo >> ks.nbits) << ks.nbits;
+  return ks;
+}
+
 // Key of the kth largest candidate (1-based; kth <= the candidate count).
 template <typename Src>
-__device__ unsigned select_kth(const Src& src, SelShared& sh, int kth) {
+__device__ unsigned select_kth(const Src& src, SelShared& sh, KeySpan ks, int kth) {
   const int tid = threadIdx.x;
-  unsigned prefix = 0, mask = 0;
+  unsigned prefix = ks.prefix;
   float need = (float)kth;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int rem = ks.nbits; rem > 0;) {
+    const int wd = min(8, rem);
+    rem -= wd;
+    const unsigned mask = (rem + wd >= 32) ? 0u : (~0u << (rem + wd));  // bits above
     sh.cnt[tid] = 0;
     __syncthreads();
-    src.each([&](float v, int) {
-      const unsigned key = fkey(v);
-      if ((key & mask) == prefix) atomicAdd(&sh.cnt[(key >> shift) & 255u], 1u);
+    src.each([&](unsigned key, int) {
+      if ((key & mask) == prefix)
+        atomicAdd(&sh.cnt[(key >> rem) & ((1u << wd) - 1)], 1u);
     });
     __syncthreads();
     scan_digits(sh, need, false);
     const int dg = sh.digit < 0 ? 0 : sh.digit;
     need -= sh.carry;
-    prefix |= (unsigned)dg << shift;
-    mask |= 255u << shift;
+    prefix |= (unsigned)dg << rem;
     __syncthreads();
   }
   return prefix;
@@ -372,18 +457,21 @@ __device__ unsigned select_kth(const Src& src, SelShared& sh, int kth) {
 // at least t of probability; the smallest candidate key >= kmin when rounding
 // leaves the candidates short of t.
 template <typename Src>
-__device__ unsigned select_mass(const Src& src, SelShared& sh, float t, unsigned kmin,
-                                float m, float kk) {
+__device__ unsigned select_mass(const Src& src, SelShared& sh, KeySpan ks, float t,
+                                unsigned kmin, float m, float kk) {
   const int tid = threadIdx.x;
-  unsigned prefix = 0, mask = 0;
+  unsigned prefix = ks.prefix;
   bool found = true;
-  for (int shift = 24; shift >= 0 && found; shift -= 8) {
+  for (int rem = ks.nbits; rem > 0 && found;) {
+    const int wd = min(8, rem);
+    rem -= wd;
+    const unsigned mask = (rem + wd >= 32) ? 0u : (~0u << (rem + wd));
     sh.mass[tid] = 0.0f;
     __syncthreads();
-    src.each([&](float v, int) {
-      const unsigned key = fkey(v);
+    src.each([&](unsigned key, int) {
       if (key >= kmin && (key & mask) == prefix)
-        atomicAdd(&sh.mass[(key >> shift) & 255u], fast_exp2((v - m) * kk));
+        atomicAdd(&sh.mass[(key >> rem) & ((1u << wd) - 1)],
+                  fast_exp2((fkey_inv(key) - m) * kk));
     });
     __syncthreads();
     scan_digits(sh, t, true);
@@ -391,16 +479,14 @@ __device__ unsigned select_mass(const Src& src, SelShared& sh, float t, unsigned
       found = false;
     } else {
       t -= sh.carry;
-      prefix |= (unsigned)sh.digit << shift;
-      mask |= 255u << shift;
+      prefix |= (unsigned)sh.digit << rem;
     }
     __syncthreads();
   }
   if (found) return prefix;
   if (tid == 0) sh.minkey = 0xffffffffu;
   __syncthreads();
-  src.each([&](float v, int) {
-    const unsigned key = fkey(v);
+  src.each([&](unsigned key, int) {
     if (key >= kmin) atomicMin(&sh.minkey, key);
   });
   __syncthreads();
@@ -411,10 +497,11 @@ template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const RowCtx rc = row_ctx(a, row);
-  if (!rc.active) return;
+  const int64_t row = listed_row(a, blockIdx.x);
+  if (row < 0) return;
   const int nc = a.nchunks;
+  const int b = (int)(row / (a.K + 1));
+  const float kk = kLog2e / a.temperature[b];
   const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
   const int mode = p1.x, krem = p1.y;
   const float m = __int_as_float(p1.z);
@@ -427,19 +514,32 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
     if (tid == 0) a.tinfo[row] = f32x4{kNegInf, base, 1.0f, 0.0f};
     return;
   }
+  const int2* list = a.cand + row * a.ccap;
   if (n <= a.ccap) {
-    const int2* in = a.cand + row * a.ccap;
-    for (int i = tid; i < n; i += kThreads) {
-      const int2 e = in[i];
-      sh.cl[i] = __int_as_float(e.x);
-      sh.ci[i] = e.y;
+    constexpr int kU = 8;  // list entries requested at once per thread
+    for (int i0 = 0; i0 < n; i0 += kU * kThreads) {
+      int2 ev[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        ev[u] = i < n ? list[i] : int2{0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + u * kThreads + tid;
+        if (i < n) {
+          sh.key[i] = fkey(__int_as_float(ev[u].x));
+          sh.chunk[i] = (unsigned char)(ev[u].y / kChunk<DT>);
+        }
+      }
     }
   }
   for (int c = tid; c < nc; c += kThreads) sh.csum[c] = 0.0f;
   __syncthreads();
-  const CandSource<DT, VP> src{&a, &sh, row, n, p0.x, p0.y, p0.z, rc.kk};
+  const CandSource<DT, VP> src{&a, &sh, row, n, p0.x, p0.y, p0.z, kk};
+  const KeySpan ks = key_span(src, sh);
   unsigned kmin = 0;
-  if (mode & 1) kmin = select_kth(src, sh, krem);
+  if (mode & 1) kmin = select_kth(src, sh, ks, krem);
   unsigned key = kmin;
   if (mode & 2) {
     // top-p's share is of what top-k kept: with top-k, base plus the
@@ -447,34 +547,37 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
     // k-th largest); without, the whole row (from the stream partials).
     float zk = 0.0f;
     if (mode & 1) {
-      src.each([&](float v, int) {
-        if (fkey(v) >= kmin) zk += fast_exp2((v - m) * rc.kk);
+      src.each([&](unsigned k2, int) {
+        if (k2 >= kmin) zk += fast_exp2((fkey_inv(k2) - m) * kk);
       });
       zk = base + block_sum(zk, sh.scratch);
     } else {
       for (int c = tid; c < nc; c += kThreads) {
         const f32x4 p = a.partials[row * nc + c];
-        zk += p.y * fast_exp2((p.x - m) * rc.kk);
+        zk += p.y * fast_exp2((p.x - m) * kk);
       }
       zk = block_sum(zk, sh.scratch);
     }
-    const float t = a.top_p[rc.b] * zk - base;
+    const float t = a.top_p[b] * zk - base;
     if (t > 0.0f) {
-      key = select_mass(src, sh, t, kmin, m, rc.kk);
+      key = select_mass(src, sh, ks, t, kmin, m, kk);
     } else {
       // The range is chosen so that this does not happen (the share above
       // it stays below top_p); keep the top candidate group if it does.
       if (tid == 0) sh.minkey = 0;
       __syncthreads();
-      src.each([&](float v, int) { atomicMax(&sh.minkey, fkey(v)); });
+      src.each([&](unsigned k2, int) { atomicMax(&sh.minkey, k2); });
       __syncthreads();
       key = sh.minkey;
     }
   }
-  // Kept candidates: their probability, per chunk.
-  src.each([&](float v, int i) {
-    if (fkey(v) >= key)
-      atomicAdd(&sh.csum[i / kChunk<DT>], fast_exp2((v - m) * rc.kk));
+  // Kept candidates: their probability, per chunk (from the LDS list, or
+  // from the token index of the row scan).
+  src.each([&](unsigned k2, int i) {
+    if (k2 >= key) {
+      const int ch = src.in_lds() ? (int)sh.chunk[i] : i / kChunk<DT>;
+      atomicAdd(&sh.csum[ch], fast_exp2((fkey_inv(k2) - m) * kk));
+    }
   });
   __syncthreads();
   float kept = 0.0f;
@@ -493,8 +596,9 @@ int launch_t(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL(trunc_plan_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, a);
   int rc = check_launch("truncation plan");
   if (rc != SS_OK) return rc;
-  const int64_t grid = rows * a.nchunks;
-  if (grid > INT_MAX) return set_error(SS_EINVAL, "truncation: grid too large");
+  // Enough workgroups to fill the chip several times over; each takes the
+  // items of the listed rows in turn.
+  const int64_t grid = std::min<int64_t>(rows * a.nchunks, kExtractGrid);
   hipLaunchKernelGGL((trunc_extract_kernel<DT, VP>), dim3((unsigned)grid),
                      dim3(kThreads), 0, s, a);
   rc = check_launch("truncation extract");

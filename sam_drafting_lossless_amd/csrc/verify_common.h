@@ -31,7 +31,11 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kHistBins = 256;
 constexpr int kBinsPerOctave = 8;
 constexpr int kRestBin = kHistBins;  // "beyond the window"
-constexpr int kCandCap = 4096;       // candidates per row held in LDS
+// The stream pass builds each chunk's histogram in kHistCopies private
+// copies (per wavefront and lane parity), so that fewer lanes of one LDS
+// atomic hit the same bin, then sums them.
+constexpr int kHistCopies = 8;
+constexpr int kCandCap = 8192;       // candidates per row held in LDS
 constexpr float kFixScale = 2147483648.0f;  // 2^31
 constexpr unsigned long long kCountOne = 1ull << 48;
 constexpr unsigned long long kMassMask = kCountOne - 1;
@@ -166,6 +170,8 @@ struct Args {
   i32x4* plan;      // [rows*2]: (row start bin, r_lo, r_hi, count above),
                     //           (active, 0, 0, 0)
   int* ccount;      // [rows] candidates found
+  int* tlist;       // [rows] truncated rows, in the order the plan found them
+  int* tcount;      // [1] their number (cleared by the stream pass)
   int2* cand;       // [rows*ccap] (logit bits, token)
   int ccap;         // candidates per row held: min(kCandCap, V)
   float* tpart;     // [rows*nchunks] kept mass per chunk (relative to row max)

@@ -42,6 +42,8 @@ class Config:
     dtype: str = "f32"       # "f32" or "bf16" logits in memory
     q_mode: str = "onehot"   # "onehot" (SAM drafts) or "model" (draft q given)
     draft_sigma: float = 0.0  # noise std added to the target for the draft model
+    top_k: int = 0           # truncation of the target per sequence (0: off)
+    top_p: float = 1.0       # (1: off)
     steps: int = 100
     warmup: int = 0
     seed: int = 0
