@@ -253,6 +253,17 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
   const float m = __int_as_float(p1.z);
   float above = 0.0f;
   int n = 0;
+  // A lane's first kHeld candidates stay in registers, so that the chunk
+  // itself need not stay live across the reservation below; a lane with more
+  // re-reads its part of the chunk afterwards.
+  constexpr int kHeld = 4;
+  float hv[kHeld];
+  int hi[kHeld];
+#pragma unroll
+  for (int q = 0; q < kHeld; ++q) {
+    hv[q] = 0.0f;
+    hi[q] = 0;
+  }
 #pragma unroll
   for (int it = 0; it < kLoads; ++it)
 #pragma unroll
@@ -260,10 +271,17 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
       const float v = elem<DT>(raw[it], k);
       if (v > kNegInf) {
         const int rb = abs_bin(v, kk) - a0;
-        if (rb < rlo)
+        if (rb < rlo) {
           above += fast_exp2((v - m) * kk);
-        else if (in_range(rb, rlo, rhi))
+        } else if (in_range(rb, rlo, rhi)) {
+#pragma unroll
+          for (int q = 0; q < kHeld; ++q)
+            if (n == q) {
+              hv[q] = v;
+              hi[q] = elem_index<DT, VP>(cstart, tid, it, k);
+            }
           ++n;
+        }
       }
     }
   above = block_sum(above, scratch);
@@ -288,17 +306,22 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
   if (n == 0) return;
   int2* out = a.cand + row * a.ccap;
 #pragma unroll
+  for (int q = 0; q < kHeld; ++q)
+    if (q < n && pos + q < a.ccap) out[pos + q] = int2{__float_as_int(hv[q]), hi[q]};
+  if (n <= kHeld) return;
+  u32x4 again[kLoads];
+  load_chunk<DT, VP, false>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid,
+                            again);
+  int seen = 0;
+#pragma unroll
   for (int it = 0; it < kLoads; ++it)
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) {
-      const float v = elem<DT>(raw[it], k);
-      if (v > kNegInf) {
-        const int rb = abs_bin(v, kk) - a0;
-        if (rb >= rlo && in_range(rb, rlo, rhi)) {
-          if (pos < a.ccap)
-            out[pos] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
-          ++pos;
-        }
+      const float v = elem<DT>(again[it], k);
+      if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi)) {
+        if (seen >= kHeld && pos + seen < a.ccap)
+          out[pos + seen] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
+        ++seen;
       }
     }
 }
