@@ -35,6 +35,7 @@ ST_NONFINITE = 1 << 3
 ST_TEMPERATURE = 1 << 4
 ST_NO_UNIFORMS = 1 << 5
 ST_TOP_P = 1 << 7
+ST_TREE = 1 << 8
 
 
 def build() -> str:
@@ -79,6 +80,9 @@ def _load():
     lib.orc_sam_static_draft.restype = None
     lib.orc_verify.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P,
                                P, P, P, P, P, P, P, P, P, P, P, i32]
+    lib.orc_verify_tree.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                    P, P, P, P, P, i32]
+    lib.orc_verify_tree.restype = None
     lib.orc_step.argtypes = [P, i32, i32, i32, P, i32, P, P, P, P, P,
                              P, P, P, P, P, P, P, i32]
     _lib = lib
@@ -276,6 +280,46 @@ def verify(logits, draft, draft_len, temperature, uniforms=None, q=None,
                    _ptr(nem), _ptr(pd), _ptr(al), _ptr(lo), _ptr(hi), _ptr(st),
                    _ptr(top_k), _ptr(top_p), _ptr(thr), _ptr(mg), int(nthreads))
     return VerifyResult(out, nem, pd, al, lo, hi, st, thr, mg)
+
+
+@dataclass
+class TreeResult:
+    out_tokens: np.ndarray   # [B,N] int32, -1 padded
+    out_nodes: np.ndarray    # [B,N] int32: node of each emitted token
+    num_emitted: np.ndarray  # [B] int32
+    gap: np.ndarray          # [B,N] float64: |u[t] - running sums| minimum
+    cdf_lo: np.ndarray       # [B]
+    cdf_hi: np.ndarray       # [B]
+    status: np.ndarray       # [B] int32
+
+
+def verify_tree(logits, tokens, parent, n_nodes, temperature, uniforms=None,
+                nthreads: int = 1) -> TreeResult:
+    """Verify a draft tree per sequence (see verify_tree_one in oracle.cpp).
+
+    logits: [B,N,V] float32 or uint16 (bfloat16 bits); tokens, parent: [B,N]
+    int32 (parent[b,0] = -1); n_nodes: [B]; uniforms: [B,N] (coins per depth,
+    the last column the final coin)."""
+    x, dt = _logits_arg(logits)
+    B, N, V = x.shape
+    tokens = _c(tokens, np.int32).reshape(B, N)
+    parent = _c(parent, np.int32).reshape(B, N)
+    n_nodes = _c(n_nodes, np.int32).reshape(B)
+    temperature = _c(temperature, np.float32).reshape(B)
+    if uniforms is not None:
+        uniforms = _c(uniforms, np.float32).reshape(B, N)
+    out = np.full((B, N), -1, np.int32)
+    onode = np.full((B, N), -1, np.int32)
+    nem = np.zeros(B, np.int32)
+    gap = np.empty((B, N), np.float64)
+    lo = np.empty(B, np.float64)
+    hi = np.empty(B, np.float64)
+    st = np.zeros(B, np.int32)
+    _load().orc_verify_tree(_ptr(x), dt, B, N, V, _ptr(tokens), _ptr(parent),
+                            _ptr(n_nodes), _ptr(temperature), _ptr(uniforms),
+                            _ptr(out), _ptr(onode), _ptr(nem), _ptr(gap), _ptr(lo),
+                            _ptr(hi), _ptr(st), int(nthreads))
+    return TreeResult(out, onode, nem, gap, lo, hi, st)
 
 
 def step(sams, logits, temperature, uniforms, nthreads: int = 1):

@@ -182,6 +182,7 @@ constexpr int32_t ST_NONFINITE = 1 << 3;
 constexpr int32_t ST_TEMPERATURE = 1 << 4;
 constexpr int32_t ST_NO_UNIFORMS = 1 << 5;
 constexpr int32_t ST_TOP_P = 1 << 7;
+constexpr int32_t ST_TREE = 1 << 8;
 
 // bfloat16 is the upper half of an IEEE binary32: widen by appending 16 zero
 // bits.
@@ -469,6 +470,140 @@ void verify_one(const VerifyIO& io, int b) {
   io.num_emitted[b] = d + 1;
 }
 
+
+// Verification of a draft tree ([P3] gogongxt notes "SGLang 的实现": the
+// target-only tree sampling walks the draft tree depth by depth; at a node the
+// children are tried in sibling order, each adding its target probability to
+// a running sum, and the first child whose running sum reaches the depth's
+// coin is accepted, the sum starting again at the next depth; when no child
+// passes, the children's probabilities are taken out of the target and the
+// final token is drawn from what is left; with both of the page's thresholds
+// at 1, which makes the walk lossless). Read as:
+//   node 0 is the root (the last committed token); node i >= 1 holds a
+//   drafted token and a parent p < i; row i of the logits scores the token
+//   after the path root..i; the children of a node are taken in increasing
+//   node index and must carry distinct tokens;
+//   T > 0: at depth t (t tokens accepted so far) with coin u[t], child c_k is
+//   accepted iff u[t] <= sum_{k' <= k} p(x_{c_k'}); if none, the final token is
+//   drawn with u[N-1] from p with the children's tokens removed; at a leaf
+//   (every draft on the path accepted) it is drawn from the leaf's row;
+//   T = 0: the child whose token is the row's argmax is accepted, else the
+//   argmax is emitted (also at a leaf).
+// Outputs per sequence: the emitted tokens, the node each came from (the
+// accepted child, or for the last token the node whose row it was drawn
+// from), their number; gap[b, t] is the smallest distance between u[t] and
+// the running sums at depth t (tie detection), cdf_lo/hi as in orc_verify.
+struct TreeIO {
+  const void* logits;
+  int dtype, B, N, V;
+  const int32_t* tokens;   // [B,N]
+  const int32_t* parent;   // [B,N]
+  const int32_t* n_nodes;  // [B]
+  const float* temperature;
+  const float* uniforms;   // [B,N]
+  int32_t* out_tokens;     // [B,N]
+  int32_t* out_nodes;      // [B,N]
+  int32_t* num_emitted;    // [B]
+  double* gap;             // [B,N]
+  double* cdf_lo;
+  double* cdf_hi;
+  int32_t* status;
+};
+
+void verify_tree_one(const TreeIO& io, int b) {
+  const int N = io.N;
+  const int64_t V = io.V;
+  int32_t* out = io.out_tokens + (int64_t)b * N;
+  int32_t* onode = io.out_nodes + (int64_t)b * N;
+  double* gap = io.gap + (int64_t)b * N;
+  for (int i = 0; i < N; ++i) {
+    out[i] = onode[i] = -1;
+    gap[i] = std::numeric_limits<double>::quiet_NaN();
+  }
+  io.cdf_lo[b] = io.cdf_hi[b] = std::numeric_limits<double>::quiet_NaN();
+  const int n = io.n_nodes[b];
+  const double T = (double)io.temperature[b];
+  const int32_t* tok = io.tokens + (int64_t)b * N;
+  const int32_t* par = io.parent + (int64_t)b * N;
+  int32_t st = 0;
+  if (!(T == 0.0 || (T >= (double)std::numeric_limits<float>::min() && std::isfinite(T))))
+    st |= ST_TEMPERATURE;
+  if (T > 0.0 && io.uniforms == nullptr) st |= ST_NO_UNIFORMS;
+  std::vector<std::vector<int>> kids;
+  if (n < 1 || n > N) {
+    st |= ST_TREE;
+  } else {
+    kids.resize((size_t)n);
+    if (par[0] != -1) st |= ST_TREE;
+    for (int i = 1; i < n; ++i) {
+      if (par[i] < 0 || par[i] >= i || tok[i] < 0 || tok[i] >= V) {
+        st |= ST_TREE;
+        continue;
+      }
+      for (int c : kids[(size_t)par[i]])
+        if (tok[c] == tok[i]) st |= ST_TREE;
+      kids[(size_t)par[i]].push_back(i);
+    }
+  }
+  std::vector<std::vector<double>> rows;
+  if (st == 0) {
+    rows.resize((size_t)n);
+    for (int i = 0; i < n; ++i) {
+      load_row(io.logits, io.dtype, (int64_t)b * N + i, V, rows[(size_t)i]);
+      if (!finite_row(rows[(size_t)i])) st |= ST_NONFINITE;
+    }
+  }
+  if (st) {
+    io.status[b] |= st;
+    return;
+  }
+  const float* u = io.uniforms ? io.uniforms + (int64_t)b * N : nullptr;
+  int cur = 0, depth = 0;
+  std::vector<double> p, w;
+  while (true) {
+    const std::vector<int>& ch = kids[(size_t)cur];
+    int next = -1;
+    if (T == 0.0) {
+      const int64_t a = argmax_lowest(rows[(size_t)cur]);
+      for (int c : ch)
+        if (tok[c] == a) next = c;
+      if (next < 0) {
+        out[depth] = (int32_t)a;
+        onode[depth] = cur;
+        io.num_emitted[b] = depth + 1;
+        return;
+      }
+    } else {
+      softmax_T(rows[(size_t)cur], T, p);
+      if (!ch.empty()) {
+        const double ut = (double)u[depth];
+        double run = 0.0, g = std::numeric_limits<double>::infinity();
+        for (int c : ch) {
+          run += p[(size_t)tok[c]];
+          g = std::min(g, std::fabs(ut - run));
+          if (next < 0 && ut <= run) next = c;
+        }
+        gap[depth] = g;
+      }
+      if (next < 0) {
+        // no child passed (or a leaf): draw from p without the children
+        w = p;
+        for (int c : ch) w[(size_t)tok[c]] = 0.0;
+        double S = 0.0;
+        for (double v : w) S += v;
+        if (!(S > 0.0)) w = p;
+        out[depth] = (int32_t)inv_cdf(w, (double)u[N - 1], &io.cdf_lo[b], &io.cdf_hi[b]);
+        onode[depth] = cur;
+        io.num_emitted[b] = depth + 1;
+        return;
+      }
+    }
+    out[depth] = tok[next];
+    onode[depth] = next;
+    cur = next;
+    ++depth;
+  }
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -583,6 +718,27 @@ void orc_verify(const void* logits, int32_t dtype, int32_t B, int32_t K,
   for (int t = 0; t < nthreads; ++t)
     ts.emplace_back([&, t] {
       for (int b = t; b < B; b += nthreads) verify_one(io, b);
+    });
+  for (auto& th : ts) th.join();
+}
+
+void orc_verify_tree(const void* logits, int32_t dtype, int32_t B, int32_t N,
+                     int32_t V, const int32_t* tokens, const int32_t* parent,
+                     const int32_t* n_nodes, const float* temperature,
+                     const float* uniforms, int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* num_emitted, double* gap, double* cdf_lo,
+                     double* cdf_hi, int32_t* status, int32_t nthreads) {
+  TreeIO io{logits,      dtype,    B,          N,         V,     tokens,
+            parent,      n_nodes,  temperature, uniforms, out_tokens, out_nodes,
+            num_emitted, gap,      cdf_lo,     cdf_hi,    status};
+  if (nthreads <= 1) {
+    for (int b = 0; b < B; ++b) verify_tree_one(io, b);
+    return;
+  }
+  std::vector<std::thread> ts;
+  for (int t = 0; t < nthreads; ++t)
+    ts.emplace_back([&, t] {
+      for (int b = t; b < B; b += nthreads) verify_tree_one(io, b);
     });
   for (auto& th : ts) th.join();
 }
