@@ -60,9 +60,11 @@ extern "C" {
 #define SS_ST_NO_UNIFORMS (1 << 5)  /* T > 0 but uniforms == NULL */
 #define SS_ST_COUNT (1 << 6)        /* extend count outside [0, ld_tokens] */
 #define SS_ST_TOP_P (1 << 7)        /* top_p NaN or outside (0, 1] */
+#define SS_ST_TREE (1 << 8)         /* malformed draft tree (spec_verify_tree) */
 
 #define SS_MAX_K 16            /* largest number of drafted tokens */
 #define SS_MAX_LEN (1 << 24)   /* largest automaton capacity, tokens */
+#define SS_MAX_TREE 64         /* largest draft tree, nodes (root included) */
 
 #define SS_DTYPE_F32 0
 #define SS_DTYPE_BF16 1
@@ -214,6 +216,48 @@ int spec_finish(const void* logits, int dtype, int B, int K, int V,
                 int32_t* next_draft, int32_t* next_draft_len,
                 int32_t* next_match_len, void* workspace, size_t ws_bytes,
                 void* stream);
+
+/*
+ * spec_verify_tree — verification of one draft tree per sequence ([P3]
+ * "SGLang 的实现": the target-only tree sampling, taken with both of its
+ * acceptance thresholds at 1, its lossless case).
+ *
+ * Tree of sequence b: node 0 is the root (the last committed token); nodes
+ * 1..n_nodes[b]-1 each carry a drafted token tokens[b,i] and a parent
+ * parent[b,i] < i (parent[b,0] = -1). Logit row i of the sequence scores the
+ * token after the path root..i. The children of a node are taken in
+ * increasing node index and must carry distinct tokens.
+ *   T = 0: from the root, move to the child whose token is the argmax of the
+ *     current node's row (lowest index on ties); when there is none, emit the
+ *     argmax and stop.
+ *   T > 0: at depth t (t tokens accepted so far), with p = softmax(l_cur / T),
+ *     the children c_1, c_2, ... add p(token) to a running sum in node order;
+ *     the first child with u[b,t] <= its running sum is accepted. When none
+ *     is, the final token is drawn with u[b,N-1] (inverse CDF in ascending
+ *     token order, as spec_verify) from p with every child's token removed;
+ *     at a leaf, from the leaf's row. Each emitted token is then distributed
+ *     as the target's p.
+ * Arguments:
+ *   logits      [B, N, V] (dtype as spec_verify); rows >= n_nodes[b] unread.
+ *   tokens, parent [B, N] int32; n_nodes [B] int32 in [1, N].
+ *   temperature [B]; uniforms [B, N] float in [0, 1) (coins per depth, the
+ *               last column the final coin), NULL only if every T is 0.
+ *   out_tokens  [B, N] int32: accepted tokens then the final token, -1 after.
+ *   out_nodes   [B, N] int32: the node each emitted token came from (the
+ *               accepted child; for the final token the node whose row it was
+ *               drawn from), -1 after.
+ *   num_emitted [B] = accepted + 1. status [B] OR-ed with SS_ST_* (SS_ST_TREE
+ *               for a malformed tree or n_nodes outside [1, N]).
+ *   workspace   ss_tree_workspace_bytes(B, N, V), 256-byte aligned.
+ * Limits: 1 <= B, 1 <= N <= SS_MAX_TREE, 1 <= V <= 2^21.
+ */
+size_t ss_tree_workspace_bytes(int B, int N, int V);
+int spec_verify_tree(const void* logits, int dtype, int B, int N, int V,
+                     const int32_t* tokens, const int32_t* parent,
+                     const int32_t* n_nodes, const float* temperature,
+                     const float* uniforms, int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* num_emitted, int32_t* status, void* workspace,
+                     size_t ws_bytes, void* stream);
 
 /* ========================================================================= *
  * Dynamic suffix automaton ([P1] §1.1, [P4] §3)

@@ -29,6 +29,8 @@ ST_TEMPERATURE = 1 << 4
 ST_NO_UNIFORMS = 1 << 5
 ST_COUNT = 1 << 6
 ST_TOP_P = 1 << 7
+ST_TREE = 1 << 8
+MAX_TREE = 64
 MAX_K = 16
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
@@ -67,6 +69,11 @@ def lib():
     L.spec_finish.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
                               P, P, P, P, i32, P, P, P, P, sz, P]
     L.spec_finish.restype = i32
+    L.ss_tree_workspace_bytes.argtypes = [i32, i32, i32]
+    L.ss_tree_workspace_bytes.restype = sz
+    L.spec_verify_tree.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                   P, sz, P]
+    L.spec_verify_tree.restype = i32
     L.sam_extend_draft.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P]
     L.sam_extend_draft.restype = i32
     L.sam_state_bytes.argtypes = [i32, i32]
@@ -256,6 +263,54 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
     _check(lib().spec_step(*args), "spec_step")
     return (out_tokens, num_emitted, p_draft, status, next_draft,
             next_draft_len, next_match_len)
+
+
+def tree_workspace(B: int, N: int, V: int, device=None):
+    """A workspace tensor for spec_verify_tree calls of this size."""
+    n = int(lib().ss_tree_workspace_bytes(B, N, V))
+    if n == 0:
+        raise SpecSamError(f"unsupported sizes B={B} N={N} V={V}")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def spec_verify_tree(logits, tokens, parent, n_nodes, temperature, uniforms=None, *,
+                     workspace=None, out_tokens=None, out_nodes=None,
+                     num_emitted=None, status=None, stream=None):
+    """Verify one draft tree per sequence (see include/specsam.h). Returns
+    (out_tokens [B,N] int32, out_nodes [B,N] int32, num_emitted [B] int32,
+    status [B] int32)."""
+    if logits.dim() != 3:
+        raise SpecSamError("logits must be [B, N, V]")
+    B, N, V = logits.shape
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(logits.dtype)
+    if dt is None:
+        raise SpecSamError("logits must be float32 or bfloat16")
+    dev = logits.device
+    i32 = torch.int32
+    if workspace is None:
+        workspace = tree_workspace(B, N, V, dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=i32, device=dev)
+    if out_nodes is None:
+        out_nodes = torch.empty((B, N), dtype=i32, device=dev)
+    if num_emitted is None:
+        num_emitted = torch.empty(B, dtype=i32, device=dev)
+    if status is None:
+        status = torch.zeros(B, dtype=i32, device=dev)
+    _check(lib().spec_verify_tree(
+        _dev(logits, "logits"), dt, B, N, V,
+        _dev(tokens, "tokens", i32, (B, N)),
+        _dev(parent, "parent", i32, (B, N)),
+        _dev(n_nodes, "n_nodes", i32, (B,)),
+        _dev(temperature, "temperature", torch.float32, (B,)),
+        _opt_f32(uniforms, "uniforms", (B, N)),
+        _dev(out_tokens, "out_tokens", i32, (B, N)),
+        _dev(out_nodes, "out_nodes", i32, (B, N)),
+        _dev(num_emitted, "num_emitted", i32, (B,)),
+        _dev(status, "status", i32, (B,)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)), "spec_verify_tree")
+    return out_tokens, out_nodes, num_emitted, status
 
 
 def _shape(logits):

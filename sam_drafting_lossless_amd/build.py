@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LIB = os.path.join(PKG, "libspecsam.so")
 HARNESS_LIB = os.path.join(PKG, "libspecsam_harness.so")
 
-LIB_SOURCES = ["api.hip", "stream.hip", "trunc.hip", "verify.hip", "sam.hip"]
+LIB_SOURCES = ["api.hip", "stream.hip", "trunc.hip", "tree.hip", "verify.hip", "sam.hip"]
 HARNESS_SOURCES = ["harness.hip"]
 
 # Packed FP32 instructions are disabled: hipcc would otherwise form them from

@@ -95,7 +95,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
   const float kk = greedy ? 0.0f : kLog2e / T;
   // The logit of the draft token, when it lies in this chunk.
   float lx = 0.0f;
-  if (!greedy && j < d && tid == 0) {
+  if (!greedy && j < d && tid == 0 && a.draft) {
     const int x = a.draft[(int64_t)b * a.K + j];
     if (x >= cstart && x < cstart + kChunk<DT> && x < a.V) lx = load_one<DT>(rowp, x);
   }
@@ -268,7 +268,7 @@ __device__ __forceinline__ Item decode_extra(int x, int nc, int B, const int* pr
 // Extra rows of one sequence: draft_len when it is in [1, K], else 0
 // (invalid lengths are reported by finalize and need no rows).
 __device__ __forceinline__ int extra_rows(const Args& a, int b) {
-  const int v = a.draft_len[b];
+  const int v = a.draft_len[b] + a.dl_offset;
   return (v >= 1 && v <= a.K) ? v : 0;
 }
 

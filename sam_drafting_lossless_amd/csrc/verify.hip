@@ -28,251 +28,10 @@
 // lands in the kernel's tail.
 #include <algorithm>
 
-#include "verify_common.h"
+#include "draw.h"
 
 namespace specsam {
 namespace {
-
-// ---------------------------------------------------------------------------
-// Draw from one row by inverse CDF in ascending token order: the first token
-// whose running weight exceeds u * total (strict, so zero weights are never
-// chosen). Weights are exp2((l - m) * kk) with token `excl` removed (one-hot
-// residual; excl < 0 for the bonus), or, for RESIDUAL, max(0, exp2((l - m) *
-// kk) / S - q).
-//
-// pick_chunk (one wavefront): the chunk weights, from the stream pass's
-// partials, are scanned in chunk order and the first chunk whose running sum
-// exceeds u * total is taken, with the target left inside it; if rounding
-// leaves none, the last chunk with positive weight (its last positive token
-// is then drawn). draw_in_chunk (whole workgroup): that chunk is re-read with
-// the stream pass's layout, in which token order is (load, lane, element).
-// Each lane sums its 8 vectors; the 32 (load, wavefront) cell totals are
-// scanned in token order to find the cell, a wavefront scan inside the cell
-// finds the lane, and that lane scans its vector. The cell totals and the
-// lane scan come from the same inclusive scan, so the search is consistent;
-// a target beyond the chunk's re-read total (a rounding difference with the
-// partials) takes the chunk's last positive weight.
-// ---------------------------------------------------------------------------
-struct ChunkPick {
-  int chunk;   // -1: every weight is 0
-  float t_in;  // target left inside the chunk; +inf: take its last positive
-};
-
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// One wavefront, all lanes active; weight(c) is called for c < nc.
-template <typename WeightFn>
-__device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight) {
-  constexpr int kGroups = kMaxChunks / kWave;
-  const int l = lane_id();
-  float W[kGroups], cum[kGroups];
-  float carry = 0.0f;
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    W[g] = 0.0f;
-    cum[g] = carry;
-    if (g * kWave < nc) {
-      const int c = g * kWave + l;
-      W[g] = c < nc ? weight(c) : 0.0f;
-      cum[g] = wave_inclusive_sum(W[g]) + carry;
-      carry = lane63(cum[g]);
-    }
-  }
-  const float t = u * carry;
-  ChunkPick r{-1, INFINITY};
-  int lastpos = -1;
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    if (g * kWave < nc) {
-      const int c = g * kWave + l;
-      const unsigned long long hit = __ballot(c < nc && cum[g] > t);
-      const unsigned long long pos = __ballot(c < nc && W[g] > 0.0f);
-      if (hit && r.chunk < 0) {
-        const int ln = __ffsll((unsigned long long)hit) - 1;
-        r.chunk = g * kWave + ln;
-        r.t_in = t - (readlane_f(cum[g], ln) - readlane_f(W[g], ln));
-      }
-      if (pos) lastpos = g * kWave + 63 - __clzll((unsigned long long)pos);
-    }
-  }
-  if (r.chunk < 0) r.chunk = lastpos;
-  return r;
-}
-
-struct DrawShared {
-  float cell[kLoads * kWaves];  // (load, wave) totals in token order
-  int wlast[kWaves];
-  int result;
-  float result_l;  // the drawn token's logit (NaN if the draw did not see it)
-};
-
-// Weight of a token with logit l (token index i); tokens below the
-// truncation threshold lam have probability 0.
-template <int DT, bool RESIDUAL>
-__device__ __forceinline__ float draw_weight(float l, int i, int excl, float m,
-                                             float kk, float invS, float qi,
-                                             float lam) {
-  const float w = (l >= lam) ? fast_exp2((l - m) * kk) : 0.0f;
-  if constexpr (RESIDUAL)
-    return fmaxf(0.0f, w * invS - qi);
-  else
-    return (i == excl) ? 0.0f : w;
-}
-
-// q values for the kVec elements of one raw vector (RESIDUAL only).
-template <int DT, bool VP>
-__device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int tid,
-                                           int it, int V, float (&qv)[kVec<DT>]) {
-#pragma unroll
-  for (int k = 0; k < kVec<DT>; ++k) {
-    const int i = elem_index<DT, VP>(cstart, tid, it, k);
-    qv[k] = i < V ? qrow[i] : 0.0f;
-  }
-}
-
-constexpr float kLn2 = 0.69314718055994531f;
-
-// Log-probability of token `tok` drawn from row r: (l - m) / T - log S with
-// the row's (m, S) at scale kk = log2(e) / T. lt is the token's logit as the
-// draw saw it; NaN (a rounding fallback) reads it from the row.
-template <int DT>
-__device__ __forceinline__ float drawn_logprob(const Args& a, int b, int r, int tok,
-                                               float lt, float m, float S, float kk) {
-  if (tok < 0) return NAN;
-  if (lt != lt)
-    lt = load_one<DT>(a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes,
-                      tok);
-  return ((lt - m) * kk - log2f(S)) * kLn2;
-}
-
-struct NoDuring {
-  __device__ void operator()() const {}
-};
-
-// Requests the chosen chunk of row r (nothing if every weight is 0).
-template <int DT, bool VP>
-__device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick pk,
-                                          u32x4 (&raw)[kLoads]) {
-  if (pk.chunk < 0) return;
-  const unsigned char* row =
-      a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes;
-  load_chunk<DT, VP, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
-}
-
-// Whole workgroup; `pk` must be the same in every thread and `raw` hold the
-// chunk draw_load requested. `during` runs first, while that chunk is still
-// in flight (the fused step appends the accepted drafts to the automaton
-// there).
-template <int DT, bool VP, bool RESIDUAL, typename During = NoDuring>
-__device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
-                             ChunkPick pk, int excl, float m, float kk,
-                             float invS, float lam, const u32x4 (&raw)[kLoads],
-                             During during = During{}) {
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  during();
-  if (pk.chunk < 0) return -1;
-  const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
-  const int cstart = pk.chunk * kChunk<DT>;
-  float vs[kLoads];
-  int tlast = -1;
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it) {
-    float qv[kVec<DT>];
-    if constexpr (RESIDUAL) load_q_vec<DT, VP>(qrow, cstart, tid, it, a.V, qv);
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const int i = elem_index<DT, VP>(cstart, tid, it, k);
-      const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
-                                                 kk, invS, RESIDUAL ? qv[k] : 0.0f,
-                                                 lam);
-      acc += wk;
-      if (wk > 0.0f) tlast = max(tlast, i);
-    }
-    vs[it] = acc;
-  }
-  // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
-  float tot[kLoads];
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum(vs[it]);
-  const int wl = wave_max_i(tlast);
-  if (l == 0) {
-#pragma unroll
-    for (int it = 0; it < kLoads; ++it) sh.cell[it * kWaves + w] = tot[it];
-    sh.wlast[w] = wl;
-  }
-  __syncthreads();
-  // Every wavefront finds the cell (the same scan gives the same answer).
-  const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
-  const float inc = wave_inclusive_sum(cv);
-  const float exc = wave_shift_up1(inc);
-  const unsigned long long hit =
-      __ballot(l < kLoads * kWaves && exc <= pk.t_in && pk.t_in < inc);
-  int clast = sh.wlast[0];
-  for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
-  const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
-  if (cell < 0) {
-    if (tid == 0) {
-      sh.result = clast;  // the chunk's last positive weight
-      sh.result_l = NAN;
-    }
-  } else if (w == cell % kWaves) {
-    const int its = cell / kWaves;
-    float v = vs[0];
-#pragma unroll
-    for (int it = 1; it < kLoads; ++it)
-      if (it == its) v = vs[it];
-    const float tc = pk.t_in - readlane_f(exc, cell);
-    const float inc2 = wave_inclusive_sum(v);
-    const float exc2 = wave_shift_up1(inc2);
-    const bool mine = exc2 <= tc && tc < inc2;
-    const unsigned long long who = __ballot(mine);
-    if (!who) {
-      if (l == 0) {
-        sh.result = clast;
-        sh.result_l = NAN;
-      }
-    } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
-      const float tl = tc - exc2;
-      u32x4 rv = raw[0];
-#pragma unroll
-      for (int it = 1; it < kLoads; ++it)
-        if (it == its) rv = raw[it];
-      float qv[kVec<DT>];
-      if constexpr (RESIDUAL) {
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) {
-          const int i = elem_index<DT, VP>(cstart, tid, its, k);
-          qv[k] = i < a.V ? qrow[i] : 0.0f;
-        }
-      }
-      float run = 0.0f, lfound = NAN, llast = NAN;
-      int found = -1, lastp = -1;
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const int i = elem_index<DT, VP>(cstart, tid, its, k);
-        const float lk = elem<DT>(rv, k);
-        const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
-                                                   RESIDUAL ? qv[k] : 0.0f, lam);
-        run += wk;
-        if (wk > 0.0f) {
-          lastp = i;
-          llast = lk;
-        }
-        if (found < 0 && run > tl) {
-          found = i;
-          lfound = lk;
-        }
-      }
-      sh.result = found >= 0 ? found : lastp;
-      sh.result_l = found >= 0 ? lfound : llast;
-    }
-  }
-  __syncthreads();
-  return sh.result;
-}
 
 // Chunk partials of all K+1 rows are cached in LDS when they fit.
 constexpr int kPartialCache = 1024;
@@ -537,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   int appended = 0;
   const bool drawn = sh.st == 0 && !greedy && !residual;
   if (drawn) {
-    const int excl = (al < d) ? sh.x[al] : -1;
+    const OneToken excl{(al < d) ? sh.x[al] : -1};
     if (!spec || al != d) draw_load<DT, VP>(a, b, al, sh.pick[al], raw);
     auto during = [&]() {
       if constexpr (SAM) {
@@ -676,10 +435,12 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   __syncthreads();
   u32x4 raw[kLoads];
   draw_load<DT, VP>(a, b, r, pick_sh, raw);
-  const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, -1, m,
-                                                        kk, 0.0f, lam, raw)
-                         : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, -1, m,
-                                                       kk, 1.0f / S, lam, raw);
+  const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh,
+                                                        OneToken{-1}, m, kk, 0.0f,
+                                                        lam, raw)
+                         : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh,
+                                                       OneToken{-1}, m, kk, 1.0f / S,
+                                                       lam, raw);
   if (tid == 0) {
     a.out[(int64_t)b * R + r] = tok;
     if (a.logprob)
@@ -806,6 +567,8 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.nchunks = nchunks_for(V, dtype);
   a.draft = draft;
   a.draft_len = draft_len;
+  a.dl_offset = 0;
+  a.dl_status = SS_ST_DRAFT_LEN;
   a.q = q;
   a.temperature = temperature;
   a.uniforms = uniforms;
@@ -878,6 +641,62 @@ extern "C" size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags) {
 
 extern "C" size_t ss_verify_workspace_bytes(int B, int K, int V) {
   return ss_verify_workspace_bytes_ex(B, K, V, 0);
+}
+
+extern "C" size_t ss_tree_workspace_bytes(int B, int N, int V) {
+  if (B < 1 || N < 1 || N > SS_MAX_TREE || V < 1 || V > kMaxV) return 0;
+  return ws_layout(B, N - 1, V, false).total;
+}
+
+extern "C" int spec_verify_tree(const void* logits, int dtype, int B, int N, int V,
+                                const int32_t* tokens, const int32_t* parent,
+                                const int32_t* n_nodes, const float* temperature,
+                                const float* uniforms, int32_t* out_tokens,
+                                int32_t* out_nodes, int32_t* num_emitted,
+                                int32_t* status, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  const char* fn = "spec_verify_tree";
+  if (B < 1 || N < 1 || N > SS_MAX_TREE || V < 1 || V > kMaxV)
+    return set_error(SS_EINVAL, "%s: need B >= 1, 1 <= N <= %d, 1 <= V <= %d "
+                                "(got B=%d N=%d V=%d)", fn, SS_MAX_TREE, kMaxV, B, N, V);
+  if (dtype != SS_DTYPE_F32 && dtype != SS_DTYPE_BF16)
+    return set_error(SS_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (!logits || !tokens || !parent || !n_nodes || !temperature || !out_tokens ||
+      !out_nodes || !num_emitted || !status || !workspace)
+    return set_error(SS_EINVAL, "%s: a required pointer is NULL", fn);
+  if ((uintptr_t)workspace & 255)
+    return set_error(SS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  const WsLayout L = ws_layout(B, N - 1, V, false);
+  if (ws_bytes < L.total)
+    return set_error(SS_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
+                     L.total);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  Args a{};
+  a.logits = reinterpret_cast<const unsigned char*>(logits);
+  a.B = B;
+  a.K = N - 1;  // rows per sequence: N, of which n_nodes[b] are read
+  a.V = V;
+  a.nchunks = nchunks_for(V, dtype);
+  a.draft = nullptr;
+  a.draft_len = n_nodes;
+  a.dl_offset = -1;
+  a.dl_status = SS_ST_TREE;
+  a.temperature = temperature;
+  a.uniforms = uniforms;
+  a.out = out_tokens;
+  a.nem = num_emitted;
+  a.status = status;
+  a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
+  a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
+  a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
+  a.rpart = reinterpret_cast<float*>(ws + L.rpart);
+  const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
+  const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0);
+  const bool f32 = dtype == SS_DTYPE_F32;
+  hipStream_t s = as_stream(stream);
+  int rc = launch_stream(a, f32, vp, s);
+  if (rc != SS_OK) return rc;
+  return launch_tree_finalize(a, f32, vp, tokens, parent, out_nodes, s);
 }
 
 extern "C" int spec_verify(const void* logits, int dtype, int B, int K, int V,

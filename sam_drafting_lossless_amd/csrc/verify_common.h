@@ -149,6 +149,8 @@ struct Args {
   int B, K, V, nchunks, rows_per_wg, ngroups;
   const int32_t* draft;
   const int32_t* draft_len;
+  int dl_offset;    // rows needed = draft_len[b] + dl_offset + 1 (trees: -1)
+  int dl_status;    // status bit for a length outside [0, K]
   const float* q;
   const float* temperature;
   const float* uniforms;
@@ -187,10 +189,10 @@ struct Args {
 
 // Per-sequence checks that need device data.
 __device__ __forceinline__ int seq_check(const Args& a, int b, int* d, float* T) {
-  *d = a.draft_len[b];
+  *d = a.draft_len[b] + a.dl_offset;
   *T = a.temperature[b];
   int st = 0;
-  if (*d < 0 || *d > a.K) st |= SS_ST_DRAFT_LEN;
+  if (*d < 0 || *d > a.K) st |= a.dl_status;
   // T = 0 is greedy; otherwise T must be a finite normal positive float so
   // that log2(e)/T stays finite.
   if (!(*T == 0.0f || (*T >= 1.17549435e-38f && isfinite(*T))))
@@ -275,6 +277,11 @@ __device__ __forceinline__ float load_f32(const float* p) { return *p; }
 // rows each sequence needs. f32 selects fp32 logits (else bf16); vp the
 // 16-byte vector path (rows 16-byte aligned and V a multiple of the vector).
 int launch_stream(Args a, bool f32, bool vp, hipStream_t s);
+
+// Launches the tree finalize kernel (tree.hip) after the stream pass over
+// every node's row: one workgroup per sequence.
+int launch_tree_finalize(const Args& a, bool f32, bool vp, const int32_t* tokens,
+                         const int32_t* parent, int32_t* out_nodes, hipStream_t s);
 
 // Launches the truncation passes (trunc.hip) after the stream pass: plan,
 // candidate extraction and threshold selection for every truncated row.

@@ -1,0 +1,163 @@
+"""Draft-tree verification ([P3] gogongxt notes "SGLang 的实现", the
+target-only tree walk with both thresholds at 1) on the GPU through the C
+ABI, against the oracle.
+
+Bars: greedy trees bit-exact (tokens, nodes, counts); T > 0 equal except
+where the oracle found a depth's coin within TIE of a running sum, or the
+final coin within TIE of a CDF breakpoint (such sequences are set aside and
+counted); status words equal."""
+import numpy as np
+import pytest
+import torch
+from scipy import special, stats
+
+import oracle
+import sam_drafting_lossless_amd as ssl
+from _parity import TIE, dev, say, to_host_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _trees(rng, B, N, V, x):
+    """Random trees with distinct sibling tokens; children are often the
+    parent row's top tokens, and their logits are raised in the parent's row
+    so that acceptances happen."""
+    tok = np.zeros((B, N), np.int32)
+    par = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            p = int(rng.integers(max(0, i - 4), i)) if rng.random() < 0.7 else int(rng.integers(0, i))
+            used = {int(tok[b, c]) for c in range(1, i) if par[b, c] == p}
+            top = np.argsort(-x[b, p])[:4]
+            t = int(top[rng.integers(0, 4)]) if rng.random() < 0.6 else int(rng.integers(0, V))
+            while t in used:
+                t = (t + 1) % V
+            par[b, i], tok[b, i] = p, t
+            x[b, p, t] += rng.uniform(0, 3)
+    return tok, par
+
+
+def _run(t, tok, par, n, T, u):
+    g = ssl.spec_verify_tree(t, dev(tok), dev(par), dev(n), dev(T, torch.float32),
+                             None if u is None else dev(u, torch.float32))
+    torch.cuda.synchronize()
+    return tuple(a.cpu().numpy() for a in g)
+
+
+def _compare(g, r, T, u, what):
+    out, nodes, nem, st = g
+    np.testing.assert_array_equal(st, r.status, err_msg=f"{what} status")
+    ties = 0
+    for b in range(len(T)):
+        if r.status[b]:
+            continue
+        same = (nem[b] == r.num_emitted[b] and (out[b] == r.out_tokens[b]).all()
+                and (nodes[b] == r.out_nodes[b]).all())
+        if T[b] == 0.0:
+            assert same, (what, b, out[b], r.out_tokens[b])
+            continue
+        if not same:
+            g_ = np.nanmin(np.where(np.isnan(r.gap[b]), np.inf, r.gap[b]))
+            fc = float(u[b, -1])
+            near = g_ <= TIE or min(abs(fc - r.cdf_lo[b]), abs(fc - r.cdf_hi[b])) <= TIE
+            assert near, (what, b, out[b], r.out_tokens[b], nodes[b], r.out_nodes[b])
+            ties += 1
+    return ties
+
+
+@pytest.mark.parametrize("B,N,V", [(16, 8, 32), (12, 16, 8193), (8, 32, 30011),
+                                   (6, 64, 151936), (5, 1, 100), (9, 5, 3 * 8192 + 4)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tree_matches_oracle(B, N, V, dtype):
+    say(f"[gpu] tree {dtype} B={B} N={N} V={V}")
+    rng = np.random.default_rng(B * 7 + N * 131 + V + (dtype == "bf16"))
+    x = (rng.standard_normal((B, N, V)) * 1.5).astype(np.float32)
+    tok, par = _trees(rng, B, N, V, x)
+    n = rng.integers(1, N + 1, B).astype(np.int32)
+    T = rng.uniform(0.4, 1.5, B).astype(np.float32)
+    T[rng.random(B) < 0.3] = 0.0
+    u = rng.random((B, N)).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    xh = to_host_logits(t)
+    g = _run(t, tok, par, n, T, u)
+    r = oracle.verify_tree(xh, tok, par, n, T, u, nthreads=8)
+    ties = _compare(g, r, T, u, f"tree {dtype}")
+    assert (g[2] > 1).any() or N == 1  # some drafts were accepted
+    say(f"    ties={ties} emitted={int(g[2][r.status == 0].sum())}")
+
+
+def test_chain_tree_equals_linear_verification():
+    """A chain is the linear case: the tree entry point and spec_verify agree
+    on the same rows, drafts and coins."""
+    say("[gpu] tree: chains against spec_verify")
+    rng = np.random.default_rng(5)
+    B, N, V = 64, 5, 8193
+    x = (rng.standard_normal((B, N, V)) * 1.5).astype(np.float32)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            tok[b, i] = x[b, i - 1].argmax() if rng.random() < 0.6 else rng.integers(0, V)
+            x[b, i - 1, tok[b, i]] += rng.uniform(0, 3)
+    par = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    n = rng.integers(1, N + 1, B).astype(np.int32)
+    T = np.where(rng.random(B) < 0.4, 0.0, 0.9).astype(np.float32)
+    u = rng.random((B, N)).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    g = _run(t, tok, par, n, T, u)
+    lin = ssl.spec_verify(t, dev(tok[:, 1:]), dev(n - 1), dev(T), dev(u))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g[0], lin[0].cpu().numpy())
+    np.testing.assert_array_equal(g[2], lin[1].cpu().numpy())
+
+
+def test_chi_square_on_device():
+    """The first emitted token follows p_root; after node 1 is accepted the
+    second follows p_1; after the leaf node 2, p_2 (V = 8, 400k sequences)."""
+    say("[gpu] tree chi-square")
+    rng = np.random.default_rng(6)
+    V, N, M = 8, 6, 400_000
+    rows = (rng.standard_normal((N, V)) * 1.2).astype(np.float32)
+    tok = np.array([0, 3, 5, 1, 2, 3], np.int32)
+    par = np.array([-1, 0, 0, 0, 1, 1], np.int32)
+    T = np.float32(0.9)
+    x = torch.from_numpy(rows).cuda().expand(M, N, V).contiguous()
+    u = rng.random((M, N)).astype(np.float32)
+    out, nodes, nem, st = _run(x, np.tile(tok, (M, 1)), np.tile(par, (M, 1)),
+                               np.full(M, N, np.int32), np.full(M, T, np.float32), u)
+    assert (st == 0).all()
+    p = special.softmax(rows.astype(np.float64) / float(T), axis=1)
+    pv = [stats.chisquare(np.bincount(out[:, 0], minlength=V), p[0] * M).pvalue]
+    for node in (1, 2):
+        sel = nodes[:, 0] == node
+        pv.append(stats.chisquare(np.bincount(out[sel, 1], minlength=V),
+                                  p[node] * sel.sum()).pvalue)
+    say(f"    p-values {pv}")
+    assert min(pv) > 1e-3
+
+
+def test_tree_status_and_errors():
+    say("[gpu] tree: status words and host errors")
+    V, N = 10, 4
+    x = np.zeros((7, N, V), np.float32)
+    tok = np.array([[0, 1, 2, 3]] * 7, np.int32)
+    par = np.array([[-1, 0, 0, 1]] * 7, np.int32)
+    n = np.full(7, N, np.int32)
+    tok[0, 2] = 1          # duplicate sibling token
+    par[1, 2] = 2          # parent not before the node
+    tok[2, 3] = V          # token out of range
+    n[3] = 0               # no root
+    par[4, 0] = 0          # root with a parent
+    x[5, 1, 3] = np.nan    # a row with NaN
+    n[6] = N + 1           # more nodes than rows
+    T = np.zeros(7, np.float32)
+    g = _run(torch.from_numpy(x).cuda(), tok, par, n, T, None)
+    r = oracle.verify_tree(x, tok, par, np.minimum(n, N + 1), T)
+    want = [ssl.ST_TREE] * 5 + [ssl.ST_NONFINITE, ssl.ST_TREE]
+    assert g[3].tolist() == want
+    assert r.status.tolist() == want
+    with pytest.raises(ssl.SpecSamError, match="N=65"):
+        ssl.spec_verify_tree(torch.zeros((1, 65, 8), device="cuda"),
+                             *(dev(np.zeros((1, 65), np.int32)) for _ in range(2)),
+                             dev(np.ones(1, np.int32)), dev(np.zeros(1, np.float32)))
