@@ -564,6 +564,89 @@ def measure_draft_model_workload(cfg, steps: int, warmup: int) -> dict:
     }
 
 
+def measure_tree_workload(cfg, steps: int, warmup: int) -> dict:
+    """Draft-tree verification (spec_verify_tree): every sequence carries an
+    8-node tree (the root with three candidate continuations, one of them
+    four deep); the stream pass reads all 8 rows of every sequence, the tree
+    kernel walks it. Two resident slots of target logits [B, 8, V] (2.5 GB at
+    c3's B and V), the nodes of the first candidate's path raised by cfg.boost
+    in their parents' rows so that walks go deep."""
+    import numpy as np
+    import torch
+
+    import sam_drafting_lossless_amd as ssl
+    import synth
+    dev = torch.device("cuda:0")
+    B, V = cfg.B, cfg.V
+    N = len(synth.TREE8_PARENTS)
+    nslots = 2
+    slots = []
+    for i in range(nslots):
+        x = synth.noise(cfg, i, dev, rows_per_seq=N)
+        tok, par, chain = synth.draft_trees(cfg, i)
+        bi, ni = np.nonzero(chain)
+        x[torch.as_tensor(bi, device=dev), torch.as_tensor(par[bi, ni], device=dev),
+          torch.as_tensor(tok[bi, ni].astype(np.int64), device=dev)] += cfg.boost
+        slots.append((x, torch.as_tensor(tok, device=dev), torch.as_tensor(par, device=dev)))
+    total = warmup + 2 * steps
+    u_all = torch.as_tensor(
+        np.stack([synth.tree_uniforms(cfg, s, N) for s in range(total)]), device=dev)
+    temp = torch.full((B,), cfg.T, dtype=torch.float32, device=dev)
+    nn = torch.full((B,), N, dtype=torch.int32, device=dev)
+    out = torch.empty((B, N), dtype=torch.int32, device=dev)
+    onode = torch.empty((B, N), dtype=torch.int32, device=dev)
+    nem_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = ssl.tree_workspace(B, N, V, dev)
+    torch.cuda.synchronize()
+    L = ssl.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    u0, nem0, rowU, rowB = u_all.data_ptr(), nem_hist.data_ptr(), B * N * 4, B * 4
+
+    def call(s):
+        x, tk, pr = slots[s % nslots]
+        rc = L.spec_verify_tree(x.data_ptr(), 0, B, N, V, tk.data_ptr(), pr.data_ptr(),
+                                nn.data_ptr(), temp.data_ptr(), u0 + s * rowU,
+                                out.data_ptr(), onode.data_ptr(), nem0 + s * rowB,
+                                status.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        if rc:
+            raise RuntimeError("spec_verify_tree failed: " + L.ss_last_error_string().decode())
+
+    for s in range(warmup):
+        call(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        call(warmup + steps + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    if int(status.cpu().abs().sum()) != 0:
+        raise RuntimeError("status words are non-zero: the run is invalid")
+    call_us = np.array([1e3 * a.elapsed_time(b) for a, b in evs])
+    nem = nem_hist[warmup:warmup + steps].cpu().numpy()
+    stream_bytes = B * N * V * 4
+    return {
+        "workload": cfg.name, "dtype": cfg.dtype, "B": B, "V": V, "tree_nodes": N,
+        "tree_parents": list(synth.TREE8_PARENTS), "T": cfg.T, "steps": steps,
+        "steps_per_s": steps / elapsed, "us_per_step": elapsed * 1e6 / steps,
+        "call_event_us_p10_p50_p90": [round(float(v), 2) for v in
+                                      np.percentile(call_us, [10, 50, 90])],
+        "rows_per_step": B * N, "stream_bytes_per_step": stream_bytes,
+        "whole_call_GBps": stream_bytes / (elapsed / steps) / 1e9,
+        "mean_tokens_per_step": float(nem.mean()),
+        "emitted_histogram": {str(k): int(c) for k, c in
+                              enumerate(np.bincount(nem.ravel(), minlength=N + 1)[1:], 1)},
+        "slots": nslots,
+    }
+
+
 # Workloads beside the headline one. c3 with truncation takes the pages'
 # sampling setting for their end-to-end throughput figure (T = 0.7,
 # top_p = 0.9), with and without top_k = 50.
@@ -577,6 +660,8 @@ def _workload_configs():
                                 T=0.7, top_p=0.9),
         "c3_topk_topp": synth.config(3, name="c3_b256_v151936_k3_t0.7_topk50_topp0.9_onehot",
                                      T=0.7, top_k=50, top_p=0.9),
+        "c3_tree8": synth.config(3, name="c3_b256_v151936_t1_tree8", q_mode="tree",
+                                 boost=12.0),
     }
 
 
@@ -590,6 +675,8 @@ def workloads_report(steps: int, warmup: int, names: str = "all"):
         cfg = cfgs[n]
         if cfg.q_mode == "model":
             line = measure_draft_model_workload(cfg, steps, warmup)
+        elif cfg.q_mode == "tree":
+            line = measure_tree_workload(cfg, steps, warmup)
         else:
             line = _sam_workload_line(cfg, measure_sam_workload(cfg, steps, warmup),
                                       steps)
@@ -608,7 +695,7 @@ def main():
                     help="report automaton work per token instead")
     ap.add_argument("--workloads", nargs="?", const="all", default=None,
                     help="measure other workloads instead: all, or a comma "
-                         "list of c2, c4, c5, c3_topp, c3_topk_topp")
+                         "list of c2, c4, c5, c3_topp, c3_topk_topp, c3_tree8")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()

@@ -97,6 +97,7 @@ def config(c: int, **overrides) -> Config:
 # ---------------------------------------------------------------------------
 STREAM_TOKENS, STREAM_BOOST_MASK, STREAM_UNIFORMS, STREAM_DRAFT = 0, 1, 2, 3
 STREAM_CORPUS, STREAM_QUERY = 4, 5
+STREAM_TREE = 6
 
 
 def rng_for(seed: int, stream: int, *sub: int) -> np.random.Generator:
@@ -299,3 +300,40 @@ def draft_model_inputs(cfg: Config, step: int, target, device="cpu"):
             pr = qh[b, j]
             draft[b, j] = rng.choice(cfg.V, p=pr / pr.sum())
     return q.contiguous(), draft
+
+
+# ---------------------------------------------------------------------------
+# Draft trees: one tree per sequence, the shape fixed (a root with several
+# candidate continuations, as drafts taken from several suffix-link ancestors
+# would give), the tokens seeded per slot and distinct among siblings.
+# ---------------------------------------------------------------------------
+TREE8_PARENTS = (-1, 0, 0, 0, 1, 4, 5, 2)  # root, 3 candidates, one 4 deep
+
+
+def draft_trees(cfg: Config, slot: int, parents=TREE8_PARENTS):
+    """(tokens [B, N] int32, parent [B, N] int32, chain [B, N] bool): random
+    tokens, distinct among siblings; `chain` marks the nodes on the first
+    candidate's path (the ones a harness would make likely)."""
+    par = np.asarray(parents, np.int32)
+    N = len(par)
+    r = rng_for(cfg.seed, STREAM_TREE, slot)
+    tok = r.integers(0, cfg.V, (cfg.B, N)).astype(np.int32)
+    tok[:, 0] = 0
+    for i in range(1, N):
+        for j in range(1, i):
+            if par[j] == par[i]:
+                same = tok[:, j] == tok[:, i]
+                tok[same, i] = (tok[same, i] + 1) % cfg.V
+    chain = np.zeros(N, bool)
+    v = 1
+    while v >= 0:
+        chain[v] = True
+        kids = [c for c in range(1, N) if par[c] == v]
+        v = kids[0] if kids else -1
+    return tok, np.tile(par, (cfg.B, 1)), np.tile(chain, (cfg.B, 1))
+
+
+def tree_uniforms(cfg: Config, step: int, N: int) -> np.ndarray:
+    """[B, N] float32 in [0, 1): coins per depth, the last the final coin."""
+    r = rng_for(cfg.seed, STREAM_TREE + 1, step)
+    return r.random((cfg.B, N), dtype=np.float32)
