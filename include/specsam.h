@@ -88,8 +88,8 @@ size_t ss_verify_workspace_bytes(int B, int K, int V);
 
 /* The same with options: flags = 0, or SS_WS_TRUNCATION for calls that pass
  * top_k or top_p (the truncation passes need per-row histograms, candidate
- * lists and per-chunk sums: about (K+1) * B * (nchunks * 2 KiB +
- * min(8192, V) * 8 B), nchunks = ceil(V / 8192)). 0 for unsupported sizes or
+ * lists and per-chunk sums: about (K+1) * B * nchunks * (2 KiB +
+ * min(512, V) * 8 B), nchunks = ceil(V / 8192)). 0 for unsupported sizes or
  * flags. */
 #define SS_WS_TRUNCATION 1
 size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);

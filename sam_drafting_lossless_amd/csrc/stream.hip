@@ -272,8 +272,14 @@ __device__ __forceinline__ int extra_rows(const Args& a, int b) {
   return (v >= 1 && v <= a.K) ? v : 0;
 }
 
+// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the histogram variant
+// needs more registers (LDS limits it to 6 workgroups per CU anyway), and a
+// tighter hint would spill them to scratch.
+template <int DT, bool TR>
+constexpr int kStreamWaves = TR ? (DT == SS_DTYPE_F32 ? 5 : 3) : (DT == SS_DTYPE_F32 ? 6 : 4);
+
 template <int DT, bool VP, bool TR>
-__global__ __launch_bounds__(kThreads, DT == SS_DTYPE_F32 ? 6 : 4) void
+__global__ __launch_bounds__(kThreads, (kStreamWaves<DT, TR>)) void
 spec_stream_balanced_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
   __shared__ unsigned long long hs[TR ? kHistCopies * kHistBins + 1 : 1];

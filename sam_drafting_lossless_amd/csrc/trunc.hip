@@ -19,8 +19,9 @@
 //           them from the top and picks the bin range that must hold the
 //           threshold (with a margin for the histogram's rounding);
 //   extract (one workgroup per row chunk) re-reads the chunk, sums the exact
-//           probability of its tokens above the range and appends the tokens
-//           inside the range to the row's candidate list;
+//           probability of its tokens above the range and writes the tokens
+//           inside the range to the chunk's own segment of the row's
+//           candidate list (no atomics);
 //   select  (one workgroup per row) finds the exact threshold among the
 //           candidates by radix selection on order-preserving keys (8-bit
 //           digits, LDS histograms of counts for top-k and of probability
@@ -29,9 +30,9 @@
 // The finalize kernel then judges and draws with the per-chunk kept sums and
 // the threshold. Selection first finds the bits all candidate keys share and
 // radix-walks only the bits below them, so that no round piles every
-// candidate into one LDS bucket. A row with more than kCandCap candidates
-// (its logits crowd into a few bins; the list holds min(kCandCap, V) per row)
-// is selected by scanning the row itself in each round: exact, but slower.
+// candidate into one LDS bucket. A row with more than kCandCap candidates,
+// or a chunk with more than kSegCap (logits crowded into a few bins), is
+// selected by scanning the row itself in each round: exact, but slower.
 #include <algorithm>
 
 #include "verify_common.h"
@@ -88,14 +89,27 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   __shared__ int cabove;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int64_t row = blockIdx.x;
-  const RowCtx rc = row_ctx(a, row);
-  if (!rc.active) return;
   const int nc = a.nchunks;
   const int64_t h0 = row * nc;
-  for (int c = tid; c < nc; c += kThreads) {
-    const i32x4 hh = a.hhdr[h0 + c];
-    s_a[c] = hh.x;
-    s_rest[c] = ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
+  // The chunk headers are requested together with the row's parameters (they
+  // are in bounds for every row; an inactive row's are never used).
+  i32x4 hh = i32x4{0, 0, 0, 0};
+  float pmv = 0.0f;
+  if (tid < nc) {
+    hh = a.hhdr[h0 + tid];
+    pmv = a.partials[h0 + tid].x;
+  }
+  const RowCtx rc = row_ctx(a, row);
+  if (!rc.active) return;
+  if (tid < nc) {
+    s_a[tid] = hh.x;
+    s_rest[tid] = ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
+    s_pm[tid] = pmv;
+  }
+  for (int c = tid + kThreads; c < nc; c += kThreads) {
+    const i32x4 h2 = a.hhdr[h0 + c];
+    s_a[c] = h2.x;
+    s_rest[c] = ((unsigned long long)(unsigned)h2.y << 32) | (unsigned)h2.z;
     s_pm[c] = a.partials[h0 + c].x;
   }
   if (tid < 3) first[tid] = kRestBin;
@@ -198,7 +212,6 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   if (rlo >= 1 && rlo <= kRestBin && tid == rlo - 1) cabove = (int)C;
   __syncthreads();
   if (tid == 0) {
-    a.ccount[row] = 0;
     a.plan[row * 2] = i32x4{a0, rlo, rhi, cabove};
     a.plan[row * 2 + 1] =
         i32x4{(kA ? 1 : 0) | (pA ? 2 : 0), k - cabove, __float_as_int(m), 0};
@@ -286,8 +299,10 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
     }
   above = block_sum(above, scratch);
   if (tid == 0) a.tpart[row * nc + c] = above;
-  // Candidates: a block-wide exclusive scan of the per-thread counts, one
-  // atomic per workgroup to reserve room in the row's list.
+  // Candidates go to this (row, chunk)'s own segment of the list: a
+  // block-wide exclusive scan of the per-thread counts gives each lane its
+  // place. A segment that would overflow is not written (its count says so,
+  // and the row is then selected by re-scanning it).
   const int inc = (int)wave_inclusive_sum((float)n);
   if (l == kWave - 1) woff[w] = inc;
   __syncthreads();
@@ -298,16 +313,18 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
       woff[i] = t;
       t += v;
     }
-    woff[kWaves] = t ? atomicAdd(&a.ccount[row], t) : 0;
+    woff[kWaves] = t;
+    a.ccount[row * nc + c] = t;
   }
   __syncthreads();
-  int pos = woff[kWaves] + woff[w] + inc - n;
+  int pos = woff[w] + inc - n;
+  const bool fits = woff[kWaves] <= a.segcap;
   __syncthreads();  // woff is reused by the next item
-  if (n == 0) return;
-  int2* out = a.cand + row * a.ccap;
+  if (n == 0 || !fits) return;
+  int2* out = a.cand + (row * nc + c) * a.segcap;
 #pragma unroll
   for (int q = 0; q < kHeld; ++q)
-    if (q < n && pos + q < a.ccap) out[pos + q] = int2{__float_as_int(hv[q]), hi[q]};
+    if (q < n) out[pos + q] = int2{__float_as_int(hv[q]), hi[q]};
   if (n <= kHeld) return;
   u32x4 again[kLoads];
   load_chunk<DT, VP, false>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid,
@@ -319,7 +336,7 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
     for (int k = 0; k < kVec<DT>; ++k) {
       const float v = elem<DT>(again[it], k);
       if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi)) {
-        if (seen >= kHeld && pos + seen < a.ccap)
+        if (seen >= kHeld)
           out[pos + seen] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
         ++seen;
       }
@@ -332,6 +349,7 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
 struct SelShared {
   unsigned key[kCandCap];  // candidate keys (fkey of the logit)
   unsigned char chunk[kCandCap];  // the chunk each candidate lies in
+  int pre[kMaxChunks + 1];  // exclusive prefix of the chunks' candidate counts
   unsigned cnt[256];
   float mass[256];
   float csum[kMaxChunks];
@@ -347,12 +365,15 @@ struct SelShared {
 // call). f(key, list position or token index).
 template <int DT, bool VP>
 struct CandSource {
-  const Args* a;
+  // (fields by value: taking the kernel argument's address would place the
+  // whole argument block in scratch memory)
+  const unsigned char* rowp;
+  int V, nchunks;
   SelShared* sh;
-  int64_t row;
   int n, a0, rlo, rhi;
   float kk;
-  __device__ __forceinline__ bool in_lds() const { return n <= a->ccap; }
+  bool lds;  // the candidates are in sh->key (else: re-scan the row)
+  __device__ __forceinline__ bool in_lds() const { return lds; }
   template <typename F>
   __device__ __forceinline__ void each(F f) const {
     const int tid = threadIdx.x;
@@ -360,11 +381,10 @@ struct CandSource {
       for (int i = tid; i < n; i += kThreads) f(sh->key[i], i);
       return;
     }
-    const unsigned char* rowp = a->logits + row * a->V * Dt<DT>::kBytes;
-    for (int c = 0; c < a->nchunks; ++c) {
+    for (int c = 0; c < nchunks; ++c) {
       const int cstart = c * kChunk<DT>;
       u32x4 raw[kLoads];
-      load_chunk<DT, VP, false>(rowp, cstart, a->V, tid, raw);
+      load_chunk<DT, VP, false>(rowp, cstart, V, tid, raw);
 #pragma unroll
       for (int it = 0; it < kLoads; ++it)
 #pragma unroll
@@ -423,7 +443,7 @@ struct KeySpan {
 };
 
 template <typename Src>
-__device__ KeySpan key_span(const Src& src, SelShared& sh) {
+__device__ KeySpan key_span(const Src src, SelShared& sh) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   int lo = INT_MAX, hi = INT_MIN;  // keys as order-preserving signed ints
   src.each([&](unsigned key, int) {
@@ -452,7 +472,7 @@ __device__ KeySpan key_span(const Src& src, SelShared& sh) {
 
 // Key of the kth largest candidate (1-based; kth <= the candidate count).
 template <typename Src>
-__device__ unsigned select_kth(const Src& src, SelShared& sh, KeySpan ks, int kth) {
+__device__ unsigned select_kth(const Src src, SelShared& sh, KeySpan ks, int kth) {
   const int tid = threadIdx.x;
   unsigned prefix = ks.prefix;
   float need = (float)kth;
@@ -480,7 +500,7 @@ __device__ unsigned select_kth(const Src& src, SelShared& sh, KeySpan ks, int kt
 // at least t of probability; the smallest candidate key >= kmin when rounding
 // leaves the candidates short of t.
 template <typename Src>
-__device__ unsigned select_mass(const Src& src, SelShared& sh, KeySpan ks, float t,
+__device__ unsigned select_mass(const Src src, SelShared& sh, KeySpan ks, float t,
                                 unsigned kmin, float m, float kk) {
   const int tid = threadIdx.x;
   unsigned prefix = ks.prefix;
@@ -519,47 +539,85 @@ __device__ unsigned select_mass(const Src& src, SelShared& sh, KeySpan ks, float
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
   __shared__ SelShared sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  // One workgroup per listed row; workgroups past the list's end leave at
+  // once (they hold this kernel's large LDS block only for one load).
   const int64_t row = listed_row(a, blockIdx.x);
   if (row < 0) return;
   const int nc = a.nchunks;
+  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
+  int cc = 0;
+  float tb = 0.0f;
+  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (tid < nc) {
+    cc = a.ccount[row * nc + tid];
+    tb = a.tpart[row * nc + tid];
+    pv = a.partials[row * nc + tid];
+  }
   const int b = (int)(row / (a.K + 1));
   const float kk = kLog2e / a.temperature[b];
-  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
   const int mode = p1.x, krem = p1.y;
   const float m = __int_as_float(p1.z);
-  const int n = a.ccount[row];
+  for (int c = tid + kThreads; c < nc; c += kThreads) tb += a.tpart[row * nc + c];
   // Probability above the range: every token there is kept.
-  float base = 0.0f;
-  for (int c = tid; c < nc; c += kThreads) base += a.tpart[row * nc + c];
-  base = block_sum(base, sh.scratch);
+  const float base = block_sum(tb, sh.scratch);
   if (mode == 0) {
     if (tid == 0) a.tinfo[row] = f32x4{kNegInf, base, 1.0f, 0.0f};
     return;
   }
-  const int2* list = a.cand + row * a.ccap;
-  if (n <= a.ccap) {
-    constexpr int kU = 8;  // list entries requested at once per thread
-    for (int i0 = 0; i0 < n; i0 += kU * kThreads) {
+  // Exclusive prefix of the chunks' candidate counts (nc <= kThreads here;
+  // more chunks than threads, or an overflowing segment, take the re-scan).
+  const bool over = nc > kThreads || cc > a.segcap;
+  const int inc = (int)wave_inclusive_sum((float)cc);
+  if (l == kWave - 1) sh.iscr[0][w] = inc;
+  __syncthreads();
+  int wb = 0, tot = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) wb += sh.iscr[0][i];
+    tot += sh.iscr[0][i];
+  }
+  if (tid < nc) sh.pre[tid] = wb + inc - cc;
+  if (tid == 0) sh.pre[nc < kThreads ? nc : kThreads] = tot;
+  const int anyover = __syncthreads_or(over);
+  const bool lds = !anyover && tot <= kCandCap;
+  const int n = tot;
+  if (lds) {
+    // Entry f of the list lies in chunk c with pre[c] <= f < pre[c+1].
+    const int2* seg = a.cand + row * nc * a.segcap;
+    constexpr int kU = 8;
+    for (int f0 = 0; f0 < n; f0 += kU * kThreads) {
       int2 ev[kU];
+      int ch[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        ev[u] = i < n ? list[i] : int2{0, 0};
+        const int f = f0 + u * kThreads + tid;
+        ev[u] = int2{0, 0};
+        ch[u] = 0;
+        if (f < n) {
+          int lo = 0, hi = nc - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.pre[mid] <= f) lo = mid;
+            else hi = mid - 1;
+          }
+          ch[u] = lo;
+          ev[u] = seg[(int64_t)lo * a.segcap + (f - sh.pre[lo])];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int i = i0 + u * kThreads + tid;
-        if (i < n) {
-          sh.key[i] = fkey(__int_as_float(ev[u].x));
-          sh.chunk[i] = (unsigned char)(ev[u].y / kChunk<DT>);
+        const int f = f0 + u * kThreads + tid;
+        if (f < n) {
+          sh.key[f] = fkey(__int_as_float(ev[u].x));
+          sh.chunk[f] = (unsigned char)ch[u];
         }
       }
     }
   }
   for (int c = tid; c < nc; c += kThreads) sh.csum[c] = 0.0f;
   __syncthreads();
-  const CandSource<DT, VP> src{&a, &sh, row, n, p0.x, p0.y, p0.z, kk};
+  const CandSource<DT, VP> src{a.logits + row * a.V * Dt<DT>::kBytes, a.V, nc, &sh,
+                               n, p0.x, p0.y, p0.z, kk, lds};
   const KeySpan ks = key_span(src, sh);
   unsigned kmin = 0;
   if (mode & 1) kmin = select_kth(src, sh, ks, krem);
@@ -575,7 +633,8 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
       });
       zk = base + block_sum(zk, sh.scratch);
     } else {
-      for (int c = tid; c < nc; c += kThreads) {
+      zk = (tid < nc) ? pv.y * fast_exp2((pv.x - m) * kk) : 0.0f;
+      for (int c = tid + kThreads; c < nc; c += kThreads) {
         const f32x4 p = a.partials[row * nc + c];
         zk += p.y * fast_exp2((p.x - m) * kk);
       }
@@ -594,14 +653,30 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
       key = sh.minkey;
     }
   }
-  // Kept candidates: their probability, per chunk (from the LDS list, or
-  // from the token index of the row scan).
-  src.each([&](unsigned k2, int i) {
-    if (k2 >= key) {
-      const int ch = src.in_lds() ? (int)sh.chunk[i] : i / kChunk<DT>;
-      atomicAdd(&sh.csum[ch], fast_exp2((fkey_inv(k2) - m) * kk));
+  // Kept candidates: their probability, per chunk. In LDS the list is grouped
+  // by chunk: each thread sums a contiguous run and adds it to its chunk when
+  // the chunk changes. The re-scan adds token by token.
+  if (lds) {
+    const int per = (n + kThreads - 1) / kThreads;
+    const int f0 = tid * per, f1 = min(n, f0 + per);
+    int cur = -1;
+    float run = 0.0f;
+    for (int f = f0; f < f1; ++f) {
+      const int ch = sh.chunk[f];
+      if (ch != cur) {
+        if (cur >= 0 && run != 0.0f) atomicAdd(&sh.csum[cur], run);
+        cur = ch;
+        run = 0.0f;
+      }
+      const unsigned k2 = sh.key[f];
+      if (k2 >= key) run += fast_exp2((fkey_inv(k2) - m) * kk);
     }
-  });
+    if (cur >= 0 && run != 0.0f) atomicAdd(&sh.csum[cur], run);
+  } else {
+    src.each([&](unsigned k2, int i) {
+      if (k2 >= key) atomicAdd(&sh.csum[i / kChunk<DT>], fast_exp2((fkey_inv(k2) - m) * kk));
+    });
+  }
   __syncthreads();
   float kept = 0.0f;
   for (int c = tid; c < nc; c += kThreads) {

@@ -483,9 +483,9 @@ WsLayout ws_layout(int B, int K, int V, bool trunc) {
   take(L.hist, t * rows * nc * kHistBins * sizeof(unsigned long long));
   take(L.hhdr, t * rows * nc * sizeof(i32x4));
   take(L.plan, t * rows * 2 * sizeof(i32x4));
-  take(L.ccount, t * rows * sizeof(int));
+  take(L.ccount, t * rows * nc * sizeof(int));
   take(L.tlist, t * (rows + 1) * sizeof(int));
-  take(L.cand, t * rows * std::min(kCandCap, V) * sizeof(int2));
+  take(L.cand, t * rows * nc * std::min(kSegCap, V) * sizeof(int2));
   take(L.tpart, t * rows * nc * sizeof(float));
   take(L.tinfo, t * rows * sizeof(f32x4));
   L.total = o;
@@ -590,7 +590,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.tlist = trunc ? reinterpret_cast<int*>(ws + L.tlist) : nullptr;
   a.tcount = trunc ? a.tlist + (size_t)B * (K + 1) : nullptr;
   a.cand = trunc ? reinterpret_cast<int2*>(ws + L.cand) : nullptr;
-  a.ccap = std::min(kCandCap, V);
+  a.segcap = std::min(kSegCap, V);
   a.tpart = trunc ? reinterpret_cast<float*>(ws + L.tpart) : nullptr;
   a.tinfo = trunc ? reinterpret_cast<f32x4*>(ws + L.tinfo) : nullptr;
   a.sam = reinterpret_cast<unsigned char*>(sam_state);

@@ -36,6 +36,7 @@ constexpr int kRestBin = kHistBins;  // "beyond the window"
 // atomic hit the same bin, then sums them.
 constexpr int kHistCopies = 8;
 constexpr int kCandCap = 8192;       // candidates per row held in LDS
+constexpr int kSegCap = 512;         // candidates per (row, chunk) segment
 constexpr float kFixScale = 2147483648.0f;  // 2^31
 constexpr unsigned long long kCountOne = 1ull << 48;
 constexpr unsigned long long kMassMask = kCountOne - 1;
@@ -171,11 +172,11 @@ struct Args {
   i32x4* hhdr;      // [rows*nchunks]: (window start bin, rest hi, rest lo, 0)
   i32x4* plan;      // [rows*2]: (row start bin, r_lo, r_hi, count above),
                     //           (active, 0, 0, 0)
-  int* ccount;      // [rows] candidates found
+  int* ccount;      // [rows*nchunks] candidates each chunk found
   int* tlist;       // [rows] truncated rows, in the order the plan found them
   int* tcount;      // [1] their number (cleared by the stream pass)
-  int2* cand;       // [rows*ccap] (logit bits, token)
-  int ccap;         // candidates per row held: min(kCandCap, V)
+  int2* cand;       // [rows*nchunks*segcap] (logit bits, token) per chunk
+  int segcap;       // candidates a chunk's segment holds: min(kSegCap, V)
   float* tpart;     // [rows*nchunks] kept mass per chunk (relative to row max)
   f32x4* tinfo;     // [rows]: (threshold logit, kept mass, active, 0)
   // Fused automaton step (sam == nullptr when only verifying).
