@@ -29,52 +29,6 @@ namespace {
 // stream: one partial per (row, chunk).
 // ---------------------------------------------------------------------------
 
-// Window histogram of one chunk of a truncated row (see kHistBins): `raw`
-// still holds the chunk, pm is the chunk max. hs (LDS, kHistCopies x
-// kHistBins words, then the rest word) was cleared before the barrier that
-// published pm.
-static_assert(kHistBins == kThreads, "one histogram bin per thread");
-static_assert(kHistCopies == 2 * kWaves, "one copy per wavefront and lane parity");
-
-template <int DT>
-__device__ __forceinline__ void chunk_histogram(const Args& a, int64_t row, int c,
-                                                float pm, float kk,
-                                                const u32x4 (&raw)[kLoads],
-                                                unsigned long long* hs) {
-  const int tid = threadIdx.x;
-  const int a0 = abs_bin(pm, kk);
-  unsigned long long* mine =
-      hs + ((tid / kWave) * 2 + (tid & 1)) * kHistBins;  // this lane's copy
-  unsigned long long rest = 0;
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const float v = elem<DT>(raw[it], k);
-      if (v > kNegInf) {  // -inf (probability 0) and NaN are not counted
-        const int jb = abs_bin(v, kk) - a0;
-        const float w = fast_exp2((v - pm) * kk);
-        const unsigned long long word =
-            kCountOne | (unsigned long long)(unsigned)(w * kFixScale);
-        if (jb >= 0 && jb < kHistBins)
-          atomicAdd(&mine[jb], word);
-        else
-          rest += word;
-      }
-    }
-  if (rest) atomicAdd(&hs[kHistCopies * kHistBins], rest);
-  __syncthreads();
-  unsigned long long sum = 0;
-#pragma unroll
-  for (int i = 0; i < kHistCopies; ++i) sum += hs[i * kHistBins + tid];
-  const int64_t hc = row * a.nchunks + c;
-  a.hist[hc * kHistBins + tid] = sum;
-  if (tid == 0) {
-    const unsigned long long r = hs[kHistCopies * kHistBins];
-    a.hhdr[hc] = i32x4{a0, (int)(unsigned)(r >> 32), (int)(unsigned)r, 0};
-  }
-}
-
 // Reduces one loaded chunk of row j of sequence b into its partial. `raw`
 // holds the chunk; `mid` runs once every element has been consumed, before
 // the workgroup reduction (the balanced kernel issues its next item's loads
@@ -149,6 +103,59 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     // The sum is relative to the chunk max pm, which equals pv except when
     // the chunk holds NaN (then the sum is NaN and the row is reported).
     part = f32x4{pv, ps, 0.0f, __int_as_float(pi)};
+  } else if (TR && trunc_active(a, b, T)) {
+    // Truncated row: the chunk max first, then one pass that adds each
+    // element's weight exp2((l - max) * log2e / T) to the sum and to the
+    // chunk's window histogram (see kHistBins): count and fixed-point weight
+    // in one 64-bit word per bin, the bin on the row's shared grid.
+    float vm = kNegInf;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
+    mid();
+    vm = wave_max(vm);
+    hs[tid] = 0;
+    if (tid == 0) hs[kHistBins] = 0;
+    if (l == 0) red[w] = f32x4{vm, 0.0f, 0.0f, 0.0f};
+    __syncthreads();
+    float pm = red[0].x;
+    for (int i = 1; i < kWaves; ++i) pm = fmaxf(pm, red[i].x);
+    const float base = (pm == kNegInf) ? 0.0f : pm;
+    const int a0 = abs_bin(pm, kk);
+    float s = 0.0f;
+    unsigned long long rest = 0;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const float v = elem<DT>(raw[it], k);
+        const float wv = fast_exp2((v - base) * kk);
+        s += wv;
+        if (v > kNegInf) {  // -inf (probability 0) and NaN are not counted
+          const int jb = abs_bin(v, kk) - a0;
+          const unsigned long long word =
+              kCountOne | (unsigned long long)(unsigned)(wv * kFixScale);
+          if (jb >= 0 && jb < kHistBins)
+            atomicAdd(&hs[jb], word);
+          else
+            rest += word;
+        }
+      }
+    if (rest) atomicAdd(&hs[kHistBins], rest);
+    s = wave_sum(s);
+    __syncthreads();  // every lane has read red[].x
+    if (l == 0) red[w].y = s;
+    __syncthreads();
+    float ps = 0.0f;
+    for (int i = 0; i < kWaves; ++i) ps += red[i].y;
+    part = f32x4{pm, ps, lx, 0.0f};
+    const int64_t hc = row * nc + c;
+    a.hist[hc * kHistBins + tid] = hs[tid];
+    if (tid == 0) {
+      const unsigned long long r = hs[kHistBins];
+      a.hhdr[hc] = i32x4{a0, (int)(unsigned)(r >> 32), (int)(unsigned)r, 0};
+    }
   } else {
     // Online (max, sum exp2) folded one 16-byte vector at a time, in the
     // order the loads return, so only the raw vectors stay live.
@@ -168,24 +175,12 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
       m = mn;
     }
     mid();
-    bool tr = false;
-    if constexpr (TR) {
-      tr = trunc_active(a, b, T);
-      if (tr) {
-#pragma unroll
-        for (int i = 0; i < kHistCopies; ++i) hs[i * kHistBins + tid] = 0;
-        if (tid == 0) hs[kHistCopies * kHistBins] = 0;
-      }
-    }
     wave_lse(m, s, kk);
     if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
     __syncthreads();
     float pm = red[0].x, ps = red[0].y;
     for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
     part = f32x4{pm, ps, lx, 0.0f};
-    if constexpr (TR) {
-      if (tr) chunk_histogram<DT>(a, row, c, pm, kk, raw, hs);
-    }
   }
   if (tid == 0) a.partials[row * nc + c] = part;
   __syncthreads();  // red[] is reused by the next row
@@ -201,7 +196,7 @@ struct NoMid {
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
-  __shared__ unsigned long long hs[TR ? kHistCopies * kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   const int tid = threadIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
   const int c = blockIdx.x % nc;
@@ -282,7 +277,7 @@ template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, (kStreamWaves<DT, TR>)) void
 spec_stream_balanced_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
-  __shared__ unsigned long long hs[TR ? kHistCopies * kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   __shared__ int pre[kPlanMaxB + 1];
   __shared__ int wsum[kWaves];
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;

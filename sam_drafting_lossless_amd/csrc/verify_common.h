@@ -31,10 +31,6 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kHistBins = 256;
 constexpr int kBinsPerOctave = 8;
 constexpr int kRestBin = kHistBins;  // "beyond the window"
-// The stream pass builds each chunk's histogram in kHistCopies private
-// copies (per wavefront and lane parity), so that fewer lanes of one LDS
-// atomic hit the same bin, then sums them.
-constexpr int kHistCopies = 8;
 constexpr int kCandCap = 8192;       // candidates per row held in LDS
 constexpr int kSegCap = 512;         // candidates per (row, chunk) segment
 constexpr float kFixScale = 2147483648.0f;  // 2^31
