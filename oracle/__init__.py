@@ -65,6 +65,8 @@ def _load():
     lib.orc_sam_extend.argtypes = [P, P, i64]
     lib.orc_sam_draft.argtypes = [P, i32, P, P]
     lib.orc_sam_draft.restype = i32
+    lib.orc_sam_draft_tree.argtypes = [P, i32, i32, P, P, P]
+    lib.orc_sam_draft_tree.restype = i32
     for name in ("orc_sam_num_states", "orc_sam_num_edges", "orc_sam_length"):
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = i64
@@ -138,6 +140,17 @@ class SAM:
         ml = np.zeros(1, np.int32)
         d = self._lib.orc_sam_draft(self._h, K, _ptr(out), _ptr(ml))
         return out, int(d), int(ml[0])
+
+    def draft_tree(self, K: int, M: int):
+        """Draft tree of up to M candidates of K tokens (see draft_tree in
+        oracle.cpp). Returns (tokens [1 + M*K], parent [1 + M*K], n_nodes,
+        match_len); entries past n_nodes are -1."""
+        N = 1 + M * K
+        tok = np.full(N, -1, np.int32)
+        par = np.full(N, -1, np.int32)
+        ml = np.zeros(1, np.int32)
+        n = self._lib.orc_sam_draft_tree(self._h, K, M, _ptr(tok), _ptr(par), _ptr(ml))
+        return tok, par, int(n), int(ml[0])
 
     @property
     def last_walk_hops(self) -> int:

@@ -125,6 +125,44 @@ struct OracleSAM {
     return d;
   }
 
+  // Draft tree from several candidates (an extension of the drafting above
+  // to the tree layout the tree verifier takes; the pages draft one
+  // candidate): the state the draft walk reaches, then up to M - 1 of its
+  // suffix-link ancestors (each a shorter suffix of S whose occurrences are a
+  // superset, down to the root, excluded), each giving the tokens after its
+  // first occurrence (K at most, cut at the end of S). The candidates are
+  // merged into a trie in that order: node 0 is the root; a candidate walks
+  // down the children with its tokens and adds a node where none matches, so
+  // a node's children appear in the order their candidates came. Returns the
+  // node count; tok/par receive node i's token and parent (root: -1, -1).
+  int32_t draft_tree(int32_t K, int32_t M, int32_t* tok, int32_t* par,
+                     int32_t* match_len) {
+    int32_t s = last;
+    while (s != 0 && next[s].empty()) s = link[s];
+    *match_len = len[s];
+    int32_t nn = 1;
+    tok[0] = par[0] = -1;
+    const int32_t n = (int32_t)text.size();
+    for (int32_t i = 0; i < M && s != 0 && len[s] > 0; ++i, s = link[s]) {
+      const int32_t p = minend[s];
+      const int32_t d = std::min<int32_t>(K, n - 1 - p);
+      int32_t cur = 0;
+      for (int32_t j = 0; j < d; ++j) {
+        const int32_t t = text[p + 1 + j];
+        int32_t found = -1;
+        for (int32_t v = 1; v < nn; ++v)
+          if (par[v] == cur && tok[v] == t) found = v;
+        if (found < 0) {
+          found = nn++;
+          par[found] = cur;
+          tok[found] = t;
+        }
+        cur = found;
+      }
+    }
+    return nn;
+  }
+
   // Match-state transfer on a fixed automaton ([P4] "Drafting with Suffix
   // Automaton", "Update of Suffix Automaton", state transfer of Algorithm 1):
   // (s, l) is the state of the longest suffix of a generated text that occurs
@@ -612,6 +650,11 @@ void verify_tree_one(const TreeIO& io, int b) {
 extern "C" {
 
 void* orc_sam_new(void) { return new OracleSAM(); }
+
+int32_t orc_sam_draft_tree(void* h, int32_t K, int32_t M, int32_t* tok, int32_t* par,
+                           int32_t* match_len) {
+  return ((OracleSAM*)h)->draft_tree(K, M, tok, par, match_len);
+}
 void orc_sam_free(void* h) { delete (OracleSAM*)h; }
 
 void orc_sam_extend(void* h, const int32_t* toks, int64_t n) {
