@@ -301,6 +301,24 @@ int sam_extend(void* state, int B, int max_len, const int32_t* tokens,
 int sam_draft(const void* state, int B, int max_len, int K, int32_t* draft,
               int32_t* draft_len, int32_t* match_len, void* stream);
 
+/*
+ * sam_draft_tree — per sequence, a draft tree for spec_verify_tree from
+ * several candidates: the state sam_draft's walk reaches, then up to M - 1 of
+ * its suffix-link ancestors (shorter suffixes of the text whose occurrences
+ * are a superset; the root ends the list), each giving the tokens after its
+ * first occurrence (K at most, cut at the end of the text). The candidates
+ * are merged into a trie in that order: node 0 is the root, a candidate walks
+ * down the children carrying its tokens and adds a node where none matches,
+ * so node order (which spec_verify_tree tries siblings in) follows the
+ * candidates' order and candidate 0 is sam_draft's draft.
+ *   K >= 1, M >= 0, 1 + M*K <= N <= SS_MAX_TREE.
+ *   tokens, parent [B, N] int32: node i's token and parent (root: -1, -1;
+ *   -1 past n_nodes); n_nodes [B]; match_len [B] (sam_draft's) or NULL.
+ */
+int sam_draft_tree(const void* state, int B, int max_len, int K, int M, int N,
+                   int32_t* tokens, int32_t* parent, int32_t* n_nodes,
+                   int32_t* match_len, void* stream);
+
 /* sam_extend followed by sam_draft in one launch (per-step use). */
 int sam_extend_draft(void* state, int B, int max_len, const int32_t* tokens,
                      int ld_tokens, const int32_t* counts, int K,

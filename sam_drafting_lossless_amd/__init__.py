@@ -86,6 +86,8 @@ def lib():
     L.sam_extend.restype = i32
     L.sam_draft.argtypes = [P, i32, i32, i32, P, P, P, P]
     L.sam_draft.restype = i32
+    L.sam_draft_tree.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P]
+    L.sam_draft_tree.restype = i32
     L.sam_extend_stats.argtypes = [P, i32, i32, P, i32, P, P, P]
     L.sam_extend_stats.restype = i32
     L.sam_match.argtypes = [P, i32, i32, P, P, i32, P, i32, i32, P, P, P, P, P,
@@ -537,6 +539,23 @@ class SamState:
               stream=None):
         return sam_draft(self.buf, self.B, self.max_len, K, draft, draft_len,
                          match_len, stream)
+
+    def draft_tree(self, K: int, M: int, N: int | None = None, stream=None):
+        """Draft trees (see include/specsam.h, sam_draft_tree): returns
+        (tokens [B, N], parent [B, N], n_nodes [B], match_len [B]) int32,
+        N = 1 + M*K by default."""
+        N = 1 + M * K if N is None else N
+        dev = self.buf.device
+        i32 = torch.int32
+        tok = torch.empty((self.B, N), dtype=i32, device=dev)
+        par = torch.empty((self.B, N), dtype=i32, device=dev)
+        nn = torch.empty(self.B, dtype=i32, device=dev)
+        ml = torch.empty(self.B, dtype=i32, device=dev)
+        _check(lib().sam_draft_tree(_dev(self.buf, "state", torch.uint8), self.B,
+                                    self.max_len, K, M, N, tok.data_ptr(),
+                                    par.data_ptr(), nn.data_ptr(), ml.data_ptr(),
+                                    _stream(stream)), "sam_draft_tree")
+        return tok, par, nn, ml
 
     def extend_draft(self, tokens, counts, K: int, draft=None, draft_len=None,
                      match_len=None, stream=None):

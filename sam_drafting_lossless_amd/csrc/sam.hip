@@ -48,6 +48,62 @@ __global__ __launch_bounds__(kWave) void sam_draft_kernel(
                 draft + (int64_t)b * K, draft_len + b, match_len + b);
 }
 
+// Draft tree of up to M candidates (one wavefront per sequence; lane v holds
+// tree node v): the state the single draft's link walk reaches, then its
+// suffix-link ancestors, each giving the tokens after its first occurrence
+// (K at most, cut at the end of the text). Each candidate is inserted into
+// the trie token by token: a ballot over the nodes finds the child of the
+// current node with that token, or the next free lane becomes one. Node 0 is
+// the root; children keep their candidates' order.
+__global__ __launch_bounds__(kWave) void sam_draft_tree_kernel(
+    const unsigned char* base, SamLayout L, int K, int M, int N, int32_t* tok_out,
+    int32_t* par_out, int32_t* n_out, int32_t* mlen_out) {
+  const int b = blockIdx.x;
+  const int l = lane_id();
+  const SamSeq S = sam_seq(const_cast<unsigned char*>(base), b, L);
+  const SamCursor cs = sam_open(S);
+  const int n = cs.h.n, nstates = cs.h.nstates;
+  int s = cs.h.last;
+  i32x4 rs = cs.rlast;
+  for (int g = 0; s > 0 && rs.w == -1 && g < nstates; ++g) {
+    s = rs.y;
+    rs = S.st[s < 0 ? 0 : s];
+  }
+  const int ml = (s <= 0) ? 0 : rs.x;
+  int ntok = -1, npar = -1;  // this lane's node
+  int nn = 1;
+  for (int i = 0; i < M && s > 0 && rs.x > 0; ++i) {
+    const int p = rs.z;
+    const int d = min(K, n - 1 - p);
+    const int tv = (l < d) ? S.text[p + 1 + l] : -1;
+    int cur = 0;
+    for (int j = 0; j < d; ++j) {
+      const int t = __builtin_amdgcn_readlane(tv, j);
+      const unsigned long long hit =
+          __ballot(l >= 1 && l < nn && npar == cur && ntok == t);
+      if (hit) {
+        cur = __ffsll((unsigned long long)hit) - 1;
+      } else {
+        if (l == nn) {
+          npar = cur;
+          ntok = t;
+        }
+        cur = nn++;
+      }
+    }
+    s = rs.y;
+    rs = S.st[s < 0 ? 0 : s];
+  }
+  if (l < N) {
+    tok_out[(int64_t)b * N + l] = (l < nn) ? ntok : -1;
+    par_out[(int64_t)b * N + l] = (l < nn) ? npar : -1;
+  }
+  if (l == 0) {
+    n_out[b] = nn;
+    if (mlen_out) mlen_out[b] = ml;
+  }
+}
+
 // Extend then draft in one pass (the per-step pair, one launch).
 __global__ __launch_bounds__(kWave) void sam_extend_draft_kernel(
     unsigned char* base, int max_len, SamLayout L, const int32_t* tokens,
@@ -244,6 +300,24 @@ extern "C" int sam_draft(const void* state, int B, int max_len, int K,
                      reinterpret_cast<const unsigned char*>(state), L, K, draft,
                      draft_len, match_len);
   return check_launch("sam_draft");
+}
+
+extern "C" int sam_draft_tree(const void* state, int B, int max_len, int K, int M,
+                              int N, int32_t* tokens, int32_t* parent,
+                              int32_t* n_nodes, int32_t* match_len, void* stream) {
+  int rc = check_dims("sam_draft_tree", state, B, max_len);
+  if (rc) return rc;
+  if (K < 1 || M < 0 || (int64_t)M * K + 1 > N || N > SS_MAX_TREE)
+    return set_error(SS_EINVAL, "sam_draft_tree: need K >= 1, M >= 0 and "
+                                "1 + M*K <= N <= %d (got K=%d M=%d N=%d)",
+                     SS_MAX_TREE, K, M, N);
+  if (!tokens || !parent || !n_nodes)
+    return set_error(SS_EINVAL, "sam_draft_tree: output pointer is NULL");
+  const SamLayout L = sam_layout(max_len);
+  hipLaunchKernelGGL(sam_draft_tree_kernel, dim3((unsigned)B), dim3(kWave), 0,
+                     as_stream(stream), reinterpret_cast<const unsigned char*>(state),
+                     L, K, M, N, tokens, parent, n_nodes, match_len);
+  return check_launch("sam_draft_tree");
 }
 
 extern "C" int sam_extend_draft(void* state, int B, int max_len,

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     for want in ["spec_verify", "sam_extend", "sam_draft", "sam_init",
                  "sam_state_bytes", "ss_verify_workspace_bytes",
                  "ss_verify_workspace_bytes_ex", "spec_step",
-                 "spec_verify_tree", "ss_tree_workspace_bytes", "spec_stream", "spec_finish", "sam_extend_draft",
+                 "spec_verify_tree", "ss_tree_workspace_bytes", "sam_draft_tree", "spec_stream", "spec_finish", "sam_extend_draft",
                  "sam_extend_stats", "sam_match",
                  "sam_status", "sam_export",
                  "sam_hash_slots", "ss_version", "ss_last_error_string"]:
