@@ -14,10 +14,12 @@
 // (8 non-temporal 16-byte loads in flight per lane, each wavefront load one
 // contiguous 1 KiB request) and write one 16-byte partial per row: nothing
 // but loads, arithmetic and one store. The balanced kernel (batches up to
-// 2048 sequences) gives every (sequence, chunk) of row 0 its own workgroup
-// and deals the chunks of rows 1..draft_len round-robin to the same
-// workgroups, so that the ones with extra work are dispatched first; larger
-// batches use a (sequence, row group, chunk) grid.
+// 2048 sequences with at least 4096 (sequence, chunk) pairs) gives every
+// (sequence, chunk) of row 0 its own workgroup and deals the chunks of rows
+// 1..draft_len round-robin to the same workgroups, so that the ones with
+// extra work are dispatched first; smaller batches give every (sequence,
+// row, chunk) a workgroup, larger ones use a (sequence, row group, chunk)
+// grid.
 #include <algorithm>
 
 #include "verify_common.h"
@@ -190,9 +192,10 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
-// Static grid over (sequence, row group, chunk), for batches too large for
-// the balanced kernel's plan: each workgroup streams its chunk of every row
-// j <= draft_len in its group, one row after another.
+// Static grid over (sequence, row group, chunk), for batches too small or
+// too large for the balanced kernel (see use_balanced): each workgroup
+// streams its chunk of every row j <= draft_len in its group, one row after
+// another (one row per group for small batches).
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves];
@@ -346,18 +349,44 @@ spec_stream_balanced_kernel(Args a) {
 // several resident workgroups.
 constexpr int64_t kTargetWorkgroups = 4096;
 
-// Grid of the stream pass: (sequence, row group, chunk).
+// Which kernel streams the rows.
+//  - Fewer (sequence, chunk) pairs than kTargetWorkgroups: the row-0
+//    workgroups alone do not fill the chip a few times over, and the
+//    balanced kernel's extra items, taken one after another by the same
+//    workgroups, would form its tail. Every (sequence, row, chunk) then gets
+//    a workgroup of its own (rows past a sequence's draft length exit at
+//    once). Measured at V = 151936: B = 64, K = 3 with most drafts full
+//    20.2 us against 25.2; B = 32, K = 5 bf16 with few rows 7.4 against 9.8;
+//    B = 128, K = 5 with every row needed 71.6 against 81.7.
+//  - Up to kPlanMaxB sequences otherwise: the balanced kernel, which needs
+//    no workgroup for the many rows that drafts leave unused (B = 256,
+//    K = 3 with 277 of 1024 rows needed: 29.7 us against 30.5 for the full
+//    grid; with no drafts 27.3 against 29.3).
+//  - Draft trees: a tree's nodes usually all need their rows, so every
+//    (sequence, node, chunk) gets a workgroup at any batch size (B = 256,
+//    8-node trees: 198 us per verification call against 210).
+//  - Larger batches: (sequence, row group, chunk), each workgroup streaming
+//    its chunk of the rows of its group one after another.
+inline bool tree_rows(const Args& a) { return a.dl_status == SS_ST_TREE; }
+
+inline bool use_balanced(const Args& a) {
+  return !tree_rows(a) && a.B <= kPlanMaxB &&
+         (int64_t)a.B * a.nchunks >= kTargetWorkgroups;
+}
+
 inline void set_row_groups(Args& a) {
   const int R = a.K + 1;
   const int64_t base = (int64_t)a.B * a.nchunks;
-  const int ngroups = (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
+  const int ngroups = (base < kTargetWorkgroups || tree_rows(a))
+                          ? R
+                          : (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
   a.rows_per_wg = (R + ngroups - 1) / ngroups;
   a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
 }
 
 template <int DT, bool VP, bool TR>
 int launch_stream_t(const Args& a, hipStream_t s) {
-  if (a.B <= kPlanMaxB) {
+  if (use_balanced(a)) {
     hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP, TR>),
                        dim3((unsigned)(a.B * a.nchunks)), dim3(kThreads), 0, s, a);
     return check_launch("spec_stream");

@@ -284,13 +284,15 @@ def test_one_workspace_serves_every_shape_that_fits():
         compare_verify(*g, r, Ta, u, Tally(), what=f"reuse B={B} K={K} V={V}")
 
 
-@pytest.mark.parametrize("B", [2048, 2049])
+@pytest.mark.parametrize("B", [64, 2048, 2049])
 @pytest.mark.parametrize("lengths", ["empty", "full", "mixed"])
 def test_row_balancing_across_batch_sizes(B, lengths):
-    """The stream pass deals (row, chunk) items round-robin to a resident grid
-    up to B = 2048 and streams rows per sequence above it; both give the oracle's
-    results for all-empty, all-full and mixed draft lengths (with invalid
-    lengths mixed in, which are reported and need no rows)."""
+    """The stream pass gives every (sequence, row, chunk) a workgroup when
+    B x nchunks < 4096 (B = 64 here), deals the (row, chunk) items of rows
+    1..d round-robin to the row-0 workgroups up to B = 2048, and streams rows
+    per sequence above it; all three give the oracle's results for all-empty,
+    all-full and mixed draft lengths (with invalid lengths mixed in, which are
+    reported and need no rows)."""
     say(f"[gpu] row balancing B={B} {lengths}")
     rng = np.random.default_rng(B + len(lengths))
     K, V = 3, 9000  # two chunks, the second ragged
