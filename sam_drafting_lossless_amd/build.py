@@ -26,10 +26,15 @@ LIB_SOURCES = ["api.hip", "stream.hip", "trunc.hip", "tree.hip", "verify.hip", "
 HARNESS_SOURCES = ["harness.hip"]
 
 # Packed FP32 instructions are disabled: hipcc would otherwise form them from
-# ordinary float code.
+# ordinary float code. Multiply-adds are fused only within one source
+# expression (-ffp-contract=on, not hipcc's default "fast", which fuses across
+# statements as the scheduler finds them): the rounding of every sum is then
+# a property of the source, the same in each template instantiation of a
+# kernel (so, for instance, the stream pass's plain and histogram variants
+# give bit-identical partials for a row that is not truncated).
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-ffp-contract=on",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -37,23 +37,59 @@ namespace {
 // into `raw` there). With TR, a truncated row also leaves its chunk's window
 // histogram (hs is the LDS histogram). Ends with a barrier, so `red` and `hs`
 // may be reused at once.
-template <int DT, bool VP, bool TR, typename Mid>
+// The draft token of row j (j < K), or -1; requested with the row's chunk.
+__device__ __forceinline__ int draft_token(const Args& a, int b, int j) {
+  return (a.draft && j < a.K) ? a.draft[(int64_t)b * a.K + j] : -1;
+}
+
+// XREG: x (the draft token, or -1) was requested with the chunk, and the
+// lane holding its logit takes it from its registers; else thread 0 loads x
+// and then its logit. The grid kernel, whose workgroups stream one row each,
+// takes the first (no dependent loads after the chunk's); the balanced
+// kernel the second (measured: as fast there, and it keeps the bf16
+// variant's register count, and so its occupancy, lower).
+template <int DT, bool VP, bool TR, bool XREG, typename Mid>
 __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
-                                           float T, int c, u32x4 (&raw)[kLoads],
-                                           f32x4* red, unsigned long long* hs,
-                                           Mid mid) {
+                                           float T, int c, int x,
+                                           u32x4 (&raw)[kLoads], f32x4* red,
+                                           unsigned long long* hs, Mid mid) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int R = a.K + 1, nc = a.nchunks;
   const int cstart = c * kChunk<DT>;
   const int64_t row = (int64_t)b * R + j;
-  const unsigned char* rowp = a.logits + row * a.V * Dt<DT>::kBytes;
   const bool greedy = (T == 0.0f);
   const float kk = greedy ? 0.0f : kLog2e / T;
-  // The logit of the draft token, when it lies in this chunk.
+  // The logit of the draft token x (row j < d), when it lies in this chunk:
+  // loaded by thread 0 into lx, or (XREG) left by the lane holding it in the
+  // slot after the reduction slots, read after the reduction's barrier.
   float lx = 0.0f;
-  if (!greedy && j < d && tid == 0 && a.draft) {
-    const int x = a.draft[(int64_t)b * a.K + j];
-    if (x >= cstart && x < cstart + kChunk<DT> && x < a.V) lx = load_one<DT>(rowp, x);
+  if constexpr (!XREG) {
+    if (!greedy && j < d && tid == 0 && a.draft) {
+      const int xl = a.draft[(int64_t)b * a.K + j];
+      if (xl >= cstart && xl < cstart + kChunk<DT> && xl < a.V)
+        lx = load_one<DT>(a.logits + row * a.V * Dt<DT>::kBytes, xl);
+    }
+  }
+  const bool hasx = XREG && !greedy && j < d && x >= cstart && x < cstart + kChunk<DT> &&
+                    x < a.V;
+  if (hasx) {
+    const int o = x - cstart;
+    const int itx = o / (kThreads * kVec<DT>);
+    const int rem = o - itx * (kThreads * kVec<DT>);
+    if (rem / kVec<DT> == tid) {
+      // its 32-bit word among the lane's 8 x 4, then the element in it
+      const int kx = rem % kVec<DT>;
+      const int wx = kx / (kVec<DT> / 4);
+      unsigned wv = 0;
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (it == itx && q == wx) wv = raw[it][q];
+      // (a bf16 word holds two elements: kx & 1 picks the half)
+      const u32x4 one = u32x4{wv, wv, wv, wv};
+      red[kWaves].x = elem<DT>(one, DT == SS_DTYPE_F32 ? 0 : (kx & 1));
+    }
   }
   f32x4 part;
   if (greedy) {
@@ -151,7 +187,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     __syncthreads();
     float ps = 0.0f;
     for (int i = 0; i < kWaves; ++i) ps += red[i].y;
-    part = f32x4{pm, ps, lx, 0.0f};
+    part = f32x4{pm, ps, hasx ? red[kWaves].x : lx, 0.0f};
     const int64_t hc = row * nc + c;
     a.hist[hc * kHistBins + tid] = hs[tid];
     if (tid == 0) {
@@ -182,7 +218,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     __syncthreads();
     float pm = red[0].x, ps = red[0].y;
     for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
-    part = f32x4{pm, ps, lx, 0.0f};
+    part = f32x4{pm, ps, hasx ? red[kWaves].x : lx, 0.0f};
   }
   if (tid == 0) a.partials[row * nc + c] = part;
   __syncthreads();  // red[] is reused by the next row
@@ -192,13 +228,24 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
+// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the histogram variant
+// needs more registers (LDS limits it to 6 workgroups per CU anyway), and a
+// tighter hint would spill them to scratch.
+template <int DT, bool TR>
+constexpr int kStreamWaves = TR ? (DT == SS_DTYPE_F32 ? 5 : 3) : (DT == SS_DTYPE_F32 ? 6 : 4);
+
 // Static grid over (sequence, row group, chunk), for batches too small or
 // too large for the balanced kernel (see use_balanced): each workgroup
 // streams its chunk of every row j <= draft_len in its group, one row after
-// another (one row per group for small batches).
+// another (one row per group for small batches). Only its histogram variant
+// takes the occupancy hint: the plain one measured faster without it (B =
+// 128, K = 5, every row needed: 68.0 us at 5 waves per SIMD against 71.4 at
+// the 8 the hint allows), and the scalar path (rows not 16-byte aligned)
+// spills under it.
 template <int DT, bool VP, bool TR>
-__global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
-  __shared__ f32x4 red[kWaves];
+__global__ __launch_bounds__(kThreads, ((VP && TR) ? kStreamWaves<DT, TR> : 1)) void
+spec_stream_kernel(Args a) {
+  __shared__ f32x4 red[kWaves + 1];
   __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   const int tid = threadIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
@@ -216,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
   if (j0 == 0)
     load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
                        a.V, tid, raw);
+  int x = draft_token(a, b, j0);
   if (TR && blockIdx.x == 0 && tid == 0) *a.tcount = 0;  // rows the plan lists
   if (st) return;
   const int j1 = min(j0 + a.rows_per_wg, d + 1);
@@ -223,7 +271,8 @@ __global__ __launch_bounds__(kThreads) void spec_stream_kernel(Args a) {
     if (j != 0)
       load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
                          cstart, a.V, tid, raw);
-    stream_row<DT, VP, TR>(a, b, j, d, T, c, raw, red, hs, NoMid{});
+    if (j != j0) x = draft_token(a, b, j);
+    stream_row<DT, VP, TR, true>(a, b, j, d, T, c, x, raw, red, hs, NoMid{});
   }
 }
 
@@ -270,16 +319,11 @@ __device__ __forceinline__ int extra_rows(const Args& a, int b) {
   return (v >= 1 && v <= a.K) ? v : 0;
 }
 
-// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the histogram variant
-// needs more registers (LDS limits it to 6 workgroups per CU anyway), and a
-// tighter hint would spill them to scratch.
-template <int DT, bool TR>
-constexpr int kStreamWaves = TR ? (DT == SS_DTYPE_F32 ? 5 : 3) : (DT == SS_DTYPE_F32 ? 6 : 4);
 
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, (kStreamWaves<DT, TR>)) void
 spec_stream_balanced_kernel(Args a) {
-  __shared__ f32x4 red[kWaves];
+  __shared__ f32x4 red[kWaves + 1];
   __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
   __shared__ int pre[kPlanMaxB + 1];
   __shared__ int wsum[kWaves];
@@ -301,7 +345,7 @@ spec_stream_balanced_kernel(Args a) {
     const int b = tid + i * kThreads;
     if (b < B) part += extra_rows(a, b);
   }
-  if (st == 0) stream_row<DT, VP, TR>(a, b0, 0, d, T, c0, raw, red, hs, NoMid{});
+  if (st == 0) stream_row<DT, VP, TR, false>(a, b0, 0, d, T, c0, -1, raw, red, hs, NoMid{});
   part = (int)wave_sum((float)part);  // exact: < 2^24
   if (l == 0) wsum[w] = part;
   __syncthreads();
@@ -341,7 +385,7 @@ spec_stream_balanced_kernel(Args a) {
     load_chunk<DT, VP>(a.logits + ((int64_t)t.b * R + t.j) * a.V * Dt<DT>::kBytes,
                        t.c * kChunk<DT>, a.V, tid, raw);
     st = seq_check(a, t.b, &d, &T);
-    if (st == 0) stream_row<DT, VP, TR>(a, t.b, t.j, d, T, t.c, raw, red, hs, NoMid{});
+    if (st == 0) stream_row<DT, VP, TR, false>(a, t.b, t.j, d, T, t.c, -1, raw, red, hs, NoMid{});
   }
 }
 
