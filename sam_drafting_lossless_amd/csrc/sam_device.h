@@ -138,6 +138,46 @@ __device__ __forceinline__ SamProbe sam_probe(const i32x4* slots, unsigned bmask
   return SamProbe{-1, false, -1, (int)bmask + 1};
 }
 
+// Two lookups in one round trip, (s0, c) and (s1, c): lanes 0..7 read the
+// first key's bucket, lanes 8..15 the second's. A lookup whose bucket holds
+// neither its key nor an empty row is left unresolved (slot -2) for
+// sam_probe to finish.
+struct SamProbe2 {
+  SamProbe a, b;
+};
+
+__device__ __forceinline__ SamProbe2 sam_probe2(const i32x4* slots, unsigned bmask,
+                                                int s0, int s1, int c) {
+  const int l = lane_id();
+  const unsigned bk0 = sam_bucket(s0, c, bmask), bk1 = sam_bucket(s1, c, bmask);
+  const bool second = l >= kBucket;
+  const int s = second ? s1 : s0;
+  const unsigned bk = second ? bk1 : bk0;
+  i32x4 v = i32x4{-2, -2, -2, -2};
+  if (l < 2 * kBucket) v = slots[(size_t)bk * kBucket + (l & (kBucket - 1))];
+  const bool m = (l < 2 * kBucket) && v.x == s && v.y == c;
+  const bool e = (l < 2 * kBucket) && v.x == -1;
+  const unsigned long long bal = __ballot(m || e);
+  const unsigned long long mb = __ballot(m);
+  SamProbe2 r;
+  SamProbe* out[2] = {&r.a, &r.b};
+  const unsigned bks[2] = {bk0, bk1};
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const unsigned long long gb = (bal >> (g * kBucket)) & ((1ull << kBucket) - 1);
+    SamProbe x{-2, false, -1, 1};
+    if (gb) {
+      const int f = __ffsll((unsigned long long)gb) - 1;
+      const int lane = g * kBucket + f;
+      x.slot = (int)(bks[g] * kBucket) + f;
+      x.found = (mb >> lane) & 1ull;
+      x.dst = __builtin_amdgcn_readlane(v.z, lane);
+    }
+    *out[g] = x;
+  }
+  return r;
+}
+
 struct SamHdrRegs {
   int n, last, nstates, nedges, status, max_len, V, slots;
 };
@@ -190,6 +230,16 @@ __device__ __forceinline__ SamCursor cursor_from_lanes(int hv, int rv) {
   return cs;
 }
 
+// Loads the record of link(last) into a cursor that does not carry it, so
+// that the next extension looks up (last, c) and (link(last), c) in one round
+// trip (the fused step issues this while its draw is in flight).
+__device__ __forceinline__ void sam_cursor_fetch_link(const SamSeq& S, SamCursor& cs) {
+  if (cs.link < 0 && cs.rlast.y >= 0) {
+    cs.rlink = S.st[cs.rlast.y];
+    cs.link = cs.rlast.y;
+  }
+}
+
 // Appends token c at position n (Blumer's online extension; `cur` is numbered
 // before `clone`) and moves the cursor to cur. Returns false if a bound check
 // trips.
@@ -209,8 +259,59 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
   i32x4 rp = cs.rlast;
   SamProbe pr;
   int guard = 0;
-  // Walk suffix links from last, adding (p, c) -> cur until (p, c) exists.
-  while (true) {
+  bool walked = false;
+  // When the cursor carries the record of link(last), (last, c) and
+  // (link(last), c) are looked up in one round trip, with the record of the
+  // next state on the walk. The second lookup ran before (last, c) was
+  // inserted: it is repeated if that insertion took the empty row it found.
+  if (cs.link >= 0 && cs.link == rp.y) {
+    const int p1 = cs.link;
+    const i32x4 rp1 = cs.rlink;
+    const int p2 = rp1.y;
+    i32x4 rp2 = i32x4{0, -1, -1, -1};
+    if (p2 != -1) rp2 = S.st[p2];  // in flight with the two lookups
+    const SamProbe2 two = sam_probe2(S.slots, bmask, p, p1, c);
+    tally(SS_STAT_PROBES, 2);
+    tally(SS_STAT_BUCKETS, 2);
+    SamProbe r0 = two.a, r1 = two.b;
+    if (r0.slot == -2) {
+      r0 = sam_probe(S.slots, bmask, p, c);
+      tally(SS_STAT_PROBES, 1);
+      tally(SS_STAT_BUCKETS, r0.buckets);
+    }
+    if (r0.slot < 0) return false;
+    if (r0.found) {
+      pr = r0;
+      walked = true;
+    } else {
+      tally(SS_STAT_WALK, 1);
+      S.slots[r0.slot] = i32x4{p, c, cur, rp.w};
+      reinterpret_cast<int*>(&S.st[p])[3] = r0.slot;
+      h.nedges++;
+      if (r1.slot == -2 || (!r1.found && r1.slot == r0.slot)) {
+        r1 = sam_probe(S.slots, bmask, p1, c);
+        tally(SS_STAT_PROBES, 1);
+        tally(SS_STAT_BUCKETS, r1.buckets);
+      }
+      if (r1.slot < 0) return false;
+      p = p1;
+      rp = rp1;
+      if (r1.found) {
+        pr = r1;
+        walked = true;
+      } else {
+        tally(SS_STAT_WALK, 1);
+        S.slots[r1.slot] = i32x4{p, c, cur, rp.w};
+        reinterpret_cast<int*>(&S.st[p])[3] = r1.slot;
+        h.nedges++;
+        p = p2;
+        rp = rp2;
+        walked = (p == -1);
+      }
+    }
+  }
+  // Walk suffix links from p, adding (p, c) -> cur until (p, c) exists.
+  while (!walked) {
     const int nxt = rp.y;
     i32x4 rn = i32x4{0, -1, -1, -1};
     if (nxt != -1) rn = S.st[nxt];  // in flight together with the probe

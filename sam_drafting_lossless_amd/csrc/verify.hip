@@ -291,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   }
   // Automaton step (wavefront 0): the emitted tokens sh.tok[0..al] are
   // appended in order; when a token is drawn, the accepted drafts before it
-  // are appended while the draw's chunk is in flight.
+  // are appended while the draw's chunk is in flight (with none, the record
+  // of link(last) is fetched then, for the drawn token's first lookups).
   bool whole = true, cs_ready = false;
   int appended = 0;
   const bool drawn = sh.st == 0 && !greedy && !residual;
@@ -300,11 +301,15 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     if (!spec || al != d) draw_load<DT, VP>(a, b, al, sh.pick[al], raw);
     auto during = [&]() {
       if constexpr (SAM) {
-        if (w == 0 && al > 0) {
+        if (w == 0) {
           cs = cursor_from_lanes(hv, rv);
           cs_ready = true;
-          whole = sam_append(S, cs, sh.tok, al, R, a.max_len);
-          appended = al;
+          if (al > 0) {
+            whole = sam_append(S, cs, sh.tok, al, R, a.max_len);
+            appended = al;
+          } else {
+            sam_cursor_fetch_link(S, cs);
+          }
         }
       }
     };
