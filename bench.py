@@ -146,6 +146,35 @@ def hbm_read_probe(torch, harness, nbytes=4 << 30, iters=5):
     return best
 
 
+def same_size_read_probe(torch, harness, ring, nbytes, reps=20, batch=8):
+    """The plain read kernel on exactly one stream launch's bytes: 8
+    back-to-back launches between events over the ring slots in turn (the
+    same way the stream kernel is timed), for a grid-stride grid of 4096
+    workgroups and for one workgroup per 32 KiB; the faster is reported."""
+    import numpy as np
+    nbytes = int(nbytes) // 16 * 16
+    views = [r.view(-1).view(torch.uint8)[:nbytes] for r in ring]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for grid in (4096, max(1, nbytes // 32768)):
+        for i in range(batch):
+            harness.read_bw(views[i % len(views)], sink, grid)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for k in range(reps):
+            evs[k][0].record()
+            for i in range(batch):
+                harness.read_bw(views[(k * batch + i) % len(views)], sink, grid)
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3 / batch
+        if best is None or us < best["us_per_launch"]:
+            best = {"bytes_per_launch": nbytes, "grid": grid, "us_per_launch": round(us, 2),
+                    "GBps": round(nbytes / us / 1e3, 1)}
+    return best
+
+
 def sam_stats_report(steps: int):
     """Automaton work per appended token (hash lookups, 128-byte bucket reads,
     suffix-link steps, clones) and time per extend call, for prefill and for
@@ -732,6 +761,8 @@ def main():
     gt_h = m["gt_h"]
 
     probe = None if args.no_probe else hbm_read_probe(torch, harness)
+    probe_same = (None if args.no_probe else
+                  same_size_read_probe(torch, harness, ring, m["bytes_per_launch"]))
     cpu = cpu_detail = None
     if args.cpu_budget > 0:
         slot_h = ring[(total - 1) % RING].cpu().numpy()
@@ -780,6 +811,7 @@ def main():
         "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
                                       np.percentile(step_us, [10, 50, 90])],
         "hbm_read_probe_GBps": probe,
+        "hbm_read_probe_same_bytes": probe_same,
         "setup_s": m["setup_s"],
     }
     print(json.dumps(res), flush=True)
