@@ -145,7 +145,9 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     // Truncated row: the chunk max first, then one pass that adds each
     // element's weight exp2((l - max) * log2e / T) to the sum and to the
     // chunk's window histogram (see kHistBins): count and fixed-point weight
-    // in one 64-bit word per bin, the bin on the row's shared grid.
+    // in one 64-bit word per bin, the bin on the row's shared grid. The
+    // chunk's finite count goes to its header (the plan's totals come from
+    // the headers and the partials, so nothing below the window is kept).
     float vm = kNegInf;
 #pragma unroll
     for (int it = 0; it < kLoads; ++it)
@@ -154,7 +156,6 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     mid();
     vm = wave_max(vm);
     hs[tid] = 0;
-    if (tid == 0) hs[kHistBins] = 0;
     if (l == 0) red[w] = f32x4{vm, 0.0f, 0.0f, 0.0f};
     __syncthreads();
     float pm = red[0].x;
@@ -162,7 +163,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     const float base = (pm == kNegInf) ? 0.0f : pm;
     const int a0 = abs_bin(pm, kk);
     float s = 0.0f;
-    unsigned long long rest = 0;
+    int nfin = 0;
 #pragma unroll
     for (int it = 0; it < kLoads; ++it)
 #pragma unroll
@@ -171,29 +172,29 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
         const float wv = fast_exp2((v - base) * kk);
         s += wv;
         if (v > kNegInf) {  // -inf (probability 0) and NaN are not counted
+          ++nfin;
           const int jb = abs_bin(v, kk) - a0;
-          const unsigned long long word =
-              kCountOne | (unsigned long long)(unsigned)(wv * kFixScale);
           if (jb >= 0 && jb < kHistBins)
-            atomicAdd(&hs[jb], word);
-          else
-            rest += word;
+            atomicAdd(&hs[jb], kCountOne | (unsigned long long)(unsigned)(wv * kFixScale));
         }
       }
-    if (rest) atomicAdd(&hs[kHistBins], rest);
     s = wave_sum(s);
+    const float nf = wave_sum((float)nfin);  // exact: < 2^24
     __syncthreads();  // every lane has read red[].x
-    if (l == 0) red[w].y = s;
+    if (l == 0) {
+      red[w].y = s;
+      red[w].z = nf;
+    }
     __syncthreads();
-    float ps = 0.0f;
-    for (int i = 0; i < kWaves; ++i) ps += red[i].y;
+    float ps = 0.0f, nft = 0.0f;
+    for (int i = 0; i < kWaves; ++i) {
+      ps += red[i].y;
+      nft += red[i].z;
+    }
     part = f32x4{pm, ps, hasx ? red[kWaves].x : lx, 0.0f};
     const int64_t hc = row * nc + c;
     a.hist[hc * kHistBins + tid] = hs[tid];
-    if (tid == 0) {
-      const unsigned long long r = hs[kHistBins];
-      a.hhdr[hc] = i32x4{a0, (int)(unsigned)(r >> 32), (int)(unsigned)r, 0};
-    }
+    if (tid == 0) a.hhdr[hc] = i32x4{a0, (int)nft, 0, 0};
   } else {
     // Online (max, sum exp2) folded one 16-byte vector at a time, in the
     // order the loads return, so only the raw vectors stay live.
@@ -246,7 +247,7 @@ template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, ((VP && TR) ? kStreamWaves<DT, TR> : 1)) void
 spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves + 1];
-  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistBins : 1];
   const int tid = threadIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
   const int c = blockIdx.x % nc;
@@ -324,7 +325,7 @@ template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, (kStreamWaves<DT, TR>)) void
 spec_stream_balanced_kernel(Args a) {
   __shared__ f32x4 red[kWaves + 1];
-  __shared__ unsigned long long hs[TR ? kHistBins + 1 : 1];
+  __shared__ unsigned long long hs[TR ? kHistBins : 1];
   __shared__ int pre[kPlanMaxB + 1];
   __shared__ int wsum[kWaves];
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;

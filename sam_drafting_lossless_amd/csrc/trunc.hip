@@ -81,8 +81,7 @@ constexpr int kPlanBatch = 24;  // chunk histograms requested at once
 __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   __shared__ int s_a[kMaxChunks];
   __shared__ float s_pm[kMaxChunks];
-  __shared__ unsigned long long s_rest[kMaxChunks];
-  __shared__ float scratch[kWaves];
+  __shared__ float scratch[2][kWaves];
   __shared__ float wtot[2][kWaves];
   __shared__ int first[3];
   __shared__ float zval[2];
@@ -91,25 +90,23 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   const int64_t row = blockIdx.x;
   const int nc = a.nchunks;
   const int64_t h0 = row * nc;
-  // The chunk headers are requested together with the row's parameters (they
-  // are in bounds for every row; an inactive row's are never used).
+  // The chunk headers and partials are requested together with the row's
+  // parameters (they are in bounds for every row; an inactive row's are
+  // never used).
   i32x4 hh = i32x4{0, 0, 0, 0};
-  float pmv = 0.0f;
+  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (tid < nc) {
     hh = a.hhdr[h0 + tid];
-    pmv = a.partials[h0 + tid].x;
+    pv = a.partials[h0 + tid];
   }
   const RowCtx rc = row_ctx(a, row);
   if (!rc.active) return;
   if (tid < nc) {
     s_a[tid] = hh.x;
-    s_rest[tid] = ((unsigned long long)(unsigned)hh.y << 32) | (unsigned)hh.z;
-    s_pm[tid] = pmv;
+    s_pm[tid] = pv.x;
   }
   for (int c = tid + kThreads; c < nc; c += kThreads) {
-    const i32x4 h2 = a.hhdr[h0 + c];
-    s_a[c] = h2.x;
-    s_rest[c] = ((unsigned long long)(unsigned)h2.y << 32) | (unsigned)h2.z;
+    s_a[c] = a.hhdr[h0 + c].x;
     s_pm[c] = a.partials[h0 + c].x;
   }
   if (tid < 3) first[tid] = kRestBin;
@@ -118,21 +115,30 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   float m = kNegInf;
   for (int c = 0; c < nc; ++c) m = fmaxf(m, s_pm[c]);
   const int a0 = abs_bin(m, rc.kk);
-  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c. Totals (every
-  // bin of every chunk, and the chunks' rest words) give the finite count N
-  // and the mass Z. The words of kPlanBatch chunks are requested together.
-  float cnt = 0.0f, mass = 0.0f, tcnt = 0.0f, tmass = 0.0f;
+  // Totals: the finite count N from the chunk headers and the mass Z
+  // (relative to the row max) from the partials.
+  float tcnt = 0.0f, tmass = 0.0f;
+  if (tid < nc) {
+    tcnt = (float)hh.y;
+    tmass = pv.y * fast_exp2((pv.x - m) * rc.kk);
+  }
+  for (int c = tid + kThreads; c < nc; c += kThreads) {
+    const f32x4 p = a.partials[h0 + c];
+    tcnt += (float)a.hhdr[h0 + c].y;
+    tmass += p.y * fast_exp2((p.x - m) * rc.kk);
+  }
+  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c. The words of
+  // kPlanBatch chunks are requested together.
+  float cnt = 0.0f, mass = 0.0f;
   for (int c0 = 0; c0 < nc; c0 += kPlanBatch) {
-    unsigned long long wt[kPlanBatch], wb[kPlanBatch];
+    unsigned long long wb[kPlanBatch];
 #pragma unroll
     for (int u = 0; u < kPlanBatch; ++u) {
       const int c = c0 + u;
-      wt[u] = wb[u] = 0;
+      wb[u] = 0;
       if (c < nc) {
-        const unsigned long long* hc = a.hist + (h0 + c) * kHistBins;
-        wt[u] = hc[tid];
         const int jb = tid - (s_a[c] - a0);
-        if (jb >= 0 && jb < kHistBins) wb[u] = hc[jb];
+        if (jb >= 0 && jb < kHistBins) wb[u] = a.hist[(h0 + c) * kHistBins + jb];
       }
     }
 #pragma unroll
@@ -140,36 +146,41 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
       const int c = c0 + u;
       if (c < nc) {
         const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
-        tcnt += (float)(unsigned)(wt[u] >> 48);
-        tmass += (float)(wt[u] & kMassMask) * sc;
         cnt += (float)(unsigned)(wb[u] >> 48);
         mass += (float)(wb[u] & kMassMask) * sc;
       }
     }
   }
-  for (int c = tid; c < nc; c += kThreads) {
-    const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
-    tcnt += (float)(unsigned)(s_rest[c] >> 48);
-    tmass += (float)(s_rest[c] & kMassMask) * sc;
-  }
-  const float N = block_sum(tcnt, scratch);  // finite tokens (exact: < 2^24)
-  const float Z = block_sum(tmass, scratch);
-  // Inclusive scans of counts and masses from the top bin down.
+  // N and Z (one reduction for both), and inclusive scans of counts and
+  // masses from the top bin down.
+  tcnt = wave_sum(tcnt);  // exact: < 2^24
+  tmass = wave_sum(tmass);
   float C = wave_inclusive_sum(cnt), M = wave_inclusive_sum(mass);
   if (l == kWave - 1) {
+    scratch[0][w] = tcnt;
+    scratch[1][w] = tmass;
     wtot[0][w] = C;
     wtot[1][w] = M;
   }
   __syncthreads();
-  for (int i = 0; i < w; ++i) {
-    C += wtot[0][i];
-    M += wtot[1][i];
+  float N = 0.0f, Z = 0.0f;
+  for (int i = 0; i < kWaves; ++i) {
+    N += scratch[0][i];
+    Z += scratch[1][i];
+    if (i < w) {
+      C += wtot[0][i];
+      M += wtot[1][i];
+    }
   }
   const int k = a.top_k ? a.top_k[rc.b] : 0;
   const float tp = a.top_p ? a.top_p[rc.b] : 1.0f;
   const bool kA = k >= 1 && k < a.V && (float)k <= N;
   const bool pA = tp < 1.0f;
-  if (kA && C >= (float)k) atomicMin(&first[0], tid);
+  // C and M do not decrease with the bin, so the first bin meeting a target
+  // is the first set lane of the first wavefront whose ballot is not empty
+  // (one LDS atomic per wavefront).
+  const unsigned long long kb = __ballot(kA && C >= (float)k);
+  if (l == 0 && kb) atomicMin(&first[0], w * kWave + __ffsll((unsigned long long)kb) - 1);
   __syncthreads();
   const int bk = kA ? first[0] : kRestBin;
   // Mass above bin bk (Z_lo) and through it (Z_hi): top-p's share is taken of
@@ -189,8 +200,9 @@ __global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
   if (pA) {
     const float tlo = tp * zval[0] * (1.0f - kPlanMargin);
     const float thi = tp * zval[1] * (1.0f + kPlanMargin);
-    if (M >= tlo) atomicMin(&first[1], tid);
-    if (M >= thi) atomicMin(&first[2], tid);
+    const unsigned long long lo = __ballot(M >= tlo), hi = __ballot(M >= thi);
+    if (l == 0 && lo) atomicMin(&first[1], w * kWave + __ffsll((unsigned long long)lo) - 1);
+    if (l == 0 && hi) atomicMin(&first[2], w * kWave + __ffsll((unsigned long long)hi) - 1);
   }
   __syncthreads();
   // Candidate range [rlo, rhi]. Top-k's own bin is always in it (the k-th

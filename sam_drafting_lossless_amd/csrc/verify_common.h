@@ -27,7 +27,9 @@ constexpr float kNegInf = -INFINITY;
 //   starting at the bin of the chunk max (32 octaves). Bins lie on one grid
 //   for all chunks of a row: the bin of logit l is floor(-l * log2e/T *
 //   kBinsPerOctave) (abs_bin), so a chunk's window is a shift of the row's.
-//   One bin is a 64-bit word: count in bits 48..63, mass in bits 0..47.
+//   One bin is a 64-bit word: count in bits 48..63, mass in bits 0..47. Logits
+//   below the window are not binned; the chunk's header holds its finite
+//   count, and its total mass is the stream partial's sum.
 constexpr int kHistBins = 256;
 constexpr int kBinsPerOctave = 8;
 constexpr int kRestBin = kHistBins;  // "beyond the window"
@@ -165,7 +167,7 @@ struct Args {
   // Truncation workspace (NULL unless top_k or top_p is given), per row
   // (b*(K+1) + j) and per (row, chunk):
   unsigned long long* hist;  // [rows*nchunks*kHistBins] window histograms
-  i32x4* hhdr;      // [rows*nchunks]: (window start bin, rest hi, rest lo, 0)
+  i32x4* hhdr;      // [rows*nchunks]: (window start bin, finite count, 0, 0)
   i32x4* plan;      // [rows*2]: (row start bin, r_lo, r_hi, count above),
                     //           (active, 0, 0, 0)
   int* ccount;      // [rows*nchunks] candidates each chunk found
