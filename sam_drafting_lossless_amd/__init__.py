@@ -497,7 +497,8 @@ def sam_status(state, B: int, max_len: int, out=None, stream=None):
 def sam_export(state, B: int, max_len: int, b: int, stream=None):
     """Sequence b's automaton as host numpy arrays: dict(n, last, num_states,
     num_edges, status, len, link, min_endpos, first_edge, edges [E,3] sorted
-    by (src, token), text). Synchronises the stream."""
+    by (src, token), text, slots [hash_slots,4] = the raw table rows (src,
+    token, dst, next)). Synchronises the stream."""
     dev = state.device
     H = sam_hash_slots(max_len)
     hdr = torch.empty(8, dtype=torch.int32, device=dev)
@@ -512,13 +513,14 @@ def sam_export(state, B: int, max_len: int, b: int, stream=None):
     n, last, S, E, status = (int(v) for v in h[:5])
     st = st[:S].cpu().numpy()
     ed = ed.cpu().numpy()
+    slots = ed.copy()
     ed = ed[ed[:, 0] >= 0][:, :3]
     order = (ed[:, 0].astype("int64") << 32) | ed[:, 1].astype("int64")
     ed = ed[order.argsort(kind="stable")]
     return {"n": n, "last": last, "num_states": S, "num_edges": E,
             "status": status, "len": st[:, 0].copy(), "link": st[:, 1].copy(),
             "min_endpos": st[:, 2].copy(), "first_edge": st[:, 3].copy(),
-            "edges": ed, "text": tx[:n].cpu().numpy()}
+            "edges": ed, "text": tx[:n].cpu().numpy(), "slots": slots}
 
 
 class SamState:

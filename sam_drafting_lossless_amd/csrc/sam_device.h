@@ -333,7 +333,7 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
   i32x4 rlink;
   if (p == -1) {
     link = 0;
-    rlink = i32x4{0, -1, 0, 0};  // only the root's len (0) is read from it
+    rlink = i32x4{0, -1, 0, 0};  // not the root's record: not carried below
   } else {
     const int q = pr.dst;
     const i32x4 rq = S.st[q];
@@ -395,7 +395,10 @@ __device__ inline bool sam_extend_one(const SamSeq& S, SamCursor& cs, int c,
   S.text[i] = c;
   h.n = i + 1;
   cs.rlast = i32x4{lencur, link, i, -1};
-  cs.link = link;
+  // The cursor carries link(cur)'s record only when it is exact: after a walk
+  // to the root (link 0) the root's record (its first transition) was not
+  // loaded, and the next extension must not insert with it.
+  cs.link = (p == -1) ? -1 : link;
   cs.rlink = rlink;
   return true;
 }

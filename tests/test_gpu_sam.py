@@ -18,7 +18,27 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "abcbc.json")
 
 
+def _check_chains(g, what):
+    """The table's `next` field chains each state's transitions (the chain a
+    clone copies): from first_edge, the chain visits exactly the rows whose
+    source is that state, each once."""
+    slots, fe = g["slots"], g["first_edge"]
+    rows = {}
+    for i, (src, _tok, _dst, _nxt) in enumerate(slots):
+        if src >= 0:
+            rows.setdefault(int(src), set()).add(i)
+    for s in range(g["num_states"]):
+        seen, e = set(), int(fe[s])
+        while e != -1:
+            assert e not in seen, (what, "cycle in the chain of state", s)
+            assert slots[e][0] == s, (what, "chain of state", s, "reaches row", e)
+            seen.add(e)
+            e = int(slots[e][3])
+        assert seen == rows.get(s, set()), (what, "chain of state", s)
+
+
 def _compare_structure(g, o, what):
+    _check_chains(g, what)
     assert g["num_states"] == len(o["len"]), what
     assert g["num_edges"] == len(o["edges"]), what
     assert g["last"] == o["last"], what
