@@ -91,6 +91,17 @@ __device__ __forceinline__ float wave_shift_up1(float v) {
   return dpp_f<kDppWaveShr1>(0.0f, v);
 }
 
+// An empty asm that reads and writes v, so that v is computed where it
+// stands: a sum used only after a loop with conditional stores is otherwise
+// sunk below the loop, and every input of it is held until then.
+__device__ __forceinline__ void keep_here(float& v) { asm volatile("" : "+v"(v)); }
+
+// Number of lanes below this one whose bit is set in a wavefront mask.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
 // Wavefront reductions; every lane ends with the result.
 __device__ __forceinline__ float wave_sum(float v) { return lane63(wave_inclusive_sum(v)); }
 

@@ -247,25 +247,30 @@ __device__ __forceinline__ int64_t listed_row(const Args& a, int e) {
 // extract: (listed row, chunk) items, grid-stride (the grid is sized for the
 // largest list; a workgroup takes items g, g + grid, ... below count x nc).
 // ---------------------------------------------------------------------------
+struct ExtractShared {
+  int2 run[kWaves][kSegCap];  // each wavefront's candidates, in its own run
+  float scratch[kWaves];
+  int cnt[kWaves];
+};
+
 template <int DT, bool VP>
 __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
-                                             float* scratch, int* woff);
+                                             ExtractShared& sh);
 
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
-  __shared__ float scratch[kWaves];
-  __shared__ int woff[kWaves + 1];
+  __shared__ ExtractShared sh;
   const int nc = a.nchunks;
   const int64_t items = (int64_t)*a.tcount * nc;
   for (int64_t x = blockIdx.x; x < items; x += gridDim.x) {
     const int e = (int)(x / nc);
-    extract_item<DT, VP>(a, a.tlist[e], (int)(x - (int64_t)e * nc), scratch, woff);
+    extract_item<DT, VP>(a, a.tlist[e], (int)(x - (int64_t)e * nc), sh);
   }
 }
 
 template <int DT, bool VP>
 __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
-                                             float* scratch, int* woff) {
+                                             ExtractShared& sh) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int nc = a.nchunks;
   const int cstart = c * kChunk<DT>;
@@ -277,82 +282,57 @@ __device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
   const int a0 = p0.x, rlo = p0.y, rhi = p0.z;
   const float m = __int_as_float(p1.z);
   float above = 0.0f;
-  int n = 0;
-  // A lane's first kHeld candidates stay in registers, so that the chunk
-  // itself need not stay live across the reservation below; a lane with more
-  // re-reads its part of the chunk afterwards.
-  constexpr int kHeld = 4;
-  float hv[kHeld];
-  int hi[kHeld];
-#pragma unroll
-  for (int q = 0; q < kHeld; ++q) {
-    hv[q] = 0.0f;
-    hi[q] = 0;
-  }
+  // Candidates are compacted per wavefront as they are found: a ballot per
+  // element gives each finding lane its place after the wavefront's earlier
+  // finds (element by element, lanes in order), in the wavefront's LDS run.
+  // A run past kSegCap is not stored; the chunk then overflows its segment
+  // (which holds at most kSegCap) and the row is selected by re-scanning it.
+  int n = 0;  // wavefront-uniform
+  int2* run = sh.run[w];
 #pragma unroll
   for (int it = 0; it < kLoads; ++it)
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) {
       const float v = elem<DT>(raw[it], k);
-      if (v > kNegInf) {
-        const int rb = abs_bin(v, kk) - a0;
-        if (rb < rlo) {
-          above += fast_exp2((v - m) * kk);
-        } else if (in_range(rb, rlo, rhi)) {
-#pragma unroll
-          for (int q = 0; q < kHeld; ++q)
-            if (n == q) {
-              hv[q] = v;
-              hi[q] = elem_index<DT, VP>(cstart, tid, it, k);
-            }
-          ++n;
-        }
+      const bool fin = v > kNegInf;
+      const int rb = abs_bin(v, kk) - a0;
+      if (fin && rb < rlo) above += fast_exp2((v - m) * kk);
+      keep_here(above);
+      const bool inr = fin && in_range(rb, rlo, rhi);
+      const unsigned long long hit = __ballot(inr);
+      if (inr) {
+        const int p = n + lanes_below(hit);
+        if (p < kSegCap)
+          run[p] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
       }
+      n += __popcll(hit);
     }
-  above = block_sum(above, scratch);
-  if (tid == 0) a.tpart[row * nc + c] = above;
-  // Candidates go to this (row, chunk)'s own segment of the list: a
-  // block-wide exclusive scan of the per-thread counts gives each lane its
-  // place. A segment that would overflow is not written (its count says so,
-  // and the row is then selected by re-scanning it).
-  const int inc = (int)wave_inclusive_sum((float)n);
-  if (l == kWave - 1) woff[w] = inc;
-  __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int i = 0; i < kWaves; ++i) {
-      const int v = woff[i];
-      woff[i] = t;
-      t += v;
-    }
-    woff[kWaves] = t;
-    a.ccount[row * nc + c] = t;
+  above = wave_sum(above);
+  if (l == 0) {
+    sh.scratch[w] = above;
+    sh.cnt[w] = n;
   }
   __syncthreads();
-  int pos = woff[w] + inc - n;
-  const bool fits = woff[kWaves] <= a.segcap;
-  __syncthreads();  // woff is reused by the next item
-  if (n == 0 || !fits) return;
-  int2* out = a.cand + (row * nc + c) * a.segcap;
+  // The runs go to this (row, chunk)'s own segment of the list in wavefront
+  // order. A segment that would overflow is not written (its count says so).
+  int base = 0, tot = 0;
+  float sum = 0.0f;
 #pragma unroll
-  for (int q = 0; q < kHeld; ++q)
-    if (q < n) out[pos + q] = int2{__float_as_int(hv[q]), hi[q]};
-  if (n <= kHeld) return;
-  u32x4 again[kLoads];
-  load_chunk<DT, VP, false>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid,
-                            again);
-  int seen = 0;
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const float v = elem<DT>(again[it], k);
-      if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi)) {
-        if (seen >= kHeld)
-          out[pos + seen] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
-        ++seen;
-      }
-    }
+  for (int i = 0; i < kWaves; ++i) {
+    const int ci = sh.cnt[i];
+    base += (i < w) ? ci : 0;
+    tot += ci;
+    sum += sh.scratch[i];
+  }
+  if (tid == 0) {
+    a.tpart[row * nc + c] = sum;
+    a.ccount[row * nc + c] = tot;
+  }
+  if (tot <= a.segcap) {
+    int2* out = a.cand + (row * nc + c) * a.segcap + base;
+    for (int p = l; p < n; p += kWave) out[p] = run[p];
+  }
+  __syncthreads();  // the runs and counts are reused by the next item
 }
 
 // ---------------------------------------------------------------------------
