@@ -95,6 +95,9 @@ __device__ __forceinline__ float wave_shift_up1(float v) {
 // stands: a sum used only after a loop with conditional stores is otherwise
 // sunk below the loop, and every input of it is held until then.
 __device__ __forceinline__ void keep_here(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void keep_here(u32x4& v) { asm volatile("" : "+v"(v)); }
+// The same for a wavefront-uniform value, kept in a scalar register.
+__device__ __forceinline__ void keep_here_uniform(int& v) { asm volatile("" : "+s"(v)); }
 
 // Number of lanes below this one whose bit is set in a wavefront mask.
 __device__ __forceinline__ int lanes_below(unsigned long long m) {

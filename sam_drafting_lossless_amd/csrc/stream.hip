@@ -162,8 +162,14 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     for (int i = 1; i < kWaves; ++i) pm = fmaxf(pm, red[i].x);
     const float base = (pm == kNegInf) ? 0.0f : pm;
     const int a0 = abs_bin(pm, kk);
+    // (bf16: the elements are re-extracted from their packed registers;
+    // converted once for both passes, the chunk would be held as 64 floats)
+    if constexpr (DT != SS_DTYPE_F32) {
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) keep_here(raw[it]);
+    }
     float s = 0.0f;
-    int nfin = 0;
+    int nfin = 0;  // wavefront-uniform
 #pragma unroll
     for (int it = 0; it < kLoads; ++it)
 #pragma unroll
@@ -171,15 +177,18 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
         const float v = elem<DT>(raw[it], k);
         const float wv = fast_exp2((v - base) * kk);
         s += wv;
-        if (v > kNegInf) {  // -inf (probability 0) and NaN are not counted
-          ++nfin;
-          const int jb = abs_bin(v, kk) - a0;
-          if (jb >= 0 && jb < kHistBins)
-            atomicAdd(&hs[jb], kCountOne | (unsigned long long)(unsigned)(wv * kFixScale));
-        }
+        keep_here(s);
+        // -inf (probability 0) and NaN are not counted; one condition, so
+        // that the element takes a single branch
+        const bool fin = v > kNegInf;
+        nfin += __popcll(__ballot(fin));
+        keep_here_uniform(nfin);
+        const int jb = abs_bin(v, kk) - a0;
+        if (fin && (unsigned)jb < (unsigned)kHistBins)
+          atomicAdd(&hs[jb], kCountOne | (unsigned long long)(unsigned)(wv * kFixScale));
       }
     s = wave_sum(s);
-    const float nf = wave_sum((float)nfin);  // exact: < 2^24
+    const float nf = (float)nfin;  // exact: < 2^24
     __syncthreads();  // every lane has read red[].x
     if (l == 0) {
       red[w].y = s;
@@ -229,11 +238,11 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
-// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the histogram variant
-// needs more registers (LDS limits it to 6 workgroups per CU anyway), and a
-// tighter hint would spill them to scratch.
+// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the bf16 histogram
+// variant needs more registers (3: a tighter hint spills them to scratch).
+// LDS limits the histogram variant to 6 workgroups per CU anyway.
 template <int DT, bool TR>
-constexpr int kStreamWaves = TR ? (DT == SS_DTYPE_F32 ? 5 : 3) : (DT == SS_DTYPE_F32 ? 6 : 4);
+constexpr int kStreamWaves = (DT == SS_DTYPE_F32) ? 6 : (TR ? 3 : 4);
 
 // Static grid over (sequence, row group, chunk), for batches too small or
 // too large for the balanced kernel (see use_balanced): each workgroup
