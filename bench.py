@@ -729,9 +729,9 @@ def main():
                     help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the step shards by sequence with no exchange; see "
-              "DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(the step would shard by sequence, with no exchange between "
+              "GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.sam_stats:
