@@ -193,6 +193,48 @@ def test_rows_beyond_the_candidate_list(case):
     say(f"    {tally}")
 
 
+@pytest.mark.parametrize("case,n_tied", [("spread", 512), ("one_wavefront", 512),
+                                         ("one_wavefront", 513)])
+def test_chunk_segment_capacity(case, n_tied):
+    """A chunk's candidates fill its 512-entry segment exactly (kept in the
+    candidate list) or overflow it by one (the row is selected by
+    re-scanning it): n_tied tokens share the top-k cut's logit in the first
+    fp32 chunk (8,192 tokens), either spread over it or all in the part one
+    wavefront reads (thread (e // 4) % 256 holds element e), ten tokens lie
+    above the cut in the second chunk and the rest far below. Ties at the cut
+    are kept, so the oracle's set is unique."""
+    say(f"[gpu] truncation: segment capacity {case} {n_tied}")
+    rng = np.random.default_rng(71 + n_tied + (case == "spread"))
+    B, K, V = 8, 2, 20000
+    R = K + 1
+    x = np.full((B, R, V), -30.0, np.float32)
+    e = np.arange(8192)
+    pool = e if case == "spread" else e[((e // 4) % 256) // 64 == 2]
+    tied = np.zeros((B, R, n_tied), np.int64)
+    for b in range(B):
+        for j in range(R):
+            tied[b, j] = rng.choice(pool, n_tied, replace=False)
+            x[b, j, tied[b, j]] = 1.0
+            x[b, j, 8192 + rng.choice(8192, 10, replace=False)] = 5.0
+    # drafts: a token raised to 10 above the cut (p ~ 0.9, mostly
+    # accepted) or a token far below it (dropped, so rejected)
+    draft = rng.integers(16384, V, (B, K)).astype(np.int32)
+    for b in range(B):
+        for j in range(K):
+            if rng.random() < 0.6:
+                draft[b, j] = 8192 + int(rng.integers(8192))
+                x[b, j, draft[b, j]] = 10.0
+    dl = np.full(B, K, np.int32)
+    T = np.full(B, 1.0, np.float32)
+    u = rng.random((B, R)).astype(np.float32)
+    top_k = np.full(B, 100, np.int32)
+    g = _run(torch.from_numpy(x).cuda(), draft, dl, T, u, top_k, None)
+    r = oracle.verify(x, draft, dl, T, u, nthreads=8, top_k=top_k)
+    tally = Tally()
+    assert _compare(g, r, T, u, f"segment {case} {n_tied}", tally) == 0
+    say(f"    {tally}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_truncation_with_given_q(dtype):
     say(f"[gpu] truncation with given q {dtype}")
