@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
   if (lds) {
     // Entry f of the list lies in chunk c with pre[c] <= f < pre[c+1].
     const int2* seg = a.cand + row * nc * a.segcap;
-    constexpr int kU = 8;
+    constexpr int kU = 16;  // loads in flight per thread: 4,096 candidates in one round trip
     for (int f0 = 0; f0 < n; f0 += kU * kThreads) {
       int2 ev[kU];
       int ch[kU];
