@@ -113,10 +113,14 @@ size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);
  *
  * Arguments:
  *   logits      [B, K+1, V], dtype SS_DTYPE_F32 (float) or SS_DTYPE_BF16
- *               (bfloat16, widened exactly to float).
+ *               (bfloat16, widened exactly to float). Must start on a
+ *               16-byte boundary (SS_EINVAL otherwise); rows are read 16
+ *               bytes at a time when V is a multiple of 4 (fp32) or 8
+ *               (bf16), element by element otherwise.
  *   draft       [B, K] int32; entries j >= draft_len[b] are ignored.
  *   draft_len   [B] int32 in [0, K].
- *   q           [B, K, V] float draft probabilities, or NULL for one-hot.
+ *   q           [B, K, V] float draft probabilities, or NULL for one-hot;
+ *               16-byte aligned like logits.
  *   temperature [B] float >= 0.
  *   uniforms    [B, K+1] float in [0, 1): columns 0..K-1 are the acceptance
  *               coins, column K the final coin. May be NULL only if every
@@ -154,7 +158,8 @@ size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);
  * Limits: 1 <= B, 1 <= K <= SS_MAX_K, 1 <= V <= 2^21. A temperature that is
  * positive but below the smallest normal float is reported as
  * SS_ST_TEMPERATURE.
- * Errors: SS_EINVAL for sizes/null pointers/dtype, SS_EWORKSPACE, SS_ELAUNCH.
+ * Errors: SS_EINVAL for sizes/null pointers/dtype/misaligned logits or q,
+ * SS_EWORKSPACE, SS_ELAUNCH.
  */
 int spec_verify(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len, const float* q,
@@ -238,7 +243,8 @@ int spec_finish(const void* logits, int dtype, int B, int K, int V,
  *     at a leaf, from the leaf's row. Each emitted token is then distributed
  *     as the target's p.
  * Arguments:
- *   logits      [B, N, V] (dtype as spec_verify); rows >= n_nodes[b] unread.
+ *   logits      [B, N, V] (dtype and alignment as spec_verify); rows >=
+ *               n_nodes[b] unread.
  *   tokens, parent [B, N] int32; n_nodes [B] int32 in [1, N].
  *   temperature [B]; uniforms [B, N] float in [0, 1) (coins per depth, the
  *               last column the final coin), NULL only if every T is 0.

@@ -27,35 +27,47 @@ namespace {
 // lane scan come from the same inclusive scan, so the search is consistent;
 // a target beyond the chunk's re-read total (a rounding difference with the
 // partials) takes the chunk's last positive weight.
+//
+// Every weight is a float32 term, but the running sums, the target u *
+// total and a chunk's rescale to the row max are taken in double: a float32
+// running sum over 2^17 tokens moves a breakpoint by a few float32 roundings
+// of the total, which at that many tokens is the width of many tokens'
+// intervals. What remains is the float32 rounding of the terms themselves.
 // ---------------------------------------------------------------------------
 struct ChunkPick {
-  int chunk;   // -1: every weight is 0
-  float t_in;  // target left inside the chunk; +inf: take its last positive
+  int chunk;    // -1: every weight is 0
+  double t_in;  // target left inside the chunk; +inf: take its last positive
 };
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// One wavefront, all lanes active; weight(c) is called for c < nc.
+// Weight of a chunk relative to the row max m: its partial sum s (relative
+// to the chunk's own max mc) times exp2((mc - m) * kk), the rescale in double.
+__device__ __forceinline__ double chunk_weight(float s, float mc, float m, float kk) {
+  return (double)s * exp2(((double)mc - (double)m) * (double)kk);
+}
+
+// One wavefront, all lanes active; weight(c) (a double) is called for c < nc.
 template <typename WeightFn>
 __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight) {
   constexpr int kGroups = kMaxChunks / kWave;
   const int l = lane_id();
-  float W[kGroups], cum[kGroups];
-  float carry = 0.0f;
+  double W[kGroups], cum[kGroups];
+  double carry = 0.0;
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    W[g] = 0.0f;
+    W[g] = 0.0;
     cum[g] = carry;
     if (g * kWave < nc) {
       const int c = g * kWave + l;
-      W[g] = c < nc ? weight(c) : 0.0f;
-      cum[g] = wave_inclusive_sum(W[g]) + carry;
-      carry = lane63(cum[g]);
+      W[g] = c < nc ? (double)weight(c) : 0.0;
+      cum[g] = wave_inclusive_sum_d(W[g]) + carry;
+      carry = readlane_d(cum[g], 63);
     }
   }
-  const float t = u * carry;
+  const double t = (double)u * carry;
   ChunkPick r{-1, INFINITY};
   int lastpos = -1;
 #pragma unroll
@@ -63,11 +75,15 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
     if (g * kWave < nc) {
       const int c = g * kWave + l;
       const unsigned long long hit = __ballot(c < nc && cum[g] > t);
-      const unsigned long long pos = __ballot(c < nc && W[g] > 0.0f);
+      const unsigned long long pos = __ballot(c < nc && W[g] > 0.0);
       if (hit && r.chunk < 0) {
         const int ln = __ffsll((unsigned long long)hit) - 1;
         r.chunk = g * kWave + ln;
-        r.t_in = t - (readlane_f(cum[g], ln) - readlane_f(W[g], ln));
+        // The sum before this chunk (its running sum less its own weight)
+        // can round above the previous chunk's running sum, which the
+        // target did not exceed: the target then lies at the start of this
+        // chunk, not before it.
+        r.t_in = fmax(0.0, t - (readlane_d(cum[g], ln) - readlane_d(W[g], ln)));
       }
       if (pos) lastpos = g * kWave + 63 - __clzll((unsigned long long)pos);
     }
@@ -77,7 +93,7 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
 }
 
 struct DrawShared {
-  float cell[kLoads * kWaves];  // (load, wave) totals in token order
+  double cell[kLoads * kWaves];  // (load, wave) totals in token order
   int wlast[kWaves];
   int result;
   float result_l;  // the drawn token's logit (NaN if the draw did not see it)
@@ -156,28 +172,28 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
   if (pk.chunk < 0) return -1;
   const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const int cstart = pk.chunk * kChunk<DT>;
-  float vs[kLoads];
+  double vs[kLoads];
   int tlast = -1;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
     float qv[kVec<DT>];
     if constexpr (RESIDUAL) load_q_vec<DT, VP>(qrow, cstart, tid, it, a.V, qv);
-    float acc = 0.0f;
+    double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) {
       const int i = elem_index<DT, VP>(cstart, tid, it, k);
       const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
                                                  kk, invS, RESIDUAL ? qv[k] : 0.0f,
                                                  lam);
-      acc += wk;
+      acc += (double)wk;
       if (wk > 0.0f) tlast = max(tlast, i);
     }
     vs[it] = acc;
   }
   // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
-  float tot[kLoads];
+  double tot[kLoads];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum(vs[it]);
+  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum_d(vs[it]);
   const int wl = wave_max_i(tlast);
   if (l == 0) {
 #pragma unroll
@@ -186,9 +202,9 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
   }
   __syncthreads();
   // Every wavefront finds the cell (the same scan gives the same answer).
-  const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
-  const float inc = wave_inclusive_sum(cv);
-  const float exc = wave_shift_up1(inc);
+  const double cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0;
+  const double inc = wave_inclusive_sum_d(cv);
+  const double exc = wave_shift_up1_d(inc);
   const unsigned long long hit =
       __ballot(l < kLoads * kWaves && exc <= pk.t_in && pk.t_in < inc);
   int clast = sh.wlast[0];
@@ -201,13 +217,13 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
     }
   } else if (w == cell % kWaves) {
     const int its = cell / kWaves;
-    float v = vs[0];
+    double v = vs[0];
 #pragma unroll
     for (int it = 1; it < kLoads; ++it)
       if (it == its) v = vs[it];
-    const float tc = pk.t_in - readlane_f(exc, cell);
-    const float inc2 = wave_inclusive_sum(v);
-    const float exc2 = wave_shift_up1(inc2);
+    const double tc = fmax(0.0, pk.t_in - readlane_d(exc, cell));
+    const double inc2 = wave_inclusive_sum_d(v);
+    const double exc2 = wave_shift_up1_d(inc2);
     const bool mine = exc2 <= tc && tc < inc2;
     const unsigned long long who = __ballot(mine);
     if (!who) {
@@ -216,7 +232,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
         sh.result_l = NAN;
       }
     } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
-      const float tl = tc - exc2;
+      const double tl = tc - exc2;
       u32x4 rv = raw[0];
 #pragma unroll
       for (int it = 1; it < kLoads; ++it)
@@ -229,7 +245,8 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
           qv[k] = i < a.V ? qrow[i] : 0.0f;
         }
       }
-      float run = 0.0f, lfound = NAN, llast = NAN;
+      double run = 0.0;
+      float lfound = NAN, llast = NAN;
       int found = -1, lastp = -1;
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
@@ -237,7 +254,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
         const float lk = elem<DT>(rv, k);
         const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
                                                    RESIDUAL ? qv[k] : 0.0f, lam);
-        run += wk;
+        run += (double)wk;
         if (wk > 0.0f) {
           lastp = i;
           llast = lk;

@@ -51,6 +51,24 @@ __device__ __forceinline__ float dpp_f(float id, float v) {
   return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(id), __float_as_int(v)));
 }
 
+// A double moves as its two 32-bit halves under the same control.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_d(double id, double v) {
+  const unsigned long long vi = (unsigned long long)__double_as_longlong(v);
+  const unsigned long long ii = (unsigned long long)__double_as_longlong(id);
+  const unsigned lo = (unsigned)dpp_i<CTRL, ROW_MASK>((int)(unsigned)ii, (int)(unsigned)vi);
+  const unsigned hi =
+      (unsigned)dpp_i<CTRL, ROW_MASK>((int)(unsigned)(ii >> 32), (int)(unsigned)(vi >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const unsigned long long x = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 __device__ __forceinline__ float lane63(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
@@ -62,7 +80,14 @@ __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(
 // 15 and 31.
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_scan(T v, T id, Op op) {
-  if constexpr (std::is_same<T, int>::value) {
+  if constexpr (std::is_same<T, double>::value) {
+    v = op(v, dpp_d<kDppRowShr1>(id, v));
+    v = op(v, dpp_d<kDppRowShr2>(id, v));
+    v = op(v, dpp_d<kDppRowShr4>(id, v));
+    v = op(v, dpp_d<kDppRowShr8>(id, v));
+    v = op(v, dpp_d<kDppRowBcast15, 0xa>(id, v));
+    v = op(v, dpp_d<kDppRowBcast31, 0xc>(id, v));
+  } else if constexpr (std::is_same<T, int>::value) {
     v = op(v, dpp_i<kDppRowShr1>(id, v));
     v = op(v, dpp_i<kDppRowShr2>(id, v));
     v = op(v, dpp_i<kDppRowShr4>(id, v));
@@ -89,6 +114,17 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
 // exclusive counterpart, bit for bit.
 __device__ __forceinline__ float wave_shift_up1(float v) {
   return dpp_f<kDppWaveShr1>(0.0f, v);
+}
+
+// The same in double precision (the draw's running sums).
+__device__ __forceinline__ double wave_inclusive_sum_d(double v) {
+  return wave_scan(v, 0.0, [](double x, double y) { return x + y; });
+}
+__device__ __forceinline__ double wave_shift_up1_d(double v) {
+  return dpp_d<kDppWaveShr1>(0.0, v);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  return readlane_d(wave_inclusive_sum_d(v), 63);
 }
 
 // An empty asm that reads and writes v, so that v is computed where it

@@ -207,14 +207,14 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
       const float m = sh.m[cur], uK = sh.u[N - 1];
       ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
         const f32x4 p = load_partial(P + c);
-        return fmaxf(0.0f, p.y * fast_exp2((p.x - m) * kk) - sh.xsum[c]);
+        return fmax(0.0, chunk_weight(p.y, p.x, m, kk) - (double)sh.xsum[c]);
       });
       int allx = 0;
       if (pk.chunk < 0) {
         // Rounding left nothing outside the children: draw from the row.
         pk = pick_chunk(nc, uK, [&](int c) {
           const f32x4 p = load_partial(P + c);
-          return p.y * fast_exp2((p.x - m) * kk);
+          return chunk_weight(p.y, p.x, m, kk);
         });
         allx = 1;
       }

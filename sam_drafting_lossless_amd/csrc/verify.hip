@@ -183,14 +183,14 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         const int cxw = (j < d) ? cx : -1;
         const float uK = sh.u[a.K];
         const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
-          float W;
+          double W;
           if (trunc) {
             W = a.tpart[rw * nc + c];
           } else {
             const f32x4 p = part(j, c);
-            W = p.y * fast_exp2((p.x - m) * kk);
+            W = chunk_weight(p.y, p.x, m, kk);
           }
-          return c == cxw ? fmaxf(0.0f, W - wx) : W;
+          return c == cxw ? fmax(0.0, W - (double)wx) : W;
         });
         if (l == 0) {
           sh.m[j] = m;
@@ -427,9 +427,9 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
       const int64_t rw = (int64_t)b * R + r;
       const f32x4* Pr = a.partials + rw * nc;
       pk = pick_chunk(nc, u, [&](int c) {
-        if (trunc) return load_f32(a.tpart + rw * nc + c);
+        if (trunc) return (double)load_f32(a.tpart + rw * nc + c);
         const f32x4 p = load_partial(Pr + c);
-        return p.y * fast_exp2((p.x - m) * kk);
+        return chunk_weight(p.y, p.x, m, kk);
       });
     }
     if (l == 0) {
@@ -542,6 +542,9 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
     return set_error(SS_EINVAL, "%s: an output pointer is NULL", fn);
   if ((uintptr_t)workspace & 255)
     return set_error(SS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (((uintptr_t)logits & 15) || ((uintptr_t)q & 15))
+    return set_error(SS_EINVAL, "%s: logits and q must start on a 16-byte boundary",
+                     fn);
   if (sam_state) {
     if (((uintptr_t)sam_state & 255) || max_len < 1 || max_len > SS_MAX_LEN)
       return set_error(SS_EINVAL, "%s: state must be 256-byte aligned and "
@@ -604,9 +607,10 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.next_draft = next_draft;
   a.next_draft_len = next_draft_len;
   a.next_match_len = next_match_len;
+  // Rows are 16-byte aligned when V is a multiple of the vector width (the
+  // base is checked above); otherwise the element-wise loads are used.
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
-  const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0) &&
-                  (q == nullptr || ((uintptr_t)q & 15) == 0);
+  const bool vp = V % vec == 0;
   hipStream_t s = as_stream(stream);
   const bool f32 = dtype == SS_DTYPE_F32;
   int rc = SS_OK;
@@ -671,6 +675,8 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, int B, int N, int
     return set_error(SS_EINVAL, "%s: a required pointer is NULL", fn);
   if ((uintptr_t)workspace & 255)
     return set_error(SS_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if ((uintptr_t)logits & 15)
+    return set_error(SS_EINVAL, "%s: logits must start on a 16-byte boundary", fn);
   const WsLayout L = ws_layout(B, N - 1, V, false);
   if (ws_bytes < L.total)
     return set_error(SS_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
@@ -696,7 +702,7 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, int B, int N, int
   a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
   const int vec = dtype == SS_DTYPE_F32 ? 4 : 8;
-  const bool vp = (V % vec == 0) && (((uintptr_t)logits & 15) == 0);
+  const bool vp = V % vec == 0;
   const bool f32 = dtype == SS_DTYPE_F32;
   hipStream_t s = as_stream(stream);
   int rc = launch_stream(a, f32, vp, s);

@@ -55,7 +55,8 @@ def _run_sam_workload(c, steps, **over):
         np.testing.assert_array_equal(e["min_endpos"], o["min_endpos"])
         np.testing.assert_array_equal(e["edges"], o["edges"])
     assert (st.status().cpu().numpy() == 0).all()
-    say(f"    {tally}; mean tokens/step {tokens_total / (steps * cfg.B):.3f}")
+    say(f"    mean tokens/step {tokens_total / (steps * cfg.B):.3f}")
+    tally.check(cfg.name)
     return tally
 
 
@@ -97,7 +98,7 @@ def test_c5_draft_model_full_size():
         r = oracle.verify(x.cpu().numpy(), draft, dl, T, u, q.cpu().numpy(),
                           nthreads=8)
         compare_verify(*g, r, T, u, tally, what=f"c5 step {s}")
-    say(f"    {tally}")
+    tally.check()
 
 
 def _run_fused_workload(c, steps, **over):
@@ -149,7 +150,7 @@ def _run_fused_workload(c, steps, **over):
         np.testing.assert_array_equal(e["min_endpos"], o["min_endpos"])
         np.testing.assert_array_equal(e["edges"], o["edges"])
     assert (st.status().cpu().numpy() == 0).all()
-    say(f"    {tally}")
+    tally.check()
 
 
 def test_fused_c1_tiny_greedy():

@@ -74,7 +74,7 @@ def test_sampling_one_hot(B, K, V, dtype):
     g, r = _run(t, draft, dl, T, u)
     tally = Tally()
     compare_verify(*g, r, T, u, tally, what=f"one-hot {dtype}")
-    say(f"    {tally}")
+    tally.check()
 
 
 @pytest.mark.parametrize("B,K,V", [(4, 3, 32), (5, 2, 8193), (3, 5, 30011),
@@ -97,7 +97,7 @@ def test_sampling_given_q(B, K, V, dtype):
     g, r = _run(t, draft, dl, T, u, q=torch.from_numpy(q.astype(np.float32)).cuda())
     tally = Tally()
     compare_verify(*g, r, T, u, tally, what=f"given-q {dtype}")
-    say(f"    {tally}")
+    tally.check()
 
 
 def test_mixed_greedy_and_sampling_batch_with_masked_tokens():
@@ -111,7 +111,7 @@ def test_mixed_greedy_and_sampling_batch_with_masked_tokens():
     draft = _drafts_near_argmax(rng, np.nan_to_num(x, neginf=-1e9), K, dl)
     u = rng.random((B, K + 1)).astype(np.float32)
     g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
-    compare_verify(*g, r, T, u, Tally(), what="mixed")
+    compare_verify(*g, r, T, u, None, what="mixed")
 
 
 def test_status_words_match_oracle():
@@ -243,7 +243,7 @@ def test_full_size_sam_draft_shapes(c):
     g, r = _run(x, draft, dl, T, u)
     tally = Tally()
     compare_verify(*g, r, T, u, tally, what=cfg.name)
-    say(f"    {tally}")
+    tally.check()
 
 
 def test_full_size_draft_model_q():
@@ -257,7 +257,8 @@ def test_full_size_draft_model_q():
     g, r = _run(x, draft, dl, T, u, q=q)
     tally = Tally()
     compare_verify(*g, r, T, u, tally, what=cfg.name)
-    say(f"    {tally}  mean tokens/step {g[1].mean():.3f}")
+    say(f"    mean tokens/step {g[1].mean():.3f}")
+    tally.check()
 
 
 def test_one_workspace_serves_every_shape_that_fits():
@@ -281,7 +282,7 @@ def test_one_workspace_serves_every_shape_that_fits():
         torch.cuda.synchronize()
         g = tuple(t.cpu().numpy() for t in g)
         r = oracle.verify(x, draft, dl, Ta, u, nthreads=8)
-        compare_verify(*g, r, Ta, u, Tally(), what=f"reuse B={B} K={K} V={V}")
+        compare_verify(*g, r, Ta, u, None, what=f"reuse B={B} K={K} V={V}")
 
 
 @pytest.mark.parametrize("B", [64, 2048, 2049])
@@ -307,4 +308,120 @@ def test_row_balancing_across_batch_sizes(B, lengths):
     T = np.where(rng.random(B) < 0.5, 0.0, 0.9).astype(np.float32)
     u = rng.random((B, K + 1)).astype(np.float32)
     g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
-    compare_verify(*g, r, T, u, Tally(), what=f"balance B={B} {lengths}")
+    compare_verify(*g, r, T, u, None, what=f"balance B={B} {lengths}")
+
+
+# ------------------------------------------- finalize: how partials arrive ---
+# The finalize kernel takes each row's chunk partials one per thread when
+# (K+1) x nchunks <= 256, through an LDS loop up to 1024, and from global
+# memory above that. fp32 chunks hold 8192 logits: K = 16 at V = 151936 gives
+# 17 x 19 = 323 (the LDS loop), K = 16 at V = 524288 gives 17 x 64 = 1088
+# (global partials).
+@pytest.mark.parametrize("V", [151936, 524288])
+@pytest.mark.parametrize("mode", ["greedy", "onehot", "given_q"])
+def test_finalize_partial_paths_at_k16(V, mode):
+    K = 16
+    B = 6 if V == 151936 else 4
+    say(f"[gpu] finalize partials K={K} V={V} {mode} ({(K + 1) * -(-V // 8192)} per row set)")
+    rng = np.random.default_rng(V + len(mode))
+    x = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(np.float32)
+    dl = np.array([K, K, K - 1, 7, 0, K][:B], np.int32)
+    q = None
+    if mode == "greedy":
+        draft = _drafts_near_argmax(rng, x, K, dl, flip=0.08)
+        T = np.zeros(B, np.float32)
+        u = None
+    else:
+        T = rng.uniform(0.7, 1.2, B).astype(np.float32)
+        u = rng.random((B, K + 1)).astype(np.float32)
+        if mode == "onehot":
+            draft = rng.integers(0, V, (B, K)).astype(np.int32)
+            # strong boosts, so that acceptance runs deep into the rows
+            for b in range(B):
+                for j in range(K):
+                    x[b, j, draft[b, j]] += rng.uniform(16, 24)
+        else:
+            ql = x[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32) * 0.3
+            qd = special.softmax(ql.astype(np.float64) / T[:, None, None], axis=-1)
+            draft = np.array([[rng.choice(V, p=qd[b, j]) for j in range(K)]
+                              for b in range(B)], np.int32)
+            q = torch.from_numpy(qd.astype(np.float32)).cuda()
+            del qd
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u, q=q)
+    compare_verify(*g, r, T, u, None, what=f"K=16 V={V} {mode}")
+    if mode != "given_q":
+        assert g[1].max() >= 8, g[1]  # deep acceptance: many rows combined
+    say(f"    emitted {g[1].tolist()}")
+
+
+# --------------------------------------- draw: a target on a chunk boundary --
+def test_draw_target_on_a_chunk_boundary():
+    """The draw picks the chunk from the running sum of chunk weights, then
+    the token inside it by the target left over. When the target falls
+    between the first chunk's total and the float sum that precedes the
+    second chunk (which rounding can leave above the first chunk's total),
+    the token is the first positive one of the second chunk, not its last.
+
+    Row: V = 3 x 8192 fp32 at T = 1; token 100 has logit -15.6 (weight
+    2^-22.5 relative to the max, in (2^-23, 2^-22)); tokens 8202, 8212 and
+    8222 have logit 0 (weight 1); all else -inf. Chunk sums W0 ~ 1.68e-7 and
+    W1 = 3, so W0 + W1 rounds up to 3 + 2^-22 and the sum before chunk 1
+    reads 2^-22 > W0. The final coin puts the target midway between W0 and
+    2^-22: the oracle (double precision) and the inverse CDF's definition
+    give token 8202. Case 2 rejects draft 8222 first, so the residual has
+    chunk weights W0 and 2 (2 + W0 also rounds up). The margins are 20 % of
+    the interval, far beyond rounding, so the token must match exactly."""
+    say("[gpu] draw: target on a chunk boundary")
+    V = 3 * 8192
+    x = np.full((2, 2, V), -np.inf, np.float32)
+    x[:, :, 100] = -15.6
+    x[:, :, [8202, 8212, 8222]] = 0.0
+    w0 = float(np.exp2(np.float32(-15.6) * np.float32(1.4426950408889634)))
+    assert 2.0 ** -23 < w0 < 2.0 ** -22
+    t = 0.5 * (w0 + 2.0 ** -22)
+    draft = np.array([[0], [8222]], np.int32)
+    dl = np.array([0, 1], np.int32)
+    T = np.ones(2, np.float32)
+    u = np.array([[0.5, t / 3.0], [0.999, t / 2.0]], np.float32)
+    g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
+    assert r.out_tokens.tolist() == [[8202, -1], [8202, -1]], r.out_tokens
+    np.testing.assert_array_equal(g[0], r.out_tokens)
+    np.testing.assert_array_equal(g[1], [1, 1])
+
+
+# ------------------------------------------------------------- alignment ---
+def test_misaligned_logits_or_q_are_rejected():
+    """Logits and q must start on a 16-byte boundary (the stream pass reads
+    them 16 bytes at a time); a contiguous view that starts elsewhere is an
+    invalid argument, while a row length that is not a multiple of the
+    vector width (aligned base) takes the element-wise loads."""
+    say("[gpu] misaligned views")
+    B, K, V = 2, 2, 64
+    base = torch.zeros(B * (K + 1) * V + 4, device="cuda")
+    x = base[1:1 + B * (K + 1) * V].view(B, K + 1, V)
+    assert x.is_contiguous() and x.data_ptr() % 16 == 4
+    d = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+    dl = torch.zeros(B, dtype=torch.int32, device="cuda")
+    T = torch.zeros(B, device="cuda")
+    with pytest.raises(ssl.SpecSamError, match="16-byte"):
+        ssl.spec_verify(x, d, dl, T)
+    xb = torch.zeros(B * (K + 1) * V + 8, dtype=torch.bfloat16, device="cuda")
+    xb = xb[1:1 + B * (K + 1) * V].view(B, K + 1, V)
+    assert xb.data_ptr() % 16 == 2
+    with pytest.raises(ssl.SpecSamError, match="16-byte"):
+        ssl.spec_verify(xb, d, dl, T)
+    qb = torch.full((B * K * V + 4,), 1.0 / V, device="cuda")
+    q = qb[2:2 + B * K * V].view(B, K, V)
+    xa = torch.zeros((B, K + 1, V), device="cuda")
+    with pytest.raises(ssl.SpecSamError, match="16-byte"):
+        ssl.spec_verify(xa, d, dl, torch.ones(B, device="cuda"),
+                        torch.full((B, K + 1), 0.5, device="cuda"), q)
+    tree_x = base[1:1 + B * 3 * V].view(B, 3, V)
+    with pytest.raises(ssl.SpecSamError, match="16-byte"):
+        ssl.spec_verify_tree(tree_x, torch.zeros((B, 3), dtype=torch.int32, device="cuda"),
+                             torch.tensor([[-1, 0, 0]] * B, dtype=torch.int32, device="cuda"),
+                             torch.ones(B, dtype=torch.int32, device="cuda"), T)
+    # an aligned base with V not a multiple of the vector width still works
+    x7 = torch.from_numpy(np.arange(B * (K + 1) * 7, dtype=np.float32).reshape(B, K + 1, 7)).cuda()
+    g, r = _run(x7, np.zeros((B, K), np.int32), np.zeros(B, np.int32), np.zeros(B, np.float32))
+    compare_verify(*g, r, np.zeros(B), None, what="V=7")
