@@ -194,6 +194,33 @@ int spec_step(const void* logits, int dtype, int B, int K, int V,
               void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * spec_step_noalloc — spec_step with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The workspace is a device array of
+ * SS_SCRATCH_BYTES inside the library; each GPU the library runs on holds
+ * its own copy until the process ends, its address taken on the first call
+ * on that device. The call allocates and frees nothing. All calls on one GPU
+ * share that array: calls that may overlap on a GPU (two streams, two host
+ * threads) race and must not be issued; consecutive calls on one stream are
+ * fine (the array needs no initialisation; whatever a previous call left in
+ * it does not matter).
+ * Arguments, outputs and status as spec_step. Errors as spec_step, and
+ * SS_EWORKSPACE when the sizes need more than SS_SCRATCH_BYTES of workspace
+ * (ss_verify_workspace_bytes_ex(B, K, V, flags) > SS_SCRATCH_BYTES, with
+ * SS_WS_TRUNCATION when top_k or top_p is given): e.g. B = 256, K = 3,
+ * V = 151936 needs about 0.34 MB; truncation needs far more.
+ */
+#define SS_SCRATCH_BYTES ((size_t)8 << 20)
+int spec_step_noalloc(const void* logits, int dtype, int B, int K, int V,
+                      const int32_t* draft, const int32_t* draft_len,
+                      const float* temperature, const float* uniforms,
+                      const int32_t* top_k, const float* top_p, void* sam_state,
+                      int max_len, int32_t* out_tokens, int32_t* num_emitted,
+                      float* p_draft, float* logprobs, int32_t* status,
+                      int32_t* next_draft, int32_t* next_draft_len,
+                      int32_t* next_match_len, void* stream);
+
+/*
  * The two passes of spec_verify / spec_step as separate calls, for callers
  * that schedule them (and for timing the HBM pass alone):
  *   spec_stream  reads the logit rows j <= draft_len once and leaves per-row

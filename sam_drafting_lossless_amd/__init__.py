@@ -64,6 +64,9 @@ def lib():
     L.spec_step.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P,
                             P, P, P, P, P, P, P, P, sz, P]
     L.spec_step.restype = i32
+    L.spec_step_noalloc.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, i32,
+                                    P, P, P, P, P, P, P, P, P]
+    L.spec_step_noalloc.restype = i32
     L.spec_stream.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.spec_stream.restype = i32
     L.spec_finish.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P,
@@ -215,6 +218,31 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
     automaton of `state` (a SamState) with the emitted tokens, and draft for
     the next step. Returns (out_tokens, num_emitted, p_draft, status,
     next_draft, next_draft_len, next_match_len); `logprobs` as spec_verify."""
+    return _step(False, logits, draft, draft_len, temperature, uniforms, state,
+                 workspace, out_tokens, num_emitted, p_draft, status, next_draft,
+                 next_draft_len, next_match_len, logprobs, top_k, top_p, stream)
+
+
+def spec_step_noalloc(logits, draft, draft_len, temperature, uniforms, state, *,
+                      out_tokens=None, num_emitted=None, p_draft=None,
+                      status=None, next_draft=None, next_draft_len=None,
+                      next_match_len=None, logprobs=None, top_k=None, top_p=None,
+                      stream=None):
+    """spec_step with the library's own device scratch as its workspace (see
+    include/specsam.h): the C call allocates nothing. Outputs that are not
+    given are allocated here, as for spec_step; pass them all to allocate
+    nothing at all. Calls that overlap on one GPU race."""
+    return _step(True, logits, draft, draft_len, temperature, uniforms, state,
+                 None, out_tokens, num_emitted, p_draft, status, next_draft,
+                 next_draft_len, next_match_len, logprobs, top_k, top_p, stream)
+
+
+SCRATCH_BYTES = 8 << 20  # SS_SCRATCH_BYTES
+
+
+def _step(noalloc, logits, draft, draft_len, temperature, uniforms, state,
+          workspace, out_tokens, num_emitted, p_draft, status, next_draft,
+          next_draft_len, next_match_len, logprobs, top_k, top_p, stream):
     if logits.dim() != 3:
         raise SpecSamError("logits must be [B, K+1, V]")
     B, R, V = logits.shape
@@ -226,7 +254,7 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
         raise SpecSamError("state holds a different number of sequences")
     dev = logits.device
     i32 = torch.int32
-    if workspace is None:
+    if workspace is None and not noalloc:
         workspace = verify_workspace(B, K, V, dev, truncation=(
             top_k is not None or top_p is not None))
     if out_tokens is None:
@@ -259,10 +287,12 @@ def spec_step(logits, draft, draft_len, temperature, uniforms, state, *,
         _dev(status, "status", i32, (B,)),
         _dev(next_draft, "next_draft", i32, (B, K)),
         _dev(next_draft_len, "next_draft_len", i32, (B,)),
-        _dev(next_match_len, "next_match_len", i32, (B,)),
-        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
-        _stream(stream))
-    _check(lib().spec_step(*args), "spec_step")
+        _dev(next_match_len, "next_match_len", i32, (B,)))
+    if noalloc:
+        _check(lib().spec_step_noalloc(*args, _stream(stream)), "spec_step_noalloc")
+    else:
+        _check(lib().spec_step(*args, _dev(workspace, "workspace", torch.uint8),
+                               workspace.numel(), _stream(stream)), "spec_step")
     return (out_tokens, num_emitted, p_draft, status, next_draft,
             next_draft_len, next_match_len)
 

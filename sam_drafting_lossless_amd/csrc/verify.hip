@@ -27,6 +27,8 @@
 // finalize code raises the stream kernel's register count and its latency
 // lands in the kernel's tail.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "draw.h"
 
@@ -766,4 +768,84 @@ extern "C" int spec_finish(const void* logits, int dtype, int B, int K, int V,
              uniforms, top_k, top_p, out_tokens, num_emitted, p_draft, logprobs,
              status, workspace, ws_bytes, sam_state, max_len, next_draft,
              next_draft_len, next_match_len, stream, "spec_finish");
+}
+
+// ---------------------------------------------------------------------------
+// spec_step_noalloc: spec_step whose workspace is the library's own device
+// array, for callers that cannot allocate. Each GPU holds its own copy of
+// the array (for the life of the process); its address on a device is taken
+// once, with that device current, and kept. The workspace needs no
+// initialisation (every region is written before it is read in the same
+// call), so nothing is cleared between calls; calls that overlap on one GPU
+// share the array and race.
+// ---------------------------------------------------------------------------
+namespace specsam {
+namespace {
+
+__device__ __align__(256) unsigned char scratch[SS_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The address of `scratch` on the current device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return set_error(SS_ELAUNCH, "spec_step_noalloc: hipGetDevice: %s",
+                     hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(SS_EINVAL, "spec_step_noalloc: device %d beyond %d", dev,
+                     kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return set_error(SS_ELAUNCH, "spec_step_noalloc: hipGetSymbolAddress: %s",
+                         hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SS_OK;
+}
+
+}  // namespace
+}  // namespace specsam
+
+extern "C" int spec_step_noalloc(const void* logits, int dtype, int B, int K, int V,
+                                 const int32_t* draft, const int32_t* draft_len,
+                                 const float* temperature, const float* uniforms,
+                                 const int32_t* top_k, const float* top_p,
+                                 void* sam_state, int max_len, int32_t* out_tokens,
+                                 int32_t* num_emitted, float* p_draft, float* logprobs,
+                                 int32_t* status, int32_t* next_draft,
+                                 int32_t* next_draft_len, int32_t* next_match_len,
+                                 void* stream) {
+  const char* fn = "spec_step_noalloc";
+  if (!sam_state) return set_error(SS_EINVAL, "%s: state is NULL", fn);
+  if (B < 1 || K < 1 || K > SS_MAX_K || V < 1 || V > kMaxV)
+    return set_error(SS_EINVAL,
+                     "%s: need B >= 1, 1 <= K <= %d, 1 <= V <= %d "
+                     "(got B=%d K=%d V=%d)",
+                     fn, SS_MAX_K, kMaxV, B, K, V);
+  const bool trunc = top_k != nullptr || top_p != nullptr;
+  const size_t need = ws_layout(B, K, V, trunc).total;
+  if (need > (size_t)SS_SCRATCH_BYTES)
+    return set_error(SS_EWORKSPACE,
+                     "%s: B=%d K=%d V=%d%s needs %zu bytes of scratch, more than "
+                     "the %zu it holds",
+                     fn, B, K, V, trunc ? " with top_k / top_p" : "", need,
+                     (size_t)SS_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int rc = scratch_on_current_device(&ws);
+  if (rc != SS_OK) return rc;
+  return run(kStream | kFinish, logits, dtype, B, K, V, draft, draft_len, nullptr,
+             temperature, uniforms, top_k, top_p, out_tokens, num_emitted, p_draft,
+             logprobs, status, ws, (size_t)SS_SCRATCH_BYTES, sam_state, max_len,
+             next_draft, next_draft_len, next_match_len, stream, fn);
 }
