@@ -378,9 +378,12 @@ int sam_extend_stats(void* state, int B, int max_len, const int32_t* tokens,
  *   match [B, 2] int32 (state, length): the state of the longest suffix of
  *     sequence b's text that occurs in the corpus, and that suffix's length.
  *     Start from zeros (root, empty match); this call updates it in place.
- *     An entry that is not a state of the automaton is taken as the root.
+ *     An entry that is not a state of the automaton, or whose length exceeds
+ *     that state's longest string, is taken as the root.
  *   tokens [B, ld_tokens] int32, counts [B] (device; NULL: no tokens): the
- *     tokens appended to each sequence since the last call. For each token t:
+ *     tokens appended to each sequence since the last call; a count outside
+ *     [0, ld_tokens] reads no token and sets SS_ST_COUNT in status[b] (status
+ *     [B] int32, or NULL). For each token t:
  *     if the state has a transition on t it is taken (length + 1); else
  *     suffix links are followed to the first state with one (length = that
  *     state's len + 1); if even the root has none, (root, 0).
@@ -400,7 +403,7 @@ int sam_match(const void* static_state, int static_max_len, int B, int32_t* matc
               const int32_t* tokens, int ld_tokens, const int32_t* counts, int K,
               int delta, const int32_t* dyn_draft, const int32_t* dyn_len,
               const int32_t* dyn_match, int32_t* draft, int32_t* draft_len,
-              int32_t* source, void* stream);
+              int32_t* source, int32_t* status, void* stream);
 
 /* Copies the sticky per-sequence status words to status_out [B] int32. */
 int sam_status(const void* state, int B, int max_len, int32_t* status_out,

@@ -94,7 +94,7 @@ def lib():
     L.sam_extend_stats.argtypes = [P, i32, i32, P, i32, P, P, P]
     L.sam_extend_stats.restype = i32
     L.sam_match.argtypes = [P, i32, i32, P, P, i32, P, i32, i32, P, P, P, P, P,
-                            P, P]
+                            P, P, P]
     L.sam_match.restype = i32
     L.sam_status.argtypes = [P, i32, i32, P, P]
     L.sam_status.restype = i32
@@ -626,7 +626,8 @@ class StaticSam:
         return torch.zeros((B, 2), dtype=torch.int32, device=device)
 
     def match(self, match, tokens=None, counts=None, K: int = 0, delta: int = 0,
-              dyn=None, draft=None, draft_len=None, source=None, stream=None):
+              dyn=None, draft=None, draft_len=None, source=None, status=None,
+              stream=None):
         """Advances `match` [B, 2] by tokens [B, L] (counts [B], all L by
         default); with K > 0 returns (draft, draft_len, source): the static
         drafts, or, with dyn = (draft, draft_len, match_len) of the dynamic
@@ -663,6 +664,7 @@ class StaticSam:
             None if draft is None else _dev(draft, "draft", i32, (B, K)),
             None if draft_len is None else _dev(draft_len, "draft_len", i32, (B,)),
             None if source is None else _dev(source, "source", i32, (B,)),
+            None if status is None else _dev(status, "status", i32, (B,)),
             _stream(stream)), "sam_match")
         if K > 0:
             return draft, draft_len, source

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kWave) void sam_match_kernel(
     const unsigned char* sbase, SamLayout L, int32_t* match, const int32_t* tokens,
     int ld, const int32_t* counts, int K, int delta, const int32_t* dyn_draft,
     const int32_t* dyn_len, const int32_t* dyn_match, int32_t* draft,
-    int32_t* draft_len, int32_t* source) {
+    int32_t* draft_len, int32_t* source, int32_t* status) {
   const int b = blockIdx.x;
   const int l = lane_id();
   const SamSeq S = sam_seq(const_cast<unsigned char*>(sbase), 0, L);
@@ -147,7 +147,17 @@ __global__ __launch_bounds__(kWave) void sam_match_kernel(
     s = 0;
     m = 0;
   }
-  const int cnt = counts ? counts[b] : 0;
+  // A match longer than the state's longest string is not a match state of
+  // this automaton either.
+  if (m > S.st[s].x) {
+    s = 0;
+    m = 0;
+  }
+  int cnt = counts ? counts[b] : 0;
+  if (cnt < 0 || cnt > ld) {  // reported; no token is read
+    if (l == 0 && status) atomicOr(status + b, SS_ST_COUNT);
+    cnt = 0;
+  }
   for (int i = 0; i < cnt; ++i) {
     const int t = tokens[(int64_t)b * ld + i];
     bool take_len = false;
@@ -346,11 +356,13 @@ extern "C" int sam_match(const void* static_state, int static_max_len, int B,
                          const int32_t* counts, int K, int delta,
                          const int32_t* dyn_draft, const int32_t* dyn_len,
                          const int32_t* dyn_match, int32_t* draft,
-                         int32_t* draft_len, int32_t* source, void* stream) {
+                         int32_t* draft_len, int32_t* source, int32_t* status,
+                         void* stream) {
   // Switched off: one GPU run of this entry point's tests ended in a memory
   // fault, and the cause has not been shown (a bounds-checked host model of
-  // the automaton kernels over the same inputs stays in bounds). The kernel
-  // stays in the source; the entry point refuses to launch it.
+  // the automaton kernels over the same inputs stays in bounds, and the
+  // kernel's gfx950 code on the faulting call's path reads only in bounds).
+  // The kernel stays in the source; the entry point refuses to launch it.
   if (kSamMatchSwitchedOff)
     return set_error(SS_EINVAL, "sam_match: switched off until the cause of a "
                                 "GPU memory fault in its tests is shown");
@@ -373,7 +385,7 @@ extern "C" int sam_match(const void* static_state, int static_max_len, int B,
                      as_stream(stream),
                      reinterpret_cast<const unsigned char*>(static_state), L, match,
                      tokens, ld_tokens, counts, K, delta, dyn_draft, dyn_len,
-                     dyn_match, draft, draft_len, source);
+                     dyn_match, draft, draft_len, source, status);
   return check_launch("sam_match");
 }
 

@@ -116,6 +116,25 @@ def test_entries_that_are_not_states_start_at_the_root():
     assert (d.cpu().numpy() == -1).all()
 
 
+def test_counts_outside_the_rows_and_overlong_entries():
+    """A count outside [0, ld] reads no token and is reported; an entry whose
+    length exceeds its state's longest string is taken as the root."""
+    say("[gpu] static matching: bad counts and overlong entries")
+    c = synth.corpus(6, 4, 100, V, EOS)
+    st = ssl.StaticSam(c, V)
+    toks = dev(c[None, :8].repeat(3, 0))
+    m = st.new_match(3)
+    status = torch.zeros(3, dtype=torch.int32, device="cuda")
+    st.match(m, toks, dev(np.array([9, -1, 8], np.int32)), status=status)
+    torch.cuda.synchronize()
+    assert status.cpu().tolist() == [ssl.ST_COUNT, ssl.ST_COUNT, 0]
+    assert m.cpu().tolist()[:2] == [[0, 0], [0, 0]] and m.cpu()[2, 1] == 8
+    m2 = torch.tensor([[int(m[2, 0]), 9]], dtype=torch.int32, device="cuda")
+    st.match(m2)
+    torch.cuda.synchronize()
+    assert m2.cpu().tolist() == [[0, 0]]
+
+
 def test_host_argument_errors():
     c = synth.corpus(5, 2, 50, V, EOS)
     st = ssl.StaticSam(c, V)
