@@ -110,21 +110,30 @@ def cpu_baseline(slot_host, gt, cfg, nthreads: int, budget_s: float = 10.0):
         t3 = time.perf_counter()
         t_sam += (t1 - t0) + (t3 - t2)
         t_ver += t2 - t1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     line = {"value": steps / el, "unit": "steps/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": (f"{steps} whole steps (draft+verify+extend) of all "
-                       f"{cfg.B} sequences on one host copy of a boosted "
+            "sample": (f"{steps} whole steps (draft, verify and extend each over "
+                       f"{nthreads} threads, sequences split between them) of "
+                       f"all {cfg.B} sequences on one host copy of a boosted "
                        f"logit slot [{cfg.B},{cfg.K + 1},{cfg.V}] fp32, "
-                       f"{nthreads} threads over sequences, {el:.1f} s")}
-    detail = {"single_thread_steps_per_s": steps1 / el1,
+                       f"{el:.1f} s")}
+    detail = {"threads_used": nthreads,
+              "host_logical_cpus": os.cpu_count(),
+              "host_cpus_available_to_process": affinity,
+              "single_thread_steps_per_s": steps1 / el1,
               "single_thread_sample": f"{steps1} steps, {el1:.1f} s",
               "verify_ms_per_step": 1e3 * t_ver / nsplit,
               "verify_threads": nthreads,
               "automata_ms_per_step": 1e3 * t_sam / nsplit,
               "automata_threads": 1,
               "split_sample": (f"{nsplit} steps: drafts and extends through the "
-                               f"oracle's per-sequence calls, verification "
-                               f"over all sequences")}
+                               f"oracle's per-sequence calls on one thread, "
+                               f"verification over all sequences on "
+                               f"{nthreads} threads")}
     return line, detail
 
 
@@ -270,8 +279,9 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
     B, K, V, R = cfg.B, cfg.K, cfg.V, cfg.K + 1
     dt = ssl.DTYPE_BF16 if cfg.dtype == "bf16" else ssl.DTYPE_F32
     # Ring slots: at least 4, and together at least twice the 256 MB
-    # Infinity Cache, so that re-reading a slot comes from HBM.
-    RING = max(4, -(-(2 * INFINITY_CACHE_BYTES) // (B * R * V * cfg.elem_bytes)))
+    # Infinity Cache, so that re-reading a slot comes from HBM (at most 64:
+    # a launch-bound workload such as B=1, V=32 is cache-resident anyway).
+    RING = max(4, min(64, -(-(2 * INFINITY_CACHE_BYTES) // (B * R * V * cfg.elem_bytes))))
     total = warmup + 4 * steps
     t_setup = time.perf_counter()
     gt_h = synth.token_streams(cfg, total)
@@ -297,6 +307,12 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
               torch.full((B,), H, dtype=torch.int32, device=dev))
     booster = harness.Booster(gt, np.full(B, H, np.int32), R, V, RING,
                               cfg.boost, dt)
+    # Rows that get the boost (all of them unless the workload boosts a
+    # share, as B=1, V=32 does), one [B, R] mask per step.
+    mask = None
+    if cfg.boost_prob < 1.0:
+        mask = torch.as_tensor(np.stack([synth.boost_mask(cfg, s) for s in range(total)])
+                               .astype(np.uint8), device=dev)
     ws = ssl.verify_workspace(B, K, V, dev, truncation=trunc)
     drafts = [torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2)]
     mlen = torch.empty(B, dtype=torch.int32, device=dev)
@@ -325,12 +341,15 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
     nc_p = [t.data_ptr() for t in booster.ncommit]
     sp_p = [booster.saved_pos[i].data_ptr() for i in range(RING)]
     sv_p = [booster.saved_val[i].data_ptr() for i in range(RING)]
+    mask_p = None if mask is None else mask.data_ptr()
 
     def boost(s):
         slot = s % RING
         rc = H_.hs_boost_step(ring_p[slot], dt, B, R, V, gt_p, gt_ld, nc_p[s % 2],
                               nc_p[(s + 1) % 2], nem0 + (s - 1) * rowB if s else None,
-                              sp_p[slot], sv_p[slot], None, float(cfg.boost), stream)
+                              sp_p[slot], sv_p[slot],
+                              None if mask_p is None else mask_p + s * B * R,
+                              float(cfg.boost), stream)
         if rc:
             raise RuntimeError("hs_boost_step failed")
 
@@ -460,6 +479,93 @@ def measure_sam_workload(cfg, steps: int, warmup: int):
 
 
 
+def stream_timing(cfg, ring, dl_host, reps: int = 20, batch: int = 8) -> dict:
+    """Per-launch time of the stream pass alone for given draft lengths
+    (seeded random draft tokens, the workload's temperature): about 50 ms of
+    settling launches, then `reps` event pairs around `batch` back-to-back
+    launches over the ring slots (as the headline stream timing); the
+    median."""
+    import numpy as np
+    import torch
+
+    import sam_drafting_lossless_amd as ssl
+    dev = ring[0].device
+    B, K, V = cfg.B, cfg.K, cfg.V
+    rng = np.random.default_rng(cfg.seed + 17)
+    draft = torch.as_tensor(rng.integers(0, V, (B, K)).astype(np.int32), device=dev)
+    dl = torch.as_tensor(np.asarray(dl_host, np.int32), device=dev)
+    temp = torch.full((B,), cfg.T, dtype=torch.float32, device=dev)
+    u = torch.as_tensor(rng.random((B, K + 1)).astype(np.float32), device=dev)
+    ws = ssl.verify_workspace(B, K, V, dev)
+    L = ssl.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    dt = ssl.DTYPE_BF16 if ring[0].dtype == torch.bfloat16 else ssl.DTYPE_F32
+
+    def launch(i):
+        rc = L.spec_stream(ring[i % len(ring)].data_ptr(), dt, B, K, V, draft.data_ptr(),
+                           dl.data_ptr(), temp.data_ptr(), u.data_ptr(), None, None,
+                           ws.data_ptr(), ws.numel(), stream)
+        if rc:
+            raise RuntimeError("spec_stream failed: " + L.ss_last_error_string().decode())
+
+    # About 50 ms of launches first: after host-side work the GPU's clocks
+    # are still ramping, and the first 30 ms or so of a long launch sequence
+    # read up to 9 % slower.
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.05:
+        for _ in range(batch):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record()
+        for i in range(batch):
+            launch(r * batch + i)
+        evs[r][1].record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3 / batch
+    rows = int((np.clip(np.asarray(dl_host), 0, K) + 1).sum())
+    nbytes = rows * V * cfg.elem_bytes
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"rows": rows, "bytes_per_launch": nbytes, "us_per_launch": round(us, 2),
+            "GBps": round(gbps, 1), "frac_of_8TBps": round(gbps / PEAK_HBM_GBPS, 4),
+            "launches_per_event_pair": batch}
+
+
+def all_rows_stream(cfg, ring, reps: int = 20, batch: int = 8) -> dict:
+    """The stream pass with every sequence's draft of length K, so that all
+    B x (K+1) rows are verified (B = 256, K = 3: 1,024 rows, 622 MB)."""
+    import numpy as np
+    return stream_timing(cfg, ring, np.full(cfg.B, cfg.K, np.int32), reps, batch)
+
+
+def stream_sweep(reps: int = 20):
+    """The stream pass alone at the headline shape (B = 256, V = 151936,
+    fp32, T = 1) for draft-length mixes from none to all, at K = 3 and
+    K = 16: one JSON line each."""
+    import numpy as np
+
+    import synth
+    for K in (3, 16):
+        cfg = synth.config(3, K=K)
+        ring = [synth.noise(cfg, s, "cuda") for s in range(4)]
+        rng = np.random.default_rng(5 + K)
+        c3like = np.zeros(cfg.B, np.int32)
+        c3like[:5], c3like[5:7], c3like[7:9] = K, min(2, K), 1
+        mixes = {"none": np.zeros(cfg.B, np.int32),
+                 "c3-like (5 x K, 2 x 2, 2 x 1, rest 0)": rng.permutation(c3like),
+                 f"uniform 0..{K}": rng.integers(0, K + 1, cfg.B).astype(np.int32),
+                 "all K": np.full(cfg.B, K, np.int32)}
+        for name, dl in mixes.items():
+            line = {"workload": f"stream pass B={cfg.B} V={cfg.V} K={K} fp32 T={cfg.T}",
+                    "draft_lengths": name, **stream_timing(cfg, ring, dl, reps)}
+            print(json.dumps(line), flush=True)
+        del ring
+
+
 def _sam_workload_line(cfg, m, steps: int) -> dict:
     import numpy as np
     line = {
@@ -478,6 +584,7 @@ def _sam_workload_line(cfg, m, steps: int) -> dict:
                                       enumerate(m["accept_hist"])},
         "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
                                       np.percentile(m["step_us"], [10, 50, 90])],
+        "library_steps_per_s": 1e6 / float(np.median(m["step_us"])),
         "ring_slots": m["RING"],
     }
     if cfg.top_k != 0 or cfg.top_p < 1.0:
@@ -682,9 +789,12 @@ def measure_tree_workload(cfg, steps: int, warmup: int) -> dict:
 def _workload_configs():
     import synth
     return {
+        "c1": synth.config(1),
         "c2": synth.config(2),
         "c4": synth.config(4),
         "c5": synth.config(5),
+        "c3_drafted": synth.config(3, name="c3_b256_v151936_k3_t1_onehot_boost12",
+                                   boost=12.0),
         "c3_topp": synth.config(3, name="c3_b256_v151936_k3_t0.7_topp0.9_onehot",
                                 T=0.7, top_p=0.9),
         "c3_topk_topp": synth.config(3, name="c3_b256_v151936_k3_t0.7_topk50_topp0.9_onehot",
@@ -724,7 +834,17 @@ def main():
                     help="report automaton work per token instead")
     ap.add_argument("--workloads", nargs="?", const="all", default=None,
                     help="measure other workloads instead: all, or a comma "
-                         "list of c2, c4, c5, c3_topp, c3_topk_topp, c3_tree8")
+                         "list of c1, c2, c4, c5, c3_drafted, c3_topp, "
+                         "c3_topk_topp, c3_tree8")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="time only the stream pass at the headline shape for "
+                         "draft-length mixes from none to all, K = 3 and 16")
+    ap.add_argument("--all-rows", action="store_true",
+                    help="time only the stream pass over all B x (K+1) rows "
+                         "of the headline shape (every draft full)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline line without the all-rows and drafted "
+                         "measurements (for profiling the headline alone)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()
@@ -752,6 +872,14 @@ def main():
         workloads_report(args.steps, args.warmup, args.workloads)
         return
     cfg = synth.config(3)
+    if args.stream_sweep:
+        stream_sweep()
+        return
+    if args.all_rows:
+        ring = [synth.noise(cfg, s, "cuda") for s in range(4)]
+        print(json.dumps({"workload": cfg.name + "_all_rows",
+                          **all_rows_stream(cfg, ring, reps=args.steps)}), flush=True)
+        return
     B, K, V = cfg.B, cfg.K, cfg.V
     m = measure_sam_workload(cfg, args.steps, args.warmup)
     elapsed, ring, total, RING = m["elapsed"], m["ring"], m["total"], m["RING"]
@@ -759,6 +887,18 @@ def main():
     rows_per_launch, achieved = m["rows_per_launch"], m["achieved"]
     nem, step_us, H = m["nem"], m["step_us"], cfg.hist_len
     gt_h = m["gt_h"]
+
+    # The same shape with every draft full (all 1,024 rows verified), and with
+    # the true next token boosted by +12, so that drafts are accepted and
+    # the automaton grows by several tokens per step.
+    all_rows = drafted = None
+    if not args.no_extras:
+        all_rows = all_rows_stream(cfg, ring)
+        dcfg = _workload_configs()["c3_drafted"]
+        dsteps = max(1, min(args.steps, 200))
+        drafted = _sam_workload_line(
+            dcfg, measure_sam_workload(dcfg, dsteps, args.warmup), dsteps)
+        drafted["boost"] = dcfg.boost
 
     probe = None if args.no_probe else hbm_read_probe(torch, harness)
     probe_same = (None if args.no_probe else
@@ -770,6 +910,8 @@ def main():
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:
             ncpu = os.cpu_count() or 1
+        # at most 16 threads: the share of a GPU machine's host cores a run
+        # may use
         cpu, cpu_detail = cpu_baseline(slot_h, gt_h, cfg, min(ncpu, 16),
                                        args.cpu_budget)
 
@@ -810,6 +952,13 @@ def main():
         "needed_rows_bytes_per_step": m["needed_bytes"],
         "step_event_us_p10_p50_p90": [round(float(x), 2) for x in
                                       np.percentile(step_us, [10, 50, 90])],
+        "library_steps_per_s": 1e6 / float(np.median(step_us)),
+        "library_steps_note": ("1 / median of per-step event intervals around the "
+                               "spec_step call alone (the harness boost kernel "
+                               "excluded; each interval includes its event's own "
+                               "gap, so this is a lower bound)"),
+        "verify_all_rows": all_rows,
+        "c3_drafted": drafted,
         "hbm_read_probe_GBps": probe,
         "hbm_read_probe_same_bytes": probe_same,
         "setup_s": m["setup_s"],

@@ -789,25 +789,39 @@ void orc_verify_tree(const void* logits, int32_t dtype, int32_t B, int32_t N,
 // One whole step for a batch of oracle automata: draft from each automaton,
 // verify against the logits, extend each automaton by what was emitted.
 // Used to time the oracle beside the GPU. draft/draft_len/match_len receive
-// the drafts used.
+// the drafts used. Sequences are independent: nthreads > 1 splits each of the
+// three phases over std::threads (every automaton is touched by one thread).
 void orc_step(void** sams, int32_t B, int32_t K, int32_t V, const void* logits,
               int32_t dtype, const float* temperature, const float* uniforms,
               int32_t* draft, int32_t* draft_len, int32_t* match_len,
               int32_t* out_tokens, int32_t* num_emitted, double* p_draft,
               double* alpha, double* cdf_lo, double* cdf_hi, int32_t* status,
               int32_t nthreads) {
-  for (int b = 0; b < B; ++b)
+  auto each = [&](auto fn) {
+    if (nthreads <= 1) {
+      for (int b = 0; b < B; ++b) fn(b);
+      return;
+    }
+    std::vector<std::thread> ts;
+    for (int t = 0; t < nthreads; ++t)
+      ts.emplace_back([&, t] {
+        for (int b = t; b < B; b += nthreads) fn(b);
+      });
+    for (auto& th : ts) th.join();
+  };
+  each([&](int b) {
     draft_len[b] =
         ((OracleSAM*)sams[b])->draft(K, draft + (int64_t)b * K, &match_len[b]);
+  });
   orc_verify(logits, dtype, B, K, V, draft, draft_len, nullptr, temperature,
              uniforms, out_tokens, num_emitted, p_draft, alpha, cdf_lo, cdf_hi,
              status, nullptr, nullptr, nullptr, nullptr, nthreads);
-  for (int b = 0; b < B; ++b) {
-    if (status[b]) continue;
+  each([&](int b) {
+    if (status[b]) return;
     OracleSAM* s = (OracleSAM*)sams[b];
     for (int j = 0; j < num_emitted[b]; ++j)
       s->extend(out_tokens[(int64_t)b * (K + 1) + j]);
-  }
+  });
 }
 
 }  // extern "C"

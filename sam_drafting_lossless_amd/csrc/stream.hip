@@ -13,13 +13,14 @@
 // Design for gfx950: 256-thread workgroups each hold one chunk in registers
 // (8 non-temporal 16-byte loads in flight per lane, each wavefront load one
 // contiguous 1 KiB request) and write one 16-byte partial per row: nothing
-// but loads, arithmetic and one store. The balanced kernel (batches up to
-// 2048 sequences with at least 4096 (sequence, chunk) pairs) gives every
-// (sequence, chunk) of row 0 its own workgroup and deals the chunks of rows
-// 1..draft_len round-robin to the same workgroups, so that the ones with
-// extra work are dispatched first; smaller batches give every (sequence,
-// row, chunk) a workgroup, larger ones use a (sequence, row group, chunk)
-// grid.
+// but loads, arithmetic and one store. The grid is (sequence, row lane,
+// chunk): lane q of a sequence streams its chunk of rows q, q + G, q + 2G,
+// ... up to the sequence's draft length. Launches whose row 0 alone gives
+// fewer than 4096 workgroups (and draft trees) take G = K + 1, a workgroup
+// per needed (row, chunk); larger ones take G = 2 for K <= 3 and 4 above,
+// so that a sequence with no drafts leaves few idle workgroups per chunk
+// (they read its draft length and leave) while drafted rows still spread
+// over several workgroups.
 #include <algorithm>
 
 #include "verify_common.h"
@@ -32,22 +33,19 @@ namespace {
 // ---------------------------------------------------------------------------
 
 // Reduces one loaded chunk of row j of sequence b into its partial. `raw`
-// holds the chunk; `mid` runs once every element has been consumed, before
-// the workgroup reduction (the balanced kernel issues its next item's loads
-// into `raw` there). With TR, a truncated row also leaves its chunk's window
-// histogram (hs is the LDS histogram). Ends with a barrier, so `red` and `hs`
-// may be reused at once.
+// holds the chunk; `mid` runs once every element has been consumed (after
+// the last pass that reads `raw`), before the workgroup reduction. With TR, a
+// truncated row also leaves its chunk's window histogram (hs is the LDS
+// histogram). Ends with a barrier, so `red` and `hs` may be reused at once.
 // The draft token of row j (j < K), or -1; requested with the row's chunk.
 __device__ __forceinline__ int draft_token(const Args& a, int b, int j) {
   return (a.draft && j < a.K) ? a.draft[(int64_t)b * a.K + j] : -1;
 }
 
-// XREG: x (the draft token, or -1) was requested with the chunk, and the
-// lane holding its logit takes it from its registers; else thread 0 loads x
-// and then its logit. The grid kernel, whose workgroups stream one row each,
-// takes the first (no dependent loads after the chunk's); the balanced
-// kernel the second (measured: as fast there, and it keeps the bf16
-// variant's register count, and so its occupancy, lower).
+// x is the draft token of row j (or -1), requested with the chunk. XREG:
+// the lane holding its logit takes it with a select as the fold consumes
+// that element (no load waited for out of order, two registers); else
+// thread 0 loads the logit. The stream kernel takes the first.
 template <int DT, bool VP, bool TR, bool XREG, typename Mid>
 __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
                                            float T, int c, int x,
@@ -72,25 +70,16 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
   }
   const bool hasx = XREG && !greedy && j < d && x >= cstart && x < cstart + kChunk<DT> &&
                     x < a.V;
+  // (XREG) Position ex of x's logit among this lane's elements (it * kVec +
+  // k), -1 in every other lane.
+  int ex = -1;
   if (hasx) {
     const int o = x - cstart;
     const int itx = o / (kThreads * kVec<DT>);
     const int rem = o - itx * (kThreads * kVec<DT>);
-    if (rem / kVec<DT> == tid) {
-      // its 32-bit word among the lane's 8 x 4, then the element in it
-      const int kx = rem % kVec<DT>;
-      const int wx = kx / (kVec<DT> / 4);
-      unsigned wv = 0;
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (it == itx && q == wx) wv = raw[it][q];
-      // (a bf16 word holds two elements: kx & 1 picks the half)
-      const u32x4 one = u32x4{wv, wv, wv, wv};
-      red[kWaves].x = elem<DT>(one, DT == SS_DTYPE_F32 ? 0 : (kx & 1));
-    }
+    if (rem / kVec<DT> == tid) ex = itx * kVec<DT> + rem % kVec<DT>;
   }
+  float xv = 0.0f;
   f32x4 part;
   if (greedy) {
     // Argmax with the lowest index on ties; position within the lane's
@@ -152,8 +141,12 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
 #pragma unroll
     for (int it = 0; it < kLoads; ++it)
 #pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
-    mid();
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const float v = elem<DT>(raw[it], k);
+        vm = fmaxf(vm, v);
+        xv = (ex == it * kVec<DT> + k) ? v : xv;
+      }
+    if (ex >= 0) red[kWaves].x = xv;  // read after the barrier below
     vm = wave_max(vm);
     hs[tid] = 0;
     if (l == 0) red[w] = f32x4{vm, 0.0f, 0.0f, 0.0f};
@@ -187,6 +180,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
         if (fin && (unsigned)jb < (unsigned)kHistBins)
           atomicAdd(&hs[jb], kCountOne | (unsigned long long)(unsigned)(wv * kFixScale));
       }
+    mid();  // the second pass was the last to read `raw`
     s = wave_sum(s);
     const float nf = (float)nfin;  // exact: < 2^24
     __syncthreads();  // every lane has read red[].x
@@ -217,11 +211,15 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
       const float base = (mn == kNegInf) ? 0.0f : mn;
       float t = s * fast_exp2((m - base) * kk);
 #pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k)
-        t += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const float v = elem<DT>(raw[it], k);
+        t += fast_exp2((v - base) * kk);
+        xv = (ex == it * kVec<DT> + k) ? v : xv;
+      }
       s = t;
       m = mn;
     }
+    if (ex >= 0) red[kWaves].x = xv;  // read after the reduction's barrier
     mid();
     wave_lse(m, s, kk);
     if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
@@ -238,213 +236,74 @@ struct NoMid {
   __device__ void operator()() const {}
 };
 
-// Occupancy hint: 6 (fp32) or 4 (bf16) waves per SIMD; the bf16 histogram
-// variant needs more registers (3: a tighter hint spills them to scratch).
-// LDS limits the histogram variant to 6 workgroups per CU anyway.
+// Occupancy hint, for the histogram variant on the 16-byte load path only:
+// 6 (fp32) or 3 (bf16) waves per SIMD (a tighter bf16 hint spills to
+// scratch; LDS limits this variant to 6 workgroups per CU anyway). The
+// plain variant takes none: the compiler then schedules it with 90
+// registers (5 waves per SIMD), against 61 (8 waves) under a hint of 6, and
+// that code streams faster once many rows are needed (B = 256, V = 151936,
+// K = 3, every draft full: 94.0 us against 97.5, equal with no drafts). The
+// element-wise path takes none either: it would spill under one.
 template <int DT, bool TR>
-constexpr int kStreamWaves = (DT == SS_DTYPE_F32) ? 6 : (TR ? 3 : 4);
+constexpr int kStreamWaves = (DT == SS_DTYPE_F32) ? 6 : 3;
 
-// Static grid over (sequence, row group, chunk), for batches too small or
-// too large for the balanced kernel (see use_balanced): each workgroup
-// streams its chunk of every row j <= draft_len in its group, one row after
-// another (one row per group for small batches). Only its histogram variant
-// takes the occupancy hint: the plain one measured faster without it (B =
-// 128, K = 5, every row needed: 68.0 us at 5 waves per SIMD against 71.4 at
-// the 8 the hint allows), and the scalar path (rows not 16-byte aligned)
-// spills under it.
+// Row lanes G (see the file comment). Measured per launch at B = 256,
+// V = 151936, fp32, K = 3 (events around 8 back-to-back launches, one box):
+//   draft lengths        G = 2    G = 4    kernel replaced (*)
+//   all 0 (256 rows)     27.4     32.3     27.9 us
+//   c3-like (277 rows)   29.4     33.2     30.3
+//   uniform 0..3         62.0     61.9     67.5
+//   all 3 (1024 rows)    94.0     90.1    103.1
+// (*) one workgroup per (sequence, chunk) of row 0, the chunks of rows
+// 1..d dealt round-robin to the same workgroups: each took its extra items
+// one after another, and every gap between them left its CU with fewer
+// loads in flight. At K = 16 two lanes serialise too many rows (a c3-like
+// mix took 48.9 us against 39.6 with four lanes).
+constexpr int64_t kRow0Fill = 4096;  // row-0 workgroups that fill the chip
+inline int row_lanes(int B, int K, int nchunks) {
+  if ((int64_t)B * nchunks < kRow0Fill) return K + 1;
+  return std::min(K + 1, K <= 3 ? 2 : 4);
+}
+
+// Grid: (sequence b, row lane q, chunk c), c fastest. Row 0, which every
+// valid sequence needs, is requested before the sequence's parameters
+// return; lanes q >= 1 first learn the draft length.
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, ((VP && TR) ? kStreamWaves<DT, TR> : 1)) void
 spec_stream_kernel(Args a) {
   __shared__ f32x4 red[kWaves + 1];
   __shared__ unsigned long long hs[TR ? kHistBins : 1];
   const int tid = threadIdx.x;
-  const int R = a.K + 1, nc = a.nchunks;
+  const int R = a.K + 1, nc = a.nchunks, G = a.ngroups;
   const int c = blockIdx.x % nc;
-  const int bg = blockIdx.x / nc;
-  const int b = bg / a.ngroups, g = bg - b * a.ngroups;
-  const int j0 = g * a.rows_per_wg;
+  const int bq = blockIdx.x / nc;
+  const int b = bq / G, q = bq - b * G;
   const int cstart = c * kChunk<DT>;
-  // Row 0, which every valid sequence needs, is requested before the
-  // sequence's parameters return.
+  u32x4 raw[kLoads];
+  if (q == 0)
+    load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
+                       a.V, tid, raw);
+  int x = draft_token(a, b, q);
   int d;
   float T;
   const int st = seq_check(a, b, &d, &T);  // reported by finalize
-  u32x4 raw[kLoads];
-  if (j0 == 0)
-    load_chunk<DT, VP>(a.logits + (int64_t)b * R * a.V * Dt<DT>::kBytes, cstart,
-                       a.V, tid, raw);
-  int x = draft_token(a, b, j0);
   if (TR && blockIdx.x == 0 && tid == 0) *a.tcount = 0;  // rows the plan lists
   if (st) return;
-  const int j1 = min(j0 + a.rows_per_wg, d + 1);
-  for (int j = j0; j < j1; ++j) {
+  for (int j = q; j <= d; j += G) {
     if (j != 0)
       load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
                          cstart, a.V, tid, raw);
-    if (j != j0) x = draft_token(a, b, j);
+    if (j != q) x = draft_token(a, b, j);
     stream_row<DT, VP, TR, true>(a, b, j, d, T, c, x, raw, red, hs, NoMid{});
   }
 }
 
-constexpr int kPlanMaxB = 2048;  // sequences whose plan fits in LDS
-constexpr int kPlanPer = kPlanMaxB / kThreads;
-
-// Balanced stream: one workgroup per (sequence, chunk) of row 0, which every
-// valid sequence needs, in (sequence, chunk) order. The items of rows
-// 1..draft_len, (row, chunk) pairs in (sequence, row, chunk) order, are dealt
-// round-robin to the same workgroups: workgroup g also takes extra items g,
-// g + n0, g + 2 n0, ... (n0 = B x nchunks). The workgroups with extra work are
-// therefore the first ones dispatched, and a sequence with several rows is
-// spread over many workgroups instead of being streamed row after row by
-// one. Every workgroup learns the number of extra rows E from the draft
-// lengths (loaded while its row-0 chunk is in flight); only
-// those with extra items build the exclusive prefix of draft lengths in LDS
-// that maps an item to its sequence and row. (A persistent grid that deals
-// every item round-robin runs its workgroups in lock-step rounds and was
-// measured slower; so was handing items out with atomic counters.)
-struct Item {
-  int b, j, c;
-};
-
-// Item x of rows >= 1: the largest b with pre[b] <= x / nc.
-__device__ __forceinline__ Item decode_extra(int x, int nc, int B, const int* pre) {
-  Item t;
-  const int r = x / nc;
-  t.c = x - r * nc;
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int m = (lo + hi + 1) >> 1;
-    if (pre[m] <= r) lo = m;
-    else hi = m - 1;
-  }
-  t.b = lo;
-  t.j = r - pre[lo] + 1;
-  return t;
-}
-
-// Extra rows of one sequence: draft_len when it is in [1, K], else 0
-// (invalid lengths are reported by finalize and need no rows).
-__device__ __forceinline__ int extra_rows(const Args& a, int b) {
-  const int v = a.draft_len[b] + a.dl_offset;
-  return (v >= 1 && v <= a.K) ? v : 0;
-}
-
-
-template <int DT, bool VP, bool TR>
-__global__ __launch_bounds__(kThreads, (kStreamWaves<DT, TR>)) void
-spec_stream_balanced_kernel(Args a) {
-  __shared__ f32x4 red[kWaves + 1];
-  __shared__ unsigned long long hs[TR ? kHistBins : 1];
-  __shared__ int pre[kPlanMaxB + 1];
-  __shared__ int wsum[kWaves];
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int B = a.B, R = a.K + 1, nc = a.nchunks;
-  const int n0 = B * nc;
-  const int g = blockIdx.x;
-  const int b0 = g / nc, c0 = g - b0 * nc;
-  u32x4 raw[kLoads];
-  load_chunk<DT, VP>(a.logits + (int64_t)b0 * R * a.V * Dt<DT>::kBytes,
-                     c0 * kChunk<DT>, a.V, tid, raw);
-  if (TR && g == 0 && tid == 0) *a.tcount = 0;  // rows the plan lists
-  int d;
-  float T;
-  int st = seq_check(a, b0, &d, &T);  // reported by finalize
-  int part = 0;
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid + i * kThreads;
-    if (b < B) part += extra_rows(a, b);
-  }
-  if (st == 0) stream_row<DT, VP, TR, false>(a, b0, 0, d, T, c0, -1, raw, red, hs, NoMid{});
-  part = (int)wave_sum((float)part);  // exact: < 2^24
-  if (l == 0) wsum[w] = part;
-  __syncthreads();
-  int E = 0;
-  for (int i = 0; i < kWaves; ++i) E += wsum[i];
-  const int nx = E * nc;  // extra items
-  if (g >= nx) return;
-  // Exclusive prefix of extra rows, kPlanPer consecutive sequences a thread.
-  int tsum = 0;
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid * kPlanPer + i;
-    if (b < B) {
-      const int v = extra_rows(a, b);
-      pre[b] = v;
-      tsum += v;
-    }
-  }
-  const int incl = (int)wave_inclusive_sum((float)tsum);
-  __syncthreads();  // wsum[0] has been read
-  if (l == kWave - 1) wsum[w] = incl;
-  __syncthreads();
-  int base = incl - tsum;
-  for (int i = 0; i < w; ++i) base += wsum[i];
-#pragma unroll
-  for (int i = 0; i < kPlanPer; ++i) {
-    const int b = tid * kPlanPer + i;
-    if (b < B) {
-      const int v = pre[b];
-      pre[b] = base;
-      base += v;
-    }
-  }
-  __syncthreads();
-  for (int x = g; x < nx; x += n0) {
-    const Item t = decode_extra(x, nc, B, pre);
-    load_chunk<DT, VP>(a.logits + ((int64_t)t.b * R + t.j) * a.V * Dt<DT>::kBytes,
-                       t.c * kChunk<DT>, a.V, tid, raw);
-    st = seq_check(a, t.b, &d, &T);
-    if (st == 0) stream_row<DT, VP, TR, false>(a, t.b, t.j, d, T, t.c, -1, raw, red, hs, NoMid{});
-  }
-}
-
-// Workgroups the stream grid aims for: enough to keep every CU busy with
-// several resident workgroups.
-constexpr int64_t kTargetWorkgroups = 4096;
-
-// Which kernel streams the rows.
-//  - Fewer (sequence, chunk) pairs than kTargetWorkgroups: the row-0
-//    workgroups alone do not fill the chip a few times over, and the
-//    balanced kernel's extra items, taken one after another by the same
-//    workgroups, would form its tail. Every (sequence, row, chunk) then gets
-//    a workgroup of its own (rows past a sequence's draft length exit at
-//    once). Measured at V = 151936: B = 64, K = 3 with most drafts full
-//    20.2 us against 25.2; B = 32, K = 5 bf16 with few rows 7.4 against 9.8;
-//    B = 128, K = 5 with every row needed 71.6 against 81.7.
-//  - Up to kPlanMaxB sequences otherwise: the balanced kernel, which needs
-//    no workgroup for the many rows that drafts leave unused (B = 256,
-//    K = 3 with 277 of 1024 rows needed: 29.7 us against 30.5 for the full
-//    grid; with no drafts 27.3 against 29.3).
-//  - Draft trees: a tree's nodes usually all need their rows, so every
-//    (sequence, node, chunk) gets a workgroup at any batch size (B = 256,
-//    8-node trees: 198 us per verification call against 210).
-//  - Larger batches: (sequence, row group, chunk), each workgroup streaming
-//    its chunk of the rows of its group one after another.
+// Draft trees: a tree's nodes usually all need their rows, so every
+// (sequence, node, chunk) gets a workgroup (G = K + 1).
 inline bool tree_rows(const Args& a) { return a.dl_status == SS_ST_TREE; }
-
-inline bool use_balanced(const Args& a) {
-  return !tree_rows(a) && a.B <= kPlanMaxB &&
-         (int64_t)a.B * a.nchunks >= kTargetWorkgroups;
-}
-
-inline void set_row_groups(Args& a) {
-  const int R = a.K + 1;
-  const int64_t base = (int64_t)a.B * a.nchunks;
-  const int ngroups = (base < kTargetWorkgroups || tree_rows(a))
-                          ? R
-                          : (int)std::min<int64_t>(R, (kTargetWorkgroups + base - 1) / base);
-  a.rows_per_wg = (R + ngroups - 1) / ngroups;
-  a.ngroups = (R + a.rows_per_wg - 1) / a.rows_per_wg;
-}
 
 template <int DT, bool VP, bool TR>
 int launch_stream_t(const Args& a, hipStream_t s) {
-  if (use_balanced(a)) {
-    hipLaunchKernelGGL((spec_stream_balanced_kernel<DT, VP, TR>),
-                       dim3((unsigned)(a.B * a.nchunks)), dim3(kThreads), 0, s, a);
-    return check_launch("spec_stream");
-  }
   const int64_t grid = (int64_t)a.B * a.nchunks * a.ngroups;
   if (grid > INT_MAX) return set_error(SS_EINVAL, "spec_stream: grid too large");
   hipLaunchKernelGGL((spec_stream_kernel<DT, VP, TR>), dim3((unsigned)grid),
@@ -461,7 +320,7 @@ int launch_stream_tr(const Args& a, hipStream_t s) {
 }  // namespace
 
 int launch_stream(Args a, bool f32, bool vp, hipStream_t s) {
-  set_row_groups(a);
+  a.ngroups = tree_rows(a) ? a.K + 1 : row_lanes(a.B, a.K, a.nchunks);
   return f32 ? (vp ? launch_stream_tr<SS_DTYPE_F32, true>(a, s)
                    : launch_stream_tr<SS_DTYPE_F32, false>(a, s))
              : (vp ? launch_stream_tr<SS_DTYPE_BF16, true>(a, s)

@@ -145,7 +145,8 @@ __device__ __forceinline__ void load_chunk(const unsigned char* row, int cstart,
 
 struct Args {
   const unsigned char* logits;
-  int B, K, V, nchunks, rows_per_wg, ngroups;
+  int B, K, V, nchunks;
+  int ngroups;      // row lanes of the stream grid (set by launch_stream)
   const int32_t* draft;
   const int32_t* draft_len;
   int dl_offset;    // rows needed = draft_len[b] + dl_offset + 1 (trees: -1)

@@ -285,30 +285,31 @@ def test_one_workspace_serves_every_shape_that_fits():
         compare_verify(*g, r, Ta, u, None, what=f"reuse B={B} K={K} V={V}")
 
 
-@pytest.mark.parametrize("B", [64, 2048, 2049])
+@pytest.mark.parametrize("B,K", [(64, 3), (2048, 3), (2049, 6)])
 @pytest.mark.parametrize("lengths", ["empty", "full", "mixed"])
-def test_row_balancing_across_batch_sizes(B, lengths):
-    """The stream pass gives every (sequence, row, chunk) a workgroup when
-    B x nchunks < 4096 (B = 64 here), deals the (row, chunk) items of rows
-    1..d round-robin to the row-0 workgroups up to B = 2048, and streams rows
-    per sequence above it; all three give the oracle's results for all-empty,
-    all-full and mixed draft lengths (with invalid lengths mixed in, which are
-    reported and need no rows)."""
-    say(f"[gpu] row balancing B={B} {lengths}")
-    rng = np.random.default_rng(B + len(lengths))
-    K, V = 3, 9000  # two chunks, the second ragged
+def test_row_lanes_across_batch_sizes(B, K, lengths):
+    """The stream grid is (sequence, row lane, chunk), lane q streaming rows
+    q, q + G, ...: G = K + 1 (a workgroup per row) when B x nchunks < 4096
+    (B = 64 here, V = 9000 gives two chunks), G = 2 for K <= 3 above it (B =
+    2048), G = 4 for larger K (B = 2049, K = 6: lanes take rows {0, 4},
+    {1, 5}, {2, 6}, {3}); all give the oracle's results for all-empty,
+    all-full and mixed draft lengths (with invalid lengths mixed in, which
+    are reported and need no rows)."""
+    say(f"[gpu] row lanes B={B} K={K} {lengths}")
+    rng = np.random.default_rng(B + K + len(lengths))
+    V = 9000  # two chunks, the second ragged
     x = (rng.standard_normal((B, K + 1, V)) * 1.5).astype(np.float32)
     if lengths == "empty":
         dl = np.zeros(B, np.int32)
     elif lengths == "full":
         dl = np.full(B, K, np.int32)
     else:
-        dl = rng.choice([0, 0, 0, 1, 2, 3, -1, 4], B).astype(np.int32)
+        dl = rng.choice([0, 0, 0, 1, 2, K - 1, K, -1, K + 1], B).astype(np.int32)
     draft = _drafts_near_argmax(rng, x, K, np.clip(dl, 0, K), flip=0.5)
     T = np.where(rng.random(B) < 0.5, 0.0, 0.9).astype(np.float32)
     u = rng.random((B, K + 1)).astype(np.float32)
     g, r = _run(torch.from_numpy(x).cuda(), draft, dl, T, u)
-    compare_verify(*g, r, T, u, None, what=f"balance B={B} {lengths}")
+    compare_verify(*g, r, T, u, None, what=f"lanes B={B} K={K} {lengths}")
 
 
 # ------------------------------------------- finalize: how partials arrive ---
