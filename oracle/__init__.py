@@ -38,13 +38,25 @@ ST_TOP_P = 1 << 7
 ST_TREE = 1 << 8
 
 
-def build() -> str:
-    """Compile oracle.cpp into liboracle.so (always recompiles)."""
-    cmd = ["g++", "-O2", "-std=c++17", "-Wall", "-fPIC", "-shared", "-pthread",
-           _SRC, "-o", _LIB + ".tmp"]
+# A build with AddressSanitizer and UndefinedBehaviorSanitizer, for running
+# the oracle's own tests under them (tests/test_oracle_sanitizers.py): loaded
+# instead of liboracle.so when ORACLE_SANITIZE=1, in a process that preloads
+# the sanitizer runtimes.
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(sanitize: bool = False) -> str:
+    """Compile oracle.cpp into liboracle.so, or with sanitize into
+    liboracle_san.so (always recompiles)."""
+    out = _LIB_SAN if sanitize else _LIB
+    cmd = ["g++", "-O1" if sanitize else "-O2", "-std=c++17", "-Wall", "-fPIC",
+           "-shared", "-pthread", *(SANITIZE_FLAGS if sanitize else []),
+           _SRC, "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
@@ -54,9 +66,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    path = _LIB_SAN if os.environ.get("ORACLE_SANITIZE") == "1" else _LIB
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        build(sanitize=path == _LIB_SAN)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.orc_sam_new.restype = P
