@@ -28,11 +28,13 @@ namespace {
 // a target beyond the chunk's re-read total (a rounding difference with the
 // partials) takes the chunk's last positive weight.
 //
-// Every weight is a float32 term, but the running sums, the target u *
-// total and a chunk's rescale to the row max are taken in double: a float32
-// running sum over 2^17 tokens moves a breakpoint by a few float32 roundings
-// of the total, which at that many tokens is the width of many tokens'
-// intervals. What remains is the float32 rounding of the terms themselves.
+// Every weight is a float32 term, but the running sum over chunks, the
+// target u * total and a chunk's rescale to the row max are taken in double:
+// a float32 running sum over 2^17 tokens moves a breakpoint by a few float32
+// roundings of the total, which at that many tokens is the width of many
+// tokens' intervals. Inside the chosen chunk (one chunk's share of the
+// total) the scans are float32: their rounding is that share of a float32
+// ulp.
 // ---------------------------------------------------------------------------
 struct ChunkPick {
   int chunk;    // -1: every weight is 0
@@ -44,9 +46,19 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 }
 
 // Weight of a chunk relative to the row max m: its partial sum s (relative
-// to the chunk's own max mc) times exp2((mc - m) * kk), the rescale in double.
+// to the chunk's own max mc) times exp2((mc - m) * kk). The exponent is
+// formed in double (a float product would round it by up to 1e-6 for
+// |exponent| ~ 20, an error shared by every token of the chunk); its integer
+// part is applied exactly by ldexp and its fraction by the hardware exp2,
+// whose error (about one float32 ulp) is that of any single term. A chunk
+// whose max is -inf weighs 0; NaN (a non-finite row) stays NaN.
 __device__ __forceinline__ double chunk_weight(float s, float mc, float m, float kk) {
-  return (double)s * exp2(((double)mc - (double)m) * (double)kk);
+  const double e = ((double)mc - (double)m) * (double)kk;
+  if (e != e) return (double)NAN;
+  if (e < -4096.0) return 0.0;  // below every double, -inf included
+  const double fl = floor(e);
+  const float fr = (float)(e - fl);  // in [0, 1)
+  return ldexp((double)s * (double)fast_exp2(fr), (int)fl);
 }
 
 // One wavefront, all lanes active; weight(c) (a double) is called for c < nc.
@@ -93,7 +105,7 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
 }
 
 struct DrawShared {
-  double cell[kLoads * kWaves];  // (load, wave) totals in token order
+  float cell[kLoads * kWaves];  // (load, wave) totals in token order
   int wlast[kWaves];
   int result;
   float result_l;  // the drawn token's logit (NaN if the draw did not see it)
@@ -172,28 +184,29 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
   if (pk.chunk < 0) return -1;
   const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const int cstart = pk.chunk * kChunk<DT>;
-  double vs[kLoads];
+  const float t_in = (float)pk.t_in;
+  float vs[kLoads];
   int tlast = -1;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
     float qv[kVec<DT>];
     if constexpr (RESIDUAL) load_q_vec<DT, VP>(qrow, cstart, tid, it, a.V, qv);
-    double acc = 0.0;
+    float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) {
       const int i = elem_index<DT, VP>(cstart, tid, it, k);
       const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
                                                  kk, invS, RESIDUAL ? qv[k] : 0.0f,
                                                  lam);
-      acc += (double)wk;
+      acc += wk;
       if (wk > 0.0f) tlast = max(tlast, i);
     }
     vs[it] = acc;
   }
   // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
-  double tot[kLoads];
+  float tot[kLoads];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum_d(vs[it]);
+  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum(vs[it]);
   const int wl = wave_max_i(tlast);
   if (l == 0) {
 #pragma unroll
@@ -202,11 +215,11 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
   }
   __syncthreads();
   // Every wavefront finds the cell (the same scan gives the same answer).
-  const double cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0;
-  const double inc = wave_inclusive_sum_d(cv);
-  const double exc = wave_shift_up1_d(inc);
+  const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
+  const float inc = wave_inclusive_sum(cv);
+  const float exc = wave_shift_up1(inc);
   const unsigned long long hit =
-      __ballot(l < kLoads * kWaves && exc <= pk.t_in && pk.t_in < inc);
+      __ballot(l < kLoads * kWaves && exc <= t_in && t_in < inc);
   int clast = sh.wlast[0];
   for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
   const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
@@ -217,13 +230,13 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
     }
   } else if (w == cell % kWaves) {
     const int its = cell / kWaves;
-    double v = vs[0];
+    float v = vs[0];
 #pragma unroll
     for (int it = 1; it < kLoads; ++it)
       if (it == its) v = vs[it];
-    const double tc = fmax(0.0, pk.t_in - readlane_d(exc, cell));
-    const double inc2 = wave_inclusive_sum_d(v);
-    const double exc2 = wave_shift_up1_d(inc2);
+    const float tc = fmaxf(0.0f, t_in - readlane_f(exc, cell));
+    const float inc2 = wave_inclusive_sum(v);
+    const float exc2 = wave_shift_up1(inc2);
     const bool mine = exc2 <= tc && tc < inc2;
     const unsigned long long who = __ballot(mine);
     if (!who) {
@@ -232,7 +245,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
         sh.result_l = NAN;
       }
     } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
-      const double tl = tc - exc2;
+      const float tl = tc - exc2;
       u32x4 rv = raw[0];
 #pragma unroll
       for (int it = 1; it < kLoads; ++it)
@@ -245,8 +258,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
           qv[k] = i < a.V ? qrow[i] : 0.0f;
         }
       }
-      double run = 0.0;
-      float lfound = NAN, llast = NAN;
+      float run = 0.0f, lfound = NAN, llast = NAN;
       int found = -1, lastp = -1;
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
@@ -254,7 +266,7 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
         const float lk = elem<DT>(rv, k);
         const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
                                                    RESIDUAL ? qv[k] : 0.0f, lam);
-        run += (double)wk;
+        run += wk;
         if (wk > 0.0f) {
           lastp = i;
           llast = lk;

@@ -448,11 +448,13 @@ __device__ inline bool sam_append(const SamSeq& S, SamCursor& cs, const int32_t*
 __device__ inline void sam_draft_from(const SamSeq& S, int n, int nstates, int s,
                                       i32x4 rs, int K, int32_t* draft,
                                       int32_t* draft_len, int32_t* match_len) {
+  // The walk ends at the root without loading its record: its length is 0,
+  // which gives no draft.
   for (int g = 0; s > 0 && rs.w == -1 && g < nstates; ++g) {
     s = rs.y;
-    rs = S.st[s < 0 ? 0 : s];
+    if (s > 0) rs = S.st[s];
   }
-  const int Lm = (s < 0) ? 0 : rs.x;
+  const int Lm = (s <= 0) ? 0 : rs.x;
   const int p = rs.z;
   const int d = (Lm == 0) ? 0 : min(K, n - 1 - p);
   const int l = lane_id();
