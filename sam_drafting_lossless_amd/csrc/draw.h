@@ -41,10 +41,6 @@ struct ChunkPick {
   double t_in;  // target left inside the chunk; +inf: take its last positive
 };
 
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
 // Weight of a chunk relative to the row max m: its partial sum s (relative
 // to the chunk's own max mc) times exp2((mc - m) * kk). The exponent is
 // formed in double (a float product would round it by up to 1e-6 for

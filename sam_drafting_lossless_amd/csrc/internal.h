@@ -62,6 +62,10 @@ __device__ __forceinline__ double dpp_d(double id, double v) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ double readlane_d(double v, int lane) {
   const unsigned long long x = (unsigned long long)__double_as_longlong(v);
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, lane);
@@ -134,6 +138,12 @@ __device__ __forceinline__ void keep_here(float& v) { asm volatile("" : "+v"(v))
 __device__ __forceinline__ void keep_here(u32x4& v) { asm volatile("" : "+v"(v)); }
 // The same for a wavefront-uniform value, kept in a scalar register.
 __device__ __forceinline__ void keep_here_uniform(int& v) { asm volatile("" : "+s"(v)); }
+
+// Mask of the lanes where b holds. The compiler's own ballot takes an int
+// and materialises the compare first; this one uses the compare's mask.
+__device__ __forceinline__ unsigned long long ballot_mask(bool b) {
+  return __builtin_amdgcn_ballot_w64(b);
+}
 
 // Number of lanes below this one whose bit is set in a wavefront mask.
 __device__ __forceinline__ int lanes_below(unsigned long long m) {

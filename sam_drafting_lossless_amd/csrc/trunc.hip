@@ -10,29 +10,32 @@
 // Design for gfx950. Finding the k-th largest logit, or the logit where the
 // running probability crosses top_p, is a selection over V values per row.
 // Sorting a 152k-entry row, or a radix select that re-reads it once per
-// digit, would cost several passes over HBM. Here the row is read twice:
+// digit, would cost several passes over HBM. Here the row is read once:
 //   stream  (stream.hip, truncated rows only) counts each chunk's logits, and
 //           sums their probability, in a 256-bin window histogram on a grid
 //           shared by all chunks of the row (1/8 octave of probability per
-//           bin, 32 octaves below the chunk max);
-//   plan    (one workgroup per row) merges the row's chunk histograms, scans
-//           them from the top and picks the bin range that must hold the
-//           threshold (with a margin for the histogram's rounding);
-//   extract (one workgroup per row chunk) re-reads the chunk, sums the exact
-//           probability of its tokens above the range and writes the tokens
-//           inside the range to the chunk's own segment of the row's
-//           candidate list (no atomics);
-//   select  (one workgroup per row) finds the exact threshold among the
-//           candidates by radix selection on order-preserving keys (8-bit
-//           digits, LDS histograms of counts for top-k and of probability
-//           for top-p), then adds the kept candidates' probability to their
-//           chunks' sums.
+//           bin, 32 octaves below the chunk max); picks a band of bins from
+//           its own histogram (its top bins down to its own k-th largest
+//           logit for top-k; a few bins around its own top_p point for top-p
+//           alone), copies the band's logits to the chunk's segment and sums
+//           the probability of its tokens above the band;
+//   select  (one 1024-thread workgroup per row) merges the row's chunk
+//           histograms, scans them from the top and picks the bin range that
+//           must hold the threshold (with a margin for the histogram's
+//           rounding); takes the candidates (the tokens in the range) and the
+//           exact probability above the range from each chunk's band when the
+//           band holds the range, else by re-reading that chunk; finds the
+//           exact threshold among the candidates by radix selection on
+//           order-preserving keys (8-bit digits, LDS histograms of counts for
+//           top-k and of probability for top-p); and leaves each chunk's kept
+//           probability.
 // The finalize kernel then judges and draws with the per-chunk kept sums and
 // the threshold. Selection first finds the bits all candidate keys share and
 // radix-walks only the bits below them, so that no round piles every
-// candidate into one LDS bucket. A row with more than kCandCap candidates,
-// or a chunk with more than kSegCap (logits crowded into a few bins), is
-// selected by scanning the row itself in each round: exact, but slower.
+// candidate into one LDS bucket. A row with more than kCandCap candidates is
+// selected by walking its chunks' tokens again in each round (from the
+// segments, or the logits for chunks whose band misses): exact, but slower.
+// The sums that reach the outputs are taken in a fixed order.
 #include <algorithm>
 
 #include "verify_common.h"
@@ -41,21 +44,13 @@ namespace specsam {
 namespace {
 
 constexpr float kPlanMargin = 1e-4f;  // relative slack for histogram rounding
-constexpr int kKeepAll = INT_MAX;     // range start when nothing is dropped
-constexpr int64_t kExtractGrid = 4096;  // extract workgroups (grid-stride)
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kPlanGroups = kSelThreads / kHistBins;  // chunk groups of the merge
+constexpr int kPlanBatch = 8;  // histogram words a thread requests at once
+static_assert(kMaxChunks <= kHistBins, "the chunk prefix uses the first 4 wavefronts");
 
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  v = wave_sum(v);
-  __syncthreads();
-  if (l == 0) scratch[w] = v;
-  __syncthreads();
-  float t = 0.0f;
-  for (int i = 0; i < kWaves; ++i) t += scratch[i];
-  return t;
-}
-
-// Row-level activity of truncation; the same test in every kernel.
+// Row-level activity of truncation; the same test as the stream pass.
 struct RowCtx {
   int b, j, d;
   float T, kk;
@@ -73,319 +68,213 @@ __device__ __forceinline__ RowCtx row_ctx(const Args& a, int64_t row) {
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// plan: one workgroup per row; thread r owns bin r of the row window.
-// ---------------------------------------------------------------------------
-constexpr int kPlanBatch = 24;  // chunk histograms requested at once
-
-__global__ __launch_bounds__(kThreads) void trunc_plan_kernel(Args a) {
-  __shared__ int s_a[kMaxChunks];
-  __shared__ float s_pm[kMaxChunks];
-  __shared__ float scratch[2][kWaves];
-  __shared__ float wtot[2][kWaves];
-  __shared__ int first[3];
-  __shared__ float zval[2];
-  __shared__ int cabove;
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int64_t row = blockIdx.x;
-  const int nc = a.nchunks;
-  const int64_t h0 = row * nc;
-  // The chunk headers and partials are requested together with the row's
-  // parameters (they are in bounds for every row; an inactive row's are
-  // never used).
-  i32x4 hh = i32x4{0, 0, 0, 0};
-  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (tid < nc) {
-    hh = a.hhdr[h0 + tid];
-    pv = a.partials[h0 + tid];
-  }
-  const RowCtx rc = row_ctx(a, row);
-  if (!rc.active) return;
-  if (tid < nc) {
-    s_a[tid] = hh.x;
-    s_pm[tid] = pv.x;
-  }
-  for (int c = tid + kThreads; c < nc; c += kThreads) {
-    s_a[c] = a.hhdr[h0 + c].x;
-    s_pm[c] = a.partials[h0 + c].x;
-  }
-  if (tid < 3) first[tid] = kRestBin;
-  if (tid == 0) cabove = 0;
-  __syncthreads();
-  float m = kNegInf;
-  for (int c = 0; c < nc; ++c) m = fmaxf(m, s_pm[c]);
-  const int a0 = abs_bin(m, rc.kk);
-  // Totals: the finite count N from the chunk headers and the mass Z
-  // (relative to the row max) from the partials.
-  float tcnt = 0.0f, tmass = 0.0f;
-  if (tid < nc) {
-    tcnt = (float)hh.y;
-    tmass = pv.y * fast_exp2((pv.x - m) * rc.kk);
-  }
-  for (int c = tid + kThreads; c < nc; c += kThreads) {
-    const f32x4 p = a.partials[h0 + c];
-    tcnt += (float)a.hhdr[h0 + c].y;
-    tmass += p.y * fast_exp2((p.x - m) * rc.kk);
-  }
-  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c. The words of
-  // kPlanBatch chunks are requested together.
-  float cnt = 0.0f, mass = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += kPlanBatch) {
-    unsigned long long wb[kPlanBatch];
-#pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u) {
-      const int c = c0 + u;
-      wb[u] = 0;
-      if (c < nc) {
-        const int jb = tid - (s_a[c] - a0);
-        if (jb >= 0 && jb < kHistBins) wb[u] = a.hist[(h0 + c) * kHistBins + jb];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u) {
-      const int c = c0 + u;
-      if (c < nc) {
-        const float sc = fast_exp2((s_pm[c] - m) * rc.kk) * (1.0f / kFixScale);
-        cnt += (float)(unsigned)(wb[u] >> 48);
-        mass += (float)(wb[u] & kMassMask) * sc;
-      }
-    }
-  }
-  // N and Z (one reduction for both), and inclusive scans of counts and
-  // masses from the top bin down.
-  tcnt = wave_sum(tcnt);  // exact: < 2^24
-  tmass = wave_sum(tmass);
-  float C = wave_inclusive_sum(cnt), M = wave_inclusive_sum(mass);
-  if (l == kWave - 1) {
-    scratch[0][w] = tcnt;
-    scratch[1][w] = tmass;
-    wtot[0][w] = C;
-    wtot[1][w] = M;
-  }
-  __syncthreads();
-  float N = 0.0f, Z = 0.0f;
-  for (int i = 0; i < kWaves; ++i) {
-    N += scratch[0][i];
-    Z += scratch[1][i];
-    if (i < w) {
-      C += wtot[0][i];
-      M += wtot[1][i];
-    }
-  }
-  const int k = a.top_k ? a.top_k[rc.b] : 0;
-  const float tp = a.top_p ? a.top_p[rc.b] : 1.0f;
-  const bool kA = k >= 1 && k < a.V && (float)k <= N;
-  const bool pA = tp < 1.0f;
-  // C and M do not decrease with the bin, so the first bin meeting a target
-  // is the first set lane of the first wavefront whose ballot is not empty
-  // (one LDS atomic per wavefront).
-  const unsigned long long kb = __ballot(kA && C >= (float)k);
-  if (l == 0 && kb) atomicMin(&first[0], w * kWave + __ffsll((unsigned long long)kb) - 1);
-  __syncthreads();
-  const int bk = kA ? first[0] : kRestBin;
-  // Mass above bin bk (Z_lo) and through it (Z_hi): top-p's share is taken of
-  // what top-k kept, which lies between the two.
-  if (tid == 0) {
-    zval[0] = 0.0f;
-    zval[1] = Z;
-  }
-  __syncthreads();
-  if (kA) {
-    if (tid == bk - 1) zval[0] = M;
-    if (tid == bk) zval[1] = M;
-  } else if (tid == 0) {
-    zval[0] = Z;
-  }
-  __syncthreads();
-  if (pA) {
-    const float tlo = tp * zval[0] * (1.0f - kPlanMargin);
-    const float thi = tp * zval[1] * (1.0f + kPlanMargin);
-    const unsigned long long lo = __ballot(M >= tlo), hi = __ballot(M >= thi);
-    if (l == 0 && lo) atomicMin(&first[1], w * kWave + __ffsll((unsigned long long)lo) - 1);
-    if (l == 0 && hi) atomicMin(&first[2], w * kWave + __ffsll((unsigned long long)hi) - 1);
-  }
-  __syncthreads();
-  // Candidate range [rlo, rhi]. Top-k's own bin is always in it (the k-th
-  // largest logit, and the share top-k keeps, are found among its tokens);
-  // top-p's threshold lies between the bins its two targets reach.
-  int rlo, rhi;
-  if (!kA && !pA) {
-    rlo = rhi = kKeepAll;  // nothing to drop
-  } else if (!pA) {
-    rlo = rhi = bk;
-  } else if (!kA) {
-    rlo = first[1];
-    rhi = first[2];
-  } else {
-    rlo = min(first[1], bk);
-    rhi = bk;
-  }
-  // Tokens above the range: the running count at bin rlo - 1.
-  if (rlo >= 1 && rlo <= kRestBin && tid == rlo - 1) cabove = (int)C;
-  __syncthreads();
-  if (tid == 0) {
-    a.plan[row * 2] = i32x4{a0, rlo, rhi, cabove};
-    a.plan[row * 2 + 1] =
-        i32x4{(kA ? 1 : 0) | (pA ? 2 : 0), k - cabove, __float_as_int(m), 0};
-    a.tlist[atomicAdd(a.tcount, 1)] = (int)row;
-  }
-}
-
 // Range test of a token's row bin rb against [rlo, rhi] (rhi = kRestBin:
 // unbounded below the window).
 __device__ __forceinline__ bool in_range(int rb, int rlo, int rhi) {
   return rb >= rlo && (rhi >= kRestBin || rb <= rhi);
 }
 
-// Row of list entry e of the truncated rows, or -1 past the list's end (the
-// grids of the passes below cover every row; entries past the count exit).
-__device__ __forceinline__ int64_t listed_row(const Args& a, int e) {
-  return e < *a.tcount ? (int64_t)a.tlist[e] : -1;
-}
-
-// ---------------------------------------------------------------------------
-// extract: (listed row, chunk) items, grid-stride (the grid is sized for the
-// largest list; a workgroup takes items g, g + grid, ... below count x nc).
-// ---------------------------------------------------------------------------
-struct ExtractShared {
-  int2 run[kWaves][kSegCap];  // each wavefront's candidates, in its own run
-  float scratch[kWaves];
-  int cnt[kWaves];
-};
-
-template <int DT, bool VP>
-__device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
-                                             ExtractShared& sh);
-
-template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void trunc_extract_kernel(Args a) {
-  __shared__ ExtractShared sh;
-  const int nc = a.nchunks;
-  const int64_t items = (int64_t)*a.tcount * nc;
-  for (int64_t x = blockIdx.x; x < items; x += gridDim.x) {
-    const int e = (int)(x / nc);
-    extract_item<DT, VP>(a, a.tlist[e], (int)(x - (int64_t)e * nc), sh);
-  }
-}
-
-template <int DT, bool VP>
-__device__ __forceinline__ void extract_item(const Args& a, int64_t row, int c,
-                                             ExtractShared& sh) {
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int nc = a.nchunks;
-  const int cstart = c * kChunk<DT>;
-  u32x4 raw[kLoads];
-  load_chunk<DT, VP>(a.logits + row * a.V * Dt<DT>::kBytes, cstart, a.V, tid, raw);
-  const int b = (int)(row / (a.K + 1));
-  const float kk = kLog2e / a.temperature[b];
-  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
-  const int a0 = p0.x, rlo = p0.y, rhi = p0.z;
-  const float m = __int_as_float(p1.z);
-  float above = 0.0f;
-  // Candidates are compacted per wavefront as they are found: a ballot per
-  // element gives each finding lane its place after the wavefront's earlier
-  // finds (element by element, lanes in order), in the wavefront's LDS run.
-  // A run past kSegCap is not stored; the chunk then overflows its segment
-  // (which holds at most kSegCap) and the row is selected by re-scanning it.
-  int n = 0;  // wavefront-uniform
-  int2* run = sh.run[w];
-#pragma unroll
-  for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const float v = elem<DT>(raw[it], k);
-      const bool fin = v > kNegInf;
-      const int rb = abs_bin(v, kk) - a0;
-      if (fin && rb < rlo) above += fast_exp2((v - m) * kk);
-      keep_here(above);
-      const bool inr = fin && in_range(rb, rlo, rhi);
-      const unsigned long long hit = __ballot(inr);
-      if (inr) {
-        const int p = n + lanes_below(hit);
-        if (p < kSegCap)
-          run[p] = int2{__float_as_int(v), elem_index<DT, VP>(cstart, tid, it, k)};
-      }
-      n += __popcll(hit);
-    }
-  above = wave_sum(above);
-  if (l == 0) {
-    sh.scratch[w] = above;
-    sh.cnt[w] = n;
-  }
-  __syncthreads();
-  // The runs go to this (row, chunk)'s own segment of the list in wavefront
-  // order. A segment that would overflow is not written (its count says so).
-  int base = 0, tot = 0;
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int ci = sh.cnt[i];
-    base += (i < w) ? ci : 0;
-    tot += ci;
-    sum += sh.scratch[i];
-  }
-  if (tid == 0) {
-    a.tpart[row * nc + c] = sum;
-    a.ccount[row * nc + c] = tot;
-  }
-  if (tot <= a.segcap) {
-    int2* out = a.cand + (row * nc + c) * a.segcap + base;
-    for (int p = l; p < n; p += kWave) out[p] = run[p];
-  }
-  __syncthreads();  // the runs and counts are reused by the next item
-}
-
-// ---------------------------------------------------------------------------
-// select: one workgroup per listed row.
-// ---------------------------------------------------------------------------
 struct SelShared {
-  unsigned key[kCandCap];  // candidate keys (fkey of the logit)
-  unsigned char chunk[kCandCap];  // the chunk each candidate lies in
-  int pre[kMaxChunks + 1];  // exclusive prefix of the chunks' candidate counts
+  unsigned key[kCandCap];  // candidate keys (fkey of the logit), a run per chunk
+  // per chunk: window start bin, finite count, max, weight sum (relative to
+  // its max), packed band, band logits, weight above the band (relative to
+  // its max); candidates found, exclusive prefix of those, weight above the
+  // range and kept weight (relative to the row max)
+  int ca[kMaxChunks];
+  int cnf[kMaxChunks];
+  float cpm[kMaxChunks];
+  float cps[kMaxChunks];
+  int cband[kMaxChunks];
+  int cn[kMaxChunks];
+  float cab[kMaxChunks];
+  int ccnt[kMaxChunks];
+  int cbeg[kMaxChunks];      // where the chunk's run of keys starts
+  float cabove[kMaxChunks];
+  float ckept[kMaxChunks];
+  int miss[kMaxChunks];      // chunks whose band misses the range, in order
+  int wcnt[kSelWaves];       // per-wavefront candidate counts of a re-read chunk
+  int ncand;                 // keys placed (runs reserved) so far
+  int over;                  // the runs would pass kCandCap
+  int mbase;
+  float pc[kPlanGroups][kHistBins];  // merge: each chunk group's count per row bin
+  float pw[kPlanGroups][kHistBins];  // and weight
   unsigned cnt[256];
   float mass[256];
-  float csum[kMaxChunks];
-  float scratch[kWaves];
-  int iscr[2][kWaves];
+  float wtot[2][kSelWaves];
+  float scratch[kSelWaves];
+  int iscr[2][kSelWaves];
+  int first[3];
+  int cabove_n;
+  float zval[2];
   int digit;
   float carry;
   unsigned minkey;
 };
 
-// Candidate keys of a row: from LDS when they fit, else by re-reading the row
-// and filtering it by the plan's range (exact, one pass over the row per
-// call). f(key, list position or token index).
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (l == 0) scratch[w] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < kSelWaves; ++i) t += scratch[i];
+  return t;
+}
+
+// Every logit of chunk c of a row, read by one wavefront, 8 16-byte loads
+// per lane in flight: f(value) in a fixed order, on every lane the same
+// number of times (past the row's end with -inf), so f may use ballots.
+template <int DT, bool VP, typename F>
+__device__ __forceinline__ void wave_chunk_each(const unsigned char* rowp, int c, int V,
+                                                F f) {
+  constexpr unsigned kNegInfWord = DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
+  constexpr int kU = 8;
+  const int l = threadIdx.x % kWave;
+  const int cstart = c * kChunk<DT>;
+  const int rem = min(kChunk<DT>, V - cstart);
+  if constexpr (VP) {
+    // (V is a multiple of the vector width on this path)
+    const u32x4* p = reinterpret_cast<const u32x4*>(rowp + (int64_t)cstart * Dt<DT>::kBytes);
+    const int nv = rem / kVec<DT>;
+    for (int v0 = 0; v0 < nv; v0 += kU * kWave) {
+      u32x4 r[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int vi = v0 + u * kWave + l;
+        r[u] = vi < nv ? __builtin_nontemporal_load(p + vi)
+                       : u32x4{kNegInfWord, kNegInfWord, kNegInfWord, kNegInfWord};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) f(elem<DT>(r[u], k));
+    }
+  } else {
+    for (int e0 = 0; e0 < rem; e0 += kU * kWave) {
+      float r[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int e = e0 + u * kWave + l;
+        r[u] = e < rem ? load_one<DT>(rowp, (int64_t)cstart + e) : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) f(r[u]);
+    }
+  }
+}
+
+// Chunk c of a row read by the whole workgroup in one round trip: element
+// i of thread t is token c * kChunk + (t + i * kSelThreads) (16-byte path:
+// vector t + u * kSelThreads, element k, in that order); -inf past the row.
+template <int DT>
+constexpr int kBlkElems = kChunk<DT> / kSelThreads;
+
 template <int DT, bool VP>
-struct CandSource {
-  // (fields by value: taking the kernel argument's address would place the
-  // whole argument block in scratch memory)
-  const unsigned char* rowp;
-  int V, nchunks;
+__device__ __forceinline__ void block_chunk_load(const unsigned char* rowp, int c, int V,
+                                                 float (&v)[kBlkElems<DT>]) {
+  const int tid = threadIdx.x;
+  const int cstart = c * kChunk<DT>;
+  const int rem = min(kChunk<DT>, V - cstart);
+  if constexpr (VP) {
+    constexpr int kNV = kBlkElems<DT> / kVec<DT>;
+    const u32x4* p = reinterpret_cast<const u32x4*>(rowp + (int64_t)cstart * Dt<DT>::kBytes);
+    const int nv = rem / kVec<DT>;
+    u32x4 r[kNV];
+#pragma unroll
+    for (int u = 0; u < kNV; ++u) {
+      const int vi = tid + u * kSelThreads;
+      r[u] = vi < nv ? __builtin_nontemporal_load(p + vi) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kNV; ++u)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k)
+        v[u * kVec<DT> + k] = (tid + u * kSelThreads < nv) ? elem<DT>(r[u], k) : kNegInf;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBlkElems<DT>; ++i) {
+      const int e = tid + i * kSelThreads;
+      v[i] = e < rem ? load_one<DT>(rowp, (int64_t)cstart + e) : kNegInf;
+    }
+  }
+}
+
+// A row's tokens at or above the bottom of its range [rlo, rhi], chunk by
+// chunk. Fields by value: taking the kernel argument's address would place
+// the whole argument block in scratch memory.
+template <int DT, bool VP>
+struct RowSrc {
+  const unsigned char* rowp;  // the row's logits
+  const float* seg;           // the row's band segments
+  int V, nc, segcap;
+  int a0, rlo, rhi;
+  float m, kk, ns;
   SelShared* sh;
-  int n, a0, rlo, rhi;
-  float kk;
-  bool lds;  // the candidates are in sh->key (else: re-scan the row)
-  __device__ __forceinline__ bool in_lds() const { return lds; }
+  bool lds;  // the candidates are in sh->key (else: walk the chunks again)
+  int n;     // candidates
+
+  __device__ __forceinline__ int row_bin(float v) const { return abs_bin_s(v, ns) - a0; }
+
+  // How chunk c's tokens at or above the range's bottom are found: kNone
+  // (it has none: its max lies below the range), kBand (its band holds
+  // them all), kReread (its band misses part of the range).
+  static constexpr int kNone = 0, kBand = 1, kReread = 2;
+  __device__ __forceinline__ int source(int c) const {
+    const int sc = sh->ca[c] - a0;  // the chunk's window starts at row bin sc
+    if (rhi < kRestBin && rhi < sc) return kNone;
+    const int bd = sh->cband[c];
+    const int blo = bd & 0xffff, bhi = bd >> 16;
+    const bool covered = blo <= bhi && blo + sc <= max(rlo, sc) &&
+                         (bhi >= kRestBin || (rhi < kRestBin && rhi <= bhi + sc));
+    return covered ? kBand : kReread;
+  }
+
+  // Wavefront-wide: chunk c's segment (a kBand chunk) into r, lane l holding
+  // entries l, l + 64, ... (-inf past its end); returns the number of
+  // wavefront rows in use. The whole segment is requested at once.
+  static constexpr int kU = kSegCap / kWave;
+  __device__ __forceinline__ int band_load(int c, float (&r)[kU]) const {
+    const int l = threadIdx.x % kWave;
+    const int cn = min(sh->cn[c], segcap);
+    const float* sp = seg + (int64_t)c * segcap;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = u * kWave + l;
+      r[u] = i < cn ? sp[i] : kNegInf;
+    }
+    return (cn + kWave - 1) / kWave;
+  }
+
+  // Wavefront-wide: f(v) for every logit of chunk c that may lie at or above
+  // the range (its band's, or all of its logits when the band misses).
   template <typename F>
-  __device__ __forceinline__ void each(F f) const {
-    const int tid = threadIdx.x;
-    if (in_lds()) {
-      for (int i = tid; i < n; i += kThreads) f(sh->key[i], i);
+  __device__ __forceinline__ void chunk(int c, F f) const {
+    const int src = source(c);
+    if (src == kNone) return;
+    if (src == kBand) {
+      float r[kU];
+      const int nu = band_load(c, r);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (u < nu) f(r[u]);
       return;
     }
-    for (int c = 0; c < nchunks; ++c) {
-      const int cstart = c * kChunk<DT>;
-      u32x4 raw[kLoads];
-      load_chunk<DT, VP, false>(rowp, cstart, V, tid, raw);
-#pragma unroll
-      for (int it = 0; it < kLoads; ++it)
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) {
-          const float v = elem<DT>(raw[it], k);
-          if (v > kNegInf && in_range(abs_bin(v, kk) - a0, rlo, rhi))
-            f(fkey(v), elem_index<DT, VP>(cstart, tid, it, k));
-        }
+    wave_chunk_each<DT, VP>(rowp, c, V, f);
+  }
+
+  // f(key) for every candidate (each round of the selection).
+  template <typename F>
+  __device__ __forceinline__ void each(F f) const {
+    const int tid = threadIdx.x, w = tid / kWave;
+    if (lds) {
+      for (int i = tid; i < n; i += kSelThreads) f(sh->key[i]);
+      return;
     }
+    for (int c = w; c < nc; c += kSelWaves)
+      chunk(c, [&](float v) {
+        if (v > kNegInf && in_range(row_bin(v), rlo, rhi)) f(fkey(v));
+      });
   }
 };
 
@@ -435,10 +324,10 @@ struct KeySpan {
 };
 
 template <typename Src>
-__device__ KeySpan key_span(const Src src, SelShared& sh) {
+__device__ __forceinline__ KeySpan key_span(const Src& src, SelShared& sh) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   int lo = INT_MAX, hi = INT_MIN;  // keys as order-preserving signed ints
-  src.each([&](unsigned key, int) {
+  src.each([&](unsigned key) {
     const int s = (int)(key ^ 0x80000000u);
     lo = min(lo, s);
     hi = max(hi, s);
@@ -450,7 +339,7 @@ __device__ KeySpan key_span(const Src src, SelShared& sh) {
     sh.iscr[1][w] = hi;
   }
   __syncthreads();
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < kSelWaves; ++i) {
     lo = min(lo, sh.iscr[0][i]);
     hi = max(hi, sh.iscr[1][i]);
   }
@@ -464,7 +353,8 @@ __device__ KeySpan key_span(const Src src, SelShared& sh) {
 
 // Key of the kth largest candidate (1-based; kth <= the candidate count).
 template <typename Src>
-__device__ unsigned select_kth(const Src src, SelShared& sh, KeySpan ks, int kth) {
+__device__ __forceinline__ unsigned select_kth(const Src& src, SelShared& sh, KeySpan ks,
+                                             int kth) {
   const int tid = threadIdx.x;
   unsigned prefix = ks.prefix;
   float need = (float)kth;
@@ -472,9 +362,9 @@ __device__ unsigned select_kth(const Src src, SelShared& sh, KeySpan ks, int kth
     const int wd = min(8, rem);
     rem -= wd;
     const unsigned mask = (rem + wd >= 32) ? 0u : (~0u << (rem + wd));  // bits above
-    sh.cnt[tid] = 0;
+    if (tid < 256) sh.cnt[tid] = 0;
     __syncthreads();
-    src.each([&](unsigned key, int) {
+    src.each([&](unsigned key) {
       if ((key & mask) == prefix)
         atomicAdd(&sh.cnt[(key >> rem) & ((1u << wd) - 1)], 1u);
     });
@@ -492,8 +382,8 @@ __device__ unsigned select_kth(const Src src, SelShared& sh, KeySpan ks, int kth
 // at least t of probability; the smallest candidate key >= kmin when rounding
 // leaves the candidates short of t.
 template <typename Src>
-__device__ unsigned select_mass(const Src src, SelShared& sh, KeySpan ks, float t,
-                                unsigned kmin, float m, float kk) {
+__device__ __forceinline__ unsigned select_mass(const Src& src, SelShared& sh, KeySpan ks,
+                                              float t, unsigned kmin, float m, float kk) {
   const int tid = threadIdx.x;
   unsigned prefix = ks.prefix;
   bool found = true;
@@ -501,9 +391,9 @@ __device__ unsigned select_mass(const Src src, SelShared& sh, KeySpan ks, float 
     const int wd = min(8, rem);
     rem -= wd;
     const unsigned mask = (rem + wd >= 32) ? 0u : (~0u << (rem + wd));
-    sh.mass[tid] = 0.0f;
+    if (tid < 256) sh.mass[tid] = 0.0f;
     __syncthreads();
-    src.each([&](unsigned key, int) {
+    src.each([&](unsigned key) {
       if (key >= kmin && (key & mask) == prefix)
         atomicAdd(&sh.mass[(key >> rem) & ((1u << wd) - 1)],
                   fast_exp2((fkey_inv(key) - m) * kk));
@@ -521,95 +411,296 @@ __device__ unsigned select_mass(const Src src, SelShared& sh, KeySpan ks, float 
   if (found) return prefix;
   if (tid == 0) sh.minkey = 0xffffffffu;
   __syncthreads();
-  src.each([&](unsigned key, int) {
+  src.each([&](unsigned key) {
     if (key >= kmin) atomicMin(&sh.minkey, key);
   });
   __syncthreads();
   return sh.minkey;
 }
 
+// ---------------------------------------------------------------------------
+// select: one workgroup per row (rows that are not truncated leave at once).
+// ---------------------------------------------------------------------------
 template <int DT, bool VP>
-__global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
+__global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  // One workgroup per listed row; workgroups past the list's end leave at
-  // once (they hold this kernel's large LDS block only for one load).
-  const int64_t row = listed_row(a, blockIdx.x);
-  if (row < 0) return;
+  // Blocks take rows j-major (block x: sequence x mod B, row x div B): the
+  // rows every sequence needs (row 0) are then consecutive blocks, which
+  // the dispatcher spreads over all XCDs, rather than every (K+1)-th block.
+  const int bx = blockIdx.x;
+  const int64_t row = (int64_t)(bx % a.B) * (a.K + 1) + bx / a.B;
   const int nc = a.nchunks;
-  const i32x4 p0 = a.plan[row * 2], p1 = a.plan[row * 2 + 1];
-  int cc = 0;
-  float tb = 0.0f;
+  const int64_t h0 = row * nc;
+  // The chunk headers, partials and above-band weights are requested
+  // together with the row's parameters (they are in bounds for every row;
+  // an inactive row's are never used).
+  i32x4 hh = i32x4{0, 0, 0, 0};
   f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ab = 0.0f;
   if (tid < nc) {
-    cc = a.ccount[row * nc + tid];
-    tb = a.tpart[row * nc + tid];
-    pv = a.partials[row * nc + tid];
+    hh = a.hhdr[h0 + tid];
+    pv = a.partials[h0 + tid];
+    ab = a.tpart[h0 + tid];
   }
-  const int b = (int)(row / (a.K + 1));
-  const float kk = kLog2e / a.temperature[b];
-  const int mode = p1.x, krem = p1.y;
-  const float m = __int_as_float(p1.z);
-  for (int c = tid + kThreads; c < nc; c += kThreads) tb += a.tpart[row * nc + c];
-  // Probability above the range: every token there is kept.
-  const float base = block_sum(tb, sh.scratch);
-  if (mode == 0) {
-    if (tid == 0) a.tinfo[row] = f32x4{kNegInf, base, 1.0f, 0.0f};
-    return;
+  const RowCtx rc = row_ctx(a, row);
+  if (!rc.active) return;
+  const float kk = rc.kk;
+  if (tid < nc) {
+    sh.ca[tid] = hh.x;
+    sh.cnf[tid] = hh.y;
+    sh.cband[tid] = hh.z;
+    sh.cn[tid] = hh.w;
+    sh.cpm[tid] = pv.x;
+    sh.cps[tid] = pv.y;
+    sh.cab[tid] = ab;
   }
-  // Exclusive prefix of the chunks' candidate counts (nc <= kThreads here;
-  // more chunks than threads, or an overflowing segment, take the re-scan).
-  const bool over = nc > kThreads || cc > a.segcap;
-  const int inc = (int)wave_inclusive_sum((float)cc);
-  if (l == kWave - 1) sh.iscr[0][w] = inc;
+  if (tid < 3) sh.first[tid] = kRestBin;
+  if (tid == 0) {
+    sh.cabove_n = 0;
+    sh.ncand = 0;
+    sh.over = 0;
+  }
   __syncthreads();
-  int wb = 0, tot = 0;
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) wb += sh.iscr[0][i];
-    tot += sh.iscr[0][i];
+  // Row max m, finite count N and weight Z (relative to m): every wavefront
+  // reduces the chunk values itself, in the same order.
+  float m = kNegInf;
+  for (int c = l; c < nc; c += kWave) m = fmaxf(m, sh.cpm[c]);
+  m = wave_max(m);
+  float tn = 0.0f, tz = 0.0f;
+  for (int c = l; c < nc; c += kWave) {
+    tn += (float)sh.cnf[c];
+    tz += sh.cps[c] * fast_exp2((sh.cpm[c] - m) * kk);
   }
-  if (tid < nc) sh.pre[tid] = wb + inc - cc;
-  if (tid == 0) sh.pre[nc < kThreads ? nc : kThreads] = tot;
-  const int anyover = __syncthreads_or(over);
-  const bool lds = !anyover && tot <= kCandCap;
-  const int n = tot;
-  if (lds) {
-    // Entry f of the list lies in chunk c with pre[c] <= f < pre[c+1].
-    const int2* seg = a.cand + row * nc * a.segcap;
-    constexpr int kU = 16;  // loads in flight per thread: 4,096 candidates in one round trip
-    for (int f0 = 0; f0 < n; f0 += kU * kThreads) {
-      int2 ev[kU];
-      int ch[kU];
+  const float N = wave_sum(tn);  // exact: < 2^24
+  const float Z = wave_sum(tz);
+  const float ns = bin_scale(kk);
+  const int a0 = abs_bin_s(m, ns);
+  // Merge: bin r of the row is bin r - (a_c - a0) of chunk c. Thread (g, r)
+  // adds the chunks c = g (mod kPlanGroups), kPlanBatch words requested at
+  // once; the groups' sums are added in group order.
+  {
+    const int r = tid % kHistBins, g = tid / kHistBins;
+    float cnt = 0.0f, mass = 0.0f;
+    for (int c0 = g; c0 < nc; c0 += kPlanGroups * kPlanBatch) {
+      unsigned long long wb[kPlanBatch];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int f = f0 + u * kThreads + tid;
-        ev[u] = int2{0, 0};
-        ch[u] = 0;
-        if (f < n) {
-          int lo = 0, hi = nc - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sh.pre[mid] <= f) lo = mid;
-            else hi = mid - 1;
-          }
-          ch[u] = lo;
-          ev[u] = seg[(int64_t)lo * a.segcap + (f - sh.pre[lo])];
+      for (int u = 0; u < kPlanBatch; ++u) {
+        const int c = c0 + u * kPlanGroups;
+        wb[u] = 0;
+        if (c < nc) {
+          const int jb = r - (sh.ca[c] - a0);
+          if (jb >= 0 && jb < kHistBins) wb[u] = a.hist[(h0 + c) * kHistBins + jb];
         }
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int f = f0 + u * kThreads + tid;
-        if (f < n) {
-          sh.key[f] = fkey(__int_as_float(ev[u].x));
-          sh.chunk[f] = (unsigned char)ch[u];
+      for (int u = 0; u < kPlanBatch; ++u) {
+        const int c = c0 + u * kPlanGroups;
+        if (c < nc) {
+          const float sc = fast_exp2((sh.cpm[c] - m) * kk) * (1.0f / kFixScale);
+          cnt += (float)(unsigned)(wb[u] >> 48);
+          mass += (float)(wb[u] & kMassMask) * sc;
         }
       }
     }
+    sh.pc[g][r] = cnt;
+    sh.pw[g][r] = mass;
   }
-  for (int c = tid; c < nc; c += kThreads) sh.csum[c] = 0.0f;
   __syncthreads();
-  const CandSource<DT, VP> src{a.logits + row * a.V * Dt<DT>::kBytes, a.V, nc, &sh,
-                               n, p0.x, p0.y, p0.z, kk, lds};
+  // Thread r < 256 owns row bin r: inclusive scans of counts (C) and
+  // weights (M) from the top bin down.
+  const bool binT = tid < kHistBins;
+  float C = 0.0f, M = 0.0f;
+  if (binT) {
+    for (int g = 0; g < kPlanGroups; ++g) {
+      C += sh.pc[g][tid];
+      M += sh.pw[g][tid];
+    }
+    C = wave_inclusive_sum(C);
+    M = wave_inclusive_sum(M);
+    if (l == kWave - 1) {
+      sh.wtot[0][w] = C;
+      sh.wtot[1][w] = M;
+    }
+  }
+  __syncthreads();
+  if (binT) {
+    for (int i = 0; i < w; ++i) {
+      C += sh.wtot[0][i];
+      M += sh.wtot[1][i];
+    }
+  }
+  const int k = a.top_k ? a.top_k[rc.b] : 0;
+  const float tp = a.top_p ? a.top_p[rc.b] : 1.0f;
+  const bool kA = k >= 1 && k < a.V && (float)k <= N;
+  const bool pA = tp < 1.0f;
+  // C and M do not decrease with the bin, so the first bin meeting a target
+  // is the first set lane of the first wavefront whose ballot is not empty
+  // (one LDS atomic per wavefront).
+  if (binT) {
+    const unsigned long long kb = __ballot(kA && C >= (float)k);
+    if (l == 0 && kb) atomicMin(&sh.first[0], w * kWave + __ffsll((unsigned long long)kb) - 1);
+  }
+  if (tid == 0) {
+    sh.zval[0] = 0.0f;
+    sh.zval[1] = Z;
+  }
+  __syncthreads();
+  const int bk = kA ? sh.first[0] : kRestBin;
+  // Weight above bin bk (Z_lo) and through it (Z_hi): top-p's share is taken
+  // of what top-k kept, which lies between the two.
+  if (kA && binT) {
+    if (tid == bk - 1) sh.zval[0] = M;
+    if (tid == bk) sh.zval[1] = M;
+  } else if (tid == 0) {
+    sh.zval[0] = Z;
+  }
+  __syncthreads();
+  if (pA && binT) {
+    const float tlo = tp * sh.zval[0] * (1.0f - kPlanMargin);
+    const float thi = tp * sh.zval[1] * (1.0f + kPlanMargin);
+    const unsigned long long lo = __ballot(M >= tlo), hi = __ballot(M >= thi);
+    if (l == 0 && lo) atomicMin(&sh.first[1], w * kWave + __ffsll((unsigned long long)lo) - 1);
+    if (l == 0 && hi) atomicMin(&sh.first[2], w * kWave + __ffsll((unsigned long long)hi) - 1);
+  }
+  __syncthreads();
+  const int mode = (kA ? 1 : 0) | (pA ? 2 : 0);
+  if (mode == 0) {
+    // Nothing is dropped (k at least the finite count, no top-p).
+    if (tid < nc) a.tpart[h0 + tid] = sh.cps[tid] * fast_exp2((sh.cpm[tid] - m) * kk);
+    if (tid == 0) a.tinfo[row] = f32x4{kNegInf, Z, 1.0f, 0.0f};
+    return;
+  }
+  // Candidate range [rlo, rhi]. Top-k's own bin is always in it (the k-th
+  // largest logit, and the share top-k keeps, are found among its tokens);
+  // top-p's threshold lies between the bins its two targets reach.
+  int rlo, rhi;
+  if (!pA) {
+    rlo = rhi = bk;
+  } else if (!kA) {
+    rlo = sh.first[1];
+    rhi = sh.first[2];
+  } else {
+    rlo = min(sh.first[1], bk);
+    rhi = bk;
+  }
+  // Tokens above the range: the running count at bin rlo - 1.
+  if (rlo >= 1 && rlo <= kRestBin && tid == rlo - 1) sh.cabove_n = (int)C;
+  __syncthreads();
+  const int krem = k - sh.cabove_n;
+  RowSrc<DT, VP> src{a.logits + row * a.V * Dt<DT>::kBytes,
+                     a.cand + h0 * a.segcap,
+                     a.V, nc, a.segcap, a0, rlo, rhi, m, kk, ns, &sh, false, 0};
+  using Src = RowSrc<DT, VP>;
+  // Chunks whose band misses the range, listed in chunk order (nc <= 256:
+  // the first four wavefronts).
+  {
+    const bool miss = tid < nc && src.source(tid) == Src::kReread;
+    const unsigned long long mb = __ballot(miss);
+    if (l == 0 && w < kHistBins / kWave) sh.iscr[1][w] = __popcll(mb);
+    __syncthreads();
+    int at = 0;
+    for (int i = 0; i < w && i < kHistBins / kWave; ++i) at += sh.iscr[1][i];
+    if (miss) sh.miss[at + lanes_below(mb)] = tid;
+  }
+  int nmiss = 0;
+  for (int i = 0; i < kHistBins / kWave; ++i) nmiss += sh.iscr[1][i];
+  __syncthreads();
+  // Each chunk's candidates, as one run of keys in LDS (its place taken with
+  // one LDS atomic; within the run, in the order met), and its weight above
+  // the range: from its band (a wavefront per chunk), or by the whole
+  // workgroup re-reading it. Runs that would pass kCandCap are not stored
+  // (the selection then walks the chunks in each round).
+  auto above_w = [&](float v) {
+    return band_t(v, ns) < (float)(a0 + rlo) ? fast_exp2((v - m) * kk) : 0.0f;
+  };
+  auto is_cand = [&](float v) { return v > kNegInf && in_range(src.row_bin(v), rlo, rhi); };
+  auto put = [&](float v, int& pos) {
+    const bool in = is_cand(v);
+    const unsigned long long hit = __ballot(in);
+    if (in) sh.key[pos + lanes_below(hit)] = fkey(v);
+    pos += __popcll(hit);
+  };
+  for (int c = w; c < nc; c += kSelWaves) {
+    const int sk = src.source(c);
+    if (sk == Src::kReread) continue;
+    float above = 0.0f;
+    int cnt = 0, at = 0;  // wavefront-uniform
+    if (sk == Src::kBand) {
+      float r[Src::kU];
+      const int nu = src.band_load(c, r);
+#pragma unroll
+      for (int u = 0; u < Src::kU; ++u)
+        if (u < nu) {
+          above += above_w(r[u]);
+          cnt += __popcll(__ballot(is_cand(r[u])));
+        }
+      if (l == 0) at = atomicAdd(&sh.ncand, cnt);
+      at = __builtin_amdgcn_readfirstlane(at);
+      if (at + cnt <= kCandCap) {
+        int pos = at;
+#pragma unroll
+        for (int u = 0; u < Src::kU; ++u)
+          if (u < nu) put(r[u], pos);
+      } else if (l == 0) {
+        sh.over = 1;
+      }
+      above = wave_sum(above) + sh.cab[c] * fast_exp2((sh.cpm[c] - m) * kk);
+    }
+    if (l == 0) {
+      sh.ccnt[c] = cnt;
+      sh.cbeg[c] = at;
+      sh.cabove[c] = above;
+    }
+  }
+  for (int i = 0; i < nmiss; ++i) {
+    const int c = sh.miss[i];
+    float v[kBlkElems<DT>];
+    block_chunk_load<DT, VP>(src.rowp, c, a.V, v);
+    float above = 0.0f;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kBlkElems<DT>; ++e) {
+      above += above_w(v[e]);
+      cnt += __popcll(__ballot(is_cand(v[e])));
+    }
+    above = wave_sum(above);
+    __syncthreads();  // the previous chunk's wcnt / scratch / mbase are read
+    if (l == 0) {
+      sh.wcnt[w] = cnt;
+      sh.scratch[w] = above;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int ct = 0;
+      float ab = 0.0f;
+      for (int q = 0; q < kSelWaves; ++q) {
+        ct += sh.wcnt[q];
+        ab += sh.scratch[q];
+      }
+      const int at = atomicAdd(&sh.ncand, ct);
+      if (at + ct > kCandCap) sh.over = 1;
+      sh.mbase = at;
+      sh.ccnt[c] = ct;
+      sh.cbeg[c] = at;
+      sh.cabove[c] = ab;
+    }
+    __syncthreads();
+    if (sh.mbase + sh.ccnt[c] <= kCandCap) {
+      int pos = sh.mbase;
+      for (int q = 0; q < w; ++q) pos += sh.wcnt[q];
+#pragma unroll
+      for (int e = 0; e < kBlkElems<DT>; ++e) put(v[e], pos);
+    }
+  }
+  __syncthreads();
+  src.n = sh.ncand;
+  src.lds = sh.over == 0;
+  // Weight above the range: every token there is kept.
+  float base = 0.0f;
+  for (int c = l; c < nc; c += kWave) base += sh.cabove[c];
+  base = wave_sum(base);
+  __syncthreads();
   const KeySpan ks = key_span(src, sh);
   unsigned kmin = 0;
   if (mode & 1) kmin = select_kth(src, sh, ks, krem);
@@ -617,22 +708,16 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
   if (mode & 2) {
     // top-p's share is of what top-k kept: with top-k, base plus the
     // candidates at or above kmin (everything below the range is below the
-    // k-th largest); without, the whole row (from the stream partials).
-    float zk = 0.0f;
+    // k-th largest); without, the whole row.
+    float zk = Z;
     if (mode & 1) {
-      src.each([&](unsigned k2, int) {
-        if (k2 >= kmin) zk += fast_exp2((fkey_inv(k2) - m) * kk);
+      float zc = 0.0f;
+      src.each([&](unsigned k2) {
+        if (k2 >= kmin) zc += fast_exp2((fkey_inv(k2) - m) * kk);
       });
-      zk = base + block_sum(zk, sh.scratch);
-    } else {
-      zk = (tid < nc) ? pv.y * fast_exp2((pv.x - m) * kk) : 0.0f;
-      for (int c = tid + kThreads; c < nc; c += kThreads) {
-        const f32x4 p = a.partials[row * nc + c];
-        zk += p.y * fast_exp2((p.x - m) * kk);
-      }
-      zk = block_sum(zk, sh.scratch);
+      zk = base + block_sum(zc, sh.scratch);
     }
-    const float t = a.top_p[b] * zk - base;
+    const float t = tp * zk - base;
     if (t > 0.0f) {
       key = select_mass(src, sh, ks, t, kmin, m, kk);
     } else {
@@ -640,61 +725,45 @@ __global__ __launch_bounds__(kThreads) void trunc_select_kernel(Args a) {
       // it stays below top_p); keep the top candidate group if it does.
       if (tid == 0) sh.minkey = 0;
       __syncthreads();
-      src.each([&](unsigned k2, int) { atomicMax(&sh.minkey, k2); });
+      src.each([&](unsigned k2) { atomicMax(&sh.minkey, k2); });
       __syncthreads();
       key = sh.minkey;
     }
   }
-  // Kept candidates: their probability, per chunk. In LDS the list is grouped
-  // by chunk: each thread sums a contiguous run and adds it to its chunk when
-  // the chunk changes. The re-scan adds token by token.
-  if (lds) {
-    const int per = (n + kThreads - 1) / kThreads;
-    const int f0 = tid * per, f1 = min(n, f0 + per);
-    int cur = -1;
-    float run = 0.0f;
-    for (int f = f0; f < f1; ++f) {
-      const int ch = sh.chunk[f];
-      if (ch != cur) {
-        if (cur >= 0 && run != 0.0f) atomicAdd(&sh.csum[cur], run);
-        cur = ch;
-        run = 0.0f;
+  // Kept weight per chunk: above the range, plus its candidates at or above
+  // the threshold (a wavefront per chunk, a fixed order).
+  for (int c = w; c < nc; c += kSelWaves) {
+    float kept = 0.0f;
+    if (src.lds) {
+      for (int f = sh.cbeg[c] + l; f < sh.cbeg[c] + sh.ccnt[c]; f += kWave) {
+        const unsigned k2 = sh.key[f];
+        if (k2 >= key) kept += fast_exp2((fkey_inv(k2) - m) * kk);
       }
-      const unsigned k2 = sh.key[f];
-      if (k2 >= key) run += fast_exp2((fkey_inv(k2) - m) * kk);
+    } else {
+      src.chunk(c, [&](float v) {
+        if (is_cand(v) && fkey(v) >= key) kept += fast_exp2((v - m) * kk);
+      });
     }
-    if (cur >= 0 && run != 0.0f) atomicAdd(&sh.csum[cur], run);
-  } else {
-    src.each([&](unsigned k2, int i) {
-      if (k2 >= key) atomicAdd(&sh.csum[i / kChunk<DT>], fast_exp2((fkey_inv(k2) - m) * kk));
-    });
+    kept = wave_sum(kept) + sh.cabove[c];
+    if (l == 0) {
+      a.tpart[h0 + c] = kept;
+      sh.ckept[c] = kept;
+    }
   }
   __syncthreads();
-  float kept = 0.0f;
-  for (int c = tid; c < nc; c += kThreads) {
-    const float t = a.tpart[row * nc + c] + sh.csum[c];
-    a.tpart[row * nc + c] = t;
-    kept += t;
+  if (w == 0) {
+    float tot = 0.0f;
+    for (int c = l; c < nc; c += kWave) tot += sh.ckept[c];
+    tot = wave_sum(tot);
+    if (l == 0) a.tinfo[row] = f32x4{fkey_inv(key), tot, 1.0f, 0.0f};
   }
-  kept = block_sum(kept, sh.scratch);
-  if (tid == 0) a.tinfo[row] = f32x4{fkey_inv(key), kept, 1.0f, 0.0f};
 }
 
 template <int DT, bool VP>
 int launch_t(const Args& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * (a.K + 1);
-  hipLaunchKernelGGL(trunc_plan_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, a);
-  int rc = check_launch("truncation plan");
-  if (rc != SS_OK) return rc;
-  // Enough workgroups to fill the chip several times over; each takes the
-  // items of the listed rows in turn.
-  const int64_t grid = std::min<int64_t>(rows * a.nchunks, kExtractGrid);
-  hipLaunchKernelGGL((trunc_extract_kernel<DT, VP>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, s, a);
-  rc = check_launch("truncation extract");
-  if (rc != SS_OK) return rc;
   hipLaunchKernelGGL((trunc_select_kernel<DT, VP>), dim3((unsigned)rows),
-                     dim3(kThreads), 0, s, a);
+                     dim3(kSelThreads), 0, s, a);
   return check_launch("truncation select");
 }
 

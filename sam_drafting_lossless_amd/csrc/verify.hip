@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
 struct WsLayout {
   size_t partials, seqinfo, seqinfo2, rpart;
   // truncation (top-k / top-p) regions; zero-sized without it
-  size_t hist, hhdr, plan, ccount, tlist, cand, tpart, tinfo;
+  size_t hist, hhdr, cand, tpart, tinfo;
   size_t total;
 };
 
@@ -489,10 +489,7 @@ WsLayout ws_layout(int B, int K, int V, bool trunc) {
   const size_t t = trunc ? 1 : 0;
   take(L.hist, t * rows * nc * kHistBins * sizeof(unsigned long long));
   take(L.hhdr, t * rows * nc * sizeof(i32x4));
-  take(L.plan, t * rows * 2 * sizeof(i32x4));
-  take(L.ccount, t * rows * nc * sizeof(int));
-  take(L.tlist, t * (rows + 1) * sizeof(int));
-  take(L.cand, t * rows * nc * std::min(kSegCap, V) * sizeof(int2));
+  take(L.cand, t * rows * nc * std::min(kSegCap, V) * sizeof(float));
   take(L.tpart, t * rows * nc * sizeof(float));
   take(L.tinfo, t * rows * sizeof(f32x4));
   L.total = o;
@@ -595,11 +592,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
   a.hist = trunc ? reinterpret_cast<unsigned long long*>(ws + L.hist) : nullptr;
   a.hhdr = trunc ? reinterpret_cast<i32x4*>(ws + L.hhdr) : nullptr;
-  a.plan = trunc ? reinterpret_cast<i32x4*>(ws + L.plan) : nullptr;
-  a.ccount = trunc ? reinterpret_cast<int*>(ws + L.ccount) : nullptr;
-  a.tlist = trunc ? reinterpret_cast<int*>(ws + L.tlist) : nullptr;
-  a.tcount = trunc ? a.tlist + (size_t)B * (K + 1) : nullptr;
-  a.cand = trunc ? reinterpret_cast<int2*>(ws + L.cand) : nullptr;
+  a.cand = trunc ? reinterpret_cast<float*>(ws + L.cand) : nullptr;
   a.segcap = std::min(kSegCap, V);
   a.tpart = trunc ? reinterpret_cast<float*>(ws + L.tpart) : nullptr;
   a.tinfo = trunc ? reinterpret_cast<f32x4*>(ws + L.tinfo) : nullptr;

@@ -30,11 +30,17 @@ constexpr float kNegInf = -INFINITY;
 //   One bin is a 64-bit word: count in bits 48..63, mass in bits 0..47. Logits
 //   below the window are not binned; the chunk's header holds its finite
 //   count, and its total mass is the stream partial's sum.
+//   Band: the window bins [lo, hi] whose logits a chunk copies to its
+//   candidate segment (at most kSegCap of them), chosen from the chunk's own
+//   histogram; hi = kRestBin takes every bin from lo down, past the window
+//   too.
 constexpr int kHistBins = 256;
 constexpr int kBinsPerOctave = 8;
 constexpr int kRestBin = kHistBins;  // "beyond the window"
 constexpr int kCandCap = 8192;       // candidates per row held in LDS
-constexpr int kSegCap = 512;         // candidates per (row, chunk) segment
+constexpr int kSegCap = 1024;        // logits per (row, chunk) segment
+constexpr int kBandHalf = 4;         // top-p band: bins either side of the estimate
+constexpr int kNoBand = 1;           // packed band (lo = 1, hi = 0): none
 constexpr float kFixScale = 2147483648.0f;  // 2^31
 constexpr unsigned long long kCountOne = 1ull << 48;
 constexpr unsigned long long kMassMask = kCountOne - 1;
@@ -168,15 +174,13 @@ struct Args {
   // Truncation workspace (NULL unless top_k or top_p is given), per row
   // (b*(K+1) + j) and per (row, chunk):
   unsigned long long* hist;  // [rows*nchunks*kHistBins] window histograms
-  i32x4* hhdr;      // [rows*nchunks]: (window start bin, finite count, 0, 0)
-  i32x4* plan;      // [rows*2]: (row start bin, r_lo, r_hi, count above),
-                    //           (active, 0, 0, 0)
-  int* ccount;      // [rows*nchunks] candidates each chunk found
-  int* tlist;       // [rows] truncated rows, in the order the plan found them
-  int* tcount;      // [1] their number (cleared by the stream pass)
-  int2* cand;       // [rows*nchunks*segcap] (logit bits, token) per chunk
-  int segcap;       // candidates a chunk's segment holds: min(kSegCap, V)
-  float* tpart;     // [rows*nchunks] kept mass per chunk (relative to row max)
+  i32x4* hhdr;      // [rows*nchunks]: (window start bin, finite count,
+                    //   band lo | hi << 16, logits in the band's segment)
+  float* cand;      // [rows*nchunks*segcap] the band's logits per chunk
+  int segcap;       // logits a chunk's segment holds: min(kSegCap, V)
+  float* tpart;     // [rows*nchunks] the stream pass: weight above the band
+                    //   (relative to the chunk max); the selection: kept
+                    //   weight per chunk (relative to the row max)
   f32x4* tinfo;     // [rows]: (threshold logit, kept mass, active, 0)
   // Fused automaton step (sam == nullptr when only verifying).
   unsigned char* sam;
@@ -214,14 +218,22 @@ __device__ __forceinline__ bool trunc_active(const Args& a, int b, float T) {
   return (k >= 1 && k < a.V) || p < 1.0f;
 }
 
-// Histogram bin of a finite logit on the row's absolute grid (see kHistBins).
-// Every kernel computes it with these same operations, so a token's bin is
-// the same wherever it is computed.
-__device__ __forceinline__ int abs_bin(float l, float kk) {
-  float t = -l * kk * (float)kBinsPerOctave;
-  t = fminf(fmaxf(t, -1.0e9f), 1.0e9f);
-  return (int)floorf(t);
+// Histogram bin of a finite logit on the row's absolute grid (see kHistBins):
+// floor(l * ns), ns = -log2e/T * kBinsPerOctave (bin_scale), the product
+// clamped to +-1e9 before the floor. Every kernel computes it with these
+// same operations, so a token's bin is the same wherever it is computed.
+// Since floor(t) >= n exactly when t >= n for an integer n, and the clamp
+// does not change that comparison for |n| < 1e9, a bin range [n0, n1] holds
+// exactly the tokens whose product l * ns lies in [n0, n1 + 1) (so -inf,
+// whose product is +inf, and NaN fall in no finite range).
+__device__ __forceinline__ float bin_scale(float kk) { return -kk * (float)kBinsPerOctave; }
+__device__ __forceinline__ float band_t(float l, float ns) {
+  return __builtin_amdgcn_fmed3f(l * ns, -1.0e9f, 1.0e9f);
 }
+__device__ __forceinline__ int abs_bin_s(float l, float ns) {
+  return (int)floorf(band_t(l, ns));
+}
+__device__ __forceinline__ int abs_bin(float l, float kk) { return abs_bin_s(l, bin_scale(kk)); }
 
 // Order-preserving key of a float (larger float, larger key; -0 as +0).
 __device__ __forceinline__ unsigned fkey(float l) {
@@ -283,8 +295,8 @@ int launch_stream(Args a, bool f32, bool vp, hipStream_t s);
 int launch_tree_finalize(const Args& a, bool f32, bool vp, const int32_t* tokens,
                          const int32_t* parent, int32_t* out_nodes, hipStream_t s);
 
-// Launches the truncation passes (trunc.hip) after the stream pass: plan,
-// candidate extraction and threshold selection for every truncated row.
+// Launches the truncation selection (trunc.hip) after the stream pass: the
+// threshold and the kept weight per chunk of every truncated row.
 int launch_truncation(const Args& a, bool f32, bool vp, hipStream_t s);
 
 }  // namespace specsam

@@ -53,9 +53,9 @@ def test_library_loads_and_answers_size_queries():
     ex = L.ss_verify_workspace_bytes_ex
     ex.restype = ctypes.c_size_t
     assert ex(256, 3, 151936, 0) == L.ss_verify_workspace_bytes(256, 3, 151936)
-    # truncation: per row chunk a 2 KiB histogram and 512 candidates
+    # truncation: per row chunk a 2 KiB histogram and a 1,024-logit segment
     rows = 256 * 4
-    assert ex(256, 3, 151936, 1) > ex(256, 3, 151936, 0) + rows * 19 * (2048 + 512 * 8)
+    assert ex(256, 3, 151936, 1) > ex(256, 3, 151936, 0) + rows * 19 * (2048 + 1024 * 4)
     assert ex(256, 3, 151936, 2) == 0  # unknown flag
     assert L.sam_state_bytes(4, 1000) % 256 == 0
     assert L.sam_state_bytes(0, 1000) == 0

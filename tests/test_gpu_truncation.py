@@ -168,9 +168,10 @@ def test_chi_square_follows_truncated_target(mode):
 
 @pytest.mark.parametrize("case", ["crowded_top_p", "crowded_top_k", "beyond_window"])
 def test_rows_beyond_the_candidate_list(case):
-    """Rows whose threshold bin range holds more than 4096 tokens (logits
-    crowded into one bin), or lies past the 32-octave window (low T, large
-    k), take the exact row-scan path."""
+    """Rows whose threshold bin range holds more than 8,192 tokens (logits
+    crowded into one or two bins: no band fits a segment, every chunk is
+    re-read, and the candidates are walked again in each selection round),
+    or lies past the 32-octave window (low T, large k)."""
     say(f"[gpu] truncation: {case}")
     rng = np.random.default_rng({"crowded_top_p": 61, "crowded_top_k": 62,
                                  "beyond_window": 63}[case])
@@ -181,18 +182,18 @@ def test_rows_beyond_the_candidate_list(case):
         top_k = np.full(B, 5000, np.int32)
         top_p = None
     else:
-        # 6,000 tokens within 0.02 of each other (one or two bins), the rest
-        # far below: each crowded token carries ~1/6000 of the mass, so a
+        # 9,000 tokens within 0.02 of each other (one or two bins), the rest
+        # far below: each crowded token carries ~1/9000 of the mass, so a
         # top-p decision rarely lands within 1e-5 of flipping.
         x = np.full((B, K + 1, V), -30.0, np.float32)
-        x[:, :, :6000] = rng.uniform(0.0, 0.02, (B, K + 1, 6000))
+        x[:, :, :9000] = rng.uniform(0.0, 0.02, (B, K + 1, 9000))
         x = np.ascontiguousarray(np.take_along_axis(
             x, rng.permuted(np.tile(np.arange(V), (B, K + 1, 1)), axis=2), axis=2))
         T = np.full(B, 1.0, np.float32)
         if case == "crowded_top_p":
             top_k, top_p = None, np.full(B, 0.5, np.float32)
         else:
-            top_k, top_p = np.full(B, 3000, np.int32), None
+            top_k, top_p = np.full(B, 4500, np.int32), None
     draft = rng.integers(0, V, (B, K)).astype(np.int32)
     dl = np.full(B, K, np.int32)
     u = rng.random((B, K + 1)).astype(np.float32)
@@ -204,16 +205,17 @@ def test_rows_beyond_the_candidate_list(case):
     tally.check()
 
 
-@pytest.mark.parametrize("case,n_tied", [("spread", 512), ("one_wavefront", 512),
-                                         ("one_wavefront", 513)])
+@pytest.mark.parametrize("case,n_tied", [("spread", 1024), ("one_wavefront", 1024),
+                                         ("one_wavefront", 1025)])
 def test_chunk_segment_capacity(case, n_tied):
-    """A chunk's candidates fill its 512-entry segment exactly (kept in the
-    candidate list) or overflow it by one (the row is selected by
-    re-scanning it): n_tied tokens share the top-k cut's logit in the first
-    fp32 chunk (8,192 tokens), either spread over it or all in the part one
-    wavefront reads (thread (e // 4) % 256 holds element e), ten tokens lie
-    above the cut in the second chunk and the rest far below. Ties at the cut
-    are kept, so the oracle's set is unique."""
+    """A chunk's band fills its 1,024-logit segment exactly (the selection
+    takes its candidates from the segment) or would overflow it by one (the
+    chunk keeps no band and the selection re-reads it): n_tied tokens share
+    the top-k cut's logit in the first fp32 chunk (8,192 tokens), either
+    spread over it or all in the part one wavefront reads (thread (e // 4) %
+    256 holds element e), ten tokens lie above the cut in the second chunk
+    and the rest far below. Ties at the cut are kept, so the oracle's set is
+    unique."""
     say(f"[gpu] truncation: segment capacity {case} {n_tied}")
     rng = np.random.default_rng(71 + n_tied + (case == "spread"))
     B, K, V = 8, 2, 20000
@@ -243,6 +245,45 @@ def test_chunk_segment_capacity(case, n_tied):
     r = oracle.verify(x, draft, dl, T, u, nthreads=8, top_k=top_k)
     tally = Tally()
     assert _compare(g, r, T, u, f"segment {case} {n_tied}", tally) == 0
+    tally.check()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_band_missing_the_row_range(dtype):
+    """Chunks whose own top_p point lies far from the row's threshold: the
+    first chunk holds N(0, 1.5^2) logits, the second 4,000 tokens in [3, 3.5]
+    that carry most of the row's probability (the rest far below), so the
+    row's top-p threshold (top_p = 0.9) falls near the first chunk's median
+    of probability, some 20 bins above the band that chunk chose around its
+    own 0.9 point, and below every token of the second chunk's band. The
+    selection re-reads both chunks."""
+    say(f"[gpu] truncation: band missing the range {dtype}")
+    rng = np.random.default_rng(81 + (dtype == "bf16"))
+    B, K = 8, 2
+    R, V = K + 1, 3 * 16384
+    x = np.full((B, R, V), -30.0, np.float32)
+    c0 = 16384 if dtype == "bf16" else 8192  # tokens per chunk
+    x[:, :, :c0] = rng.standard_normal((B, R, c0)) * 1.5
+    for b in range(B):
+        for j in range(R):
+            x[b, j, c0 + rng.choice(c0, 4000, replace=False)] = rng.uniform(3.0, 3.5, 4000)
+    draft = rng.integers(0, V, (B, K)).astype(np.int32)
+    for b in range(B):
+        for j in range(K):
+            if rng.random() < 0.6:
+                draft[b, j] = int(np.argmax(x[b, j]))
+    dl = rng.integers(0, K + 1, B).astype(np.int32)
+    T = np.full(B, 1.0, np.float32)
+    u = rng.random((B, R)).astype(np.float32)
+    top_p = np.full(B, 0.9, np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    xh = to_host_logits(t)
+    g = _run(t, draft, dl, T, u, None, top_p)
+    r = oracle.verify(xh, draft, dl, T, u, nthreads=8, top_p=top_p)
+    tally = Tally()
+    _compare(g, r, T, u, f"band miss {dtype}", tally)
     tally.check()
 
 
