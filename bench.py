@@ -589,8 +589,8 @@ def _sam_workload_line(cfg, m, steps: int) -> dict:
     }
     if cfg.top_k != 0 or cfg.top_p < 1.0:
         line["top_k"], line["top_p"] = cfg.top_k, cfg.top_p
-        line["finish_pass_contents"] = ("truncation plan, extract (second read of "
-                                        "each verified row), select; finalize")
+        line["finish_pass_contents"] = ("truncation select (plan, candidates from the "
+                                        "chunks' band segments, selection); finalize")
     return line
 
 

@@ -87,10 +87,9 @@ const char* ss_last_error_string(void);
 size_t ss_verify_workspace_bytes(int B, int K, int V);
 
 /* The same with options: flags = 0, or SS_WS_TRUNCATION for calls that pass
- * top_k or top_p (the truncation passes need per-row histograms, candidate
- * lists and per-chunk sums: about (K+1) * B * nchunks * (2 KiB +
- * min(512, V) * 8 B), nchunks = ceil(V / 8192)). 0 for unsupported sizes or
- * flags. */
+ * top_k or top_p (truncation needs per-(row, chunk) histograms, band
+ * segments and sums: about (K+1) * B * nchunks * (2 KiB + min(1024, V) *
+ * 4 B), nchunks = ceil(V / 8192)). 0 for unsupported sizes or flags. */
 #define SS_WS_TRUNCATION 1
 size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);
 
@@ -231,8 +230,9 @@ int spec_step_noalloc(const void* logits, int dtype, int B, int K, int V,
  *                (then q must be NULL and the next-draft outputs non-NULL).
  * spec_finish must follow spec_stream on the same stream with the same
  * logits, sizes, drafts, temperatures, uniforms, top_k, top_p and workspace
- * (with truncation, spec_finish also runs the truncation passes, which read
- * each truncated row a second time).
+ * (with truncation, spec_stream also leaves each truncated row's chunk
+ * histograms and band segments, and spec_finish first runs the truncation
+ * selection over them).
  */
 int spec_stream(const void* logits, int dtype, int B, int K, int V,
                 const int32_t* draft, const int32_t* draft_len,

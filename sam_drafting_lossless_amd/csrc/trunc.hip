@@ -68,12 +68,6 @@ __device__ __forceinline__ RowCtx row_ctx(const Args& a, int64_t row) {
   return r;
 }
 
-// Range test of a token's row bin rb against [rlo, rhi] (rhi = kRestBin:
-// unbounded below the window).
-__device__ __forceinline__ bool in_range(int rb, int rlo, int rhi) {
-  return rb >= rlo && (rhi >= kRestBin || rb <= rhi);
-}
-
 struct SelShared {
   unsigned key[kCandCap];  // candidate keys (fkey of the logit), a run per chunk
   // per chunk: window start bin, finite count, max, weight sum (relative to
@@ -213,8 +207,17 @@ struct RowSrc {
   SelShared* sh;
   bool lds;  // the candidates are in sh->key (else: walk the chunks again)
   int n;     // candidates
+  // The range on the product t = l * ns (see band_t): a token lies above
+  // it when t < t_lo, in it when t_lo <= t < t_hi (t_hi = +inf for a range
+  // open below the window; -inf, whose product is +inf, and NaN lie in
+  // neither).
+  float t_lo, t_hi;
 
-  __device__ __forceinline__ int row_bin(float v) const { return abs_bin_s(v, ns) - a0; }
+  __device__ __forceinline__ bool above(float v) const { return v * ns < t_lo; }
+  __device__ __forceinline__ bool cand(float v) const {
+    const float t = v * ns;
+    return (t >= t_lo) & (t < t_hi);
+  }
 
   // How chunk c's tokens at or above the range's bottom are found: kNone
   // (it has none: its max lies below the range), kBand (its band holds
@@ -273,7 +276,7 @@ struct RowSrc {
     }
     for (int c = w; c < nc; c += kSelWaves)
       chunk(c, [&](float v) {
-        if (v > kNegInf && in_range(row_bin(v), rlo, rhi)) f(fkey(v));
+        if (cand(v)) f(fkey(v));
       });
   }
 };
@@ -462,6 +465,25 @@ __global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
     sh.over = 0;
   }
   __syncthreads();
+  // Each wavefront's first segment (wavefront w takes chunks w, w +
+  // kSelWaves, ...) is requested now, while the plan below decides whether
+  // it is used.
+  constexpr int kSegU = kSegCap / kWave;
+  float sg[kSegU];
+  int nuc = 0;  // wavefront rows of sg in use
+  if (w < nc) {
+    const int bd = sh.cband[w];
+    if ((bd & 0xffff) <= (bd >> 16)) {
+      const int cn = min(sh.cn[w], a.segcap);
+      const float* sp = a.cand + (h0 + w) * a.segcap;
+#pragma unroll
+      for (int u = 0; u < kSegU; ++u) {
+        const int i = u * kWave + l;
+        sg[u] = i < cn ? sp[i] : kNegInf;
+      }
+      nuc = (cn + kWave - 1) / kWave;
+    }
+  }
   // Row max m, finite count N and weight Z (relative to m): every wavefront
   // reduces the chunk values itself, in the same order.
   float m = kNegInf;
@@ -590,7 +612,9 @@ __global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
   const int krem = k - sh.cabove_n;
   RowSrc<DT, VP> src{a.logits + row * a.V * Dt<DT>::kBytes,
                      a.cand + h0 * a.segcap,
-                     a.V, nc, a.segcap, a0, rlo, rhi, m, kk, ns, &sh, false, 0};
+                     a.V, nc, a.segcap, a0, rlo, rhi, m, kk, ns, &sh, false, 0,
+                     (float)(a0 + rlo),
+                     rhi >= kRestBin ? INFINITY : (float)(a0 + rhi + 1)};
   using Src = RowSrc<DT, VP>;
   // Chunks whose band misses the range, listed in chunk order (nc <= 256:
   // the first four wavefronts).
@@ -611,47 +635,55 @@ __global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
   // the range: from its band (a wavefront per chunk), or by the whole
   // workgroup re-reading it. Runs that would pass kCandCap are not stored
   // (the selection then walks the chunks in each round).
-  auto above_w = [&](float v) {
-    return band_t(v, ns) < (float)(a0 + rlo) ? fast_exp2((v - m) * kk) : 0.0f;
-  };
-  auto is_cand = [&](float v) { return v > kNegInf && in_range(src.row_bin(v), rlo, rhi); };
+  auto above_w = [&](float v) { return src.above(v) ? fast_exp2((v - m) * kk) : 0.0f; };
+  auto is_cand = [&](float v) { return src.cand(v); };
   auto put = [&](float v, int& pos) {
     const bool in = is_cand(v);
     const unsigned long long hit = __ballot(in);
     if (in) sh.key[pos + lanes_below(hit)] = fkey(v);
     pos += __popcll(hit);
   };
+  // (a wavefront's next segment is requested before it works on the
+  // current one)
+  auto seg_of = [&](int c, float (&r)[Src::kU]) {
+    return (c < nc && src.source(c) == Src::kBand) ? src.band_load(c, r) : 0;
+  };
+  static_assert(Src::kU == kSegU, "one segment layout");
   for (int c = w; c < nc; c += kSelWaves) {
+    float rn[Src::kU];
+    const int nun = seg_of(c + kSelWaves, rn);
     const int sk = src.source(c);
-    if (sk == Src::kReread) continue;
-    float above = 0.0f;
-    int cnt = 0, at = 0;  // wavefront-uniform
-    if (sk == Src::kBand) {
-      float r[Src::kU];
-      const int nu = src.band_load(c, r);
-#pragma unroll
-      for (int u = 0; u < Src::kU; ++u)
-        if (u < nu) {
-          above += above_w(r[u]);
-          cnt += __popcll(__ballot(is_cand(r[u])));
-        }
-      if (l == 0) at = atomicAdd(&sh.ncand, cnt);
-      at = __builtin_amdgcn_readfirstlane(at);
-      if (at + cnt <= kCandCap) {
-        int pos = at;
+    if (sk != Src::kReread) {
+      float above = 0.0f;
+      int cnt = 0, at = 0;  // wavefront-uniform
+      if (sk == Src::kBand) {
 #pragma unroll
         for (int u = 0; u < Src::kU; ++u)
-          if (u < nu) put(r[u], pos);
-      } else if (l == 0) {
-        sh.over = 1;
+          if (u < nuc) {
+            above += above_w(sg[u]);
+            cnt += __popcll(__ballot(is_cand(sg[u])));
+          }
+        if (l == 0) at = atomicAdd(&sh.ncand, cnt);
+        at = __builtin_amdgcn_readfirstlane(at);
+        if (at + cnt <= kCandCap) {
+          int pos = at;
+#pragma unroll
+          for (int u = 0; u < Src::kU; ++u)
+            if (u < nuc) put(sg[u], pos);
+        } else if (l == 0) {
+          sh.over = 1;
+        }
+        above = wave_sum(above) + sh.cab[c] * fast_exp2((sh.cpm[c] - m) * kk);
       }
-      above = wave_sum(above) + sh.cab[c] * fast_exp2((sh.cpm[c] - m) * kk);
+      if (l == 0) {
+        sh.ccnt[c] = cnt;
+        sh.cbeg[c] = at;
+        sh.cabove[c] = above;
+      }
     }
-    if (l == 0) {
-      sh.ccnt[c] = cnt;
-      sh.cbeg[c] = at;
-      sh.cabove[c] = above;
-    }
+#pragma unroll
+    for (int u = 0; u < Src::kU; ++u) sg[u] = rn[u];
+    nuc = nun;
   }
   for (int i = 0; i < nmiss; ++i) {
     const int c = sh.miss[i];
