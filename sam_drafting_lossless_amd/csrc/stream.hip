@@ -394,25 +394,33 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     }
   } else {
     // Online (max, sum exp2) folded one 16-byte vector at a time, in the
-    // order the loads return, so only the raw vectors stay live.
+    // order the loads return, so only the raw vectors stay live. The draft
+    // token's logit is taken in a copy of the loop that only the chunk
+    // holding it runs (hasx is the same for the whole workgroup).
     float m = kNegInf, s = 0.0f;
+    auto fold = [&](auto take_x) {
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      float vm = kNegInf;
+      for (int it = 0; it < kLoads; ++it) {
+        float vm = kNegInf;
 #pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
-      const float mn = fmaxf(m, vm);
-      const float base = (mn == kNegInf) ? 0.0f : mn;
-      float t = s * fast_exp2((m - base) * kk);
+        for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
+        const float mn = fmaxf(m, vm);
+        const float base = (mn == kNegInf) ? 0.0f : mn;
+        float t = s * fast_exp2((m - base) * kk);
 #pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const float v = elem<DT>(raw[it], k);
-        t += fast_exp2((v - base) * kk);
-        xv = (ex == it * kVec<DT> + k) ? v : xv;
+        for (int k = 0; k < kVec<DT>; ++k) {
+          const float v = elem<DT>(raw[it], k);
+          t += fast_exp2((v - base) * kk);
+          if constexpr (decltype(take_x)::value) xv = (ex == it * kVec<DT> + k) ? v : xv;
+        }
+        s = t;
+        m = mn;
       }
-      s = t;
-      m = mn;
-    }
+    };
+    if (hasx)
+      fold(std::true_type{});
+    else
+      fold(std::false_type{});
     if (ex >= 0) red[kWaves].x = xv;  // read after the reduction's barrier
     mid();
     wave_lse(m, s, kk);
