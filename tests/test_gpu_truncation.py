@@ -96,6 +96,29 @@ def test_truncated_sampling_matches_oracle(B, K, V, dtype):
     tally.check()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_chunks_per_wavefront(dtype):
+    """V = 1,000,000 (123 fp32 chunks, 62 bf16): the select kernel's
+    wavefronts each take several chunks' segments in turn (the next one
+    requested while the current one is worked), with top-k, top-p and both."""
+    say(f"[gpu] truncation: V = 1,000,000 {dtype}")
+    rng = np.random.default_rng(91 + (dtype == "bf16"))
+    B, K, V = 6, 1, 1_000_000
+    x, draft, dl, T, u = _inputs(rng, B, K, V, greedy_share=0.0)
+    top_k = np.array([0, 40, 0, 2000, 0, 7], np.int32)
+    top_p = np.array([0.9, 1.0, 0.5, 0.95, 0.99, 0.8], np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    xh = to_host_logits(t)
+    g = _run(t, draft, dl, T, u, top_k, top_p)
+    r = oracle.verify(xh, draft, dl, T, u, nthreads=8, top_k=top_k, top_p=top_p)
+    tally = Tally()
+    near = _compare(g, r, T, u, f"many chunks {dtype}", tally)
+    assert near <= 1
+    tally.check()
+
+
 def test_boundary_tokens():
     """K = 1 drafts at the k-th and (k+1)-th largest logits and at the tokens
     around the top-p cut: p_draft (p'(x), 0 when x is dropped) follows the
