@@ -230,10 +230,43 @@ __device__ __forceinline__ float bin_scale(float kk) { return -kk * (float)kBins
 __device__ __forceinline__ float band_t(float l, float ns) {
   return __builtin_amdgcn_fmed3f(l * ns, -1.0e9f, 1.0e9f);
 }
-__device__ __forceinline__ int abs_bin_s(float l, float ns) {
-  return (int)floorf(band_t(l, ns));
+// floor(x) as an int, in one instruction (exact for |x| < 2^31).
+__device__ __forceinline__ int floor_i32(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
 }
+__device__ __forceinline__ int abs_bin_s(float l, float ns) { return floor_i32(band_t(l, ns)); }
 __device__ __forceinline__ int abs_bin(float l, float kk) { return abs_bin_s(l, bin_scale(kk)); }
+
+// Neighbour of f on the ordered line of floats (dir = +1: next larger, -1:
+// next smaller; -0 and +0 are adjacent points).
+__device__ __forceinline__ float float_step(float f, int dir) {
+  unsigned u = __float_as_uint(f);
+  unsigned k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  k += (unsigned)dir;
+  u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// The largest logit v whose product v * ns (rounded, as every bin test
+// computes it) is at least c, for ns < 0. The rounded product does not
+// increase with v, so {v : v * ns >= c} is exactly {v <= result}: a test of
+// a logit against the result is the product test. Found from c / ns by
+// single steps along the floats; false if it did not settle within a few
+// (degenerate scales), and then the caller must not use it.
+__device__ __forceinline__ bool logit_upto(float c, float ns, float* out) {
+  float v = (c == INFINITY) ? (3.40282347e38f / ns) : (c / ns);
+  int i = 0;
+  for (; i < 8 && !(v * ns >= c); ++i) v = float_step(v, -1);
+  for (; i < 16; ++i) {
+    const float u = float_step(v, 1);
+    if (!(u * ns >= c)) break;
+    v = u;
+  }
+  *out = v;
+  return (v * ns >= c) && !(float_step(v, 1) * ns >= c);
+}
 
 // Order-preserving key of a float (larger float, larger key; -0 as +0).
 __device__ __forceinline__ unsigned fkey(float l) {
