@@ -25,7 +25,13 @@
 // A design that let the last workgroup of each sequence finalize inside the
 // stream kernel (agent-scope atomic hand-off) was measured slower: the
 // finalize code raises the stream kernel's register count and its latency
-// lands in the kernel's tail.
+// lands in the kernel's tail. For small launches too: with the partials
+// stored at device scope, a ticket per streaming workgroup and one acquire
+// in the last, a step took 22.8 us against 21.6 for the two kernels
+// (B = 32, V = 151936, bf16, K = 5) and 14.9 against 14.6 (B = 1, V = 32):
+// the hand-off's write-through, returning atomic and invalidate cost what
+// the kernel boundary does. (A whole-cache fence in every workgroup took
+// 89 us.)
 #include <algorithm>
 #include <atomic>
 #include <mutex>
