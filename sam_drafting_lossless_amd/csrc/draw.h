@@ -120,15 +120,55 @@ __device__ __forceinline__ float draw_weight(float l, int i, Excl excl, float m,
     return excl(i) ? 0.0f : w;
 }
 
-// q values for the kVec elements of one raw vector (RESIDUAL only).
+// q of a chunk for the residual, in the stream layout (element (it, k) of
+// the lane is token elem_index(cstart, tid, it, k)); 0 past the row's end.
+template <int DT>
+struct QChunk {
+  float v[kLoads][kVec<DT>];
+  __device__ __forceinline__ float at(int it, int k) const { return v[it][k]; }
+};
+// No q (the draws from p).
+struct NoQ {
+  __device__ __forceinline__ float at(int, int) const { return 0.0f; }
+};
+
+// Requests every q value of the chunk at once: one load per vector, none
+// behind a branch (an index past the row's end is clamped into the row).
+// q_tail_zero then sets the values past the end to 0, once the kernel's
+// loads are all requested (see load_chunk_flat).
 template <int DT, bool VP>
-__device__ __forceinline__ void load_q_vec(const float* qrow, int cstart, int tid,
-                                           int it, int V, float (&qv)[kVec<DT>]) {
+__device__ __forceinline__ void load_q_chunk(const float* qrow, int cstart, int V, int tid,
+                                             QChunk<DT>& q) {
+  constexpr int kH = kVec<DT> / 4;  // 16-byte q vectors per logit vector
+  if constexpr (VP) {
+    // (V is a multiple of the logit vector width, so a vector is either
+    // wholly in the row or wholly past its end)
+    const int last = (V - cstart) / 4 - 1;  // the row's last q vector here
+    const f32x4* p = reinterpret_cast<const f32x4*>(qrow + cstart);
 #pragma unroll
-  for (int k = 0; k < kVec<DT>; ++k) {
-    const int i = elem_index<DT, VP>(cstart, tid, it, k);
-    qv[k] = i < V ? qrow[i] : 0.0f;
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int h = 0; h < kH; ++h) {
+        const f32x4 x =
+            __builtin_nontemporal_load(p + min((it * kThreads + tid) * kH + h, last));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q.v[it][4 * h + k] = x[k];
+      }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k)
+        q.v[it][k] = qrow[min(elem_index<DT, false>(cstart, tid, it, k), V - 1)];
   }
+}
+template <int DT, bool VP>
+__device__ __forceinline__ void q_tail_zero(int cstart, int V, int tid, QChunk<DT>& q) {
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k)
+      q.v[it][k] = elem_index<DT, VP>(cstart, tid, it, k) < V ? q.v[it][k] : 0.0f;
 }
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -170,30 +210,29 @@ __device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick
 // chunk draw_load requested. `during` runs first, while that chunk is still
 // in flight (the fused step appends the accepted drafts to the automaton
 // there).
-template <int DT, bool VP, bool RESIDUAL, typename Excl, typename During = NoDuring>
-__device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
-                             ChunkPick pk, Excl excl, float m, float kk,
-                             float invS, float lam, const u32x4 (&raw)[kLoads],
-                             During during = During{}) {
+// RESIDUAL: q holds the chunk's q (load_q_chunk), requested with `raw`.
+template <int DT, bool VP, bool RESIDUAL, typename Excl, typename During = NoDuring,
+          typename Q = NoQ>
+__device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
+                                             ChunkPick pk, Excl excl, float m, float kk,
+                                             float invS, float lam,
+                                             const u32x4 (&raw)[kLoads],
+                                             During during = During{}, const Q& q = Q{}) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   during();
   if (pk.chunk < 0) return -1;
-  const float* qrow = RESIDUAL ? a.q + ((int64_t)b * a.K + r) * a.V : nullptr;
   const int cstart = pk.chunk * kChunk<DT>;
   const float t_in = (float)pk.t_in;
   float vs[kLoads];
   int tlast = -1;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
-    float qv[kVec<DT>];
-    if constexpr (RESIDUAL) load_q_vec<DT, VP>(qrow, cstart, tid, it, a.V, qv);
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) {
       const int i = elem_index<DT, VP>(cstart, tid, it, k);
       const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
-                                                 kk, invS, RESIDUAL ? qv[k] : 0.0f,
-                                                 lam);
+                                                 kk, invS, q.at(it, k), lam);
       acc += wk;
       if (wk > 0.0f) tlast = max(tlast, i);
     }
@@ -243,25 +282,23 @@ __device__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
     } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
       const float tl = tc - exc2;
       u32x4 rv = raw[0];
+      float qv[kVec<DT>];
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) qv[k] = q.at(0, k);
 #pragma unroll
       for (int it = 1; it < kLoads; ++it)
-        if (it == its) rv = raw[it];
-      float qv[kVec<DT>];
-      if constexpr (RESIDUAL) {
+        if (it == its) {
+          rv = raw[it];
 #pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) {
-          const int i = elem_index<DT, VP>(cstart, tid, its, k);
-          qv[k] = i < a.V ? qrow[i] : 0.0f;
+          for (int k = 0; k < kVec<DT>; ++k) qv[k] = q.at(it, k);
         }
-      }
       float run = 0.0f, lfound = NAN, llast = NAN;
       int found = -1, lastp = -1;
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
         const int i = elem_index<DT, VP>(cstart, tid, its, k);
         const float lk = elem<DT>(rv, k);
-        const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS,
-                                                   RESIDUAL ? qv[k] : 0.0f, lam);
+        const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS, qv[k], lam);
         run += wk;
         if (wk > 0.0f) {
           lastp = i;

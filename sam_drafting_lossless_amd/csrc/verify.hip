@@ -366,38 +366,31 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
   const unsigned char* rowp =
       a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
   const float* qrow = a.q + ((int64_t)b * a.K + r) * a.V;
+  // The chunk's q and logits are all requested before either is used (past
+  // the row's end the logits are -inf and q is 0: those terms are 0). q
+  // goes first: requested after the logits, its loads were scheduled behind
+  // the exps of the logits, a second round trip.
+  QChunk<DT> qc;
+  load_q_chunk<DT, VP>(qrow, cstart, a.V, tid, qc);
   u32x4 raw[kLoads];
-  load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
+  if constexpr (VP)
+    load_chunk_flat<DT>(rowp, cstart, a.V, tid, raw);
+  else
+    load_chunk<DT, VP>(rowp, cstart, a.V, tid, raw);
+  // (no instruction moves across this point: every load is requested before
+  // the first result is used)
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (VP) chunk_tail_neginf<DT>(cstart, a.V, tid, raw);
+  q_tail_zero<DT, VP>(cstart, a.V, tid, qc);
   float s = 0.0f;
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) {
-    if constexpr (VP) {
-      const int i0 = cstart + (it * kThreads + tid) * kVec<DT>;
-      if (i0 < a.V) {
+  for (int it = 0; it < kLoads; ++it)
 #pragma unroll
-        for (int h = 0; h < kVec<DT> / 4; ++h) {
-          const f32x4 qv = __builtin_nontemporal_load(
-              reinterpret_cast<const f32x4*>(qrow + i0) + h);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float v = elem<DT>(raw[it], 4 * h + k);
-            const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
-            s += fmaxf(0.0f, wv * invS - qv[k]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kVec<DT>; ++k) {
-        const int i = elem_index<DT, false>(cstart, tid, it, k);
-        if (i < a.V) {
-          const float v = elem<DT>(raw[it], k);
-          const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
-          s += fmaxf(0.0f, wv * invS - qrow[i]);
-        }
-      }
+    for (int k = 0; k < kVec<DT>; ++k) {
+      const float v = elem<DT>(raw[it], k);
+      const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
+      s += fmaxf(0.0f, wv * invS - qc.at(it, k));
     }
-  }
   s = wave_sum(s);
   if (l == 0) red[w] = s;
   __syncthreads();
@@ -447,13 +440,29 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   }
   __syncthreads();
   u32x4 raw[kLoads];
-  draw_load<DT, VP>(a, b, r, pick_sh, raw);
-  const int tok = from_p ? draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh,
-                                                        OneToken{-1}, m, kk, 0.0f,
-                                                        lam, raw)
-                         : draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh,
-                                                       OneToken{-1}, m, kk, 1.0f / S,
-                                                       lam, raw);
+  int tok;
+  if (from_p) {
+    draw_load<DT, VP>(a, b, r, pick_sh, raw);
+    tok = draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, OneToken{-1}, m, kk, 0.0f,
+                                       lam, raw);
+  } else {
+    // (q first, as in the residual sums)
+    QChunk<DT> qc;
+    if (pick_sh.chunk >= 0) {
+      const int cstart = pick_sh.chunk * kChunk<DT>;
+      load_q_chunk<DT, VP>(a.q + ((int64_t)b * a.K + r) * a.V, cstart, a.V, tid, qc);
+      const unsigned char* rowp = a.logits + ((int64_t)b * R + r) * a.V * Dt<DT>::kBytes;
+      if constexpr (VP)
+        load_chunk_flat<DT, false>(rowp, cstart, a.V, tid, raw);
+      else
+        load_chunk<DT, VP, false>(rowp, cstart, a.V, tid, raw);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (VP) chunk_tail_neginf<DT>(cstart, a.V, tid, raw);
+      q_tail_zero<DT, VP>(cstart, a.V, tid, qc);
+    }
+    tok = draw_in_chunk<DT, VP, true>(a, dsh, b, r, pick_sh, OneToken{-1}, m, kk,
+                                      1.0f / S, lam, raw, NoDuring{}, qc);
+  }
   if (tid == 0) {
     a.out[(int64_t)b * R + r] = tok;
     if (a.logprob)

@@ -95,6 +95,40 @@ __device__ __forceinline__ int elem_index(int cstart, int tid, int it, int k) {
   return cstart + (it * kThreads + tid) * kVec<DT> + k;
 }
 
+// load_chunk in two phases, without a branch (vector rows, VP): the loads
+// (load_chunk_flat: the index of a vector past the row's end is clamped into
+// the row), then, once every load of the kernel's batch is requested,
+// chunk_tail_neginf replaces the vectors past the end by -inf words. The
+// branches of load_chunk's tail path, a select next to its load, and the
+// register copies where load_chunk's two paths join each wait for the loads
+// in flight; split this way, all of them are in flight together. A vector
+// is wholly in the row or wholly past its end, as V is a multiple of kVec.
+template <int DT, bool NT = true>
+__device__ __forceinline__ void load_chunk_flat(const unsigned char* row, int cstart,
+                                                int V, int tid, u32x4 (&raw)[kLoads]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + (int64_t)cstart * Dt<DT>::kBytes);
+  const int last = (V - cstart) / kVec<DT> - 1;
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int vi = min(it * kThreads + tid, last);
+    raw[it] = NT ? __builtin_nontemporal_load(p + vi) : p[vi];
+  }
+}
+template <int DT>
+__device__ __forceinline__ void chunk_tail_neginf(int cstart, int V, int tid,
+                                                  u32x4 (&raw)[kLoads]) {
+  constexpr unsigned kNegInfWord =
+      DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
+  const int rem = V - cstart;
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const bool in = (it * kThreads + tid) * kVec<DT> < rem;
+    const u32x4 x = raw[it];
+    raw[it] = u32x4{in ? x[0] : kNegInfWord, in ? x[1] : kNegInfWord,
+                    in ? x[2] : kNegInfWord, in ? x[3] : kNegInfWord};
+  }
+}
+
 // Loads one chunk of a row into registers. Elements past V read as -inf.
 // NT: non-temporal loads for the streaming pass (measured faster there);
 // the draw's single-chunk re-read uses ordinary loads, which can still find
