@@ -465,24 +465,38 @@ __global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
     sh.over = 0;
   }
   __syncthreads();
-  // Each wavefront's first segment (wavefront w takes chunks w, w +
-  // kSelWaves, ...) is requested now, while the plan below decides whether
-  // it is used.
+  // Each wavefront's segments (wavefront w takes chunks w, w + kSelWaves,
+  // ...), each requested one chunk ahead of its use, the first now, while
+  // the plan below decides whether it is used. The loads take no branch (an
+  // index past the segment's count is clamped into it and the entry masked
+  // where it is used) and two buffers alternate, so that the wait for one
+  // segment leaves the next in flight: a load behind a branch, or a
+  // register copy of a loaded value, makes the compiler wait for every load
+  // in flight.
+  // A row whose segments all hold at most kSmallSegU wavefront rows (top-k's
+  // bands) requests that many per segment, others all kSegU.
   constexpr int kSegU = kSegCap / kWave;
-  float sg[kSegU];
-  int nuc = 0;  // wavefront rows of sg in use
+  constexpr int kSmallSegU = 2;
+  using SmallSeg = std::integral_constant<int, kSmallSegU>;
+  using FullSeg = std::integral_constant<int, kSegU>;
+  int mcn = 0;
+  for (int c = l; c < nc; c += kWave) mcn = max(mcn, min(sh.cn[c], a.segcap));
+  const bool small_seg = wave_max_i(mcn) <= kSmallSegU * kWave;
+  auto seg_issue = [&](auto nu, int c, bool banded, float (&r)[kSegU])
+                       __attribute__((always_inline)) {
+    const int cn = banded ? min(sh.cn[c], a.segcap) : 0;
+    const float* sp = a.cand + (h0 + c) * a.segcap;
+    const int last = max(cn, 1) - 1;
+#pragma unroll
+    for (int u = 0; u < decltype(nu)::value; ++u) r[u] = sp[min(u * kWave + l, last)];
+    return cn;
+  };
+  float sa[kSegU], sb[kSegU];
+  int na = 0;  // entries of sa in use
   if (w < nc) {
     const int bd = sh.cband[w];
-    if ((bd & 0xffff) <= (bd >> 16)) {
-      const int cn = min(sh.cn[w], a.segcap);
-      const float* sp = a.cand + (h0 + w) * a.segcap;
-#pragma unroll
-      for (int u = 0; u < kSegU; ++u) {
-        const int i = u * kWave + l;
-        sg[u] = i < cn ? sp[i] : kNegInf;
-      }
-      nuc = (cn + kWave - 1) / kWave;
-    }
+    const bool banded = (bd & 0xffff) <= (bd >> 16);
+    na = small_seg ? seg_issue(SmallSeg{}, w, banded, sa) : seg_issue(FullSeg{}, w, banded, sa);
   }
   // Row max m, finite count N and weight Z (relative to m): every wavefront
   // reduces the chunk values itself, in the same order.
@@ -643,48 +657,60 @@ __global__ __launch_bounds__(kSelThreads) void trunc_select_kernel(Args a) {
     if (in) sh.key[pos + lanes_below(hit)] = fkey(v);
     pos += __popcll(hit);
   };
-  // (a wavefront's next segment is requested before it works on the
-  // current one)
-  auto seg_of = [&](int c, float (&r)[Src::kU]) {
-    return (c < nc && src.source(c) == Src::kBand) ? src.band_load(c, r) : 0;
-  };
-  static_assert(Src::kU == kSegU, "one segment layout");
-  for (int c = w; c < nc; c += kSelWaves) {
-    float rn[Src::kU];
-    const int nun = seg_of(c + kSelWaves, rn);
+  // The candidates and the weight above the range of chunk c from its
+  // segment sg of cn entries (a kBand chunk), or nothing (kNone).
+  auto take_band = [&](auto nu_max, int c, const float (&sg)[kSegU], int cn)
+                       __attribute__((always_inline)) {
     const int sk = src.source(c);
-    if (sk != Src::kReread) {
-      float above = 0.0f;
-      int cnt = 0, at = 0;  // wavefront-uniform
-      if (sk == Src::kBand) {
+    if (sk == Src::kReread) return;
+    float above = 0.0f;
+    int cnt = 0, at = 0;  // wavefront-uniform
+    if (sk == Src::kBand) {
+      const int nu = (cn + kWave - 1) / kWave;
 #pragma unroll
-        for (int u = 0; u < Src::kU; ++u)
-          if (u < nuc) {
-            above += above_w(sg[u]);
-            cnt += __popcll(__ballot(is_cand(sg[u])));
-          }
-        if (l == 0) at = atomicAdd(&sh.ncand, cnt);
-        at = __builtin_amdgcn_readfirstlane(at);
-        if (at + cnt <= kCandCap) {
-          int pos = at;
-#pragma unroll
-          for (int u = 0; u < Src::kU; ++u)
-            if (u < nuc) put(sg[u], pos);
-        } else if (l == 0) {
-          sh.over = 1;
+      for (int u = 0; u < decltype(nu_max)::value; ++u)
+        if (u < nu) {
+          const float v = u * kWave + l < cn ? sg[u] : kNegInf;
+          above += above_w(v);
+          cnt += __popcll(__ballot(is_cand(v)));
         }
-        above = wave_sum(above) + sh.cab[c] * fast_exp2((sh.cpm[c] - m) * kk);
-      }
-      if (l == 0) {
-        sh.ccnt[c] = cnt;
-        sh.cbeg[c] = at;
-        sh.cabove[c] = above;
-      }
-    }
+      if (l == 0) at = atomicAdd(&sh.ncand, cnt);
+      at = __builtin_amdgcn_readfirstlane(at);
+      if (at + cnt <= kCandCap) {
+        int pos = at;
 #pragma unroll
-    for (int u = 0; u < Src::kU; ++u) sg[u] = rn[u];
-    nuc = nun;
-  }
+        for (int u = 0; u < decltype(nu_max)::value; ++u)
+          if (u < nu) put(u * kWave + l < cn ? sg[u] : kNegInf, pos);
+      } else if (l == 0) {
+        sh.over = 1;
+      }
+      above = wave_sum(above) + sh.cab[c] * fast_exp2((sh.cpm[c] - m) * kk);
+    }
+    if (l == 0) {
+      sh.ccnt[c] = cnt;
+      sh.cbeg[c] = at;
+      sh.cabove[c] = above;
+    }
+  };
+  // The next segment's request (a chunk past the last, or one without a
+  // band, requests the wavefront's own first segment and uses none of it).
+  auto next_seg = [&](auto nu, int c, float (&r)[kSegU]) __attribute__((always_inline)) {
+    const bool band = c < nc && src.source(c) == Src::kBand;
+    return seg_issue(nu, band ? c : w, band, r);
+  };
+  auto gather = [&](auto nu) __attribute__((always_inline)) {
+    for (int c = w; c < nc; c += 2 * kSelWaves) {
+      const int nb = next_seg(nu, c + kSelWaves, sb);
+      take_band(nu, c, sa, na);
+      if (c + kSelWaves >= nc) break;
+      na = next_seg(nu, c + 2 * kSelWaves, sa);
+      take_band(nu, c + kSelWaves, sb, nb);
+    }
+  };
+  if (small_seg)
+    gather(SmallSeg{});
+  else
+    gather(FullSeg{});
   for (int i = 0; i < nmiss; ++i) {
     const int c = sh.miss[i];
     float v[kBlkElems<DT>];
