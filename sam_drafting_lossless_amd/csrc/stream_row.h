@@ -32,6 +32,7 @@ struct TrShared {
   float run[kWaves][kSegCap + kWave];
   int band[4];
   float vb[2];
+  float above;  // weight above the band, from the masses (see kFixAboveBins)
   int cnt[kWaves];
 };
 template <bool TR>
@@ -283,7 +284,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
         keep_here(s);
         const unsigned jb = min((unsigned)(abs_bin_s(v, ns) - a0), below);
         atomicAdd(&ts->hs[v > kNegInf ? jb : nonfin],
-                  kCountOne | (unsigned long long)(unsigned)(wv * kFixScale));
+                  kCountOne | (unsigned long long)(unsigned)fmaf(wv, kFixScale, 0.5f));
       }
     s = wave_sum(s);
     if (l == 0) red[w].y = s;  // (red[].x, read above, stays)
@@ -310,12 +311,23 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
           hi = 0;
         }
       }
+      // The weight above a band near the chunk max: the masses of the bins
+      // above it (each below 2^46, exact in double; the sum below 2^54).
+      float abf = 0.0f;
+      if (lo > 0 && lo <= hi && lo <= kFixAboveBins) {
+        double mb = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * l + q < lo) mb += (double)(ts->hs[4 * l + q] & kMassMask);
+        abf = (float)(wave_sum_d(mb) * (1.0 / (double)kFixScale));
+      }
       if (l == 0) {
         ts->band[0] = lo;
         ts->band[1] = hi;
         ts->band[2] = bd.z;
         ts->vb[0] = float_step(vex, 1);
         ts->vb[1] = vtop;
+        ts->above = abf;
       }
     }
     __syncthreads();
@@ -329,8 +341,9 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     // a ballot, the lane's rank among the hits, an exec-masked LDS store. n
     // counts every hit; positions stop at kSegCap, so that a run that
     // overflows (the band is then reported as none) stays inside its room.
-    // The weight above the band is summed only when the band does not
-    // start at the chunk max (top-p alone).
+    // The weight above the band is summed here only for a band that starts
+    // deeper than kFixAboveBins below the chunk max (top-p alone); nearer
+    // ones took it from the histogram.
     float above = 0.0f;
     int n = 0, np = 0;  // wavefront-uniform
     float* run = ts->run[w];
@@ -352,8 +365,9 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
           np = min(n, kSegCap);
         }
     };
+    const bool fix_above = blo <= kFixAboveBins;  // (or no weight above: blo = 0)
     if (blo > bhi) {
-    } else if (blo > 0) {
+    } else if (!fix_above) {
       band_pass(std::true_type{});
     } else {
       band_pass(std::false_type{});
@@ -372,6 +386,7 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
       tot += ts->cnt[i];
       ab += red[i].w;
     }
+    if (fix_above) ab = ts->above;
     // A band whose tokens do not fit (possible only for non-finite logits,
     // which the histogram does not count) is reported as none.
     const bool ok = blo <= bhi && tot <= a.segcap;

@@ -42,6 +42,12 @@ constexpr int kSegCap = 1024;        // logits per (row, chunk) segment
 constexpr int kBandHalf = 4;         // top-p band: bins either side of the estimate
 constexpr int kNoBand = 1;           // packed band (lo = 1, hi = 0): none
 constexpr float kFixScale = 2147483648.0f;  // 2^31
+// A top-p band that starts within this many bins (12 octaves) of the chunk
+// max takes its weight above the band from the histogram's masses: each
+// token's mass is rounded to 2^-32 of the chunk max, and every token above
+// the band weighs at least 2^-12 of it, so the sum is off by at most 2^-20
+// of itself. Deeper bands sum the tokens' weights instead.
+constexpr int kFixAboveBins = 12 * kBinsPerOctave;
 constexpr unsigned long long kCountOne = 1ull << 48;
 constexpr unsigned long long kMassMask = kCountOne - 1;
 

@@ -310,6 +310,55 @@ def test_band_missing_the_row_range(dtype):
     tally.check()
 
 
+@pytest.mark.parametrize("octaves", [9.5, 10.5, 11.5, 13.0])
+def test_weight_above_band_near_and_deep(octaves):
+    """The weight above a top-p band is taken from the histogram's
+    fixed-point masses when the band starts within 12 octaves (96 bins) of
+    its chunk's max, and summed from the tokens' weights when it starts
+    deeper. Rows built to put the bands at a chosen depth: per 8,192-token
+    chunk one token at the top, 20 tokens spread over the octaves between,
+    and the rest spread over the 6 octaves from `octaves` below the top
+    down; top_p is about the row's share above `octaves` + 1, so each chunk's band
+    (it fits its segment) starts about 8 * octaves bins down: bins 79-83,
+    87-91, 95-101 (both ways within one row) and 105-114 for the four cases
+    (found by replaying the chunks' band choice on the CPU). Everything
+    above the band is kept, so p_draft and the draws depend on its weight,
+    at the usual bar."""
+    say(f"[gpu] truncation: weight above a band {octaves} octaves down")
+    rng = np.random.default_rng(int(octaves * 10))
+    B, K, C = 4, 2, 8192
+    R, V = K + 1, 16 * C
+    ln2 = float(np.log(2.0))
+    x = np.empty((B, R, V), np.float32)
+    draft = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for j in range(R):
+            row = -(octaves + rng.uniform(0.0, 6.0, V)) * ln2
+            mids = []
+            for c in range(V // C):
+                row[c * C + rng.integers(C)] = rng.uniform(-0.1, 0.0)
+                mid = c * C + rng.choice(C, 20, replace=False)
+                row[mid] = -rng.uniform(1.0, octaves - 1.0, 20) * ln2
+                mids.extend(mid.tolist())
+            x[b, j] = row
+            if j < K:
+                draft[b, j] = int(np.argmax(row)) if rng.random() < 0.5 else int(rng.choice(mids))
+    x64 = x[:, 0].astype(np.float64)
+    w = np.exp(x64 - x64.max(-1, keepdims=True))
+    # (0.1 % past that share, so that no row's decision sits on a tie)
+    top_p = (1.001 * (w * (w > 2.0 ** -(octaves + 1))).sum(-1) / w.sum(-1)).astype(np.float32)
+    dl = np.full(B, K, np.int32)
+    T = np.ones(B, np.float32)
+    u = rng.random((B, R)).astype(np.float32)
+    t = torch.from_numpy(x).cuda()
+    g = _run(t, draft, dl, T, u, None, top_p)
+    r = oracle.verify(to_host_logits(t), draft, dl, T, u, nthreads=8, top_p=top_p)
+    tally = Tally()
+    _compare(g, r, T, u, f"above band {octaves}", tally)
+    tally.check()
+    assert (np.asarray(g[2]) >= 0).any()  # some draft probability was compared
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_truncation_with_given_q(dtype):
     say(f"[gpu] truncation with given q {dtype}")
