@@ -47,7 +47,8 @@ constexpr float kPlanMargin = 1e-4f;  // relative slack for histogram rounding
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kPlanGroups = kSelThreads / kHistBins;  // chunk groups of the merge
-constexpr int kPlanBatch = 8;  // histogram words a thread requests at once
+constexpr int kPlanBatch = 10;  // histogram words a thread requests at once (one batch
+                                // for V = 151,936 fp32: 19 chunks over two groups)
 static_assert(kMaxChunks <= kHistBins, "the chunk prefix uses the first 4 wavefronts");
 
 // Row-level activity of truncation; the same test as the stream pass.
