@@ -15,7 +15,8 @@
 // partials. This kernel takes one workgroup per sequence: wavefront 0 holds
 // node i in lane i (trees of at most 64 nodes), gathers each node's token
 // logit from its parent's row (one load per lane, all at once), the four
-// wavefronts combine the rows' partials, and wavefront 0 walks the tree: the
+// wavefronts combine the rows' partials (requested with the sequence's
+// parameters and cached in LDS when they fit), and wavefront 0 walks the tree: the
 // children of the current node are a ballot of parent == node, their running
 // sum is one wavefront prefix sum in node order, the accepted child the first
 // lane of a ballot. The final draw picks its chunk from the partials minus
@@ -38,11 +39,15 @@ struct TokenList {
   }
 };
 
+// Chunk partials of all N rows are cached in LDS when they fit.
+constexpr int kTreeCache = 1024;
+constexpr int kTreePer = kTreeCache / kThreads;  // partials a thread requests
+
 struct TreeShared {
+  f32x4 pc[kTreeCache];
   int tok[kWave];
   int par[kWave];
   float u[kWave];
-  float lx[kWave];  // logit of node i's token in its parent's row
   float m[kWave];
   float s[kWave];
   int idx[kWave];
@@ -64,9 +69,35 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int b = blockIdx.x;
   const int N = a.K + 1, nc = a.nchunks;
+  const int64_t row0 = (int64_t)b * N;
+  // Everything that depends on no other load is requested at once: the
+  // sequence's parameters, every node's token, parent and coin (lanes of
+  // wavefront 0), and the chunk partials of all N rows when they fit the
+  // LDS cache (kTreePer per thread, the index clamped rather than tested, so
+  // that none of them waits for another). Rows and nodes past n_nodes are
+  // read but not used.
+  const bool cached = N * nc <= kTreeCache;  // uniform
+  const f32x4* P0 = a.partials + row0 * nc;
+  f32x4 pv[kTreePer];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kTreePer; ++i) pv[i] = P0[min(tid + i * kThreads, N * nc - 1)];
+  }
+  int tk = 0, pr = -1;
+  float uu = 0.0f;
+  if (w == 0) {
+    tk = tokens[row0 + min(l, N - 1)];
+    pr = parent[row0 + min(l, N - 1)];
+    if (l < N && a.uniforms) uu = a.uniforms[row0 + l];
+  }
   int d;
   float T;
   const int st0 = seq_check(a, b, &d, &T);  // d = n_nodes - 1
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kTreePer; ++i)
+      if (tid + i * kThreads < N * nc) sh.pc[tid + i * kThreads] = pv[i];
+  }
   if (st0) {
     if (tid == 0) atomicOr(&a.status[b], st0);
     return;
@@ -76,13 +107,10 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
   const float kk = greedy ? 0.0f : kLog2e / T;
   // Nodes, one per lane of wavefront 0, and the tree's validity.
   if (w == 0) {
-    int tk = 0, pr = -1;
-    float uu = 0.0f;
-    if (l < n) {
-      tk = tokens[(int64_t)b * N + l];
-      pr = parent[(int64_t)b * N + l];
+    if (l >= n) {
+      tk = 0;
+      pr = -1;
     }
-    if (l < N && a.uniforms) uu = a.uniforms[(int64_t)b * N + l];
     int bad = 0;
     if (l == 0) bad = pr != -1;
     else if (l < n) bad = pr < 0 || pr >= l || tk < 0 || tk >= a.V;
@@ -106,41 +134,53 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
     if (tid == 0) atomicOr(&a.status[b], sh.st);
     return;
   }
-  const int64_t row0 = (int64_t)b * N;
-  // Each node's token logit in its parent's row (T > 0 only).
+  // Each node's token logit in its parent's row (T > 0 only), kept by its
+  // lane until the walk (stored to LDS, it would be waited for at once).
+  float lxr = 0.0f;
   if (w == 0 && !greedy && l >= 1 && l < n)
-    sh.lx[l] = load_one<DT>(a.logits + (row0 + sh.par[l]) * a.V * Dt<DT>::kBytes, sh.tok[l]);
-  // Row statistics from the chunk partials, one wavefront per row.
-  for (int j = w; j < n; j += kWaves) {
-    const f32x4* P = a.partials + (row0 + j) * nc;
-    if (greedy) {
-      float bv = kNegInf, m1 = kNegInf, s1 = 0.0f;
-      int bi = INT_MAX;
-      for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = load_partial(P + c);
-        argmax_merge(bv, bi, p.x, __float_as_int(p.w));
-        lse_merge(m1, s1, p.x, p.y, kLog2e);
-      }
-      wave_argmax(bv, bi);
-      wave_lse(m1, s1, kLog2e);
-      if (l == 0) {
-        sh.idx[j] = bi;
-        sh.bad[j] = !(s1 > 0.0f) || !isfinite(s1) || bv == INFINITY || bv == kNegInf;
-      }
-    } else {
-      float m = kNegInf, s = 0.0f;
-      for (int c = l; c < nc; c += kWave) {
-        const f32x4 p = load_partial(P + c);
-        lse_merge(m, s, p.x, p.y, kk);
-      }
-      wave_lse(m, s, kk);
-      if (l == 0) {
-        sh.m[j] = m;
-        sh.s[j] = s;
-        sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
+    lxr = load_one<DT>(a.logits + (row0 + sh.par[l]) * a.V * Dt<DT>::kBytes, sh.tok[l]);
+  // Partial of chunk c of row j: from the cache, or from the workspace.
+  auto part = [&](int j, int c) {
+    return cached ? sh.pc[j * nc + c] : load_partial(P0 + (int64_t)j * nc + c);
+  };
+  // Row statistics from the chunk partials, one wavefront per row. (The two
+  // sources are separate instantiations: a choice per access would make the
+  // LDS reads wait for the loads in flight, the node logits among them.)
+  auto combine_rows = [&](auto partf) {
+    for (int j = w; j < n; j += kWaves) {
+      if (greedy) {
+        float bv = kNegInf, m1 = kNegInf, s1 = 0.0f;
+        int bi = INT_MAX;
+        for (int c = l; c < nc; c += kWave) {
+          const f32x4 p = partf(j, c);
+          argmax_merge(bv, bi, p.x, __float_as_int(p.w));
+          lse_merge(m1, s1, p.x, p.y, kLog2e);
+        }
+        wave_argmax(bv, bi);
+        wave_lse(m1, s1, kLog2e);
+        if (l == 0) {
+          sh.idx[j] = bi;
+          sh.bad[j] = !(s1 > 0.0f) || !isfinite(s1) || bv == INFINITY || bv == kNegInf;
+        }
+      } else {
+        float m = kNegInf, s = 0.0f;
+        for (int c = l; c < nc; c += kWave) {
+          const f32x4 p = partf(j, c);
+          lse_merge(m, s, p.x, p.y, kk);
+        }
+        wave_lse(m, s, kk);
+        if (l == 0) {
+          sh.m[j] = m;
+          sh.s[j] = s;
+          sh.bad[j] = !(s > 0.0f) || !isfinite(s) || !isfinite(m);
+        }
       }
     }
-  }
+  };
+  if (cached)
+    combine_rows([&](int j, int c) { return sh.pc[j * nc + c]; });
+  else
+    combine_rows([&](int j, int c) { return load_partial(P0 + (int64_t)j * nc + c); });
   __syncthreads();
   // The walk (wavefront 0).
   if (w == 0) {
@@ -154,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
     } else {
       const int mytok = (l < n) ? sh.tok[l] : -1;
       const int mypar = (l >= 1 && l < n) ? sh.par[l] : -2;
-      const float mylx = (l >= 1 && l < n && !greedy) ? sh.lx[l] : 0.0f;
+      const float mylx = (l >= 1 && l < n && !greedy) ? lxr : 0.0f;
       int cur = 0, depth = 0;
       while (true) {
         const bool child = (mypar == cur);
@@ -203,17 +243,16 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
     if (w == 0 && l < sh.nexcl) atomicAdd(&sh.xsum[sh.excl[l] / kChunk<DT>], sh.exw[l]);
     __syncthreads();
     if (w == 0) {
-      const f32x4* P = a.partials + (row0 + cur) * nc;
       const float m = sh.m[cur], uK = sh.u[N - 1];
       ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
-        const f32x4 p = load_partial(P + c);
+        const f32x4 p = part(cur, c);
         return fmax(0.0, chunk_weight(p.y, p.x, m, kk) - (double)sh.xsum[c]);
       });
       int allx = 0;
       if (pk.chunk < 0) {
         // Rounding left nothing outside the children: draw from the row.
         pk = pick_chunk(nc, uK, [&](int c) {
-          const f32x4 p = load_partial(P + c);
+          const f32x4 p = part(cur, c);
           return chunk_weight(p.y, p.x, m, kk);
         });
         allx = 1;
