@@ -39,7 +39,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "spec_stream_c3_traffic.json")
 
 
-STREAM_SOURCES = ("stream.hip", "verify_common.h", "internal.h")
+STREAM_SOURCES = ("stream.hip", "stream_row.h", "verify_common.h", "internal.h")
 
 
 def stream_source_hash() -> str:
