@@ -817,6 +817,14 @@ def _workload_configs():
     }
 
 
+def _measure_workload(cfg, steps: int, warmup: int) -> dict:
+    if cfg.q_mode == "model":
+        return measure_draft_model_workload(cfg, steps, warmup)
+    if cfg.q_mode == "tree":
+        return measure_tree_workload(cfg, steps, warmup)
+    return _sam_workload_line(cfg, measure_sam_workload(cfg, steps, warmup), steps)
+
+
 def workloads_report(steps: int, warmup: int, names: str = "all"):
     """One JSON line per workload: c2 (greedy), c4 (bf16 logits, long
     histories) and the truncated c3 variants through the automaton step, c5
@@ -824,15 +832,25 @@ def workloads_report(steps: int, warmup: int, names: str = "all"):
     cfgs = _workload_configs()
     pick = list(cfgs) if names == "all" else names.split(",")
     for n in pick:
-        cfg = cfgs[n]
-        if cfg.q_mode == "model":
-            line = measure_draft_model_workload(cfg, steps, warmup)
-        elif cfg.q_mode == "tree":
-            line = measure_tree_workload(cfg, steps, warmup)
-        else:
-            line = _sam_workload_line(cfg, measure_sam_workload(cfg, steps, warmup),
-                                      steps)
-        print(json.dumps(line), flush=True)
+        print(json.dumps(_measure_workload(cfgs[n], steps, warmup)), flush=True)
+
+
+# The measures of each workload's own line kept in the headline line.
+SUMMARY_KEYS = ("steps", "steps_per_s", "us_per_step", "library_steps_per_s",
+                "stream_pass_avg_us", "verified_rows_per_launch",
+                "stream_frac_of_8TBps", "finish_pass_event_us", "mean_tokens_per_step",
+                "rows_per_step", "whole_call_GBps")
+
+
+def workloads_summary(warmup: int) -> dict:
+    """Every other workload measured in the headline run too, in compact
+    form (C1 over its 500 steps, the others over 200; `--workloads` prints
+    their full lines)."""
+    out = {}
+    for n, cfg in _workload_configs().items():
+        line = _measure_workload(cfg, 500 if n == "c1" else 200, warmup)
+        out[line["workload"]] = {k: line[k] for k in SUMMARY_KEYS if k in line}
+    return out
 
 
 def main():
@@ -856,8 +874,9 @@ def main():
                     help="time only the stream pass over all B x (K+1) rows "
                          "of the headline shape (every draft full)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="headline line without the all-rows and drafted "
-                         "measurements (for profiling the headline alone)")
+                    help="headline line without the all-rows, drafted and "
+                         "other workloads' measurements (for profiling the "
+                         "headline alone)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run a copy kernel of this many bytes instead")
     args = ap.parse_args()
@@ -913,6 +932,7 @@ def main():
             dcfg, measure_sam_workload(dcfg, dsteps, args.warmup), dsteps)
         drafted["boost"] = dcfg.boost
 
+    others = None if args.no_extras else workloads_summary(min(args.warmup, 20))
     probe = None if args.no_probe else hbm_read_probe(torch, harness)
     probe_same = (None if args.no_probe else
                   same_size_read_probe(torch, harness, ring, m["bytes_per_launch"]))
@@ -974,6 +994,7 @@ def main():
                                "harness in"),
         "verify_all_rows": all_rows,
         "c3_drafted": drafted,
+        "workloads": others,
         "hbm_read_probe_GBps": probe,
         "hbm_read_probe_same_bytes": probe_same,
         "setup_s": m["setup_s"],
