@@ -100,9 +100,12 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
   return r;
 }
 
+// draw_in_chunk's mark for a target past the chunk's re-read total.
+constexpr int kDrawPastEnd = INT_MIN;
+
 struct DrawShared {
   float cell[kLoads * kWaves];  // (load, wave) totals in token order
-  int wlast[kWaves];
+  int wlast[kWaves];            // each wavefront's last positive weight
   int result;
   float result_l;  // the drawn token's logit (NaN if the draw did not see it)
 };
@@ -196,57 +199,69 @@ struct NoDuring {
   __device__ void operator()() const {}
 };
 
-// Requests the chosen chunk of row r (nothing if every weight is 0).
+// Requests the chosen chunk of row r (nothing if every weight is 0). On the
+// vector path the loads are branch-free (clamped into the row, see
+// load_chunk_flat) and draw_in_chunk sets the values past the row's end:
+// load_chunk's two paths, joined here, made the compiler wait for every
+// load in flight before the full-chunk path's loads.
 template <int DT, bool VP>
 __device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick pk,
                                           u32x4 (&raw)[kLoads]) {
   if (pk.chunk < 0) return;
   const unsigned char* row =
       a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes;
-  load_chunk<DT, VP, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
+  if constexpr (VP)
+    load_chunk_flat<DT, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
+  else
+    load_chunk<DT, VP, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
 }
 
-// Whole workgroup; `pk` must be the same in every thread and `raw` hold the
+// Whole workgroup; `pk` must be the same in every thread and `raw_in` hold the
 // chunk draw_load requested. `during` runs first, while that chunk is still
 // in flight (the fused step appends the accepted drafts to the automaton
 // there).
-// RESIDUAL: q holds the chunk's q (load_q_chunk), requested with `raw`.
+// RESIDUAL: q holds the chunk's q (load_q_chunk), requested with `raw_in`.
 template <int DT, bool VP, bool RESIDUAL, typename Excl, typename During = NoDuring,
           typename Q = NoQ>
 __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
                                              ChunkPick pk, Excl excl, float m, float kk,
                                              float invS, float lam,
-                                             const u32x4 (&raw)[kLoads],
+                                             const u32x4 (&raw_in)[kLoads],
                                              During during = During{}, const Q& q = Q{}) {
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   during();
   if (pk.chunk < 0) return -1;
   const int cstart = pk.chunk * kChunk<DT>;
+  u32x4 raw[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) raw[it] = raw_in[it];
+  if constexpr (VP) {
+    if (a.V - cstart < kChunk<DT>) chunk_tail_neginf<DT>(cstart, a.V, tid, raw);
+  }
   const float t_in = (float)pk.t_in;
+  auto weight = [&](int it, int k) {
+    return draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k),
+                                     elem_index<DT, VP>(cstart, tid, it, k), excl, m, kk,
+                                     invS, q.at(it, k), lam);
+  };
   float vs[kLoads];
-  int tlast = -1;
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
     float acc = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const int i = elem_index<DT, VP>(cstart, tid, it, k);
-      const float wk = draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), i, excl, m,
-                                                 kk, invS, q.at(it, k), lam);
-      acc += wk;
-      if (wk > 0.0f) tlast = max(tlast, i);
-    }
+    for (int k = 0; k < kVec<DT>; ++k) acc += weight(it, k);
     vs[it] = acc;
   }
   // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
   float tot[kLoads];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = wave_sum(vs[it]);
-  const int wl = wave_max_i(tlast);
+  for (int it = 0; it < kLoads; ++it) tot[it] = vs[it];
+  wave_inclusive_sum_n(tot);
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) tot[it] = lane63(tot[it]);
   if (l == 0) {
 #pragma unroll
     for (int it = 0; it < kLoads; ++it) sh.cell[it * kWaves + w] = tot[it];
-    sh.wlast[w] = wl;
   }
   __syncthreads();
   // Every wavefront finds the cell (the same scan gives the same answer).
@@ -255,14 +270,9 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
   const float exc = wave_shift_up1(inc);
   const unsigned long long hit =
       __ballot(l < kLoads * kWaves && exc <= t_in && t_in < inc);
-  int clast = sh.wlast[0];
-  for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
   const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
   if (cell < 0) {
-    if (tid == 0) {
-      sh.result = clast;  // the chunk's last positive weight
-      sh.result_l = NAN;
-    }
+    if (tid == 0) sh.result = kDrawPastEnd;
   } else if (w == cell % kWaves) {
     const int its = cell / kWaves;
     float v = vs[0];
@@ -275,10 +285,7 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
     const bool mine = exc2 <= tc && tc < inc2;
     const unsigned long long who = __ballot(mine);
     if (!who) {
-      if (l == 0) {
-        sh.result = clast;
-        sh.result_l = NAN;
-      }
+      if (l == 0) sh.result = kDrawPastEnd;
     } else if (mine && l == __ffsll((unsigned long long)who) - 1) {
       const float tl = tc - exc2;
       u32x4 rv = raw[0];
@@ -314,6 +321,28 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
     }
   }
   __syncthreads();
+  if (sh.result == kDrawPastEnd) {
+    // The target lies past the re-read total (rounding): the chunk's last
+    // token of positive weight, found only now, as the common path needs
+    // none of it. The weights are the same instructions on the same inputs
+    // as above, so the same ones are positive.
+    int tlast = -1;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k)
+        if (weight(it, k) > 0.0f) tlast = max(tlast, elem_index<DT, VP>(cstart, tid, it, k));
+    tlast = wave_max_i(tlast);
+    if (l == 0) sh.wlast[w] = tlast;
+    __syncthreads();
+    if (tid == 0) {
+      int clast = sh.wlast[0];
+      for (int i = 1; i < kWaves; ++i) clast = max(clast, sh.wlast[i]);
+      sh.result = clast;
+      sh.result_l = NAN;
+    }
+    __syncthreads();
+  }
   return sh.result;
 }
 

@@ -114,6 +114,39 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   return wave_scan(v, 0.0f, [](float x, float y) { return x + y; });
 }
 
+// N independent wavefront inclusive sums, each step taken on all N values
+// before the next, so that their shuffles overlap (one after another, each
+// sum's chain of dependent steps is exposed when a SIMD runs one
+// wavefront). Each value gets exactly wave_inclusive_sum's additions.
+template <int N>
+__device__ __forceinline__ void wave_inclusive_sum_n(float (&v)[N]) {
+  float t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowShr1>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowShr2>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowShr4>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowShr8>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowBcast15, 0xa>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = dpp_f<kDppRowBcast31, 0xc>(0.0f, v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += t[i];
+}
+
 // The value of the previous lane (0 in lane 0): an inclusive scan's
 // exclusive counterpart, bit for bit.
 __device__ __forceinline__ float wave_shift_up1(float v) {

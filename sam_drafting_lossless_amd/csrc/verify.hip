@@ -60,6 +60,8 @@ struct FinalShared {
   ChunkPick pick[kMaxRows];  // chunk choice of a draw at each row (T > 0)
   int acc_len;
   int st;
+  int hdr[8];  // the automaton's header, one dword per lane of wavefront 0
+  int rec[4];  // the record of its last state
   DrawShared draw;
 };
 
@@ -71,10 +73,13 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   const int b = blockIdx.x;
   const int R = a.K + 1, nc = a.nchunks;
   // Everything that does not depend on another load is requested at once:
-  // the sequence's parameters, drafts, coins and the partials of every row.
-  // The automaton step's header and last-state record are requested in the
-  // following phases, so that no barrier waits for them and both are in
-  // registers when the step needs them.
+  // the sequence's parameters, drafts, coins, the partials of every row and
+  // the automaton's header. The last wavefront then requests the record of
+  // the automaton's last state and leaves both in LDS for the step
+  // (wavefront 0): the step's first loads then wait for nothing but
+  // themselves and the draw's chunk, requested just before (load counters
+  // are in order: a header still in flight in registers would make them
+  // wait for the chunk, and then take their own round trip).
   int d;
   float T;
   const int st0 = seq_check(a, b, &d, &T);
@@ -98,6 +103,11 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   float uv = 0.0f;
   if (tid < a.K) xv = a.draft[(int64_t)b * a.K + tid];
   if (tid < R && a.uniforms) uv = a.uniforms[(int64_t)b * R + tid];
+  constexpr int kSamWave = kWaves - 1;
+  int hv = 0, rv = 0;
+  if constexpr (SAM) {
+    if (w == kSamWave && l < 8) hv = S.hdr[l];
+  }
   if (one && tid < R * nc) sh.pc[tid] = pv;
   if (tid < a.K) sh.x[tid] = xv;
   if (tid < R) sh.u[tid] = uv;
@@ -116,12 +126,9 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     }
     return;
   }
-  // The header is fetched one dword per lane: a lane-varying value is not
-  // moved to scalar registers, so nothing waits for it before the step reads
-  // it with readlane.
-  int hv = 0, rv = 0;
   if constexpr (SAM) {
-    if (w == 0 && l < 8) hv = S.hdr[l];
+    if (w == kSamWave && l < 4)
+      rv = reinterpret_cast<const int*>(S.st)[__builtin_amdgcn_readlane(hv, H_LAST) * 4 + l];
   }
   const bool greedy = (T == 0.0f);
   const float kk = greedy ? 0.0f : kLog2e / T;
@@ -216,24 +223,62 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     combine_rows([&](int j, int c) { return sh.pc[j * nc + c]; });
   else
     combine_rows([&](int j, int c) { return load_partial(Pb + (int64_t)j * nc + c); });
+  if constexpr (SAM) {
+    if (w == kSamWave && l < 8) {
+      sh.hdr[l] = hv;
+      if (l < 4) sh.rec[l] = rv;
+    }
+  }
   __syncthreads();
   if constexpr (SAM) {
-    if (w == 0 && l < 4)
-      rv = reinterpret_cast<const int*>(S.st)[__builtin_amdgcn_readlane(hv, H_LAST) * 4 + l];
-  }
-  // The bonus row's chosen chunk is requested before the accept scan: row d
-  // is the draw row whenever every draft is accepted, and always when d = 0.
-  u32x4 raw[kLoads];
-  const bool spec = !greedy && sh.pick[d].chunk >= 0;
-  if (spec) draw_load<DT, VP>(a, b, d, sh.pick[d], raw);
-  if (w == 0) {
-    int st = 0, x = -1;
-    if (l < d) {
-      x = sh.x[l];
-      if (x < 0 || x >= a.V) st |= SS_ST_TOKEN_RANGE;
+    if (w == 0) {
+      hv = (l < 8) ? sh.hdr[l] : 0;
+      rv = (l < 4) ? sh.rec[l] : 0;
     }
-    if (l <= d && sh.bad[l]) st |= SS_ST_NONFINITE;
-    st = wave_or(st);
+  }
+  // Draw rows: row 0 (the first draft rejected, or no drafts) and row d
+  // (every draft accepted) are the likely ones. Their chosen chunks are
+  // requested before the accept scan; another row's after it. With q given,
+  // a rejection's draw is the residual kernels' work: only row d is drawn
+  // here.
+  u32x4 raw[kLoads], rawd[kLoads];
+  if (!greedy) {
+    if constexpr (Q) {
+      draw_load<DT, VP>(a, b, d, sh.pick[d], raw);
+    } else {
+      draw_load<DT, VP>(a, b, 0, sh.pick[0], raw);
+      if (d > 0) draw_load<DT, VP>(a, b, d, sh.pick[d], rawd);
+    }
+  }
+  // The accept scan. Every wavefront takes it (the same LDS inputs through
+  // the same instructions: the same result), so that each can request the
+  // draw row's chunk with no barrier in between; wavefront 0 writes the
+  // outputs.
+  int st = 0, x = -1;
+  if (l < d) {
+    x = sh.x[l];
+    if (x < 0 || x >= a.V) st |= SS_ST_TOKEN_RANGE;
+  }
+  if (l <= d && sh.bad[l]) st |= SS_ST_NONFINITE;
+  st = wave_or(st);
+  bool acc = true;
+  float px = -1.0f;
+  if (!st && l < d) {
+    if (greedy) {
+      acc = (x == sh.idx[l]);
+    } else {
+      px = (sh.lx[l] >= sh.lam[l]) ? fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l]
+                                   : 0.0f;
+      const float qx = Q ? sh.qx[l] : 1.0f;
+      acc = (qx > 0.0f) ? (sh.u[l] <= px / qx) : (px > 0.0f);
+    }
+  }
+  // Wavefront scan of the accept flags: the first rejection ends the run.
+  const unsigned long long rej = __ballot(!acc);
+  const int ral = rej ? __ffsll((unsigned long long)rej) - 1 : d;
+  if (!Q && !st && !greedy && ral > 0 && ral < d)
+    draw_load<DT, VP>(a, b, ral, sh.pick[ral], raw);
+  if (w == 0) {
     if (st) {
       if (l == 0) {
         atomicOr(&a.status[b], st);
@@ -241,22 +286,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         sh.acc_len = 0;
       }
     } else {
-      bool acc = true;
-      float px = -1.0f;
-      if (l < d) {
-        if (greedy) {
-          acc = (x == sh.idx[l]);
-        } else {
-          px = (sh.lx[l] >= sh.lam[l])
-                   ? fast_exp2((sh.lx[l] - sh.m[l]) * kk) / sh.s[l]
-                   : 0.0f;
-          const float qx = Q ? sh.qx[l] : 1.0f;
-          acc = (qx > 0.0f) ? (sh.u[l] <= px / qx) : (px > 0.0f);
-        }
-      }
-      // Wavefront scan of the accept flags: the first rejection ends the run.
-      const unsigned long long rej = __ballot(!acc);
-      const int al = rej ? __ffsll((unsigned long long)rej) - 1 : d;
+      const int al = ral;
       if (l < R) {
         int tok = -1;
         if (l < al)
@@ -306,24 +336,27 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   const bool drawn = sh.st == 0 && !greedy && !residual;
   if (drawn) {
     const OneToken excl{(al < d) ? sh.x[al] : -1};
-    if (!spec || al != d) draw_load<DT, VP>(a, b, al, sh.pick[al], raw);
-    auto during = [&]() {
-      if constexpr (SAM) {
-        if (w == 0) {
-          cs = cursor_from_lanes(hv, rv);
-          cs_ready = true;
-          if (al > 0) {
-            whole = sam_append(S, cs, sh.tok, al, R, a.max_len);
-            appended = al;
-          } else {
-            sam_cursor_fetch_link(S, cs);
-          }
+    if constexpr (SAM) {
+      if (w == 0) {
+        cs = cursor_from_lanes(hv, rv);
+        cs_ready = true;
+        if (al > 0) {
+          whole = sam_append(S, cs, sh.tok, al, R, a.max_len);
+          appended = al;
+        } else {
+          sam_cursor_fetch_link(S, cs);
         }
       }
-    };
+    }
+    // Row d's chunk is taken when it is the draw row: a copy, which waits
+    // for it, so it comes after the automaton step.
+    if (!Q && al == d && d > 0) {
+#pragma unroll
+      for (int it = 0; it < kLoads; ++it) raw[it] = rawd[it];
+    }
     const int tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, sh.pick[al],
                                                  excl, sh.m[al], kk, 0.0f, sh.lam[al],
-                                                 raw, during);
+                                                 raw);
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
