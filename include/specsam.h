@@ -121,9 +121,10 @@ size_t ss_verify_workspace_bytes_ex(int B, int K, int V, int flags);
  *   q           [B, K, V] float draft probabilities, or NULL for one-hot;
  *               16-byte aligned like logits.
  *   temperature [B] float >= 0.
- *   uniforms    [B, K+1] float in [0, 1): columns 0..K-1 are the acceptance
+ *   uniforms    [B, K+1] float in [0, 1]: columns 0..K-1 are the acceptance
  *               coins, column K the final coin. May be NULL only if every
- *               temperature is 0.
+ *               temperature is 0. A final coin of 1 takes the distribution's
+ *               last token of positive weight (the inverse CDF's limit).
  *   top_k       [B] int32 or NULL; top_p [B] float or NULL: truncation of the
  *               target distribution of a sequence at T > 0 before it is used
  *               anywhere above ([P3] "SGLang 的实现": the target probabilities
@@ -207,7 +208,7 @@ int spec_step(const void* logits, int dtype, int B, int K, int V,
  * SS_EWORKSPACE when the sizes need more than SS_SCRATCH_BYTES of workspace
  * (ss_verify_workspace_bytes_ex(B, K, V, flags) > SS_SCRATCH_BYTES, with
  * SS_WS_TRUNCATION when top_k or top_p is given): e.g. B = 256, K = 3,
- * V = 151936 needs about 0.34 MB; truncation needs far more.
+ * V = 151936 needs about 0.65 MB; truncation needs far more.
  */
 #define SS_SCRATCH_BYTES ((size_t)8 << 20)
 int spec_step_noalloc(const void* logits, int dtype, int B, int K, int V,
@@ -273,7 +274,7 @@ int spec_finish(const void* logits, int dtype, int B, int K, int V,
  *   logits      [B, N, V] (dtype and alignment as spec_verify); rows >=
  *               n_nodes[b] unread.
  *   tokens, parent [B, N] int32; n_nodes [B] int32 in [1, N].
- *   temperature [B]; uniforms [B, N] float in [0, 1) (coins per depth, the
+ *   temperature [B]; uniforms [B, N] float in [0, 1] (coins per depth, the
  *               last column the final coin), NULL only if every T is 0.
  *   out_tokens  [B, N] int32: accepted tokens then the final token, -1 after.
  *   out_nodes   [B, N] int32: the node each emitted token came from (the

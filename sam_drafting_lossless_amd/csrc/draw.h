@@ -38,7 +38,10 @@ namespace {
 // ---------------------------------------------------------------------------
 struct ChunkPick {
   int chunk;    // -1: every weight is 0
-  double t_in;  // target left inside the chunk; +inf: take its last positive
+  double t_in;  // target left inside the chunk (the slice, when one is
+                // chosen); +inf: take its last positive
+  int slice;    // -1: the whole chunk; else the quarter that holds the
+                // target (pick_slice)
 };
 
 // Weight of a chunk relative to the row max m: its partial sum s (relative
@@ -55,6 +58,45 @@ __device__ __forceinline__ double chunk_weight(float s, float mc, float m, float
   const double fl = floor(e);
   const float fr = (float)(e - fl);  // in [0, 1)
   return ldexp((double)s * (double)fast_exp2(fr), (int)fl);
+}
+
+// A chunk split in quarters, in token order (quarter q: the stream layout's
+// loads 2q and 2q + 1, 2 * 256 contiguous vectors), with weights w0..w3
+// (double). The chunk's weight is (w0 + w1) + (w2 + w3), and the running
+// sums in pick_slice are formed so that the last one is that same value: a
+// target the chunk pick left below the chunk's weight always falls in a
+// quarter.
+// Scale of a chunk's sums (relative to its max mc) to the row max m:
+// exp2((mc - m) * kk), as chunk_weight forms it (0 below every double, NaN
+// for a NaN exponent).
+__device__ __forceinline__ double chunk_scale(float mc, float m, float kk) {
+  const double e = ((double)mc - (double)m) * (double)kk;
+  if (e != e) return (double)NAN;
+  if (e < -4096.0) return 0.0;
+  const double fl = floor(e);
+  return ldexp((double)fast_exp2((float)(e - fl)), (int)fl);
+}
+struct QuarterW {
+  double w0, w1, w2, w3;
+  __device__ double chunk() const { return (w0 + w1) + (w2 + w3); }
+};
+__device__ __forceinline__ void pick_slice(ChunkPick& pk, const QuarterW& q) {
+  const double w0 = q.w0, w1 = q.w1, w2 = q.w2, w3 = q.w3;
+  const double c1 = w0 + w1, c2 = c1 + w2, c3 = c1 + (w2 + w3);
+  const double t = pk.t_in;
+  // (scalar selects: an indexed local array would live in scratch memory)
+  const int hit = w0 > t ? 0 : c1 > t ? 1 : c2 > t ? 2 : c3 > t ? 3 : -1;
+  const int lastpos = w3 > 0.0 ? 3 : w2 > 0.0 ? 2 : w1 > 0.0 ? 1 : w0 > 0.0 ? 0 : -1;
+  if (hit >= 0) {
+    const double before = hit == 0 ? 0.0 : hit == 1 ? w0 : hit == 2 ? c1 : c2;
+    pk.slice = hit;
+    pk.t_in = fmax(0.0, t - before);
+  } else {
+    // Rounding put the target past the chunk: its last positive quarter,
+    // and that quarter's last positive token.
+    pk.slice = lastpos < 0 ? 3 : lastpos;
+    pk.t_in = INFINITY;
+  }
 }
 
 // One wavefront, all lanes active; weight(c) (a double) is called for c < nc.
@@ -76,7 +118,7 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
     }
   }
   const double t = (double)u * carry;
-  ChunkPick r{-1, INFINITY};
+  ChunkPick r{-1, INFINITY, -1};
   int lastpos = -1;
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
@@ -204,16 +246,44 @@ struct NoDuring {
 // load_chunk_flat) and draw_in_chunk sets the values past the row's end:
 // load_chunk's two paths, joined here, made the compiler wait for every
 // load in flight before the full-chunk path's loads.
+// With a quarter chosen (vector path only) each thread requests two
+// vectors: the stream layout's loads 2q and 2q + 1.
+constexpr int kSliceLoads = 2;
+
+// Vector index, within the chunk, of load `it` of this thread: the stream
+// layout, for the whole chunk or from quarter qs on.
+template <bool SLICE>
+__device__ __forceinline__ int draw_vec(int it, int qs) {
+  return ((SLICE ? 2 * qs : 0) + it) * kThreads + (int)threadIdx.x;
+}
+
+// The whole chunk (pk.slice < 0).
 template <int DT, bool VP>
 __device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick pk,
                                           u32x4 (&raw)[kLoads]) {
   if (pk.chunk < 0) return;
   const unsigned char* row =
       a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes;
+  const int cstart = pk.chunk * kChunk<DT>;
   if constexpr (VP)
-    load_chunk_flat<DT, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
+    load_chunk_flat<DT, false>(row, cstart, a.V, threadIdx.x, raw);
   else
-    load_chunk<DT, VP, false>(row, pk.chunk * kChunk<DT>, a.V, threadIdx.x, raw);
+    load_chunk<DT, VP, false>(row, cstart, a.V, threadIdx.x, raw);
+}
+// The chosen quarter (pk.slice >= 0, vector path). A separate array from
+// the whole chunk's: one array written by both, with different lengths, was
+// given a memory home by the compiler.
+template <int DT>
+__device__ __forceinline__ void draw_load_slice(const Args& a, int b, int r, ChunkPick pk,
+                                                u32x4 (&rs)[kSliceLoads]) {
+  if (pk.chunk < 0) return;
+  const unsigned char* row =
+      a.logits + ((int64_t)b * (a.K + 1) + r) * a.V * Dt<DT>::kBytes;
+  const int cstart = pk.chunk * kChunk<DT>;
+  const u32x4* p = reinterpret_cast<const u32x4*>(row + (int64_t)cstart * Dt<DT>::kBytes);
+  const int last = (a.V - cstart) / kVec<DT> - 1;
+#pragma unroll
+  for (int it = 0; it < kSliceLoads; ++it) rs[it] = p[min(draw_vec<true>(it, pk.slice), last)];
 }
 
 // Whole workgroup; `pk` must be the same in every thread and `raw_in` hold the
@@ -221,55 +291,77 @@ __device__ __forceinline__ void draw_load(const Args& a, int b, int r, ChunkPick
 // in flight (the fused step appends the accepted drafts to the automaton
 // there).
 // RESIDUAL: q holds the chunk's q (load_q_chunk), requested with `raw_in`.
+// SLICE: pk.slice >= 0 and `raw_in` holds that quarter (draw_load_slice);
+// the cells are then its 2 loads times 4 wavefronts, in token order as for
+// a whole chunk.
 template <int DT, bool VP, bool RESIDUAL, typename Excl, typename During = NoDuring,
-          typename Q = NoQ>
+          typename Q = NoQ, bool SLICE = false>
 __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int b, int r,
                                              ChunkPick pk, Excl excl, float m, float kk,
                                              float invS, float lam,
-                                             const u32x4 (&raw_in)[kLoads],
+                                             const u32x4 (&raw_in)[SLICE ? kSliceLoads : kLoads],
                                              During during = During{}, const Q& q = Q{}) {
+  static_assert(!SLICE || (VP && !RESIDUAL), "slices: vector path, draws from p");
+  constexpr int NL = SLICE ? kSliceLoads : kLoads;
+  constexpr unsigned kNegInfWord = DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   during();
   if (pk.chunk < 0) return -1;
   const int cstart = pk.chunk * kChunk<DT>;
-  u32x4 raw[kLoads];
+  const int qs = SLICE ? pk.slice : 0;
+  u32x4 raw[NL];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) raw[it] = raw_in[it];
+  for (int it = 0; it < NL; ++it) raw[it] = raw_in[it];
   if constexpr (VP) {
-    if (a.V - cstart < kChunk<DT>) chunk_tail_neginf<DT>(cstart, a.V, tid, raw);
+    // vectors past the row's end (their loads were clamped into the row)
+    const int rem = a.V - cstart;
+    if (rem < kChunk<DT>) {
+#pragma unroll
+      for (int it = 0; it < NL; ++it) {
+        const bool in = draw_vec<SLICE>(it, qs) * kVec<DT> < rem;
+        const u32x4 x = raw[it];
+        raw[it] = u32x4{in ? x[0] : kNegInfWord, in ? x[1] : kNegInfWord,
+                        in ? x[2] : kNegInfWord, in ? x[3] : kNegInfWord};
+      }
+    }
   }
+  auto index = [&](int it, int k) {
+    if constexpr (SLICE)
+      return cstart + draw_vec<true>(it, qs) * kVec<DT> + k;
+    else
+      return elem_index<DT, VP>(cstart, tid, it, k);
+  };
   const float t_in = (float)pk.t_in;
   auto weight = [&](int it, int k) {
-    return draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k),
-                                     elem_index<DT, VP>(cstart, tid, it, k), excl, m, kk,
+    return draw_weight<DT, RESIDUAL>(elem<DT>(raw[it], k), index(it, k), excl, m, kk,
                                      invS, q.at(it, k), lam);
   };
-  float vs[kLoads];
+  float vs[NL];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) {
+  for (int it = 0; it < NL; ++it) {
     float acc = 0.0f;
 #pragma unroll
     for (int k = 0; k < kVec<DT>; ++k) acc += weight(it, k);
     vs[it] = acc;
   }
   // Cell (it, wave) totals: lane 63 of each wavefront's inclusive scan.
-  float tot[kLoads];
+  float tot[NL];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = vs[it];
+  for (int it = 0; it < NL; ++it) tot[it] = vs[it];
   wave_inclusive_sum_n(tot);
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it) tot[it] = lane63(tot[it]);
+  for (int it = 0; it < NL; ++it) tot[it] = lane63(tot[it]);
   if (l == 0) {
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) sh.cell[it * kWaves + w] = tot[it];
+    for (int it = 0; it < NL; ++it) sh.cell[it * kWaves + w] = tot[it];
   }
   __syncthreads();
   // Every wavefront finds the cell (the same scan gives the same answer).
-  const float cv = (l < kLoads * kWaves) ? sh.cell[l] : 0.0f;
+  const float cv = (l < NL * kWaves) ? sh.cell[l] : 0.0f;
   const float inc = wave_inclusive_sum(cv);
   const float exc = wave_shift_up1(inc);
   const unsigned long long hit =
-      __ballot(l < kLoads * kWaves && exc <= t_in && t_in < inc);
+      __ballot(l < NL * kWaves && exc <= t_in && t_in < inc);
   const int cell = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
   if (cell < 0) {
     if (tid == 0) sh.result = kDrawPastEnd;
@@ -277,7 +369,7 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
     const int its = cell / kWaves;
     float v = vs[0];
 #pragma unroll
-    for (int it = 1; it < kLoads; ++it)
+    for (int it = 1; it < NL; ++it)
       if (it == its) v = vs[it];
     const float tc = fmaxf(0.0f, t_in - readlane_f(exc, cell));
     const float inc2 = wave_inclusive_sum(v);
@@ -293,7 +385,7 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) qv[k] = q.at(0, k);
 #pragma unroll
-      for (int it = 1; it < kLoads; ++it)
+      for (int it = 1; it < NL; ++it)
         if (it == its) {
           rv = raw[it];
 #pragma unroll
@@ -303,7 +395,7 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
       int found = -1, lastp = -1;
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k) {
-        const int i = elem_index<DT, VP>(cstart, tid, its, k);
+        const int i = index(its, k);
         const float lk = elem<DT>(rv, k);
         const float wk = draw_weight<DT, RESIDUAL>(lk, i, excl, m, kk, invS, qv[k], lam);
         run += wk;
@@ -322,16 +414,16 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
   }
   __syncthreads();
   if (sh.result == kDrawPastEnd) {
-    // The target lies past the re-read total (rounding): the chunk's last
-    // token of positive weight, found only now, as the common path needs
+    // The target lies past the re-read total (rounding): the last token of
+    // positive weight it re-read, found only now, as the common path needs
     // none of it. The weights are the same instructions on the same inputs
     // as above, so the same ones are positive.
     int tlast = -1;
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it)
+    for (int it = 0; it < NL; ++it)
 #pragma unroll
       for (int k = 0; k < kVec<DT>; ++k)
-        if (weight(it, k) > 0.0f) tlast = max(tlast, elem_index<DT, VP>(cstart, tid, it, k));
+        if (weight(it, k) > 0.0f) tlast = max(tlast, index(it, k));
     tlast = wave_max_i(tlast);
     if (l == 0) sh.wlast[w] = tlast;
     __syncthreads();

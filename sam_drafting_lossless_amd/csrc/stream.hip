@@ -68,7 +68,7 @@ inline int row_lanes(int B, int K, int nchunks) {
 template <int DT, bool VP, bool TR>
 __global__ __launch_bounds__(kThreads, ((VP && TR) ? kStreamWaves<DT, TR> : 1)) void
 spec_stream_kernel(Args a) {
-  __shared__ f32x4 red[kWaves + 1];
+  __shared__ f32x4 red[2 * kWaves + 1];
   __shared__ TrLds<TR> tl;
   TrShared* ts = nullptr;
   if constexpr (TR) ts = &tl.s;

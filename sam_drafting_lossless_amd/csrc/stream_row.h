@@ -128,7 +128,8 @@ __device__ __forceinline__ int3 choose_band(const unsigned long long* hs, float 
 // holds the chunk; `mid` runs once every element has been consumed (after
 // the last pass that reads `raw`), before the workgroup reduction. With TR, a
 // truncated row also leaves its chunk's window histogram and band (ts is the
-// LDS for them). Ends with a barrier, so `red` and `ts` may be reused at once.
+// LDS for them). `red` holds 2 * kWaves + 1 entries. Ends with a barrier, so
+// `red` and `ts` may be reused at once.
 
 // x is the draft token of row j (or -1), requested with the chunk. XREG:
 // the lane holding its logit takes it with a select as the fold consumes
@@ -401,42 +402,57 @@ __device__ __forceinline__ void stream_row(const Args& a, int b, int j, int d,
     part = f32x4{pm, ps, hasx ? red[kWaves].x : lx, 0.0f};
     }
   } else {
-    // Online (max, sum exp2) folded one 16-byte vector at a time, in the
-    // order the loads return, so only the raw vectors stay live. The draft
-    // token's logit is taken in a copy of the loop that only the chunk
-    // holding it runs (hasx is the same for the whole workgroup).
-    float m = kNegInf, s = 0.0f;
-    auto fold = [&](auto take_x) {
+    // Two passes over the registers: the chunk max M, then each element's
+    // weight exp2((l - M) * log2e / T), summed per quarter of the chunk
+    // (loads 2q and 2q + 1: a contiguous quarter of its tokens). The
+    // partial's sum is the quarters' (s0 + s1) + (s2 + s3); the quarter sums
+    // let a draw from this chunk re-read one quarter. The draft token's
+    // logit is taken in a copy of the max loop that only the chunk holding
+    // it runs (hasx is the same for the whole workgroup).
+    static_assert(kLoads == 8 && kWaves == 4, "quarters of two loads");
+    float vm = kNegInf;
+    auto max_pass = [&](auto take_x) {
 #pragma unroll
-      for (int it = 0; it < kLoads; ++it) {
-        float vm = kNegInf;
-#pragma unroll
-        for (int k = 0; k < kVec<DT>; ++k) vm = fmaxf(vm, elem<DT>(raw[it], k));
-        const float mn = fmaxf(m, vm);
-        const float base = (mn == kNegInf) ? 0.0f : mn;
-        float t = s * fast_exp2((m - base) * kk);
+      for (int it = 0; it < kLoads; ++it)
 #pragma unroll
         for (int k = 0; k < kVec<DT>; ++k) {
           const float v = elem<DT>(raw[it], k);
-          t += fast_exp2((v - base) * kk);
+          vm = fmaxf(vm, v);
           if constexpr (decltype(take_x)::value) xv = (ex == it * kVec<DT> + k) ? v : xv;
         }
-        s = t;
-        m = mn;
-      }
     };
     if (hasx)
-      fold(std::true_type{});
+      max_pass(std::true_type{});
     else
-      fold(std::false_type{});
-    if (ex >= 0) red[kWaves].x = xv;  // read after the reduction's barrier
-    mid();
-    wave_lse(m, s, kk);
-    if (l == 0) red[w] = f32x4{m, s, 0.0f, 0.0f};
+      max_pass(std::false_type{});
+    if (ex >= 0) red[kWaves].x = xv;  // read after the barriers below
+    vm = wave_max(vm);
+    if (l == 0) red[w].x = vm;
     __syncthreads();
-    float pm = red[0].x, ps = red[0].y;
-    for (int i = 1; i < kWaves; ++i) lse_merge(pm, ps, red[i].x, red[i].y, kk);
-    part = f32x4{pm, ps, hasx ? red[kWaves].x : lx, 0.0f};
+    float pm = red[0].x;
+    for (int i = 1; i < kWaves; ++i) pm = fmaxf(pm, red[i].x);
+    const float base = (pm == kNegInf) ? 0.0f : pm;
+    float sq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float t = 0.0f;
+#pragma unroll
+      for (int it = 2 * q; it < 2 * q + 2; ++it)
+#pragma unroll
+        for (int k = 0; k < kVec<DT>; ++k) t += fast_exp2((elem<DT>(raw[it], k) - base) * kk);
+      sq[q] = t;
+    }
+    mid();
+    wave_inclusive_sum_n(sq);
+    if (l == kWave - 1) red[kWaves + 1 + w] = f32x4{sq[0], sq[1], sq[2], sq[3]};
+    __syncthreads();
+    f32x4 qs = red[kWaves + 1];
+    for (int i = 1; i < kWaves; ++i) {
+      const f32x4 o = red[kWaves + 1 + i];
+      qs = f32x4{qs.x + o.x, qs.y + o.y, qs.z + o.z, qs.w + o.w};
+    }
+    part = f32x4{pm, (qs.x + qs.y) + (qs.z + qs.w), hasx ? red[kWaves].x : lx, 0.0f};
+    if (tid == 0 && a.wparts) a.wparts[row * nc + c] = qs;
   }
   if (tid == 0) a.partials[row * nc + c] = part;
   __syncthreads();  // red[] is reused by the next row

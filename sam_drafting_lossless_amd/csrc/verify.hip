@@ -46,6 +46,7 @@ constexpr int kPartialCache = 1024;
 
 struct FinalShared {
   f32x4 pc[kPartialCache];
+  f32x4 wc[kPartialCache];  // the chunks' quarter sums (cached with pc)
   float m[kMaxRows];
   float s[kMaxRows];         // sum of the weights the row's decisions use
   float su[kMaxRows];        // untruncated sum (log-probabilities)
@@ -65,8 +66,10 @@ struct FinalShared {
   DrawShared draw;
 };
 
-// Q: draft probabilities q are given (then SAM is false).
-template <int DT, bool VP, bool SAM, bool Q>
+// Q: draft probabilities q are given (then SAM is false). SL: draws re-read
+// one quarter of the chosen chunk (vector path, no truncation, partials
+// cached: the launch guarantees all three).
+template <int DT, bool VP, bool SAM, bool Q, bool SL>
 __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   __shared__ FinalShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
@@ -93,11 +96,20 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   // (The common case has at most one partial per thread; more go through a
   // plain loop.)
   const bool one = cached && R * nc <= kThreads;  // uniform
-  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Quarter sums (the draw's slices); a row that was not streamed, or a
+  // greedy one, leaves stale values no draw reads.
+  constexpr bool slices = VP && SL;
+  const f32x4* Wb = slices ? a.wparts + (int64_t)b * R * nc : nullptr;
+  f32x4 pv = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, wv = pv;
   if (one) {
-    pv = Pb[min(tid, R * nc - 1)];
+    const int e = min(tid, R * nc - 1);
+    pv = Pb[e];
+    if constexpr (slices) wv = Wb[e];
   } else if (cached) {
-    for (int e = tid; e < R * nc; e += kThreads) sh.pc[e] = Pb[e];
+    for (int e = tid; e < R * nc; e += kThreads) {
+      sh.pc[e] = Pb[e];
+      if constexpr (slices) sh.wc[e] = Wb[e];
+    }
   }
   int xv = -1;
   float uv = 0.0f;
@@ -108,7 +120,10 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   if constexpr (SAM) {
     if (w == kSamWave && l < 8) hv = S.hdr[l];
   }
-  if (one && tid < R * nc) sh.pc[tid] = pv;
+  if (one && tid < R * nc) {
+    sh.pc[tid] = pv;
+    if constexpr (slices) sh.wc[tid] = wv;
+  }
   if (tid < a.K) sh.x[tid] = xv;
   if (tid < R) sh.u[tid] = uv;
   __syncthreads();
@@ -197,16 +212,43 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         const float wx = (j < d && hb && lxv >= lam) ? fast_exp2((lxv - m) * kk) : 0.0f;
         const int cxw = (j < d) ? cx : -1;
         const float uK = sh.u[a.K];
-        const ChunkPick pk = pick_chunk(nc, uK, [&](int c) {
-          double W;
-          if (trunc) {
-            W = a.tpart[rw * nc + c];
-          } else {
-            const f32x4 p = part(j, c);
-            W = chunk_weight(p.y, p.x, m, kk);
-          }
-          return c == cxw ? fmax(0.0, W - (double)wx) : W;
-        });
+        ChunkPick pk;
+        if constexpr (slices) {
+          // From the quarter sums: a chunk weighs the sum of its quarters',
+          // and x_j leaves its quarter in the chunk's own frame (its term as
+          // the stream pass formed it): a quarter holding nothing else but
+          // x_j then weighs exactly 0.
+          const int xq = (cxw >= 0 && hb)
+                             ? (xj - cx * kChunk<DT>) / kVec<DT> / kThreads / 2
+                             : -1;
+          auto quarters = [&](int c) {
+            const f32x4 qs = sh.wc[j * nc + c];
+            const float mc = sh.pc[j * nc + c].x;
+            const double sc = chunk_scale(mc, m, kk);
+            double s0 = qs.x, s1 = qs.y, s2 = qs.z, s3 = qs.w;
+            if (c == cxw) {
+              const double wxr = fast_exp2((lxv - mc) * kk);
+              s0 = xq == 0 ? fmax(0.0, s0 - wxr) : s0;
+              s1 = xq == 1 ? fmax(0.0, s1 - wxr) : s1;
+              s2 = xq == 2 ? fmax(0.0, s2 - wxr) : s2;
+              s3 = xq == 3 ? fmax(0.0, s3 - wxr) : s3;
+            }
+            return QuarterW{s0 * sc, s1 * sc, s2 * sc, s3 * sc};
+          };
+          pk = pick_chunk(nc, uK, [&](int c) { return quarters(c).chunk(); });
+          if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk));
+        } else {
+          pk = pick_chunk(nc, uK, [&](int c) {
+            double W;
+            if (trunc) {
+              W = a.tpart[rw * nc + c];
+            } else {
+              const f32x4 p = part(j, c);
+              W = chunk_weight(p.y, p.x, m, kk);
+            }
+            return c == cxw ? fmax(0.0, W - (double)wx) : W;
+          });
+        }
         if (l == 0) {
           sh.m[j] = m;
           sh.s[j] = st;
@@ -241,13 +283,21 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   // requested before the accept scan; another row's after it. With q given,
   // a rejection's draw is the residual kernels' work: only row d is drawn
   // here.
-  u32x4 raw[kLoads], rawd[kLoads];
+  // A row's pick takes either its chunk's quarter (rs) or the whole chunk
+  // (raw).
+  u32x4 raw[kLoads], rawd[kLoads], rs[kSliceLoads], rsd[kSliceLoads];
+  auto load_pick = [&](int r, u32x4 (&full)[kLoads], u32x4 (&part)[kSliceLoads]) {
+    if constexpr (slices)
+      draw_load_slice<DT>(a, b, r, sh.pick[r], part);
+    else
+      draw_load<DT, VP>(a, b, r, sh.pick[r], full);
+  };
   if (!greedy) {
     if constexpr (Q) {
-      draw_load<DT, VP>(a, b, d, sh.pick[d], raw);
+      load_pick(d, raw, rs);
     } else {
-      draw_load<DT, VP>(a, b, 0, sh.pick[0], raw);
-      if (d > 0) draw_load<DT, VP>(a, b, d, sh.pick[d], rawd);
+      load_pick(0, raw, rs);
+      if (d > 0) load_pick(d, rawd, rsd);
     }
   }
   // The accept scan. Every wavefront takes it (the same LDS inputs through
@@ -276,8 +326,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   // Wavefront scan of the accept flags: the first rejection ends the run.
   const unsigned long long rej = __ballot(!acc);
   const int ral = rej ? __ffsll((unsigned long long)rej) - 1 : d;
-  if (!Q && !st && !greedy && ral > 0 && ral < d)
-    draw_load<DT, VP>(a, b, ral, sh.pick[ral], raw);
+  if (!Q && !st && !greedy && ral > 0 && ral < d) load_pick(ral, raw, rs);
   if (w == 0) {
     if (st) {
       if (l == 0) {
@@ -350,13 +399,23 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     }
     // Row d's chunk is taken when it is the draw row: a copy, which waits
     // for it, so it comes after the automaton step.
+    const ChunkPick pk = sh.pick[al];
     if (!Q && al == d && d > 0) {
+      if constexpr (slices) {
 #pragma unroll
-      for (int it = 0; it < kLoads; ++it) raw[it] = rawd[it];
+        for (int it = 0; it < kSliceLoads; ++it) rs[it] = rsd[it];
+      } else {
+#pragma unroll
+        for (int it = 0; it < kLoads; ++it) raw[it] = rawd[it];
+      }
     }
-    const int tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, sh.pick[al],
-                                                 excl, sh.m[al], kk, 0.0f, sh.lam[al],
-                                                 raw);
+    int tok;
+    if constexpr (slices)
+      tok = draw_in_chunk<DT, VP, false, OneToken, NoDuring, NoQ, true>(
+          a, sh.draw, b, al, pk, excl, sh.m[al], kk, 0.0f, sh.lam[al], rs);
+    else
+      tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, pk, excl, sh.m[al], kk, 0.0f,
+                                         sh.lam[al], raw);
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
@@ -508,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
 // Workspace layout (bytes, each region 256-byte aligned).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t partials, seqinfo, seqinfo2, rpart;
+  size_t partials, wparts, seqinfo, seqinfo2, rpart;
   // truncation (top-k / top-p) regions; zero-sized without it
   size_t hist, hhdr, cand, tpart, tinfo;
   size_t total;
@@ -531,6 +590,7 @@ WsLayout ws_layout(int B, int K, int V, bool trunc) {
     o = align256(o + bytes);
   };
   take(L.partials, rows * nc * sizeof(f32x4));
+  take(L.wparts, rows * nc * sizeof(f32x4));
   take(L.seqinfo, (size_t)B * sizeof(i32x4));
   take(L.seqinfo2, (size_t)B * sizeof(f32x4));
   take(L.rpart, (size_t)B * nc * sizeof(float));
@@ -544,14 +604,26 @@ WsLayout ws_layout(int B, int K, int V, bool trunc) {
   return L;
 }
 
-template <int DT, bool VP, bool SAM>
-int launch_finish(const Args& a, hipStream_t s) {
+template <int DT, bool VP, bool SAM, bool SL>
+void launch_finalize(const Args& a, hipStream_t s) {
   if (a.q)
-    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, false, true>), dim3((unsigned)a.B),
+    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, false, true, SL>), dim3((unsigned)a.B),
                        dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM, false>), dim3((unsigned)a.B),
+    hipLaunchKernelGGL((spec_finalize_kernel<DT, VP, SAM, false, SL>), dim3((unsigned)a.B),
                        dim3(kThreads), 0, s, a);
+}
+
+template <int DT, bool VP, bool SAM>
+int launch_finish(const Args& a, hipStream_t s) {
+  // Quarters: their sums exist (vector path), no row truncates, and every
+  // row's partials fit the finalize's cache.
+  const bool sl = VP && a.wparts != nullptr && a.tinfo == nullptr &&
+                  (a.K + 1) * a.nchunks <= kPartialCache;
+  if (sl)
+    launch_finalize<DT, VP, SAM, true>(a, s);
+  else
+    launch_finalize<DT, VP, SAM, false>(a, s);
   int rc = check_launch("spec_finish");
   if (rc != SS_OK || a.q == nullptr) return rc;
   hipLaunchKernelGGL((verify_residual_sums<DT, VP>),
@@ -635,6 +707,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.top_p = top_p;
   a.status = status;
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
+  a.wparts = reinterpret_cast<f32x4*>(ws + L.wparts);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
   a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);

@@ -210,6 +210,8 @@ struct Args {
   const float* top_p;    // [B] or NULL
   int32_t* status;
   f32x4* partials;  // [B*(K+1)*nchunks]: (max, sumexp | nan flag, l[x], argidx)
+  f32x4* wparts;    // [B*(K+1)*nchunks] or NULL: an untruncated T > 0 chunk's
+                    //   sums per quarter (loads 2q, 2q+1), relative to its max
   i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
   float* rpart;     // [B*nchunks] residual chunk sums
   f32x4* seqinfo2;  // [B]: (truncation threshold, untruncated S, 0, 0)

@@ -390,6 +390,106 @@ def test_draw_target_on_a_chunk_boundary():
     np.testing.assert_array_equal(g[1], [1, 1])
 
 
+# ------------------------- draw: quarters of a chunk, the top coin, gaps ---
+# Token positions on both sides of every quarter boundary (2048 fp32 tokens,
+# 4096 bf16) and chunk boundary (8192 / 16384) of the first two chunks, and
+# in a ragged last chunk.
+def _boundary_tokens(V, per_chunk):
+    q = per_chunk // 4
+    pos = [5]
+    for c in range(2):
+        for i in range(1, 5):
+            e = c * per_chunk + i * q
+            pos += [e - 1, e]
+    pos += [V - 3, V - 1]
+    return sorted(p for p in set(pos) if p < V)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_draw_every_quarter_and_chunk_boundary(dtype):
+    """Equal logits on tokens placed on both sides of each quarter and chunk
+    boundary (all others -inf), and one coin per CDF interval, at its middle:
+    the inverse CDF in token order must give exactly the k-th token for the
+    k-th interval. Rows without drafts draw from the row (n tokens); rows whose
+    single draft (one of the tokens) is rejected (its coin 1, p(x) = 1/n < 1)
+    draw from the rest (n - 1 tokens, the draft left out). A draw that took
+    quarters, chunks or their sums out of token order, or lost a boundary
+    token, fails here."""
+    say(f"[gpu] draw: quarter and chunk boundaries {dtype}")
+    per_chunk = 8192 if dtype == "f32" else 16384
+    V = 2 * per_chunk + 3 * 1024 + 8
+    pos = _boundary_tokens(V, per_chunk)
+    n = len(pos)
+    rows = []  # (draft token or -1, coin)
+    for k in range(n):
+        rows.append((-1, (k + 0.5) / n))
+    for xi in (0, n // 2, n - 1):
+        for k in range(n - 1):
+            rows.append((pos[xi], (k + 0.5) / (n - 1)))
+    B, K = len(rows), 1
+    x = np.full((B, K + 1, V), -np.inf, np.float32)
+    x[:, :, pos] = 0.0
+    draft = np.array([[max(t, 0)] for t, _ in rows], np.int32)
+    dl = np.array([0 if t < 0 else 1 for t, _ in rows], np.int32)
+    u = np.array([[1.0 if t >= 0 else 0.5, c] for t, c in rows], np.float32)
+    T = np.ones(B, np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    g, r = _run(t, draft, dl, T, u)
+    for b, (tx, c) in enumerate(rows):
+        rest = [p for p in pos if p != tx]
+        want = rest[int(c * len(rest))]
+        assert r.out_tokens[b].tolist() == [want, -1], (b, r.out_tokens[b], want)
+    np.testing.assert_array_equal(g[0], r.out_tokens)
+    np.testing.assert_array_equal(g[1], r.num_emitted)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_coin_takes_the_last_positive_token(dtype):
+    """A final coin of 1 (the top of its range) puts the draw's target at the
+    total weight, which no running sum exceeds: the inverse CDF's definition
+    then takes the last token of positive weight. Rows: random logits in
+    [-3, 0] up to a per-row cut, -inf from there on, except (half the rows)
+    the draft token x at logit 2.5, alone past the cut in its own chunk, and
+    one token before the cut at logit 3 (the row max, so that x's weight is
+    not the row's reference). x's coin is 1, so x is rejected (p(x) < 1) and
+    the draw is from the row without x: its last positive token is the one
+    just before the cut. x's quarter, and its chunk, must then weigh exactly
+    nothing: a rounding residue left by taking x's weight out would send the
+    top coin past every token the draw can still take. The other rows have
+    no drafts: their draw is the token just before the cut."""
+    say(f"[gpu] draw: top coin {dtype}")
+    per_chunk = 8192 if dtype == "f32" else 16384
+    V = 4 * per_chunk + 512
+    rng = np.random.default_rng(77 + (dtype == "bf16"))
+    B, K = 24, 1
+    x = np.full((B, K + 1, V), -np.inf, np.float32)
+    draft = np.zeros((B, K), np.int32)
+    dl = np.zeros(B, np.int32)
+    want = np.zeros(B, np.int64)
+    for b in range(B):
+        cut = int(rng.integers(per_chunk // 2, 3 * per_chunk))
+        x[b, :, :cut] = rng.uniform(-3.0, 0.0, (K + 1, cut)).astype(np.float32)
+        x[b, :, int(rng.integers(0, cut - 1))] = 3.0
+        want[b] = cut - 1
+        if b % 2 == 0:
+            xc = (cut // per_chunk + 1) * per_chunk + int(rng.integers(0, per_chunk))
+            xc = min(xc, V - 1)
+            x[b, 0, xc] = 2.5
+            draft[b, 0] = xc
+            dl[b] = 1
+    u = np.ones((B, K + 1), np.float32)
+    T = np.ones(B, np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    g, r = _run(t, draft, dl, T, u)
+    np.testing.assert_array_equal(r.out_tokens[:, 0], want)
+    np.testing.assert_array_equal(g[0], r.out_tokens)
+    np.testing.assert_array_equal(g[1], r.num_emitted)
+
+
 # ------------------------------------------------------------- alignment ---
 def test_misaligned_logits_or_q_are_rejected():
     """Logits and q must start on a 16-byte boundary (the stream pass reads
