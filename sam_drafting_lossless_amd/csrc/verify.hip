@@ -79,10 +79,11 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
   // the sequence's parameters, drafts, coins, the partials of every row and
   // the automaton's header. The last wavefront then requests the record of
   // the automaton's last state and leaves both in LDS for the step
-  // (wavefront 0): the step's first loads then wait for nothing but
-  // themselves and the draw's chunk, requested just before (load counters
-  // are in order: a header still in flight in registers would make them
-  // wait for the chunk, and then take their own round trip).
+  // (wavefront 0) at the accept scan's barrier: the step's first loads then
+  // wait for nothing but themselves and the draw's loads, requested just
+  // before (load counters are in order: a record still in flight in
+  // registers would make them wait for the draw's loads, and then take their
+  // own round trip).
   int d;
   float T;
   const int st0 = seq_check(a, b, &d, &T);
@@ -265,19 +266,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     combine_rows([&](int j, int c) { return sh.pc[j * nc + c]; });
   else
     combine_rows([&](int j, int c) { return load_partial(Pb + (int64_t)j * nc + c); });
-  if constexpr (SAM) {
-    if (w == kSamWave && l < 8) {
-      sh.hdr[l] = hv;
-      if (l < 4) sh.rec[l] = rv;
-    }
-  }
   __syncthreads();
-  if constexpr (SAM) {
-    if (w == 0) {
-      hv = (l < 8) ? sh.hdr[l] : 0;
-      rv = (l < 4) ? sh.rec[l] : 0;
-    }
-  }
   // Draw rows: row 0 (the first draft rejected, or no drafts) and row d
   // (every draft accepted) are the likely ones. Their chosen chunks are
   // requested before the accept scan; another row's after it. With q given,
@@ -366,7 +355,22 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
       }
     }
   }
+  // The automaton's header and last record, handed to wavefront 0 across the
+  // barrier below: the record, requested after the first barrier, has had
+  // the combine and the accept scan to arrive.
+  if constexpr (SAM) {
+    if (w == kSamWave && l < 8) {
+      sh.hdr[l] = hv;
+      if (l < 4) sh.rec[l] = rv;
+    }
+  }
   __syncthreads();
+  if constexpr (SAM) {
+    if (w == 0) {
+      hv = (l < 8) ? sh.hdr[l] : 0;
+      rv = (l < 4) ? sh.rec[l] : 0;
+    }
+  }
   const int al = sh.acc_len;
   const bool residual = Q && sh.st == 0 && !greedy && al < d;
   if (tid == 0) {
@@ -416,6 +420,8 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
     else
       tok = draw_in_chunk<DT, VP, false>(a, sh.draw, b, al, pk, excl, sh.m[al], kk, 0.0f,
                                          sh.lam[al], raw);
+    // (No barrier after this: the one reader of sh.tok[al], the automaton
+    // step, runs in wavefront 0, as does the thread that writes it.)
     if (tid == 0) {
       a.out[(int64_t)b * R + al] = tok;
       sh.tok[al] = tok;
@@ -423,7 +429,6 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
         a.logprob[(int64_t)b * R + al] =
             drawn_logprob<DT>(a, b, al, tok, sh.draw.result_l, sh.m[al], sh.su[al], kk);
     }
-    __syncthreads();
   }
   if constexpr (SAM) {
     if (w == 0) {
