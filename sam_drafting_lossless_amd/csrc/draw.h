@@ -167,9 +167,10 @@ __device__ __forceinline__ float draw_weight(float l, int i, Excl excl, float m,
 
 // q of a chunk for the residual, in the stream layout (element (it, k) of
 // the lane is token elem_index(cstart, tid, it, k)); 0 past the row's end.
-template <int DT>
+// NL = 2: the q of one quarter (draw_vec<true>).
+template <int DT, int NL = kLoads>
 struct QChunk {
-  float v[kLoads][kVec<DT>];
+  float v[NL][kVec<DT>];
   __device__ __forceinline__ float at(int it, int k) const { return v[it][k]; }
 };
 // No q (the draws from p).
@@ -291,6 +292,33 @@ __device__ __forceinline__ void draw_load_slice(const Args& a, int b, int r, Chu
 // in flight (the fused step appends the accepted drafts to the automaton
 // there).
 // RESIDUAL: q holds the chunk's q (load_q_chunk), requested with `raw_in`.
+// q of the chosen quarter qs (vector path), requested like load_q_chunk's,
+// and its values past the row's end set to 0 once every load is requested.
+template <int DT>
+__device__ __forceinline__ void load_q_slice(const float* qrow, int cstart, int V, int qs,
+                                             QChunk<DT, kSliceLoads>& q) {
+  constexpr int kH = kVec<DT> / 4;
+  const int last = (V - cstart) / 4 - 1;
+  const f32x4* p = reinterpret_cast<const f32x4*>(qrow + cstart);
+#pragma unroll
+  for (int it = 0; it < kSliceLoads; ++it)
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const f32x4 x = __builtin_nontemporal_load(p + min(draw_vec<true>(it, qs) * kH + h, last));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q.v[it][4 * h + k] = x[k];
+    }
+}
+template <int DT>
+__device__ __forceinline__ void q_slice_tail_zero(int cstart, int V, int qs,
+                                                  QChunk<DT, kSliceLoads>& q) {
+#pragma unroll
+  for (int it = 0; it < kSliceLoads; ++it)
+#pragma unroll
+    for (int k = 0; k < kVec<DT>; ++k)
+      q.v[it][k] = cstart + draw_vec<true>(it, qs) * kVec<DT> + k < V ? q.v[it][k] : 0.0f;
+}
+
 // SLICE: pk.slice >= 0 and `raw_in` holds that quarter (draw_load_slice);
 // the cells are then its 2 loads times 4 wavefronts, in token order as for
 // a whole chunk.
@@ -301,7 +329,7 @@ __device__ __forceinline__ int draw_in_chunk(const Args& a, DrawShared& sh, int 
                                              float invS, float lam,
                                              const u32x4 (&raw_in)[SLICE ? kSliceLoads : kLoads],
                                              During during = During{}, const Q& q = Q{}) {
-  static_assert(!SLICE || (VP && !RESIDUAL), "slices: vector path, draws from p");
+  static_assert(!SLICE || VP, "quarters: vector path");
   constexpr int NL = SLICE ? kSliceLoads : kLoads;
   constexpr unsigned kNegInfWord = DT == SS_DTYPE_F32 ? 0xff800000u : 0xff80ff80u;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;

@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
 
 template <int DT, bool VP>
 __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
-  __shared__ float red[kWaves];
+  __shared__ f32x4 red[kWaves];
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int nc = a.nchunks;
   const int b = blockIdx.x / nc;
@@ -479,22 +479,31 @@ __global__ __launch_bounds__(kThreads) void verify_residual_sums(Args a) {
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (VP) chunk_tail_neginf<DT>(cstart, a.V, tid, raw);
   q_tail_zero<DT, VP>(cstart, a.V, tid, qc);
-  float s = 0.0f;
+  // Summed per quarter of the chunk (loads 2q, 2q + 1), so that the draw
+  // can re-read one quarter; the chunk's sum is (s0 + s1) + (s2 + s3).
+  float sq[4];
 #pragma unroll
-  for (int it = 0; it < kLoads; ++it)
+  for (int q = 0; q < 4; ++q) {
+    float s = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kVec<DT>; ++k) {
-      const float v = elem<DT>(raw[it], k);
-      const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
-      s += fmaxf(0.0f, wv * invS - qc.at(it, k));
-    }
-  s = wave_sum(s);
-  if (l == 0) red[w] = s;
+    for (int it = 2 * q; it < 2 * q + 2; ++it)
+#pragma unroll
+      for (int k = 0; k < kVec<DT>; ++k) {
+        const float v = elem<DT>(raw[it], k);
+        const float wv = (v >= lam) ? fast_exp2((v - m) * kk) : 0.0f;
+        s += fmaxf(0.0f, wv * invS - qc.at(it, k));
+      }
+    sq[q] = s;
+  }
+  wave_inclusive_sum_n(sq);
+  if (l == kWave - 1) red[w] = f32x4{sq[0], sq[1], sq[2], sq[3]};
   __syncthreads();
   if (tid == 0) {
-    float t = 0.0f;
-    for (int i = 0; i < kWaves; ++i) t += red[i];
-    a.rpart[(int64_t)b * nc + c] = t;
+    f32x4 t = red[0];
+    for (int i = 1; i < kWaves; ++i) t = f32x4{t.x + red[i].x, t.y + red[i].y,
+                                               t.z + red[i].z, t.w + red[i].w};
+    a.rpart[(int64_t)b * nc + c] = (t.x + t.y) + (t.z + t.w);
+    a.rqpart[(int64_t)b * nc + c] = t;
   }
 }
 
@@ -518,7 +527,19 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
   if (w == 0) {
     const float u = a.uniforms[(int64_t)b * R + a.K];
     const float* rp = a.rpart + (int64_t)b * nc;
-    ChunkPick pk = pick_chunk(nc, u, [&](int c) { return load_f32(rp + c); });
+    ChunkPick pk;
+    if constexpr (VP) {
+      // The quarter sums: the chunk, then its quarter (as the finalize picks).
+      const f32x4* rq = a.rqpart + (int64_t)b * nc;
+      auto quarters = [&](int c) {
+        const f32x4 t = rq[c];
+        return QuarterW{t.x, t.y, t.z, t.w};
+      };
+      pk = pick_chunk(nc, u, [&](int c) { return quarters(c).chunk(); });
+      if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk));
+    } else {
+      pk = pick_chunk(nc, u, [&](int c) { return load_f32(rp + c); });
+    }
     // max(0, p - q) vanishes everywhere only when p == q: then draw from p.
     const bool fallback = pk.chunk < 0;
     if (fallback) {
@@ -542,6 +563,20 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
     draw_load<DT, VP>(a, b, r, pick_sh, raw);
     tok = draw_in_chunk<DT, VP, false>(a, dsh, b, r, pick_sh, OneToken{-1}, m, kk, 0.0f,
                                        lam, raw);
+  } else if constexpr (VP) {
+    // One quarter of the chosen chunk: its q, then its logits, all requested
+    // before either is used.
+    QChunk<DT, kSliceLoads> qc;
+    u32x4 rs[kSliceLoads];
+    if (pick_sh.chunk >= 0) {
+      const int cstart = pick_sh.chunk * kChunk<DT>;
+      load_q_slice<DT>(a.q + ((int64_t)b * a.K + r) * a.V, cstart, a.V, pick_sh.slice, qc);
+      draw_load_slice<DT>(a, b, r, pick_sh, rs);
+      __builtin_amdgcn_sched_barrier(0);
+      q_slice_tail_zero<DT>(cstart, a.V, pick_sh.slice, qc);
+    }
+    tok = draw_in_chunk<DT, VP, true, OneToken, NoDuring, QChunk<DT, kSliceLoads>, true>(
+        a, dsh, b, r, pick_sh, OneToken{-1}, m, kk, 1.0f / S, lam, rs, NoDuring{}, qc);
   } else {
     // (q first, as in the residual sums)
     QChunk<DT> qc;
@@ -572,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
 // Workspace layout (bytes, each region 256-byte aligned).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t partials, wparts, seqinfo, seqinfo2, rpart;
+  size_t partials, wparts, seqinfo, seqinfo2, rpart, rqpart;
   // truncation (top-k / top-p) regions; zero-sized without it
   size_t hist, hhdr, cand, tpart, tinfo;
   size_t total;
@@ -599,6 +634,7 @@ WsLayout ws_layout(int B, int K, int V, bool trunc) {
   take(L.seqinfo, (size_t)B * sizeof(i32x4));
   take(L.seqinfo2, (size_t)B * sizeof(f32x4));
   take(L.rpart, (size_t)B * nc * sizeof(float));
+  take(L.rqpart, (size_t)B * nc * sizeof(f32x4));
   const size_t t = trunc ? 1 : 0;
   take(L.hist, t * rows * nc * kHistBins * sizeof(unsigned long long));
   take(L.hhdr, t * rows * nc * sizeof(i32x4));
@@ -716,6 +752,7 @@ int run(int passes, const void* logits, int dtype, int B, int K, int V,
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
   a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
+  a.rqpart = reinterpret_cast<f32x4*>(ws + L.rqpart);
   a.hist = trunc ? reinterpret_cast<unsigned long long*>(ws + L.hist) : nullptr;
   a.hhdr = trunc ? reinterpret_cast<i32x4*>(ws + L.hhdr) : nullptr;
   a.cand = trunc ? reinterpret_cast<float*>(ws + L.cand) : nullptr;

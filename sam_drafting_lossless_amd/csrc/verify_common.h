@@ -214,6 +214,7 @@ struct Args {
                     //   sums per quarter (loads 2q, 2q+1), relative to its max
   i32x4* seqinfo;   // [B]: (rejected row + 1 or 0, m, S, log2e/T)
   float* rpart;     // [B*nchunks] residual chunk sums
+  f32x4* rqpart;    // [B*nchunks] residual sums per quarter of the chunk
   f32x4* seqinfo2;  // [B]: (truncation threshold, untruncated S, 0, 0)
   // Truncation workspace (NULL unless top_k or top_p is given), per row
   // (b*(K+1) + j) and per (row, chunk):
