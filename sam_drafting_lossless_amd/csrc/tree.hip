@@ -20,7 +20,9 @@
 // children of the current node are a ballot of parent == node, their running
 // sum is one wavefront prefix sum in node order, the accepted child the first
 // lane of a ballot. The final draw picks its chunk from the partials minus
-// the children's weight per chunk and re-reads only that chunk.
+// the children's weight per chunk and re-reads only that chunk (one quarter
+// of it on the vector path: the stream pass's quarter sums, minus the
+// children's terms in their quarters).
 #include "draw.h"
 
 namespace specsam {
@@ -45,6 +47,7 @@ constexpr int kTreePer = kTreeCache / kThreads;  // partials a thread requests
 
 struct TreeShared {
   f32x4 pc[kTreeCache];
+  f32x4 wc[kTreeCache];  // the chunks' quarter sums (SL)
   int tok[kWave];
   int par[kWave];
   float u[kWave];
@@ -62,9 +65,13 @@ struct TreeShared {
   DrawShared draw;
 };
 
-template <int DT, bool VP>
+// SL: the final draw re-reads one quarter of its chunk (vector path, the
+// partials and quarter sums of all N rows cached; the launch guarantees
+// both).
+template <int DT, bool VP, bool SL>
 __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
     Args a, const int32_t* tokens, const int32_t* parent, int32_t* out_nodes) {
+  constexpr bool slices = VP && SL;
   __shared__ TreeShared sh;
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int b = blockIdx.x;
@@ -78,10 +85,13 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
   // read but not used.
   const bool cached = N * nc <= kTreeCache;  // uniform
   const f32x4* P0 = a.partials + row0 * nc;
-  f32x4 pv[kTreePer];
+  f32x4 pv[kTreePer], wv[kTreePer];
   if (cached) {
 #pragma unroll
-    for (int i = 0; i < kTreePer; ++i) pv[i] = P0[min(tid + i * kThreads, N * nc - 1)];
+    for (int i = 0; i < kTreePer; ++i) {
+      pv[i] = P0[min(tid + i * kThreads, N * nc - 1)];
+      if constexpr (slices) wv[i] = a.wparts[row0 * nc + min(tid + i * kThreads, N * nc - 1)];
+    }
   }
   int tk = 0, pr = -1;
   float uu = 0.0f;
@@ -96,7 +106,10 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
   if (cached) {
 #pragma unroll
     for (int i = 0; i < kTreePer; ++i)
-      if (tid + i * kThreads < N * nc) sh.pc[tid + i * kThreads] = pv[i];
+      if (tid + i * kThreads < N * nc) {
+        sh.pc[tid + i * kThreads] = pv[i];
+        if constexpr (slices) sh.wc[tid + i * kThreads] = wv[i];
+      }
   }
   if (st0) {
     if (tid == 0) atomicOr(&a.status[b], st0);
@@ -222,7 +235,11 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
       if (child) {
         const int k = __popcll(cm & ((1ull << l) - 1));
         sh.excl[k] = mytok;
-        sh.exw[k] = greedy ? 0.0f : fast_exp2((mylx - sh.m[cur]) * kk);
+        // (with quarters: the token's term in its chunk's own frame, as the
+        // stream pass formed it)
+        const float ref =
+            slices ? sh.pc[cur * nc + mytok / kChunk<DT>].x : sh.m[cur];
+        sh.exw[k] = greedy ? 0.0f : fast_exp2((mylx - ref) * kk);
       }
       if (l == 0) {
         sh.cur = cur;
@@ -239,6 +256,60 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
   int tok;
   if (greedy) {
     tok = sh.idx[cur];
+  } else if constexpr (slices) {
+    if (w == 0) {
+      // Quarter weights of chunk c in row cur, the children's terms taken
+      // out of their quarters in node order. A quarter that only the removed
+      // tokens filled is left with a rounding residue of either sign when
+      // several of them share it; a remainder within 2^-20 of what was
+      // removed counts as nothing (a coin that only such a sliver would
+      // separate is within 1e-6 of a breakpoint of the exact draw).
+      const float m = sh.m[cur], uK = sh.u[N - 1];
+      const int nx = sh.nexcl;
+      auto quarters = [&](int c, bool excl) {
+        const f32x4 qs = sh.wc[cur * nc + c];
+        const double sc = chunk_scale(sh.pc[cur * nc + c].x, m, kk);
+        double sq[4] = {qs.x, qs.y, qs.z, qs.w}, rm[4] = {0.0, 0.0, 0.0, 0.0};
+        if (excl) {
+          for (int k = 0; k < nx; ++k) {
+            const int t = sh.excl[k];
+            if (t / kChunk<DT> != c) continue;
+            const int q = (t - c * kChunk<DT>) / kVec<DT> / kThreads / 2;
+            const double x = sh.exw[k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i == q) {
+                sq[i] -= x;
+                rm[i] += x;
+              }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sq[i] = (rm[i] > 0.0 && sq[i] <= rm[i] * 0x1p-20) ? 0.0 : fmax(0.0, sq[i]);
+        }
+        return QuarterW{sq[0] * sc, sq[1] * sc, sq[2] * sc, sq[3] * sc};
+      };
+      ChunkPick pk = pick_chunk(nc, uK, [&](int c) { return quarters(c, true).chunk(); });
+      int allx = 0;
+      if (pk.chunk >= 0) {
+        pick_slice(pk, quarters(pk.chunk, true));
+      } else {
+        // Rounding left nothing outside the children: draw from the row.
+        pk = pick_chunk(nc, uK, [&](int c) { return quarters(c, false).chunk(); });
+        if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk, false));
+        allx = 1;
+      }
+      if (l == 0) {
+        sh.pick = pk;
+        sh.all_excluded = allx;
+      }
+    }
+    __syncthreads();
+    u32x4 rs[kSliceLoads];
+    draw_load_slice<DT>(a, b, cur, sh.pick, rs);
+    tok = draw_in_chunk<DT, VP, false, TokenList, NoDuring, NoQ, true>(
+        a, sh.draw, b, cur, sh.pick, TokenList{sh.excl, sh.all_excluded ? 0 : sh.nexcl},
+        sh.m[cur], kk, 0.0f, kNegInf, rs);
   } else {
     if (w == 0 && l < sh.nexcl) atomicAdd(&sh.xsum[sh.excl[l] / kChunk<DT>], sh.exw[l]);
     __syncthreads();
@@ -287,8 +358,13 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
 template <int DT, bool VP>
 int launch_tree_t(const Args& a, const int32_t* tokens, const int32_t* parent,
                   int32_t* out_nodes, hipStream_t s) {
-  hipLaunchKernelGGL((spec_tree_finalize_kernel<DT, VP>), dim3((unsigned)a.B),
-                     dim3(kThreads), 0, s, a, tokens, parent, out_nodes);
+  const bool sl = VP && a.wparts != nullptr && (a.K + 1) * a.nchunks <= kTreeCache;
+  if (sl)
+    hipLaunchKernelGGL((spec_tree_finalize_kernel<DT, VP, true>), dim3((unsigned)a.B),
+                       dim3(kThreads), 0, s, a, tokens, parent, out_nodes);
+  else
+    hipLaunchKernelGGL((spec_tree_finalize_kernel<DT, VP, false>), dim3((unsigned)a.B),
+                       dim3(kThreads), 0, s, a, tokens, parent, out_nodes);
   return check_launch("spec_verify_tree");
 }
 

@@ -856,6 +856,7 @@ extern "C" int spec_verify_tree(const void* logits, int dtype, int B, int N, int
   a.nem = num_emitted;
   a.status = status;
   a.partials = reinterpret_cast<f32x4*>(ws + L.partials);
+  a.wparts = reinterpret_cast<f32x4*>(ws + L.wparts);
   a.seqinfo = reinterpret_cast<i32x4*>(ws + L.seqinfo);
   a.seqinfo2 = reinterpret_cast<f32x4*>(ws + L.seqinfo2);
   a.rpart = reinterpret_cast<float*>(ws + L.rpart);
