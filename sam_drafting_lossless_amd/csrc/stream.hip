@@ -36,11 +36,13 @@ namespace {
 // spills a few registers to scratch, and the reloads, each a memory round
 // trip, cost more than the extra wavefront gains (B = 256, V = 151936, no
 // drafts, top-p: 56.4 us at 5 against 63.0 at 6). The plain variant takes
-// none: the compiler then schedules it with 90
-// registers (5 waves per SIMD), against 61 (8 waves) under a hint of 6, and
-// that code streams faster once many rows are needed (B = 256, V = 151936,
-// K = 3, every draft full: 94.0 us against 97.5, equal with no drafts). The
-// element-wise path takes none either: it would spill under one.
+// none: the compiler then schedules it with 110 registers (4 waves per
+// SIMD; 90 before the next row's loads were moved into the row, which that
+// move more than repays), and such code streamed faster once many rows are
+// needed than the 61 registers (8 waves) a hint of 6 gives (B = 256,
+// V = 151936, K = 3, every draft full: 94.0 us against 97.5, equal with no
+// drafts). The element-wise path takes none either: it would spill under
+// one.
 template <int DT, bool TR>
 constexpr int kStreamWaves = (DT == SS_DTYPE_F32) ? 5 : 3;
 
@@ -87,12 +89,33 @@ spec_stream_kernel(Args a) {
   float T;
   const int st = seq_check(a, b, &d, &T);  // reported by finalize
   if (st) return;
-  for (int j = q; j <= d; j += G) {
-    if (j != 0)
-      load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
-                         cstart, a.V, tid, raw);
-    if (j != q) x = draft_token(a, b, j);
-    stream_row<DT, VP, TR, true>(a, b, j, d, T, c, x, raw, red, ts, NoMid{});
+  if constexpr (VP && !TR && DT == SS_DTYPE_F32) {
+    // The lane's next row is requested as soon as this one's registers are
+    // consumed, before its reductions and barriers: every row needed at
+    // B = 256, K = 3 (two rows per lane) 96.4 -> 94.1 us per launch, c3
+    // 28.4 -> 28.1 us. Only on the plain fp32 vector path: the other
+    // variants would hold more registers across it, or spill (bf16's c4
+    // launch, 32 x 5 rows: 6.78 -> 6.89 us).
+    for (int j = q; j <= d; j += G) {
+      if (j != 0 && j == q)
+        load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
+                           cstart, a.V, tid, raw);
+      if (j != q) x = draft_token(a, b, j);
+      auto next = [&]() {
+        if (j + G <= d)
+          load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j + G) * a.V * Dt<DT>::kBytes,
+                             cstart, a.V, tid, raw);
+      };
+      stream_row<DT, VP, TR, true>(a, b, j, d, T, c, x, raw, red, ts, next);
+    }
+  } else {
+    for (int j = q; j <= d; j += G) {
+      if (j != 0)
+        load_chunk<DT, VP>(a.logits + ((int64_t)b * R + j) * a.V * Dt<DT>::kBytes,
+                           cstart, a.V, tid, raw);
+      if (j != q) x = draft_token(a, b, j);
+      stream_row<DT, VP, TR, true>(a, b, j, d, T, c, x, raw, red, ts, NoMid{});
+    }
   }
 }
 
