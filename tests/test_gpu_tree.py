@@ -142,3 +142,52 @@ def test_tree_status_and_errors():
         ssl.spec_verify_tree(torch.zeros((1, 65, 8), device="cuda"),
                              *(dev(np.zeros((1, 65), np.int32)) for _ in range(2)),
                              dev(np.ones(1, np.int32)), dev(np.zeros(1, np.float32)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_coin_leaves_the_children_out(dtype):
+    """Every coin 1 (the top of its range): no child's running sum reaches it
+    (their probabilities sum below 1), so the final token is drawn at the
+    root with the children left out, and the top coin takes the last token of
+    positive weight among the rest. Rows: random logits in [-3, 0] up to a
+    per-row cut, -inf after it, one token before the cut at 3 (the row max);
+    three children past the cut at logit 2.5, two of them in one quarter of
+    one chunk and the third alone in a later chunk, so that nothing else
+    weighs anything in their quarters. Taken out of the quarter sums, they
+    must leave those quarters empty: a rounding residue would send the top
+    coin past every token the draw can take. The draw must give the token
+    just before the cut, as the oracle does."""
+    say(f"[gpu] tree: top coin {dtype}")
+    per_chunk = 8192 if dtype == "f32" else 16384
+    q = per_chunk // 4
+    V = 5 * per_chunk + 256
+    rng = np.random.default_rng(91 + (dtype == "bf16"))
+    B, N = 12, 4
+    x = np.full((B, N, V), -np.inf, np.float32)
+    tok = np.zeros((B, N), np.int32)
+    par = np.array([[-1, 0, 0, 0]] * B, np.int32)
+    want = np.zeros(B, np.int64)
+    for b in range(B):
+        cut = int(rng.integers(per_chunk // 2, 2 * per_chunk))
+        x[b, :, :cut] = rng.uniform(-3.0, 0.0, (N, cut)).astype(np.float32)
+        x[b, :, int(rng.integers(0, cut - 1))] = 3.0
+        c0 = cut // per_chunk + 1
+        qq = int(rng.integers(0, 4))
+        t1 = c0 * per_chunk + qq * q + int(rng.integers(0, q // 2))
+        t2 = t1 + 1 + int(rng.integers(0, q // 2 - 1))
+        t3 = (c0 + 2) * per_chunk + int(rng.integers(0, per_chunk))
+        tok[b, 1:] = [t1, t2, t3]
+        x[b, 0, [t1, t2, t3]] = 2.5
+        want[b] = cut - 1
+    n = np.full(B, N, np.int32)
+    T = np.ones(B, np.float32)
+    u = np.ones((B, N), np.float32)
+    t = torch.from_numpy(x).cuda()
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    g = _run(t, tok, par, n, T, u)
+    r = oracle.verify_tree(to_host_logits(t), tok, par, n, T, u, nthreads=8)
+    np.testing.assert_array_equal(r.out_tokens[:, 0], want)
+    np.testing.assert_array_equal(g[0], r.out_tokens)
+    np.testing.assert_array_equal(g[1], r.out_nodes)
+    np.testing.assert_array_equal(g[2], r.num_emitted)
