@@ -19,14 +19,17 @@ namespace {
 // partials, are scanned in chunk order and the first chunk whose running sum
 // exceeds u * total is taken, with the target left inside it; if rounding
 // leaves none, the last chunk with positive weight (its last positive token
-// is then drawn). draw_in_chunk (whole workgroup): that chunk is re-read with
-// the stream pass's layout, in which token order is (load, lane, element).
-// Each lane sums its 8 vectors; the 32 (load, wavefront) cell totals are
-// scanned in token order to find the cell, a wavefront scan inside the cell
-// finds the lane, and that lane scans its vector. The cell totals and the
-// lane scan come from the same inclusive scan, so the search is consistent;
-// a target beyond the chunk's re-read total (a rounding difference with the
-// partials) takes the chunk's last positive weight.
+// is then drawn). On the vector path the chunk weights are the sums of the
+// stream pass's quarter sums, and pick_slice then takes the quarter (a
+// contiguous quarter of the chunk's tokens) the same way. draw_in_chunk
+// (whole workgroup): that chunk, or quarter, is re-read with the stream
+// pass's layout, in which token order is (load, lane, element). Each lane
+// sums its vectors; the (load, wavefront) cell totals (32 for a chunk, 8 for
+// a quarter) are scanned in token order to find the cell, a wavefront scan
+// inside the cell finds the lane, and that lane scans its vector. The cell
+// totals and the lane scan come from the same inclusive scan arithmetic, so
+// the search is consistent; a target beyond the re-read total (a rounding
+// difference with the partials) takes the last positive weight re-read.
 //
 // Every weight is a float32 term, but the running sum over chunks, the
 // target u * total and a chunk's rescale to the row max are taken in double:

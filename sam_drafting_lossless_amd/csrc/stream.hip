@@ -4,9 +4,10 @@
 // Method ([P2] m.nxbn.cn guide §2.2; [P3] gogongxt notes "贪婪采样",
 // "拒绝采样"): row j of sequence b is needed iff j <= draft_len[b] (rows past
 // the drafts are never read). At T = 0 a partial is (max, lowest index of the
-// max, NaN flag); at T > 0 it is the online (max m, sum of exp2((l - m) *
-// log2e / T)) plus the logit of the draft token x_j when x_j falls in the
-// chunk. The finish pass combines them. When the request truncates its
+// max, NaN flag); at T > 0 it is (max m, sum of exp2((l - m) * log2e / T))
+// plus the logit of the draft token x_j when x_j falls in the chunk, and the
+// sum is also left per quarter of the chunk (the draws re-read one quarter).
+// The finish pass combines them. When the request truncates its
 // target (top-k / top-p), each chunk of a row at T > 0 also leaves a window
 // histogram of its logits and copies the logits of a band of its bins (the
 // ones that probably hold the row's threshold) to its candidate segment, for

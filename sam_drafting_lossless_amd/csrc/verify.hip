@@ -15,13 +15,14 @@
 //   finalize  one workgroup per sequence: combines the chunk partials of each
 //             row, judges the drafts with one wavefront (lane j judges draft
 //             j; a ballot finds the first rejection), writes the outputs and,
-//             for one-hot drafts or the bonus, draws the token (the chunk is
-//             picked from the rescaled partials and only that chunk is
-//             re-read). In the fused step it then extends the sequence's
+//             for one-hot drafts or the bonus, draws the token (the chunk,
+//             then one quarter of it, is picked from the rescaled quarter
+//             sums and only that quarter is re-read; the whole chunk under
+//             truncation). In the fused step it then extends the sequence's
 //             automaton with the emitted tokens and writes the next draft.
 //   residual  only when q is given: chunk sums of max(0, p - q) over the
-//             rejected row (sequence x chunk), then one workgroup per
-//             sequence draws from them.
+//             rejected row, per quarter (sequence x chunk), then one
+//             workgroup per sequence draws from them, re-reading a quarter.
 // A design that let the last workgroup of each sequence finalize inside the
 // stream kernel (agent-scope atomic hand-off) was measured slower: the
 // finalize code raises the stream kernel's register count and its latency
