@@ -145,6 +145,27 @@ __device__ __forceinline__ ChunkPick pick_chunk(int nc, float u, WeightFn weight
   return r;
 }
 
+// pick_chunk over chunks given by their quarters, then pick_slice in the
+// chosen chunk. Each lane forms the quarters of its own chunk among the first
+// 64 once (a lane past nc forms the last chunk's, which the pick ignores);
+// the chosen chunk's quarters then come from its lane instead of being
+// formed (or fetched) again. The arithmetic is that of quarters(c) either
+// way, so the pick is the same.
+template <typename QuartersFn>
+__device__ __forceinline__ ChunkPick pick_chunk_slice(int nc, float u, QuartersFn quarters) {
+  const QuarterW mine = quarters(min(lane_id(), nc - 1));
+  ChunkPick pk = pick_chunk(
+      nc, u, [&](int c) { return c < kWave ? mine.chunk() : quarters(c).chunk(); });
+  if (pk.chunk >= kWave) {
+    pick_slice(pk, quarters(pk.chunk));
+  } else if (pk.chunk >= 0) {
+    const int ln = pk.chunk;
+    pick_slice(pk, QuarterW{readlane_d(mine.w0, ln), readlane_d(mine.w1, ln),
+                            readlane_d(mine.w2, ln), readlane_d(mine.w3, ln)});
+  }
+  return pk;
+}
+
 // draw_in_chunk's mark for a target past the chunk's re-read total.
 constexpr int kDrawPastEnd = INT_MIN;
 

@@ -289,14 +289,11 @@ __global__ __launch_bounds__(kThreads) void spec_tree_finalize_kernel(
         }
         return QuarterW{sq[0] * sc, sq[1] * sc, sq[2] * sc, sq[3] * sc};
       };
-      ChunkPick pk = pick_chunk(nc, uK, [&](int c) { return quarters(c, true).chunk(); });
+      ChunkPick pk = pick_chunk_slice(nc, uK, [&](int c) { return quarters(c, true); });
       int allx = 0;
-      if (pk.chunk >= 0) {
-        pick_slice(pk, quarters(pk.chunk, true));
-      } else {
+      if (pk.chunk < 0) {
         // Rounding left nothing outside the children: draw from the row.
-        pk = pick_chunk(nc, uK, [&](int c) { return quarters(c, false).chunk(); });
-        if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk, false));
+        pk = pick_chunk_slice(nc, uK, [&](int c) { return quarters(c, false); });
         allx = 1;
       }
       if (l == 0) {

@@ -237,8 +237,7 @@ __global__ __launch_bounds__(kThreads) void spec_finalize_kernel(Args a) {
             }
             return QuarterW{s0 * sc, s1 * sc, s2 * sc, s3 * sc};
           };
-          pk = pick_chunk(nc, uK, [&](int c) { return quarters(c).chunk(); });
-          if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk));
+          pk = pick_chunk_slice(nc, uK, quarters);
         } else {
           pk = pick_chunk(nc, uK, [&](int c) {
             double W;
@@ -536,8 +535,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_draw(Args a) {
         const f32x4 t = rq[c];
         return QuarterW{t.x, t.y, t.z, t.w};
       };
-      pk = pick_chunk(nc, u, [&](int c) { return quarters(c).chunk(); });
-      if (pk.chunk >= 0) pick_slice(pk, quarters(pk.chunk));
+      pk = pick_chunk_slice(nc, u, quarters);
     } else {
       pk = pick_chunk(nc, u, [&](int c) { return load_f32(rp + c); });
     }
