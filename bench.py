@@ -943,8 +943,8 @@ def main():
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:
             ncpu = os.cpu_count() or 1
-        # at most 16 threads: the share of a GPU machine's host cores a run
-        # may use
+        # at most 16 threads: the share of the host's cores that one GPU's
+        # process is given on an 8-GPU MI355X node
         cpu, cpu_detail = cpu_baseline(slot_h, gt_h, cfg, min(ncpu, 16),
                                        args.cpu_budget)
 

@@ -48,7 +48,7 @@ template <int DT, bool TR>
 constexpr int kStreamWaves = (DT == SS_DTYPE_F32) ? 5 : 3;
 
 // Row lanes G (see the file comment). Measured per launch at B = 256,
-// V = 151936, fp32, K = 3 (events around 8 back-to-back launches, one box):
+// V = 151936, fp32, K = 3 (events around 8 back-to-back launches, one MI355X):
 //   draft lengths        G = 2    G = 4    kernel replaced (*)
 //   all 0 (256 rows)     27.4     32.3     27.9 us
 //   c3-like (277 rows)   29.4     33.2     30.3
